@@ -1,0 +1,209 @@
+/*
+ * zs.h - one data-parallel rank's ZeRO-1/2 optimizer step on MI355X (gfx950).
+ *
+ * The operation (CS336 lecture 8 notes "Parallelism basics", section "Code
+ * example: ZeRO-1"; podcast summary of N. Tazi's "Training at thousands of
+ * GPUs", section "ZeRO optimizer"): reduce-scatter the gradients so that
+ * each rank holds the summed gradient of its own slice, update only that
+ * slice with AdamW on rank-local fp32 state, then all-gather the updated
+ * parameters.  Mixed precision follows the 16 bytes per parameter of the
+ * same notes ("Core concepts"): bf16 parameter, bf16 gradient, fp32 master
+ * weight and two fp32 Adam moments.  Gradients travel in buckets of
+ * bucket_cap_mb = 25 (podcast summary, section "Data parallelism";
+ * DDP-to-ZeRO blog, section 2.1).
+ *
+ * On one GPU the W ranks' gradient slices for this rank's shard are W
+ * resident bf16 arrays; the library performs the arithmetic of the
+ * reduce-scatter (sum in fp32 in rank order 0..W-1, then divide by W), the
+ * AdamW update and the bf16 copy in one pass, and places the bf16 result
+ * where the all-gather reads or writes it.
+ *
+ * Conventions for every call:
+ *  - Return 0 on success or a negative ZS_E* code; nothing aborts and no
+ *    exception crosses this interface.  zs_last_error() gives a text for the
+ *    last failure on the calling thread.
+ *  - Device pointers are HIP device memory on the current device, owned by
+ *    the caller.  The library never allocates device memory.
+ *  - Device calls are asynchronous on the given hipStream_t (passed as
+ *    void*, NULL = the null stream).  Faults surface at the caller's next
+ *    synchronisation.  Calls that touch the same arrays must be ordered by
+ *    the caller (same stream or events).
+ *  - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *  - NaN and Inf propagate element by element: no clipping, loss scaling or
+ *    step skipping (the pages describe none).
+ */
+#ifndef ZS_H
+#define ZS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZS_OK        0
+#define ZS_EINVAL  (-1)  /* null pointer, bad count, W < 1, rank >= W, t < 1 */
+#define ZS_EALIGN  (-2)  /* device pointer or stride not 16-byte aligned    */
+#define ZS_ERANGE  (-3)  /* id out of range, size overflow, short stride    */
+#define ZS_ENOMEM  (-4)  /* host allocation failed                          */
+#define ZS_EDEVICE (-5)  /* HIP launch error                                */
+
+/* Opaque host-side layout of one rank.  Created by zs_layout_build, released
+ * by zs_layout_free; read-only afterwards, so it may be shared by threads. */
+typedef struct zs_layout zs_layout;
+
+/* One bucket: flat window [flat_off, flat_off + numel) of the flat bf16
+ * buffer; rank r owns [flat_off + r*slice_numel, + slice_numel), which sits
+ * at [shard_off, shard_off + slice_numel) of the rank's shard. */
+typedef struct {
+    int64_t flat_off;
+    int64_t numel;
+    int64_t slice_numel;
+    int64_t shard_off;
+} zs_bucket;
+
+/* One chunk: a maximal run of the rank's shard inside one tensor.
+ * Elements [tensor_off, tensor_off + numel) of tensor tensor_id are shard
+ * elements [shard_off, shard_off + numel), all inside bucket bucket_id. */
+typedef struct {
+    int32_t tensor_id;
+    int32_t bucket_id;
+    int64_t tensor_off;
+    int64_t numel;
+    int64_t shard_off;
+} zs_chunk;
+
+/* AdamW hyper-parameters (DDP-to-ZeRO blog, section 3.3: the optimizer is
+ * AdamW).  Decoupled weight decay multiplies the master by (1 - lr*wd). */
+typedef struct {
+    float lr;
+    float beta1;
+    float beta2;
+    float eps;
+    float weight_decay;
+} zs_adamw;
+
+/* ---- layout (host only) ------------------------------------------------ */
+
+/* Build the layout of rank `rank` of `world` for a parameter list of
+ * n_tensors tensors with tensor_numel[k] >= 0 elements, in list order.
+ *
+ * Flattening (podcast summary, "ZeRO optimizer": FSDP1 flattens before it
+ * shards; DDP-to-ZeRO blog 3.3: contiguous_gradients): tensor k starts at
+ * the first multiple of align_bytes/2 elements at or after the end of
+ * tensor k-1.  Bucketing: a full bucket is the largest multiple of
+ * world*align_bytes/2 elements whose bf16 size is <= bucket_cap_bytes
+ * (25<<20 for bucket_cap_mb = 25); buckets are consecutive windows of the
+ * flat buffer and may cut through tensors; the last bucket is the rest,
+ * rounded up to world*align_bytes/2 with zero padding.  bucket_cap_bytes
+ * <= 0 means one bucket (the single reduce_scatter_tensor of the sketch).
+ * Ownership: rank r owns slice r of every bucket; its shard is those
+ * slices in bucket order.
+ *
+ * align_bytes: positive multiple of 16 (256 recommended).  n_tensors may be
+ * 0 (empty layout, every device call is then a no-op).
+ * Errors: ZS_EINVAL for null out/tensor_numel (when n_tensors > 0),
+ * n_tensors < 0, numel < 0, world < 1, rank outside [0, world),
+ * bad align_bytes, or 0 < bucket_cap_bytes < world*align_bytes;
+ * ZS_ERANGE on int64 overflow; ZS_ENOMEM. */
+int zs_layout_build(const int64_t* tensor_numel, int32_t n_tensors,
+                    int32_t world, int32_t rank, int64_t bucket_cap_bytes,
+                    int32_t align_bytes, zs_layout** out);
+
+/* Sizes: flat buffer elements (padding included), this rank's shard
+ * elements, bucket count, this rank's chunk count.  Null outputs skipped. */
+int zs_layout_info(const zs_layout* layout, int64_t* flat_numel,
+                   int64_t* shard_numel, int32_t* n_buckets,
+                   int32_t* n_chunks);
+
+/* Copy the bucket table / chunk table / tensor start offsets (flat element
+ * index of each tensor's first element) into caller memory holding `cap`
+ * entries.  Return the number of entries, or ZS_ERANGE if cap is short. */
+int zs_layout_buckets(const zs_layout* layout, zs_bucket* out, int32_t cap);
+int zs_layout_chunks(const zs_layout* layout, zs_chunk* out, int32_t cap);
+int zs_layout_tensor_offsets(const zs_layout* layout, int64_t* out,
+                             int32_t cap);
+
+/* world and rank the layout was built for. */
+int zs_layout_rank(const zs_layout* layout, int32_t* world, int32_t* rank);
+
+void zs_layout_free(zs_layout* layout);
+
+/* ---- device calls -------------------------------------------------------- */
+
+/* One optimizer step over the whole shard of `layout`'s rank.
+ *
+ * grads: bf16 [W][grad_stride]; element i of slice s (source rank s's
+ *   gradient at shard position i) is grads[s*grad_stride + i].
+ *   grad_stride >= shard_numel and a multiple of 8.
+ * master, m, v: fp32 [shard_numel], updated in place.
+ * param_shard: bf16 [shard_numel] output, or NULL.
+ * full_flat: bf16 [flat_numel] all-gather buffer, or NULL; when given, the
+ *   updated bf16 values are also written to this rank's positions
+ *   (bucket.flat_off + rank*slice_numel + j); no other element is touched.
+ *   At least one of param_shard and full_flat must be non-NULL.
+ * step: the 1-based AdamW step counter t (bias corrections 1 - beta^t).
+ *
+ * Per element, with one fp32 rounding per operation and no contraction:
+ *   g = (G0 + G1 + ... + G_{W-1}) / W
+ *   m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g)
+ *   master = master*(1-lr*wd) - (lr/(1-b1^t)) * (m / (sqrt(v)/sqrt(1-b2^t)
+ *            + eps))
+ *   param = bf16(master), round to nearest even
+ * where the constants are computed in double on the host and rounded to
+ * fp32 once.  Padding elements (all-zero inputs) stay exactly zero.
+ * All device pointers must be 16-byte aligned (ZS_EALIGN otherwise). */
+int zs_step(const zs_layout* layout, const uint16_t* grads,
+            int64_t grad_stride, float* master, float* m, float* v,
+            uint16_t* param_shard, uint16_t* full_flat, const zs_adamw* hp,
+            int64_t step, void* hip_stream);
+
+/* The same step over one bucket's part of the shard, for the ZeRO-2
+ * streaming mode in which buckets arrive one by one (podcast summary, "Data
+ * parallelism": a bucket's collective starts as soon as backward fills it;
+ * "ZeRO optimizer": ZeRO-2 drops the gradients it does not own once they are
+ * reduced).
+ *
+ * grads: bf16 [W][grad_stride] holding only bucket bucket_id's W slices
+ *   (a staging buffer); grad_stride >= slice_numel, multiple of 8.
+ * master, m, v, param_shard: the SHARD base pointers (the call offsets them
+ *   by the bucket's shard_off); full_flat: as in zs_step.
+ * Buckets may be processed in any order, on any stream; the result equals
+ * zs_step bit for bit once every bucket has been stepped once. */
+int zs_bucket_step(const zs_layout* layout, int32_t bucket_id,
+                   const uint16_t* grads, int64_t grad_stride, float* master,
+                   float* m, float* v, uint16_t* param_shard,
+                   uint16_t* full_flat, const zs_adamw* hp, int64_t step,
+                   void* hip_stream);
+
+/* Local part of the all-gather (CS336 notes, "Code example: ZeRO-1": the
+ * all-gather concatenates the updated slices in rank order; "Code example:
+ * FSDP": per-layer weights are views of the gathered parameters).
+ *
+ * param_shard: bf16 [shard_numel] input.
+ * full_flat: bf16 [flat_numel] or NULL: this rank's slice of every bucket
+ *   is written at bucket.flat_off + rank*slice_numel.
+ * dev_chunks / n_chunks / dev_tensor_ptrs, all or none: a DEVICE copy of
+ *   the layout's chunk table (n_chunks entries, as zs_layout_chunks writes
+ *   it) and a DEVICE array of per-tensor bf16 base pointers indexed by
+ *   tensor_id; every chunk's elements are written to its tensor.  Tensor
+ *   pointers need only 2-byte alignment (16-byte aligned ones go faster).
+ * At least one destination must be given. */
+int zs_pack(const zs_layout* layout, const uint16_t* param_shard,
+            uint16_t* full_flat, const zs_chunk* dev_chunks,
+            int32_t n_chunks, uint16_t* const* dev_tensor_ptrs,
+            void* hip_stream);
+
+/* ---- errors --------------------------------------------------------------- */
+
+/* Static text of a ZS_E* code. */
+const char* zs_strerror(int code);
+
+/* Text describing the last failure on the calling thread ("" if none). */
+const char* zs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZS_H */

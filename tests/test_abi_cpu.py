@@ -1,0 +1,169 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol that
+include/zs.h declares, its layout tables equal the layout oracle's bit for
+bit, and its argument checks return the documented codes before any device
+work."""
+
+import ctypes
+import os
+import random
+import re
+
+import pytest
+
+import zero_sharded_optimizer_shard_amd as zs
+from oracle.layout import LayoutError, build_layout
+from synth import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "zs.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zs_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) == 12
+    L = zs.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(zs.EXPORTS) == names
+
+
+def tables(lay_c, n_tensors):
+    f, s, nb, nc = zs.zs_layout_info(lay_c)
+    b = [(x.flat_off, x.numel, x.slice_numel, x.shard_off)
+         for x in zs.zs_layout_buckets(lay_c)]
+    c = [(x.tensor_id, x.bucket_id, x.tensor_off, x.numel, x.shard_off)
+         for x in zs.zs_layout_chunks(lay_c)]
+    t = zs.zs_layout_tensor_offsets(lay_c, n_tensors)
+    return f, s, b, c, t
+
+
+def oracle_tables(lay):
+    b = [(x.flat_off, x.numel, x.slice_numel, x.shard_off)
+         for x in lay.buckets]
+    c = [(x.tensor_id, x.bucket_id, x.tensor_off, x.numel, x.shard_off)
+         for x in lay.chunks]
+    return lay.flat_numel, lay.shard_numel, b, c, lay.tensor_flat_off
+
+
+def same(numels, world, rank, cap, align):
+    try:
+        o = build_layout(numels, world, rank, cap, align)
+    except LayoutError:
+        with pytest.raises(zs.ZsError) as ei:
+            zs.zs_layout_build(numels, world, rank, cap, align)
+        assert ei.value.code == -1
+        return
+    lay = zs.zs_layout_build(numels, world, rank, cap, align)
+    assert tables(lay, len(numels)) == oracle_tables(o)
+    assert zs.zs_layout_rank(lay) == (world, rank)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_layout_matches_oracle_random(seed):
+    rng = random.Random(1000 + seed)
+    numels = [rng.choice([0, 1, 2, 7, 8, 9, 127, 128, 129, 255, 1000, 4095,
+                          50257, 70000]) for _ in range(rng.randint(0, 12))]
+    world = rng.choice([1, 2, 3, 5, 7, 8, 16, 64])
+    align = rng.choice([16, 48, 256, 4096])
+    cap = rng.choice([0, -5, 1, 4096, 10000, 1 << 16, 25 << 20])
+    for rank in sorted({0, world - 1, rng.randrange(world)}):
+        same(numels, world, rank, cap, align)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2", "llama8b", "dense7b",
+                                  "llama70b"])
+def test_layout_matches_oracle_workloads(name):
+    w = wl.presets()[name]
+    for rank in sorted({0, 1 % w.world, w.world - 1}):
+        same(w.numels, w.world, rank, 25 << 20, 256)
+
+
+def test_layout_errors():
+    L = zs.lib()
+    out = ctypes.c_void_p()
+    arr = (ctypes.c_int64 * 2)(10, 20)
+    assert L.zs_layout_build(arr, 2, 4, 1, 25 << 20, 256, None) == -1
+    assert L.zs_layout_build(None, 2, 4, 1, 25 << 20, 256,
+                             ctypes.byref(out)) == -1
+    assert L.zs_layout_build(arr, -1, 4, 1, 25 << 20, 256,
+                             ctypes.byref(out)) == -1
+    assert L.zs_layout_build(arr, 2, 0, 0, 25 << 20, 256,
+                             ctypes.byref(out)) == -1
+    assert L.zs_layout_build(arr, 2, 4, 4, 25 << 20, 256,
+                             ctypes.byref(out)) == -1
+    assert L.zs_layout_build(arr, 2, 4, 1, 25 << 20, 100,
+                             ctypes.byref(out)) == -1
+    big = (ctypes.c_int64 * 2)(2 ** 62, 2 ** 62)
+    assert L.zs_layout_build(big, 2, 4, 1, 25 << 20, 256,
+                             ctypes.byref(out)) == -3
+    assert b"overflow" in L.zs_last_error()
+    neg = (ctypes.c_int64 * 2)(10, -1)
+    assert L.zs_layout_build(neg, 2, 4, 1, 25 << 20, 256,
+                             ctypes.byref(out)) == -1
+    # short output capacity
+    lay = zs.zs_layout_build([10, 20, 30000000], 4, 0)
+    nb = zs.zs_layout_info(lay)[2]
+    buf = (zs.zs_bucket * nb)()
+    assert L.zs_layout_buckets(lay.handle, buf, nb - 1) == -3
+    assert L.zs_layout_buckets(lay.handle, buf, nb) == nb
+    assert zs.zs_strerror(-2).startswith("pointer")
+
+
+def test_step_argument_checks_need_no_device():
+    """Every check below fails before any HIP call, so it runs on the CPU."""
+    L = zs.lib()
+    lay = zs.zs_layout_build(wl.tiny(), 4, 0)
+    hp = zs.zs_adamw(3e-4, 0.9, 0.95, 1e-8, 0.1)
+    A = 1 << 20                                  # fake, 16-byte aligned
+    shard = zs.zs_layout_info(lay)[1]
+    h = lay.handle
+    ok = dict(g=A, st=shard, ma=A, m=A, v=A, p=A, f=None, hp=ctypes.byref(hp),
+              t=1)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return L.zs_step(h if "h" not in kw else kw["h"], a["g"], a["st"],
+                         a["ma"], a["m"], a["v"], a["p"], a["f"], a["hp"],
+                         a["t"], None)
+
+    assert call(h=None) == -1
+    assert call(hp=None) == -1
+    assert call(t=0) == -1
+    assert call(g=None) == -1
+    assert call(v=None) == -1
+    assert call(p=None, f=None) == -1
+    assert call(g=A + 2) == -2
+    assert call(ma=A + 8) == -2
+    assert call(f=A + 4, p=None) == -2
+    assert call(st=shard + 4) == -2
+    assert call(st=shard - 8) == -3
+    assert call(st=(2 ** 62) // 8 * 8) == -3
+    # bucket step: id range, staging stride vs the bucket's slice
+    assert L.zs_bucket_step(h, 1, A, shard, A, A, A, A, None,
+                            ctypes.byref(hp), 1, None) == -3
+    assert L.zs_bucket_step(h, -1, A, shard, A, A, A, A, None,
+                            ctypes.byref(hp), 1, None) == -3
+    assert L.zs_bucket_step(h, 0, A, shard - 8, A, A, A, A, None,
+                            ctypes.byref(hp), 1, None) == -3
+    # pack
+    assert L.zs_pack(h, A, None, None, 0, None, None) == -1
+    assert L.zs_pack(h, None, A, None, 0, None, None) == -1
+    assert L.zs_pack(h, A, A + 2, None, 0, None, None) == -2
+    assert L.zs_pack(h, A, None, A, 1, None, None) == -1
+    assert L.zs_pack(h, A, None, A, 5, A, None) == -1       # wrong n_chunks
+
+
+def test_empty_layout_calls_are_noops():
+    L = zs.lib()
+    lay = zs.zs_layout_build([], 8, 3)
+    assert zs.zs_layout_info(lay) == (0, 0, 0, 0)
+    hp = zs.zs_adamw(3e-4, 0.9, 0.95, 1e-8, 0.1)
+    # no device pointers at all: nothing to do, success
+    assert L.zs_step(lay.handle, None, 0, None, None, None, None, None,
+                     ctypes.byref(hp), 1, None) == 0
+    assert L.zs_pack(lay.handle, None, 1 << 20, None, 0, None, None) == 0

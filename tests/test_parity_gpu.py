@@ -1,0 +1,404 @@
+"""Parity of the HIP path (through the C-ABI) with the CPU oracle.
+
+Every case runs the same seeded inputs through both sides and compares
+every element (small and GPT-2-sized shards) or sampled windows (the
+Llama-3-8B-shaped and 7B-shaped shards at full size, in the launch
+configuration the benchmark times).  The step is elementwise, so a window
+is checked independently of the rest of the shard.
+"""
+
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import zero_sharded_optimizer_shard_amd as zs
+from oracle import step as O
+from oracle.layout import build_layout
+from oracle.pack import pack_flat, pack_tensors
+from synth import state as S
+from synth import workloads as wl
+
+from parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+OHP = O.AdamW(**HP)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev_bf16(n):
+    return torch.empty(n, dtype=torch.bfloat16, device="cuda")
+
+
+def np16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def npf(t):
+    return t.cpu().numpy()
+
+
+class Case:
+    """One rank's step on the GPU and on the oracle, full arrays."""
+
+    def __init__(self, numels, W, rank, cap=25 << 20, align=256, sigma=1e-3,
+                 stride_pad=0, warm=None, seed=0):
+        self.lay_o = build_layout(numels, W, rank, cap, align)
+        self.lay = zs.zs_layout_build(numels, W, rank, cap, align)
+        self.W, self.rank, self.sigma, self.seed = W, rank, sigma, seed
+        n = self.n = self.lay_o.shard_numel
+        self.stride = n + stride_pad
+        self.pad = S.padding_runs(n, self.lay_o.chunks)
+        self.G = torch.empty((W, self.stride), dtype=torch.bfloat16,
+                             device="cuda")
+        self.G.view(torch.int16).fill_(0x7fc0)      # NaN beyond n: never read
+        self.master = torch.empty(n, dtype=torch.float32, device="cuda")
+        self.m = torch.empty_like(self.master)
+        self.v = torch.empty_like(self.master)
+        S.dev_state(self.master, self.m, self.v, 0.02, seed, self.pad, warm)
+        self.p = dev_bf16(n)
+        self.om, self.omm, self.ov = S.cpu_state(0, n, 0.02, seed, self.pad,
+                                                 warm)
+
+    def step(self, t, full_flat=None, check=True, exact=True):
+        S.dev_grads(self.G, self.W, self.n, t, self.sigma, self.seed,
+                    self.pad)
+        zs.zs_step(self.lay, self.G, self.stride, self.master, self.m,
+                   self.v, self.p, full_flat, step=t, **HP)
+        Gc = S.cpu_grads(self.W, 0, self.n, t, self.sigma, self.seed,
+                         self.pad)
+        p16 = O.step(Gc, self.om, self.omm, self.ov, OHP, t)
+        self.op = p16
+        if check:
+            torch.cuda.synchronize()
+            assert_parity(
+                dict(master=npf(self.master), m=npf(self.m), v=npf(self.v),
+                     p=np16(self.p)),
+                dict(master=self.om, m=self.omm, v=self.ov, p=p16),
+                f"W={self.W} rank={self.rank} t={t}", exact)
+
+
+def test_generator_device_matches_host():
+    n = 1 << 20
+    for base in (0, 12345, (1 << 33) + 7):
+        t = dev_bf16(n)
+        synth.dev_normal_bf16(t, 3, synth.TAG_GRAD, 2, 5, base, 1e-4)
+        c = synth.cpu_normal_bf16(n, 3, synth.TAG_GRAD, 2, 5, base, 1e-4)
+        assert np.array_equal(np16(t), c)
+        f = torch.empty(n, dtype=torch.float32, device="cuda")
+        synth.dev_normal_f32(f, 0, synth.TAG_V, 0, 0, base, 1e-8, absval=True)
+        c = synth.cpu_normal_f32(n, 0, synth.TAG_V, 0, 0, base, 1e-8, True)
+        assert np.array_equal(npf(f).view(np.uint32), c.view(np.uint32))
+
+
+def test_tiny_three_steps():
+    w = wl.presets()["tiny"]
+    say("case tiny W=4 rank 0")
+    c = Case(w.numels, w.world, w.rank, sigma=w.grad_sigma)
+    for t in range(1, w.steps + 1):
+        c.step(t)
+
+
+def test_gpt2_thirteen_steps_and_flat_output():
+    """GPT-2-small-shaped, W=8, rank 0: ten warm-up steps then three more,
+    compared after every step; the bf16 result also lands in the flat
+    all-gather buffer at this rank's positions and nowhere else."""
+    w = wl.presets()["gpt2"]
+    say("case gpt2 W=8 rank 0")
+    c = Case(w.numels, w.world, w.rank, sigma=w.grad_sigma)
+    F = c.lay_o.flat_numel
+    flat = dev_bf16(F)
+    synth.dev_bits16(flat, 9, synth.TAG_SENTINEL, 0, 0, 0)
+    sentinel = synth.cpu_bits16(F, 9, synth.TAG_SENTINEL, 0, 0, 0)
+    for t in range(1, w.warm_steps + w.steps + 1):
+        c.step(t, full_flat=flat)
+    torch.cuda.synchronize()
+    ref = sentinel.copy()
+    pack_flat(c.lay_o, c.op, ref)
+    assert np.array_equal(np16(flat), ref)
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 7, 8, 16, 32, 64])
+def test_every_world_size(W):
+    """Each compiled world size and the runtime-W kernel, several buckets, a
+    ragged last bucket, a staging stride longer than the shard, warm
+    moments."""
+    rng = random.Random(W)
+    numels = [rng.choice([7, 129, 1000, 4096, 33333, 65536])
+              for _ in range(9)]
+    cap = W * 256 * rng.choice([3, 17, 40])
+    for rank in sorted({0, W - 1}):
+        say(f"case W={W} rank={rank} cap={cap}")
+        c = Case(numels, W, rank, cap=cap, stride_pad=24,
+                 warm=(1e-4, 1e-8), seed=W)
+        for t in (1, 2, 3):
+            c.step(t)
+
+
+@pytest.mark.parametrize("W", [3, 8])
+def test_all_ranks_reassemble_to_the_unsharded_step(W):
+    """all-reduce = reduce-scatter + all-gather on the GPU: every rank steps
+    its own shard into one shared flat buffer; the flat buffer equals the
+    oracle's step on the whole mean gradient, bit for bit."""
+    numels = [5000, 7, 129, 70000, 300, 2047]
+    cap = W * 256 * 20
+    lay0 = build_layout(numels, W, 0, cap)
+    F = lay0.flat_numel
+    pad = np.ones(F, bool)
+    for s0, n in zip(lay0.tensor_flat_off, numels):
+        pad[s0:s0 + n] = False
+    # the full local gradient of every source rank and the full master
+    fullG = [np.zeros((W, F), np.uint16) for _ in range(2)]
+    for t in (1, 2):
+        for s in range(W):
+            fullG[t - 1][s] = synth.cpu_normal_bf16(F, 0, synth.TAG_GRAD, t,
+                                                    s, 0, 1e-3)
+        fullG[t - 1][:, pad] = 0
+    full_master = synth.cpu_normal_f32(F, 0, synth.TAG_MASTER, 0, 0, 0, 0.02)
+    full_master[pad] = 0
+    flat = dev_bf16(F)
+    flat.view(torch.int16).fill_(0x7fc0)
+    for r in range(W):
+        say(f"case all-ranks W={W} rank={r}")
+        lay_o = build_layout(numels, W, r, cap)
+        lay = zs.zs_layout_build(numels, W, r, cap)
+        idx = np.concatenate([np.arange(b.flat_off + r * b.slice_numel,
+                                        b.flat_off + (r + 1) * b.slice_numel)
+                              for b in lay_o.buckets])
+        n = idx.size
+        master = torch.from_numpy(full_master[idx].copy()).cuda()
+        m = torch.zeros(n, dtype=torch.float32, device="cuda")
+        v = torch.zeros_like(m)
+        for t in (1, 2):
+            G = torch.from_numpy(np.ascontiguousarray(
+                fullG[t - 1][:, idx]).view(np.int16)).cuda()
+            zs.zs_step(lay, G, n, master, m, v, None, flat, step=t, **HP)
+        torch.cuda.synchronize()
+    # oracle: the whole mean gradient, one unsharded update
+    om = full_master.copy()
+    omm = np.zeros(F, np.float32)
+    ov = np.zeros(F, np.float32)
+    for t in (1, 2):
+        acc = O.bf16_to_f32(fullG[t - 1][0]).copy()
+        for s in range(1, W):
+            acc = acc + O.bf16_to_f32(fullG[t - 1][s])
+        p16 = O.adamw(acc / np.float32(W), om, omm, ov, OHP, t)
+    assert np.array_equal(np16(flat), p16)
+
+
+def test_bucket_steps_in_any_order_equal_the_whole_step():
+    """ZeRO-2 streaming on a second stream: buckets arrive in reverse order
+    into a ring of S staging slots; the result equals zs_step bit for bit."""
+    w = wl.presets()["gpt2"]
+    lay_o = build_layout(w.numels, w.world, 0)
+    lay = zs.zs_layout_build(w.numels, w.world, 0)
+    n = lay_o.shard_numel
+    W = w.world
+    ref = Case(w.numels, W, 0, sigma=w.grad_sigma)
+    for t in (1, 2):
+        ref.step(t, check=False)
+    torch.cuda.synchronize()
+    want = [npf(ref.master), npf(ref.m), npf(ref.v), np16(ref.p)]
+    del ref
+    slice_max = max(b.slice_numel for b in lay_o.buckets)
+    for slots in (1, 2, 3):
+        say(f"case streaming slots={slots}")
+        master = torch.empty(n, dtype=torch.float32, device="cuda")
+        m = torch.empty_like(master)
+        v = torch.empty_like(master)
+        S.dev_state(master, m, v, 0.02)
+        p = dev_bf16(n)
+        full = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
+        staging = [torch.empty((W, slice_max), dtype=torch.bfloat16,
+                               device="cuda") for _ in range(slots)]
+        up = torch.cuda.Stream()
+        st = torch.cuda.Stream()
+        done = [None] * slots
+        order = list(range(len(lay_o.buckets)))[::-1]
+        for t in (1, 2):
+            S.dev_grads(full, W, n, t, w.grad_sigma)
+            torch.cuda.synchronize()
+            for k, b_id in enumerate(order):
+                b = lay_o.buckets[b_id]
+                slot = k % slots
+                with torch.cuda.stream(up):
+                    if done[slot] is not None:
+                        up.wait_event(done[slot])
+                    staging[slot][:, :b.slice_numel].copy_(
+                        full[:, b.shard_off:b.shard_off + b.slice_numel])
+                    landed = torch.cuda.Event()
+                    landed.record(up)
+                st.wait_event(landed)
+                zs.zs_bucket_step(lay, b_id, staging[slot], slice_max, master,
+                                  m, v, p, None, step=t, stream=st, **HP)
+                ev = torch.cuda.Event()
+                ev.record(st)
+                done[slot] = ev
+            torch.cuda.synchronize()
+        got = [npf(master), npf(m), npf(v), np16(p)]
+        for g_, w_ in zip(got, want):
+            assert np.array_equal(g_.view(np.uint8), w_.view(np.uint8))
+
+
+def test_pack_flat_and_per_tensor():
+    w = wl.presets()["gpt2"]
+    for rank in (0, 5, 7):
+        say(f"case pack rank={rank}")
+        lay_o = build_layout(w.numels, w.world, rank)
+        lay = zs.zs_layout_build(w.numels, w.world, rank)
+        n = lay_o.shard_numel
+        shard = dev_bf16(n)
+        synth.dev_bits16(shard, rank, synth.TAG_SENTINEL, 1, 0, 0)
+        host_shard = synth.cpu_bits16(n, rank, synth.TAG_SENTINEL, 1, 0, 0)
+        F = lay_o.flat_numel
+        flat = dev_bf16(F)
+        synth.dev_bits16(flat, 2, synth.TAG_SENTINEL, 2, 0, 0)
+        ref_flat = synth.cpu_bits16(F, 2, synth.TAG_SENTINEL, 2, 0, 0)
+        # per-tensor storage; odd element offsets make some pointers
+        # unaligned so both copy paths run
+        tensors = []
+        for k, numel in enumerate(w.numels):
+            off = 1 if k % 3 == 1 else 0
+            base = dev_bf16(numel + off)
+            base.view(torch.int16).fill_(k)
+            tensors.append(base[off:])
+        ptrs = torch.tensor([t.data_ptr() for t in tensors],
+                            dtype=torch.int64, device="cuda")
+        chunks = zs.zs_layout_chunks(lay)
+        raw = np.frombuffer(zs.chunks_bytes(chunks), np.uint8).copy()
+        dchunks = torch.from_numpy(raw).cuda()
+        zs.zs_pack(lay, shard, flat, dchunks, len(chunks), ptrs)
+        torch.cuda.synchronize()
+        pack_flat(lay_o, host_shard, ref_flat)
+        assert np.array_equal(np16(flat), ref_flat)
+        ref_t = [np.full(nm, k, np.uint16) for k, nm in enumerate(w.numels)]
+        pack_tensors(lay_o, host_shard, ref_t)
+        for t_, r_ in zip(tensors, ref_t):
+            assert np.array_equal(np16(t_), r_)
+
+
+def test_nan_is_local_and_padding_stays_zero():
+    numels = [1000, 3]          # rank 2 of 4: two tensors and two pads
+    lay_o = build_layout(numels, 4, 2, 0)
+    lay = zs.zs_layout_build(numels, 4, 2, 0)
+    n = lay_o.shard_numel
+    pad = S.padding_runs(n, lay_o.chunks)
+    assert pad
+    G = torch.zeros((4, n), dtype=torch.bfloat16, device="cuda")
+    S.dev_grads(G, 4, n, 1, 1e-3, pad=pad)
+    G.view(torch.int16)[2, 5] = 0x7fc0
+    master = torch.zeros(n, dtype=torch.float32, device="cuda")
+    m = torch.zeros_like(master)
+    v = torch.zeros_like(master)
+    S.dev_state(master, m, v, 0.02, pad=pad)
+    p = dev_bf16(n)
+    for t in (1, 2):
+        zs.zs_step(lay, G, n, master, m, v, p, None, step=t, **HP)
+    torch.cuda.synchronize()
+    mm = npf(master)
+    assert np.isnan(mm[5]) and np.isfinite(np.delete(mm, 5)).all()
+    for s0, e0 in pad:
+        assert not npf(master)[s0:e0].view(np.uint32).any()
+        assert not npf(m)[s0:e0].view(np.uint32).any()
+        assert not npf(v)[s0:e0].view(np.uint32).any()
+        assert not np16(p)[s0:e0].any()
+
+
+def sample_windows(lay_o, per_bucket=2048, n_random=16, span=1 << 16,
+                   seed=0):
+    """Shard windows: both ends of every bucket slice, both sides of every
+    chunk boundary, and random spans."""
+    n = lay_o.shard_numel
+    wins = []
+    for b in lay_o.buckets:
+        wins.append((b.shard_off, min(per_bucket, b.slice_numel)))
+        e = b.shard_off + b.slice_numel
+        wins.append((max(b.shard_off, e - per_bucket), min(per_bucket,
+                                                           b.slice_numel)))
+    for c in lay_o.chunks:
+        a = max(0, c.shard_off - 256) // 8 * 8
+        wins.append((a, min(512, n - a)))
+    rng = random.Random(seed)
+    for _ in range(n_random):
+        a = rng.randrange(0, max(1, n - span)) // 8 * 8
+        wins.append((a, min(span, n - a)))
+    return wins
+
+
+@pytest.mark.parametrize("name", ["llama8b", "dense7b"])
+def test_full_size_sampled(name):
+    """The full Llama-3-8B-shaped (W=8) and 7B-shaped (W=64) rank-0 shards,
+    in the launch configuration the benchmark times; sampled windows
+    against the oracle after each step, and the bf16 output both in the
+    shard and in the flat all-gather buffer."""
+    w = wl.presets()[name]
+    lay_o = build_layout(w.numels, w.world, 0)
+    lay = zs.zs_layout_build(w.numels, w.world, 0)
+    n, W = lay_o.shard_numel, w.world
+    say(f"case full-size {name}: W={W} shard={n}")
+    G = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
+    master = torch.empty(n, dtype=torch.float32, device="cuda")
+    m = torch.empty_like(master)
+    v = torch.empty_like(master)
+    S.dev_state(master, m, v, w.master_sigma)
+    flat = dev_bf16(lay_o.flat_numel)
+    flat.view(torch.int16).fill_(0x7fc0)
+    wins = sample_windows(lay_o)
+    ref = [S.cpu_state(a, k, w.master_sigma) for a, k in wins]
+    for t in (1, 2):
+        S.dev_grads(G, W, n, t, w.grad_sigma)
+        zs.zs_step(lay, G, n, master, m, v, None, flat, step=t, **HP)
+        torch.cuda.synchronize()
+        for (a, k), st in zip(wins, ref):
+            Gc = S.cpu_grads(W, a, k, t, w.grad_sigma)
+            p16 = O.step(Gc, *st, OHP, t)
+            fpos = []
+            for b in lay_o.buckets:   # flat position of each shard element
+                lo, hi = max(a, b.shard_off), min(a + k, b.shard_off
+                                                  + b.slice_numel)
+                if hi > lo:
+                    fpos.append((lo - a, hi - a, b.flat_off + (lo
+                                                               - b.shard_off)))
+            got_p = np.empty(k, np.uint16)
+            for s0, e0, f0 in fpos:
+                got_p[s0:e0] = np16(flat[f0:f0 + (e0 - s0)])
+            assert_parity(
+                dict(master=npf(master[a:a + k]), m=npf(m[a:a + k]),
+                     v=npf(v[a:a + k]), p=got_p),
+                dict(master=st[0], m=st[1], v=st[2], p=p16),
+                f"{name} t={t} window {a}+{k}")
+    # rank 0 writes nothing outside its slices
+    for b in lay_o.buckets[:3] + lay_o.buckets[-2:]:
+        other = np16(flat[b.flat_off + b.slice_numel:
+                          b.flat_off + b.slice_numel + 4096])
+        assert np.all(other == 0x7fc0)
+
+
+def test_two_runs_are_bit_identical():
+    w = wl.presets()["tiny"]
+    outs = []
+    for _ in range(2):
+        c = Case(w.numels, w.world, 1)
+        for t in (1, 2, 3):
+            c.step(t, check=False)
+        torch.cuda.synchronize()
+        outs.append(np.concatenate([npf(c.master).view(np.uint32),
+                                    npf(c.m).view(np.uint32),
+                                    npf(c.v).view(np.uint32)]))
+    assert np.array_equal(outs[0], outs[1])

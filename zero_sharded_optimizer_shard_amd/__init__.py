@@ -1,0 +1,17 @@
+"""One data-parallel rank's ZeRO-1/2 optimizer step on MI355X (gfx950).
+
+The HIP library libzs.so (C-ABI in include/zs.h) does all the work; this
+package is its ctypes binding, with the same names.
+"""
+
+from ._zs import (EXPORTS, LIB_PATH, Layout, ZsError, chunks_bytes, lib,
+                  zs_adamw, zs_bucket, zs_bucket_step, zs_chunk,
+                  zs_last_error, zs_layout_buckets, zs_layout_build,
+                  zs_layout_chunks, zs_layout_info, zs_layout_rank,
+                  zs_layout_tensor_offsets, zs_pack, zs_step, zs_strerror)
+
+__all__ = ["EXPORTS", "LIB_PATH", "Layout", "ZsError", "chunks_bytes", "lib",
+           "zs_adamw", "zs_bucket", "zs_bucket_step", "zs_chunk",
+           "zs_last_error", "zs_layout_buckets", "zs_layout_build",
+           "zs_layout_chunks", "zs_layout_info", "zs_layout_rank",
+           "zs_layout_tensor_offsets", "zs_pack", "zs_step", "zs_strerror"]

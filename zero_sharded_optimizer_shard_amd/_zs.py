@@ -1,0 +1,245 @@
+"""ctypes binding of libzs (include/zs.h).  Argument marshalling only: every
+step of the path runs in the HIP library; there is no fallback.  torch
+tensors are used only as device memory and torch streams only as
+hipStream_t handles.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libzs.so")
+
+ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ERANGE, ZS_ENOMEM, ZS_EDEVICE = \
+    0, -1, -2, -3, -4, -5
+
+
+class ZsError(RuntimeError):
+    def __init__(self, code: int, func: str, detail: str):
+        super().__init__(f"{func}: {detail} (code {code})")
+        self.code = code
+
+
+class zs_bucket(ctypes.Structure):
+    _fields_ = [("flat_off", ctypes.c_int64), ("numel", ctypes.c_int64),
+                ("slice_numel", ctypes.c_int64),
+                ("shard_off", ctypes.c_int64)]
+
+
+class zs_chunk(ctypes.Structure):
+    _fields_ = [("tensor_id", ctypes.c_int32), ("bucket_id", ctypes.c_int32),
+                ("tensor_off", ctypes.c_int64), ("numel", ctypes.c_int64),
+                ("shard_off", ctypes.c_int64)]
+
+
+class zs_adamw(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float),
+                ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+                ("weight_decay", ctypes.c_float)]
+
+
+_lib = None
+
+EXPORTS = ["zs_layout_build", "zs_layout_info", "zs_layout_buckets",
+           "zs_layout_chunks", "zs_layout_tensor_offsets", "zs_layout_rank",
+           "zs_layout_free", "zs_step", "zs_bucket_step", "zs_pack",
+           "zs_strerror", "zs_last_error"]
+
+
+def lib():
+    """Load libzs.so; raise loudly if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run "
+                          "__graft_entry__.build() (the HIP library is the "
+                          "only implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    P = ctypes.POINTER
+    L.zs_layout_build.argtypes = [P(i64), i32, i32, i32, i64, i32, P(p)]
+    L.zs_layout_info.argtypes = [p, P(i64), P(i64), P(i32), P(i32)]
+    L.zs_layout_buckets.argtypes = [p, P(zs_bucket), i32]
+    L.zs_layout_chunks.argtypes = [p, P(zs_chunk), i32]
+    L.zs_layout_tensor_offsets.argtypes = [p, P(i64), i32]
+    L.zs_layout_rank.argtypes = [p, P(i32), P(i32)]
+    L.zs_layout_free.argtypes = [p]
+    L.zs_layout_free.restype = None
+    L.zs_step.argtypes = [p, p, i64, p, p, p, p, p, P(zs_adamw), i64, p]
+    L.zs_bucket_step.argtypes = [p, i32, p, i64, p, p, p, p, p, P(zs_adamw),
+                                 i64, p]
+    L.zs_pack.argtypes = [p, p, p, p, i32, p, p]
+    L.zs_strerror.argtypes = [ctypes.c_int]
+    L.zs_strerror.restype = ctypes.c_char_p
+    L.zs_last_error.argtypes = []
+    L.zs_last_error.restype = ctypes.c_char_p
+    for name in ("zs_layout_build", "zs_layout_info", "zs_layout_buckets",
+                 "zs_layout_chunks", "zs_layout_tensor_offsets",
+                 "zs_layout_rank", "zs_step", "zs_bucket_step", "zs_pack"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc: int, func: str) -> int:
+    if rc < 0:
+        raise ZsError(rc, func, lib().zs_last_error().decode() or
+                      zs_strerror(rc))
+    return rc
+
+
+def zs_strerror(code: int) -> str:
+    return lib().zs_strerror(code).decode()
+
+
+def zs_last_error() -> str:
+    return lib().zs_last_error().decode()
+
+
+class Layout:
+    """Owning handle of a zs_layout*."""
+
+    def __init__(self, handle: int):
+        self._h = ctypes.c_void_p(handle)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None and self._h.value and _lib:
+            _lib.zs_layout_free(self._h)
+            self._h = None
+
+
+def zs_layout_build(tensor_numel: Sequence[int], world: int, rank: int,
+                    bucket_cap_bytes: int = 25 << 20,
+                    align_bytes: int = 256) -> Layout:
+    n = len(tensor_numel)
+    arr = (ctypes.c_int64 * max(n, 1))(*tensor_numel)
+    out = ctypes.c_void_p()
+    _check(lib().zs_layout_build(arr, n, world, rank, bucket_cap_bytes,
+                                 align_bytes, ctypes.byref(out)),
+           "zs_layout_build")
+    return Layout(out.value)
+
+
+def zs_layout_info(layout: Layout):
+    f, s = ctypes.c_int64(), ctypes.c_int64()
+    nb, nc = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().zs_layout_info(layout.handle, ctypes.byref(f),
+                                ctypes.byref(s), ctypes.byref(nb),
+                                ctypes.byref(nc)), "zs_layout_info")
+    return f.value, s.value, nb.value, nc.value
+
+
+def zs_layout_rank(layout: Layout):
+    w, r = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().zs_layout_rank(layout.handle, ctypes.byref(w),
+                                ctypes.byref(r)), "zs_layout_rank")
+    return w.value, r.value
+
+
+def zs_layout_buckets(layout: Layout) -> List[zs_bucket]:
+    nb = zs_layout_info(layout)[2]
+    out = (zs_bucket * max(nb, 1))()
+    n = _check(lib().zs_layout_buckets(layout.handle, out, nb),
+               "zs_layout_buckets")
+    return list(out[:n])
+
+
+def zs_layout_chunks(layout: Layout) -> List[zs_chunk]:
+    nc = zs_layout_info(layout)[3]
+    out = (zs_chunk * max(nc, 1))()
+    n = _check(lib().zs_layout_chunks(layout.handle, out, nc),
+               "zs_layout_chunks")
+    return list(out[:n])
+
+
+def zs_layout_tensor_offsets(layout: Layout, n_tensors: int) -> List[int]:
+    out = (ctypes.c_int64 * max(n_tensors, 1))()
+    n = _check(lib().zs_layout_tensor_offsets(layout.handle, out, n_tensors),
+               "zs_layout_tensor_offsets")
+    return list(out[:n])
+
+
+def chunks_bytes(chunks: List[zs_chunk]) -> bytes:
+    """The chunk table as raw bytes, for a device copy (zs_pack)."""
+    arr = (zs_chunk * len(chunks))(*chunks)
+    return bytes(arr)
+
+
+# ---- device calls ------------------------------------------------------------
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _bf16(t, name):
+    if t is not None and t.element_size() != 2:
+        raise TypeError(f"{name}: need a 2-byte (bf16 bits) tensor")
+    return _ptr(t)
+
+
+def _f32(t, name):
+    import torch
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name}: need float32")
+    return _ptr(t)
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _hp(lr, beta1, beta2, eps, weight_decay):
+    return zs_adamw(lr, beta1, beta2, eps, weight_decay)
+
+
+def zs_step(layout: Layout, grads, grad_stride: int, master, m, v,
+            param_shard=None, full_flat=None, *, lr: float, beta1: float,
+            beta2: float, eps: float, weight_decay: float, step: int,
+            stream=None) -> None:
+    hp = _hp(lr, beta1, beta2, eps, weight_decay)
+    _check(lib().zs_step(layout.handle, _bf16(grads, "grads"), grad_stride,
+                         _f32(master, "master"), _f32(m, "m"), _f32(v, "v"),
+                         _bf16(param_shard, "param_shard"),
+                         _bf16(full_flat, "full_flat"), ctypes.byref(hp),
+                         step, _stream(stream)), "zs_step")
+
+
+def zs_bucket_step(layout: Layout, bucket_id: int, grads, grad_stride: int,
+                   master, m, v, param_shard=None, full_flat=None, *,
+                   lr: float, beta1: float, beta2: float, eps: float,
+                   weight_decay: float, step: int, stream=None) -> None:
+    hp = _hp(lr, beta1, beta2, eps, weight_decay)
+    _check(lib().zs_bucket_step(layout.handle, bucket_id,
+                                _bf16(grads, "grads"), grad_stride,
+                                _f32(master, "master"), _f32(m, "m"),
+                                _f32(v, "v"),
+                                _bf16(param_shard, "param_shard"),
+                                _bf16(full_flat, "full_flat"),
+                                ctypes.byref(hp), step, _stream(stream)),
+           "zs_bucket_step")
+
+
+def zs_pack(layout: Layout, param_shard, full_flat=None, dev_chunks=None,
+            n_chunks: int = 0, dev_tensor_ptrs=None, stream=None) -> None:
+    """dev_chunks: device tensor holding chunks_bytes(); dev_tensor_ptrs:
+    device int64 tensor of per-tensor data pointers."""
+    _check(lib().zs_pack(layout.handle, _bf16(param_shard, "param_shard"),
+                         _bf16(full_flat, "full_flat"), _ptr(dev_chunks),
+                         n_chunks, _ptr(dev_tensor_ptrs), _stream(stream)),
+           "zs_pack")
