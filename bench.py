@@ -8,6 +8,13 @@ positions of the flat all-gather buffer (the local half of the
 all-gather).  All of it is one kernel launch of zs_step.  The layout is
 built once, before timing, as a training job builds it once.
 
+Operand layouts: the optimizer state lives in the library's tiled layout
+(per 8192-element tile, fp32 master | m | v), and the W gradient slices are
+tile-interleaved (per tile, the W source ranks' 8192 values one after
+another), the form a receive-side placement of the reduce-scatter's raw
+slices would give.  The same step on plain [W][n] slices is timed too and
+reported as "slices_layout".
+
 Default workload: the Llama-3-8B-shaped parameter list (291 tensors,
 8,030,261,248 parameters) in 25 MiB buckets, W = 8 simulated ranks, rank 0's
 shard of 1,003,782,656 parameters; gradients N(0, 1e-4) in bf16, master
@@ -81,22 +88,45 @@ def cpu_baseline(W, seconds: float):
                        f"{el:.1f} s")
 
 
-def ceiling(G, n, W, master, m, v, p, reps=10):
-    """Same access pattern as the step, no arithmetic: the achievable
-    bandwidth for this read/write mix on this device."""
+def ceiling(Gt, state, flat, lay, W, n, reps=10):
+    """The step's exact access pattern (tiled gradients and state, flat
+    output), no arithmetic: the achievable bandwidth for this read/write
+    mix on this device."""
     import torch
     import synth
+    import zero_sharded_optimizer_shard_amd as zs
     st = torch.cuda.current_stream()
+    buckets = zs.zs_layout_buckets(lay)
+    b0 = buckets[0]
+    args = (Gt, state, flat, W, b0.slice_numel, buckets[-1].slice_numel,
+            b0.numel, len(buckets), st)
     for _ in range(2):
-        synth.dev_mix_stream(G, n, W, master, m, v, p, n, stream=st)
+        synth.dev_mix_stream(*args)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(st)
     for _ in range(reps):
-        synth.dev_mix_stream(G, n, W, master, m, v, p, n, stream=st)
+        synth.dev_mix_stream(*args)
     ev[1].record(st)
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[1]) / reps
     return (2 * W + 26) * n / (ms * 1e-3) / 1e9, ms
+
+
+def time_steps(fn, K, st):
+    """K launches of fn, each between two events on stream st; returns the
+    per-launch kernel times (ms) and the wall time of the K launches."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [a.elapsed_time(b) for a, b in evs], wall
 
 
 def main():
@@ -121,6 +151,7 @@ def main():
         sys.exit(2)
 
     import torch
+    import synth
     import zero_sharded_optimizer_shard_amd as zs
     from synth import state as S
     from synth import workloads as wl
@@ -136,57 +167,70 @@ def main():
     log(f"workload {w.name}: W={W} shard={n} flat={flat_n} buckets={nb} "
         f"chunks={nc}")
 
+    n_tiles = zs.zs_layout_tiles(lay)
+    T = zs.ZS_TILE
     G = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
-    master = torch.empty(n, dtype=torch.float32, device="cuda")
-    m = torch.empty_like(master)
-    v = torch.empty_like(master)
+    Gt = torch.empty(n_tiles * W * T, dtype=torch.bfloat16, device="cuda")
+    state = torch.empty(n_tiles * 3 * T, dtype=torch.float32, device="cuda")
     flat = torch.zeros(flat_n, dtype=torch.bfloat16, device="cuda")
     S.dev_grads(G, W, n, 1, w.grad_sigma)
-    S.dev_state(master, m, v, w.master_sigma)
+    zs.zs_grads_tile(lay, -1, G, n, Gt)
+    master = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.dev_normal_f32(master, 0, synth.TAG_MASTER, 0, 0, 0,
+                         w.master_sigma)
+    zs.zs_state_pack(lay, master, None, None, state)
+    del master
     torch.cuda.synchronize()
-    log("inputs resident")
+    log(f"inputs resident ({n_tiles} tiles)")
 
     st = torch.cuda.current_stream()
     t = 0
 
-    def one_step():
+    def step_tiled():
         nonlocal t
         t += 1
-        zs.zs_step(lay, G, n, master, m, v, None, flat, step=t, stream=st,
-                   **HP)
+        zs.zs_step(lay, Gt, state, None, flat, grad_layout="tiled", step=t,
+                   stream=st, **HP)
+
+    def step_slices():
+        nonlocal t
+        t += 1
+        zs.zs_step(lay, G, state, None, flat, grad_layout="slices",
+                   grad_stride=n, step=t, stream=st, **HP)
 
     for _ in range(args.warmup):
-        one_step()
+        step_tiled()
     torch.cuda.synchronize()
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in evs:
-        a.record(st)
-        one_step()
-        b.record(st)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_ms, wall = time_steps(step_tiled, K, st)
     ms_per_step = wall * 1e3 / K
     avg_ms = sum(kern_ms) / K
     bpp = 2 * W + 26
     achieved = bpp * n / (avg_ms * 1e-3) / 1e9
-    log(f"zs_step: avg {avg_ms:.3f} ms  min {min(kern_ms):.3f} ms  "
+    log(f"zs_step (tiled): avg {avg_ms:.3f} ms  min {min(kern_ms):.3f} ms  "
         f"-> {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.1%} of 8 TB/s)")
 
     extra = {}
+    for _ in range(2):
+        step_slices()
+    sl_ms, _ = time_steps(step_slices, K, st)
+    sl_avg = sum(sl_ms) / K
+    sl_gbs = bpp * n / (sl_avg * 1e-3) / 1e9
+    extra["slices_layout"] = dict(kernel_ms_avg=sl_avg,
+                                  params_per_s=n / (sl_avg * 1e-3),
+                                  GBps=sl_gbs, frac=sl_gbs / PEAK_HBM_GBS)
+    log(f"zs_step (plain slices): avg {sl_avg:.3f} ms -> {sl_gbs:.0f} GB/s "
+        f"({sl_gbs / PEAK_HBM_GBS:.1%})")
     if args.unfused:
         p = torch.empty(n, dtype=torch.bfloat16, device="cuda")
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         for _ in range(2):
-            zs.zs_step(lay, G, n, master, m, v, p, None, step=t, stream=st,
-                       **HP)
+            zs.zs_step(lay, Gt, state, p, None, grad_layout="tiled", step=t,
+                       stream=st, **HP)
             zs.zs_pack(lay, p, flat, stream=st)
         e[0].record(st)
-        zs.zs_step(lay, G, n, master, m, v, p, None, step=t, stream=st, **HP)
+        zs.zs_step(lay, Gt, state, p, None, grad_layout="tiled", step=t,
+                   stream=st, **HP)
         e[1].record(st)
         zs.zs_pack(lay, p, flat, stream=st)
         e[2].record(st)
@@ -195,12 +239,10 @@ def main():
                                    pack=e[1].elapsed_time(e[2]))
         del p
     if args.ceiling:
-        p = torch.empty(n, dtype=torch.bfloat16, device="cuda")
-        gbs, cms = ceiling(G, n, W, master, m, v, p)
+        gbs, cms = ceiling(Gt, state, flat, lay, W, n)
         extra["same_mix_ceiling"] = dict(GBps=gbs, ms=cms,
                                          frac_of_peak=gbs / PEAK_HBM_GBS)
         log(f"same-mix ceiling: {gbs:.0f} GB/s ({cms:.3f} ms)")
-        del p
 
     traffic = traffic_record(args.workload)
     out = {
@@ -219,7 +261,9 @@ def main():
         "config": {"workload": f"{w.name} rank-0 shard, W={W}",
                    "params_total": sum(w.numels), "shard_params": n,
                    "buckets": nb, "bucket_cap_mb": 25,
-                   "bytes_per_param": bpp},
+                   "bytes_per_param": bpp,
+                   "grads_layout": "tiled [tile][W][8192]",
+                   "state_layout": "tiled [tile][master|m|v][8192]"},
         "roofline": {"bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
@@ -228,7 +272,7 @@ def main():
         "achieved_GBps_per_step": bpp * n / (ms_per_step * 1e-3) / 1e9,
         **extra,
     }
-    del G, master, m, v, flat
+    del G, Gt, state, flat
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")

@@ -54,12 +54,15 @@ typedef struct zs_layout zs_layout;
 
 /* One bucket: flat window [flat_off, flat_off + numel) of the flat bf16
  * buffer; rank r owns [flat_off + r*slice_numel, + slice_numel), which sits
- * at [shard_off, shard_off + slice_numel) of the rank's shard. */
+ * at [shard_off, shard_off + slice_numel) of the rank's shard.  In the tiled
+ * layouts below the slice occupies ceil(slice_numel / ZS_TILE) tiles from
+ * tile tile_off on. */
 typedef struct {
     int64_t flat_off;
     int64_t numel;
     int64_t slice_numel;
     int64_t shard_off;
+    int64_t tile_off;
 } zs_bucket;
 
 /* One chunk: a maximal run of the rank's shard inside one tensor.
@@ -116,6 +119,11 @@ int zs_layout_info(const zs_layout* layout, int64_t* flat_numel,
                    int64_t* shard_numel, int32_t* n_buckets,
                    int32_t* n_chunks);
 
+/* Number of tiles of this rank's shard: sum over buckets of
+ * ceil(slice_numel / ZS_TILE).  The tiled state holds n_tiles*3*ZS_TILE
+ * floats, tiled gradients n_tiles*W*ZS_TILE bf16 values. */
+int zs_layout_tiles(const zs_layout* layout, int64_t* n_tiles);
+
 /* Copy the bucket table / chunk table / tensor start offsets (flat element
  * index of each tensor's first element) into caller memory holding `cap`
  * entries.  Return the number of entries, or ZS_ERANGE if cap is short. */
@@ -129,14 +137,42 @@ int zs_layout_rank(const zs_layout* layout, int32_t* world, int32_t* rank);
 
 void zs_layout_free(zs_layout* layout);
 
+/* ---- HBM layouts of the step's operands --------------------------------- */
+
+/* A tile is ZS_TILE consecutive elements of one bucket's slice: slice
+ * element j of bucket b lies in tile b.tile_off + j / ZS_TILE at position
+ * j % ZS_TILE; a slice's last tile is padded when slice_numel is not a
+ * multiple of ZS_TILE.  One workgroup of the step owns one tile, and the
+ * tiled layouts keep everything that workgroup reads or writes in a few
+ * long contiguous runs, which is what keeps a read/write stream of this mix
+ * near the HBM peak on MI355X. */
+#define ZS_TILE 8192
+
+/* Optimizer state, tiled (the layout zs_step works on): fp32
+ * [n_tiles][3][ZS_TILE]; in tile i, row 0 holds the fp32 master weights,
+ * row 1 the first moment m, row 2 the second moment v (CS336 notes, "Core
+ * concepts": fp32 master plus two fp32 Adam moments per parameter; "Code
+ * example: ZeRO-1": this state lives only on the owning rank).  Padding
+ * positions of a tile are never read or written by the step.  Use
+ * zs_state_pack / zs_state_unpack to convert from / to three plain
+ * [shard_numel] arrays (set-up, checkpoints). */
+
+/* Gradient layouts: the W source ranks' bf16 slices of this rank's shard,
+ * i.e. what the reduce-scatter delivers before it reduces (CS336 notes,
+ * "Code example: ZeRO-1"). */
+#define ZS_GRADS_SLICES 0  /* [W][grad_stride]: element i of the shard from
+                              source rank s at s*grad_stride + i */
+#define ZS_GRADS_TILED  1  /* [n_tiles][W][ZS_TILE]: position j of tile i
+                              from source rank s at (i*W + s)*ZS_TILE + j */
+
 /* ---- device calls -------------------------------------------------------- */
 
 /* One optimizer step over the whole shard of `layout`'s rank.
  *
- * grads: bf16 [W][grad_stride]; element i of slice s (source rank s's
- *   gradient at shard position i) is grads[s*grad_stride + i].
- *   grad_stride >= shard_numel and a multiple of 8.
- * master, m, v: fp32 [shard_numel], updated in place.
+ * grads, grad_layout, grad_stride: the W gradient slices in one of the two
+ *   layouts above.  ZS_GRADS_SLICES: grad_stride >= shard_numel and a
+ *   multiple of 8.  ZS_GRADS_TILED: grad_stride is ignored.
+ * state: the tiled fp32 state [n_tiles][3][ZS_TILE], updated in place.
  * param_shard: bf16 [shard_numel] output, or NULL.
  * full_flat: bf16 [flat_numel] all-gather buffer, or NULL; when given, the
  *   updated bf16 values are also written to this rank's positions
@@ -145,16 +181,17 @@ void zs_layout_free(zs_layout* layout);
  * step: the 1-based AdamW step counter t (bias corrections 1 - beta^t).
  *
  * Per element, with one fp32 rounding per operation and no contraction:
- *   g = (G0 + G1 + ... + G_{W-1}) / W
+ *   g = (G0 + G1 + ... + G_{W-1}) / W          (sum in rank order)
  *   m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g)
  *   master = master*(1-lr*wd) - (lr/(1-b1^t)) * (m / (sqrt(v)/sqrt(1-b2^t)
  *            + eps))
  *   param = bf16(master), round to nearest even
  * where the constants are computed in double on the host and rounded to
- * fp32 once.  Padding elements (all-zero inputs) stay exactly zero.
- * All device pointers must be 16-byte aligned (ZS_EALIGN otherwise). */
+ * fp32 once.  Shard padding (all-zero inputs) stays exactly zero.
+ * All device pointers must be 16-byte aligned (ZS_EALIGN otherwise);
+ * ZS_EINVAL for an unknown grad_layout. */
 int zs_step(const zs_layout* layout, const uint16_t* grads,
-            int64_t grad_stride, float* master, float* m, float* v,
+            int32_t grad_layout, int64_t grad_stride, float* state,
             uint16_t* param_shard, uint16_t* full_flat, const zs_adamw* hp,
             int64_t step, void* hip_stream);
 
@@ -164,17 +201,40 @@ int zs_step(const zs_layout* layout, const uint16_t* grads,
  * "ZeRO optimizer": ZeRO-2 drops the gradients it does not own once they are
  * reduced).
  *
- * grads: bf16 [W][grad_stride] holding only bucket bucket_id's W slices
- *   (a staging buffer); grad_stride >= slice_numel, multiple of 8.
- * master, m, v, param_shard: the SHARD base pointers (the call offsets them
- *   by the bucket's shard_off); full_flat: as in zs_step.
+ * grads: bucket bucket_id's W slices only (a staging buffer):
+ *   ZS_GRADS_SLICES [W][grad_stride], grad_stride >= slice_numel and a
+ *   multiple of 8; ZS_GRADS_TILED [tiles_b][W][ZS_TILE] with
+ *   tiles_b = ceil(slice_numel / ZS_TILE).
+ * state, param_shard: the SHARD base pointers (the call finds the bucket's
+ *   tiles and elements itself); full_flat: as in zs_step.
  * Buckets may be processed in any order, on any stream; the result equals
  * zs_step bit for bit once every bucket has been stepped once. */
 int zs_bucket_step(const zs_layout* layout, int32_t bucket_id,
-                   const uint16_t* grads, int64_t grad_stride, float* master,
-                   float* m, float* v, uint16_t* param_shard,
+                   const uint16_t* grads, int32_t grad_layout,
+                   int64_t grad_stride, float* state, uint16_t* param_shard,
                    uint16_t* full_flat, const zs_adamw* hp, int64_t step,
                    void* hip_stream);
+
+/* Plain [shard_numel] fp32 master / m / v -> tiled state [n_tiles][3]
+ * [ZS_TILE].  m or v may be NULL: that row is set to zero (a fresh
+ * optimizer).  Padding positions of the tiles are set to zero.  master must
+ * not be NULL. */
+int zs_state_pack(const zs_layout* layout, const float* master,
+                  const float* m, const float* v, float* state,
+                  void* hip_stream);
+
+/* Tiled state -> plain [shard_numel] arrays; NULL outputs are skipped. */
+int zs_state_unpack(const zs_layout* layout, const float* state,
+                    float* master, float* m, float* v, void* hip_stream);
+
+/* Gradient slices [W][stride] -> tiled [tiles][W][ZS_TILE]; padding
+ * positions of the tiles are set to zero.  bucket_id < 0: the whole shard
+ * (stride >= shard_numel, output n_tiles tiles); otherwise bucket
+ * bucket_id's slices (stride >= its slice_numel, output tiles_b tiles),
+ * the staging form zs_bucket_step takes.  stride: a multiple of 8. */
+int zs_grads_tile(const zs_layout* layout, int32_t bucket_id,
+                  const uint16_t* slices, int64_t stride, uint16_t* tiled,
+                  void* hip_stream);
 
 /* Local part of the all-gather (CS336 notes, "Code example: ZeRO-1": the
  * all-gather concatenates the updated slices in rank order; "Code example:

@@ -26,12 +26,24 @@ HIP library):
 * The chunk table lists, for one rank, the maximal runs of its shard that lie
   inside one tensor: (tensor_id, bucket_id, tensor_off, numel, shard_off).
   Padding is in no chunk.
+* Tiles.  The tiled HBM layouts of the optimizer state and of the gradient
+  slices are a storage format of the implementation, not part of the method;
+  they are stated here so that tests can place and read values in them
+  without the library.  Each bucket's slice is cut into ``TILE``-element
+  tiles, the last one padded; tiles are numbered across buckets in bucket
+  order (``Bucket.tile_off`` is the first tile of the slice).  Tiled state:
+  tile i holds ``[master | m | v]`` of ``TILE`` floats each.  Tiled
+  gradients: tile i holds source ranks 0..W-1, ``TILE`` bf16 values each.
 """
 
 from __future__ import annotations
 
 from dataclasses import dataclass, field
 from typing import List, Sequence
+
+import numpy as np
+
+TILE = 8192          # elements per tile of the tiled layouts
 
 
 def _roundup(x: int, a: int) -> int:
@@ -44,6 +56,7 @@ class Bucket:
     numel: int
     slice_numel: int
     shard_off: int
+    tile_off: int = 0
 
 
 @dataclass
@@ -65,6 +78,8 @@ class Layout:
     tensor_flat_off: List[int]
     flat_numel: int
     shard_numel: int
+    n_tiles: int = 0
+    tile: int = TILE
     buckets: List[Bucket] = field(default_factory=list)
     chunks: List[Chunk] = field(default_factory=list)
 
@@ -75,7 +90,7 @@ class LayoutError(ValueError):
 
 def build_layout(tensor_numel: Sequence[int], world: int, rank: int,
                  bucket_cap_bytes: int = 25 << 20,
-                 align_bytes: int = 256) -> Layout:
+                 align_bytes: int = 256, tile: int = TILE) -> Layout:
     """Build the layout of one rank.  See the module docstring for the rule.
 
     ``bucket_cap_bytes <= 0`` means one bucket holding the whole flat buffer,
@@ -112,12 +127,14 @@ def build_layout(tensor_numel: Sequence[int], world: int, rank: int,
     buckets = []
     off = 0
     shard_off = 0
+    tiles = 0
     while off < content_end:
         numel = min(full, _roundup(content_end - off, unit))
         sl = numel // world
-        buckets.append(Bucket(off, numel, sl, shard_off))
+        buckets.append(Bucket(off, numel, sl, shard_off, tiles))
         off += numel
         shard_off += sl
+        tiles += _roundup(sl, tile) // tile
     flat_numel = off
     shard_numel = shard_off
 
@@ -136,7 +153,7 @@ def build_layout(tensor_numel: Sequence[int], world: int, rank: int,
     return Layout(world=world, rank=rank, align_elems=align, bucket_elems=full,
                   tensor_numel=list(tensor_numel), tensor_flat_off=starts,
                   flat_numel=flat_numel, shard_numel=shard_numel,
-                  buckets=buckets, chunks=chunks)
+                  n_tiles=tiles, tile=tile, buckets=buckets, chunks=chunks)
 
 
 def shard_flat_index(lay: Layout) -> List[range]:
@@ -144,3 +161,48 @@ def shard_flat_index(lay: Layout) -> List[range]:
     return [range(b.flat_off + lay.rank * b.slice_numel,
                   b.flat_off + (lay.rank + 1) * b.slice_numel)
             for b in lay.buckets]
+
+
+def tile_slot(lay: Layout) -> np.ndarray:
+    """int64 [shard_numel]: for shard element e, tile * T + position of e
+    in the tiled layouts, T = lay.tile (element j of bucket b's slice sits in
+    tile b.tile_off + j // T at position j % T)."""
+    T = lay.tile
+    out = np.empty(lay.shard_numel, np.int64)
+    for b in lay.buckets:
+        j = np.arange(b.slice_numel, dtype=np.int64)
+        out[b.shard_off:b.shard_off + b.slice_numel] = \
+            (b.tile_off + j // T) * T + j % T
+    return out
+
+
+def to_tiled_state(lay: Layout, master, m, v) -> np.ndarray:
+    """Plain fp32 master/m/v [shard_numel] -> tiled state
+    [n_tiles * 3 * lay.tile]; padding positions 0."""
+    st = np.zeros((lay.n_tiles, 3, lay.tile), np.float32)
+    slot = tile_slot(lay)
+    t, p = slot // lay.tile, slot % lay.tile
+    st[t, 0, p] = master
+    st[t, 1, p] = m
+    st[t, 2, p] = v
+    return st.reshape(-1)
+
+
+def from_tiled_state(lay: Layout, state):
+    """Tiled state -> plain (master, m, v)."""
+    st = np.asarray(state, np.float32).reshape(lay.n_tiles, 3, lay.tile)
+    slot = tile_slot(lay)
+    t, p = slot // lay.tile, slot % lay.tile
+    return st[t, 0, p].copy(), st[t, 1, p].copy(), st[t, 2, p].copy()
+
+
+def to_tiled_grads(lay: Layout, G) -> np.ndarray:
+    """Gradient slices uint16 [W][shard_numel] -> tiled [n_tiles*W*lay.tile];
+    padding positions 0."""
+    W = lay.world
+    out = np.zeros((lay.n_tiles, W, lay.tile), np.uint16)
+    slot = tile_slot(lay)
+    t, p = slot // lay.tile, slot % lay.tile
+    for s in range(W):
+        out[t, s, p] = G[s]
+    return out.reshape(-1)

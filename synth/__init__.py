@@ -60,7 +60,8 @@ def _dev_lib():
                                             ctypes.c_double, p]
         L.synth_bits16_dev.argtypes = [p, i64, u64, u64, u64, u64, i64, p]
         L.synth_copy_dev.argtypes = [p, p, i64, p]
-        L.synth_mix_stream_dev.argtypes = [p, i64, i32, p, p, p, p, i64, p]
+        L.synth_mix_stream_dev.argtypes = [p, p, p, i32, i64, i64, i64,
+                                           i32, p]
         for f in (L.synth_normal_f32_dev, L.synth_normal_bf16_dev,
                   L.synth_bits16_dev, L.synth_copy_dev,
                   L.synth_mix_stream_dev):
@@ -137,9 +138,11 @@ def dev_copy(dst, src, nbytes, stream=None):
                                   _stream_handle(stream)), "synth_copy_dev")
 
 
-def dev_mix_stream(grads, grad_stride, W, a, b, c, p, n, stream=None):
-    _ok(_dev_lib().synth_mix_stream_dev(grads.data_ptr(), grad_stride, W,
-                                        a.data_ptr(), b.data_ptr(),
-                                        c.data_ptr(), p.data_ptr(), n,
+def dev_mix_stream(grads_tiled, state, flat, W, S, S_last, B, nb,
+                   stream=None):
+    """The step's access pattern on tiled gradients/state (bench ceiling)."""
+    _ok(_dev_lib().synth_mix_stream_dev(grads_tiled.data_ptr(),
+                                        state.data_ptr(), flat.data_ptr(), W,
+                                        S, S_last, B, nb,
                                         _stream_handle(stream)),
         "synth_mix_stream_dev")

@@ -15,9 +15,9 @@
  *   synth_copy_dev       - plain 16-byte copy of a known byte count, the
  *                          reference for scaling the HBM byte counters;
  *   synth_mix_stream_dev - the optimizer step's exact memory access pattern
- *                          (W bf16 slices + three fp32 arrays read, three
- *                          fp32 arrays + one bf16 array written, 16-byte
- *                          accesses) with only integer XORs in between, the
+ *                          (tiled gradients and state read, tiled state and
+ *                          the flat bf16 buffer written) with only integer
+ *                          XORs in between, the
  *                          achievable bandwidth ceiling for that mix.
  */
 #include <hip/hip_runtime.h>
@@ -174,49 +174,106 @@ extern "C" int synth_copy_dev(void* dst, const void* src, int64_t nbytes,
     return finish();
 }
 
-/* One thread per group of 8 elements: W x 16 B of bf16 read, 3 x 32 B of
- * fp32 read and written, 16 B of bf16 written. */
-__global__ __launch_bounds__(256) void k_mix_stream(
-    const u32x4* __restrict__ grads, int64_t stride16, int W,
-    u32x4* __restrict__ a, u32x4* __restrict__ b, u32x4* __restrict__ c,
-    u32x4* __restrict__ p, int64_t n_groups)
+/* The step's access pattern with integer XORs in place of the arithmetic:
+ * one 512-thread workgroup per 8192-element tile of a bucket slice, four
+ * 4-element units per thread at stride 512 units; reads W tiled gradient
+ * rows (8 B per unit each) and the three tiled fp32 state rows (16 B per
+ * unit each), writes the three state rows back and 8 B per unit of bf16
+ * into the flat buffer at the rank-0 position of the bucket. */
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <int WT>
+__global__ __launch_bounds__(512) void k_mix_stream(
+    const u32x2* __restrict__ grads, u32x4* __restrict__ state,
+    u32x2* __restrict__ flat, int Wrt, int64_t S, int64_t S_last, int64_t B,
+    int64_t tpb, int q_last)
 {
-    int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gi >= n_groups)
+    const int W = WT > 0 ? WT : Wrt;
+    const int q = blockIdx.y;
+    const int64_t slice = q == q_last ? S_last : S;
+    const int64_t j0 = (int64_t)blockIdx.x * 8192;
+    if (j0 >= slice)
         return;
-    u32x4 x = __builtin_nontemporal_load(&grads[gi]);
-    for (int s = 1; s < W; ++s)
-        x ^= __builtin_nontemporal_load(&grads[(int64_t)s * stride16 + gi]);
-    u32x4 a0 = a[2 * gi], a1 = a[2 * gi + 1];
-    u32x4 b0 = b[2 * gi], b1 = b[2 * gi + 1];
-    u32x4 c0 = c[2 * gi], c1 = c[2 * gi + 1];
-    a0 ^= x; a1 ^= x; b0 ^= a0; b1 ^= a1; c0 ^= b0; c1 ^= b1;
-    __builtin_nontemporal_store(a0, &a[2 * gi]);
-    __builtin_nontemporal_store(a1, &a[2 * gi + 1]);
-    __builtin_nontemporal_store(b0, &b[2 * gi]);
-    __builtin_nontemporal_store(b1, &b[2 * gi + 1]);
-    __builtin_nontemporal_store(c0, &c[2 * gi]);
-    __builtin_nontemporal_store(c1, &c[2 * gi + 1]);
-    __builtin_nontemporal_store(c0 ^ c1, &p[gi]);
+    const int64_t tile = (int64_t)q * tpb + blockIdx.x;
+    const int64_t nv = slice - j0 < 8192 ? slice - j0 : 8192;
+    const u32x2* g = grads + tile * W * 2048;
+    u32x4* st = state + tile * 3 * 2048;
+    u32x2* f = flat + ((int64_t)q * B + j0) / 4;
+    u32x4 a[4], b[4], c[4];
+    u32x2 x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int u = k * 512 + threadIdx.x;
+        if (4 * u < nv) {
+            a[k] = __builtin_nontemporal_load(st + u);
+            b[k] = __builtin_nontemporal_load(st + 2048 + u);
+            c[k] = __builtin_nontemporal_load(st + 4096 + u);
+        }
+        x[k] = u32x2{0u, 0u};
+    }
+    /* slices in batches of 8, all loads of a batch issued before use */
+    for (int s0 = 0; s0 < W; s0 += 8) {
+        u32x2 y[4][8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int u = k * 512 + threadIdx.x;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (4 * u < nv && s0 + i < W)
+                    y[k][i] = __builtin_nontemporal_load(
+                        g + (int64_t)(s0 + i) * 2048 + u);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int u = k * 512 + threadIdx.x;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (4 * u < nv && s0 + i < W)
+                    x[k] ^= y[k][i];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int u = k * 512 + threadIdx.x;
+        if (4 * u >= nv)
+            continue;
+        const u32x4 xx = {x[k].x, x[k].y, x[k].x, x[k].y};
+        a[k] ^= xx;
+        b[k] ^= a[k];
+        c[k] ^= b[k];
+        __builtin_nontemporal_store(a[k], st + u);
+        __builtin_nontemporal_store(b[k], st + 2048 + u);
+        __builtin_nontemporal_store(c[k], st + 4096 + u);
+        __builtin_nontemporal_store(u32x2{c[k].x ^ c[k].z, c[k].y ^ c[k].w},
+                                    f + u);
+    }
 }
 
-extern "C" int synth_mix_stream_dev(const void* grads, int64_t grad_stride,
-                                    int32_t W, void* a, void* b, void* c,
-                                    void* p, int64_t n, void* stream)
+/* grads: tiled [tiles][W][8192] bf16; state: tiled [tiles][3][8192] fp32;
+ * flat: the bf16 flat buffer; S, B: slice and numel of a full bucket,
+ * S_last the last bucket's slice, nb buckets (all but the last full).
+ * Sizes must describe the buffers (the caller's layout). */
+extern "C" int synth_mix_stream_dev(const void* grads, void* state,
+                                    void* flat, int32_t W, int64_t S,
+                                    int64_t S_last, int64_t B, int32_t nb,
+                                    void* stream)
 {
-    if (W < 1 || n < 0 || (n % 8) || (grad_stride % 8) || grad_stride < n)
+    if (W < 1 || nb < 1 || nb > 65535 || S < 1 || S_last < 1 ||
+        S_last > S || (S % 128) || (S_last % 128) || B < W * S)
         return -1;
-    if (n == 0) return 0;
-    if (!grads || !a || !b || !c || !p) return -1;
-    if (((uintptr_t)grads | (uintptr_t)a | (uintptr_t)b | (uintptr_t)c |
-         (uintptr_t)p) & 15u)
+    if (!grads || !state || !flat) return -1;
+    if (((uintptr_t)grads | (uintptr_t)state | (uintptr_t)flat) & 15u)
         return -2;
-    int64_t groups = n / 8;
-    int64_t blocks = (groups + 255) / 256;
-    if (blocks > 0x7fffffff) return -3;
-    hipLaunchKernelGGL(k_mix_stream, dim3((unsigned)blocks), dim3(256), 0,
-                       (hipStream_t)stream, (const u32x4*)grads,
-                       grad_stride / 8, (int)W, (u32x4*)a, (u32x4*)b,
-                       (u32x4*)c, (u32x4*)p, groups);
+    const int64_t tpb = (S + 8191) / 8192;
+    if (W == 8)
+        hipLaunchKernelGGL(k_mix_stream<8>, dim3((unsigned)tpb, (unsigned)nb),
+                           dim3(512), 0, (hipStream_t)stream,
+                           (const u32x2*)grads, (u32x4*)state, (u32x2*)flat,
+                           (int)W, S, S_last, B, tpb, nb - 1);
+    else
+        hipLaunchKernelGGL(k_mix_stream<0>, dim3((unsigned)tpb, (unsigned)nb),
+                           dim3(512), 0, (hipStream_t)stream,
+                           (const u32x2*)grads, (u32x4*)state, (u32x2*)flat,
+                           (int)W, S, S_last, B, tpb, nb - 1);
     return finish();
 }

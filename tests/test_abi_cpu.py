@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 16
     L = zs.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -34,20 +34,21 @@ def test_exports_every_declared_symbol():
 
 def tables(lay_c, n_tensors):
     f, s, nb, nc = zs.zs_layout_info(lay_c)
-    b = [(x.flat_off, x.numel, x.slice_numel, x.shard_off)
+    b = [(x.flat_off, x.numel, x.slice_numel, x.shard_off, x.tile_off)
          for x in zs.zs_layout_buckets(lay_c)]
     c = [(x.tensor_id, x.bucket_id, x.tensor_off, x.numel, x.shard_off)
          for x in zs.zs_layout_chunks(lay_c)]
     t = zs.zs_layout_tensor_offsets(lay_c, n_tensors)
-    return f, s, b, c, t
+    return f, s, zs.zs_layout_tiles(lay_c), b, c, t
 
 
 def oracle_tables(lay):
-    b = [(x.flat_off, x.numel, x.slice_numel, x.shard_off)
+    b = [(x.flat_off, x.numel, x.slice_numel, x.shard_off, x.tile_off)
          for x in lay.buckets]
     c = [(x.tensor_id, x.bucket_id, x.tensor_off, x.numel, x.shard_off)
          for x in lay.chunks]
-    return lay.flat_numel, lay.shard_numel, b, c, lay.tensor_flat_off
+    return (lay.flat_numel, lay.shard_numel, lay.n_tiles, b, c,
+            lay.tensor_flat_off)
 
 
 def same(numels, world, rank, cap, align):
@@ -122,34 +123,52 @@ def test_step_argument_checks_need_no_device():
     A = 1 << 20                                  # fake, 16-byte aligned
     shard = zs.zs_layout_info(lay)[1]
     h = lay.handle
-    ok = dict(g=A, st=shard, ma=A, m=A, v=A, p=A, f=None, hp=ctypes.byref(hp),
+    ok = dict(g=A, gl=0, gs=shard, st=A, p=A, f=None, hp=ctypes.byref(hp),
               t=1)
 
     def call(**kw):
         a = {**ok, **kw}
-        return L.zs_step(h if "h" not in kw else kw["h"], a["g"], a["st"],
-                         a["ma"], a["m"], a["v"], a["p"], a["f"], a["hp"],
-                         a["t"], None)
+        return L.zs_step(h if "h" not in kw else kw["h"], a["g"], a["gl"],
+                         a["gs"], a["st"], a["p"], a["f"], a["hp"], a["t"],
+                         None)
 
     assert call(h=None) == -1
     assert call(hp=None) == -1
     assert call(t=0) == -1
     assert call(g=None) == -1
-    assert call(v=None) == -1
+    assert call(st=None) == -1
+    assert call(gl=2) == -1
+    assert call(gl=-1) == -1
     assert call(p=None, f=None) == -1
     assert call(g=A + 2) == -2
-    assert call(ma=A + 8) == -2
+    assert call(st=A + 8) == -2
     assert call(f=A + 4, p=None) == -2
-    assert call(st=shard + 4) == -2
-    assert call(st=shard - 8) == -3
-    assert call(st=(2 ** 62) // 8 * 8) == -3
+    assert call(gs=shard + 4) == -2
+    assert call(gs=shard - 8) == -3
+    assert call(gs=(2 ** 62) // 8 * 8) == -3
+    # the tiled layout takes no stride: any value is accepted
+    for gs in (0, 3, -8):
+        assert call(gl=1, gs=gs, g=A + 2) == -2      # fails on alignment only
     # bucket step: id range, staging stride vs the bucket's slice
-    assert L.zs_bucket_step(h, 1, A, shard, A, A, A, A, None,
+    assert L.zs_bucket_step(h, 1, A, 0, shard, A, A, None,
                             ctypes.byref(hp), 1, None) == -3
-    assert L.zs_bucket_step(h, -1, A, shard, A, A, A, A, None,
+    assert L.zs_bucket_step(h, -1, A, 0, shard, A, A, None,
                             ctypes.byref(hp), 1, None) == -3
-    assert L.zs_bucket_step(h, 0, A, shard - 8, A, A, A, A, None,
+    assert L.zs_bucket_step(h, 0, A, 0, shard - 8, A, A, None,
                             ctypes.byref(hp), 1, None) == -3
+    assert L.zs_bucket_step(h, 0, A, 7, shard, A, A, None,
+                            ctypes.byref(hp), 1, None) == -1
+    # layout conversions
+    assert L.zs_state_pack(h, None, A, A, A, None) == -1
+    assert L.zs_state_pack(h, A, A, A, None, None) == -1
+    assert L.zs_state_pack(h, A, A + 4, A, A, None) == -2
+    assert L.zs_state_unpack(h, None, A, A, A, None) == -1
+    assert L.zs_state_unpack(h, A + 4, A, None, None, None) == -2
+    assert L.zs_grads_tile(h, -1, None, shard, A, None) == -1
+    assert L.zs_grads_tile(h, -1, A, shard - 8, A, None) == -3
+    assert L.zs_grads_tile(h, -1, A, shard + 4, A, None) == -2
+    assert L.zs_grads_tile(h, 1, A, shard, A, None) == -3
+    assert L.zs_grads_tile(h, 0, A + 2, shard, A, None) == -2
     # pack
     assert L.zs_pack(h, A, None, None, 0, None, None) == -1
     assert L.zs_pack(h, None, A, None, 0, None, None) == -1
@@ -164,6 +183,10 @@ def test_empty_layout_calls_are_noops():
     assert zs.zs_layout_info(lay) == (0, 0, 0, 0)
     hp = zs.zs_adamw(3e-4, 0.9, 0.95, 1e-8, 0.1)
     # no device pointers at all: nothing to do, success
-    assert L.zs_step(lay.handle, None, 0, None, None, None, None, None,
+    assert zs.zs_layout_tiles(lay) == 0
+    assert L.zs_step(lay.handle, None, 0, 0, None, None, None,
                      ctypes.byref(hp), 1, None) == 0
     assert L.zs_pack(lay.handle, None, 1 << 20, None, 0, None, None) == 0
+    assert L.zs_state_pack(lay.handle, None, None, None, None, None) == 0
+    assert L.zs_state_unpack(lay.handle, None, None, None, None, None) == 0
+    assert L.zs_grads_tile(lay.handle, -1, None, 0, None, None) == 0

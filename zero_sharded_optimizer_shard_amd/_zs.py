@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(_PKG, "libzs.so")
 
 ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ERANGE, ZS_ENOMEM, ZS_EDEVICE = \
     0, -1, -2, -3, -4, -5
+ZS_TILE = 8192
+ZS_GRADS_SLICES, ZS_GRADS_TILED = 0, 1
 
 
 class ZsError(RuntimeError):
@@ -26,7 +28,7 @@ class ZsError(RuntimeError):
 class zs_bucket(ctypes.Structure):
     _fields_ = [("flat_off", ctypes.c_int64), ("numel", ctypes.c_int64),
                 ("slice_numel", ctypes.c_int64),
-                ("shard_off", ctypes.c_int64)]
+                ("shard_off", ctypes.c_int64), ("tile_off", ctypes.c_int64)]
 
 
 class zs_chunk(ctypes.Structure):
@@ -43,10 +45,11 @@ class zs_adamw(ctypes.Structure):
 
 _lib = None
 
-EXPORTS = ["zs_layout_build", "zs_layout_info", "zs_layout_buckets",
-           "zs_layout_chunks", "zs_layout_tensor_offsets", "zs_layout_rank",
-           "zs_layout_free", "zs_step", "zs_bucket_step", "zs_pack",
-           "zs_strerror", "zs_last_error"]
+EXPORTS = ["zs_layout_build", "zs_layout_info", "zs_layout_tiles",
+           "zs_layout_buckets", "zs_layout_chunks",
+           "zs_layout_tensor_offsets", "zs_layout_rank", "zs_layout_free",
+           "zs_step", "zs_bucket_step", "zs_state_pack", "zs_state_unpack",
+           "zs_grads_tile", "zs_pack", "zs_strerror", "zs_last_error"]
 
 
 def lib():
@@ -63,23 +66,29 @@ def lib():
     P = ctypes.POINTER
     L.zs_layout_build.argtypes = [P(i64), i32, i32, i32, i64, i32, P(p)]
     L.zs_layout_info.argtypes = [p, P(i64), P(i64), P(i32), P(i32)]
+    L.zs_layout_tiles.argtypes = [p, P(i64)]
     L.zs_layout_buckets.argtypes = [p, P(zs_bucket), i32]
     L.zs_layout_chunks.argtypes = [p, P(zs_chunk), i32]
     L.zs_layout_tensor_offsets.argtypes = [p, P(i64), i32]
     L.zs_layout_rank.argtypes = [p, P(i32), P(i32)]
     L.zs_layout_free.argtypes = [p]
     L.zs_layout_free.restype = None
-    L.zs_step.argtypes = [p, p, i64, p, p, p, p, p, P(zs_adamw), i64, p]
-    L.zs_bucket_step.argtypes = [p, i32, p, i64, p, p, p, p, p, P(zs_adamw),
+    L.zs_step.argtypes = [p, p, i32, i64, p, p, p, P(zs_adamw), i64, p]
+    L.zs_bucket_step.argtypes = [p, i32, p, i32, i64, p, p, p, P(zs_adamw),
                                  i64, p]
+    L.zs_state_pack.argtypes = [p, p, p, p, p, p]
+    L.zs_state_unpack.argtypes = [p, p, p, p, p, p]
+    L.zs_grads_tile.argtypes = [p, i32, p, i64, p, p]
     L.zs_pack.argtypes = [p, p, p, p, i32, p, p]
     L.zs_strerror.argtypes = [ctypes.c_int]
     L.zs_strerror.restype = ctypes.c_char_p
     L.zs_last_error.argtypes = []
     L.zs_last_error.restype = ctypes.c_char_p
-    for name in ("zs_layout_build", "zs_layout_info", "zs_layout_buckets",
-                 "zs_layout_chunks", "zs_layout_tensor_offsets",
-                 "zs_layout_rank", "zs_step", "zs_bucket_step", "zs_pack"):
+    for name in ("zs_layout_build", "zs_layout_info", "zs_layout_tiles",
+                 "zs_layout_buckets", "zs_layout_chunks",
+                 "zs_layout_tensor_offsets", "zs_layout_rank", "zs_step",
+                 "zs_bucket_step", "zs_state_pack", "zs_state_unpack",
+                 "zs_grads_tile", "zs_pack"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -135,6 +144,13 @@ def zs_layout_info(layout: Layout):
                                 ctypes.byref(s), ctypes.byref(nb),
                                 ctypes.byref(nc)), "zs_layout_info")
     return f.value, s.value, nb.value, nc.value
+
+
+def zs_layout_tiles(layout: Layout) -> int:
+    n = ctypes.c_int64()
+    _check(lib().zs_layout_tiles(layout.handle, ctypes.byref(n)),
+           "zs_layout_tiles")
+    return n.value
 
 
 def zs_layout_rank(layout: Layout):
@@ -208,31 +224,71 @@ def _hp(lr, beta1, beta2, eps, weight_decay):
     return zs_adamw(lr, beta1, beta2, eps, weight_decay)
 
 
-def zs_step(layout: Layout, grads, grad_stride: int, master, m, v,
-            param_shard=None, full_flat=None, *, lr: float, beta1: float,
-            beta2: float, eps: float, weight_decay: float, step: int,
-            stream=None) -> None:
+def _layout_code(grad_layout) -> int:
+    codes = {"slices": ZS_GRADS_SLICES, "tiled": ZS_GRADS_TILED,
+             ZS_GRADS_SLICES: ZS_GRADS_SLICES, ZS_GRADS_TILED: ZS_GRADS_TILED}
+    if grad_layout not in codes:
+        # unknown codes go through unchanged so the library reports them
+        return int(grad_layout)
+    return codes[grad_layout]
+
+
+def zs_step(layout: Layout, grads, state, param_shard=None, full_flat=None,
+            *, grad_layout="slices", grad_stride: int = 0, lr: float,
+            beta1: float, beta2: float, eps: float, weight_decay: float,
+            step: int, stream=None) -> None:
+    """grads: [W][grad_stride] slices (grad_layout "slices") or
+    [n_tiles][W][ZS_TILE] ("tiled"); state: tiled fp32 state."""
     hp = _hp(lr, beta1, beta2, eps, weight_decay)
-    _check(lib().zs_step(layout.handle, _bf16(grads, "grads"), grad_stride,
-                         _f32(master, "master"), _f32(m, "m"), _f32(v, "v"),
+    _check(lib().zs_step(layout.handle, _bf16(grads, "grads"),
+                         _layout_code(grad_layout), grad_stride,
+                         _f32(state, "state"),
                          _bf16(param_shard, "param_shard"),
                          _bf16(full_flat, "full_flat"), ctypes.byref(hp),
                          step, _stream(stream)), "zs_step")
 
 
-def zs_bucket_step(layout: Layout, bucket_id: int, grads, grad_stride: int,
-                   master, m, v, param_shard=None, full_flat=None, *,
-                   lr: float, beta1: float, beta2: float, eps: float,
+def zs_bucket_step(layout: Layout, bucket_id: int, grads, state,
+                   param_shard=None, full_flat=None, *,
+                   grad_layout="slices", grad_stride: int = 0, lr: float,
+                   beta1: float, beta2: float, eps: float,
                    weight_decay: float, step: int, stream=None) -> None:
     hp = _hp(lr, beta1, beta2, eps, weight_decay)
     _check(lib().zs_bucket_step(layout.handle, bucket_id,
-                                _bf16(grads, "grads"), grad_stride,
-                                _f32(master, "master"), _f32(m, "m"),
-                                _f32(v, "v"),
+                                _bf16(grads, "grads"),
+                                _layout_code(grad_layout), grad_stride,
+                                _f32(state, "state"),
                                 _bf16(param_shard, "param_shard"),
                                 _bf16(full_flat, "full_flat"),
                                 ctypes.byref(hp), step, _stream(stream)),
            "zs_bucket_step")
+
+
+def zs_state_pack(layout: Layout, master, m, v, state, stream=None) -> None:
+    """Plain master/m/v (m, v may be None: zeros) -> tiled state."""
+    _check(lib().zs_state_pack(layout.handle, _f32(master, "master"),
+                               None if m is None else _f32(m, "m"),
+                               None if v is None else _f32(v, "v"),
+                               _f32(state, "state"), _stream(stream)),
+           "zs_state_pack")
+
+
+def zs_state_unpack(layout: Layout, state, master=None, m=None, v=None,
+                    stream=None) -> None:
+    _check(lib().zs_state_unpack(layout.handle, _f32(state, "state"),
+                                 None if master is None
+                                 else _f32(master, "master"),
+                                 None if m is None else _f32(m, "m"),
+                                 None if v is None else _f32(v, "v"),
+                                 _stream(stream)), "zs_state_unpack")
+
+
+def zs_grads_tile(layout: Layout, bucket_id: int, slices, stride: int,
+                  tiled, stream=None) -> None:
+    _check(lib().zs_grads_tile(layout.handle, bucket_id,
+                               _bf16(slices, "slices"), stride,
+                               _bf16(tiled, "tiled"), _stream(stream)),
+           "zs_grads_tile")
 
 
 def zs_pack(layout: Layout, param_shard, full_flat=None, dev_chunks=None,

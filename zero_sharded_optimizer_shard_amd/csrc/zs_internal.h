@@ -15,6 +15,7 @@ struct zs_layout {
     int64_t bucket_elems = 0;   // numel of a full bucket
     int64_t flat_numel = 0;
     int64_t shard_numel = 0;
+    int64_t n_tiles = 0;        // tiles of the shard in the tiled layouts
     std::vector<int64_t> tensor_numel;
     std::vector<int64_t> tensor_off;
     std::vector<zs_bucket> buckets;

@@ -130,8 +130,9 @@ extern "C" int zs_layout_build(const int64_t* tensor_numel, int32_t n_tensors,
         }
         L->bucket_elems = full;
 
-        // 3. buckets
-        int64_t off = 0, shard = 0;
+        // 3. buckets, and where each slice's tiles start in the tiled
+        //    layouts
+        int64_t off = 0, shard = 0, tiles = 0;
         while (off < content_end) {
             int64_t rest;
             if (!roundup_ok(content_end - off, unit, &rest)) {
@@ -143,9 +144,11 @@ extern "C" int zs_layout_build(const int64_t* tensor_numel, int32_t n_tensors,
             b.numel = rest < full ? rest : full;
             b.slice_numel = b.numel / world;
             b.shard_off = shard;
+            b.tile_off = tiles;
             L->buckets.push_back(b);
             off += b.numel;
             shard += b.slice_numel;
+            tiles += (b.slice_numel + ZS_TILE - 1) / ZS_TILE;
         }
         if ((int64_t)L->buckets.size() > std::numeric_limits<int32_t>::max()) {
             delete L;
@@ -153,6 +156,7 @@ extern "C" int zs_layout_build(const int64_t* tensor_numel, int32_t n_tensors,
         }
         L->flat_numel = off;
         L->shard_numel = shard;
+        L->n_tiles = tiles;
 
         // 4. chunks: sweep tensors and this rank's slices together.  `first`
         //    is the first tensor that ends after the current slice start;
@@ -203,6 +207,14 @@ extern "C" int zs_layout_info(const zs_layout* L, int64_t* flat_numel,
     if (shard_numel) *shard_numel = L->shard_numel;
     if (n_buckets) *n_buckets = (int32_t)L->buckets.size();
     if (n_chunks) *n_chunks = (int32_t)L->chunks.size();
+    return ZS_OK;
+}
+
+extern "C" int zs_layout_tiles(const zs_layout* L, int64_t* n_tiles)
+{
+    zs::clear_error();
+    if (!L) return zs::fail(ZS_EINVAL, "layout is NULL");
+    if (n_tiles) *n_tiles = L->n_tiles;
     return ZS_OK;
 }
 

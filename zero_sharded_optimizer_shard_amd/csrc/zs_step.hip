@@ -1,28 +1,38 @@
-// Device side of libzs: the fused shard step and the all-gather pack, with
-// their host launchers and argument checks.  Written for gfx950 (CDNA4,
+// Device side of libzs: the fused shard step, the all-gather pack, the
+// layout conversions, and their host launchers.  Written for gfx950 (CDNA4,
 // wave64).
 //
-// The step is one pass over the rank's shard.  Per 8-element group a thread
-// reads W x 16 B of bf16 gradient (one 16-byte load per source rank, in rank
-// order), 3 x 32 B of fp32 state, and writes 3 x 32 B of fp32 state plus
-// 16 B of bf16 parameter: 2W + 26 bytes per element, nothing else.  The
-// reduced gradient lives only in registers.  No LDS, no MFMA: the work is an
-// elementwise stream bounded by HBM bandwidth.
+// The step is one pass over the rank's shard.  Per element it reads W x 2 B
+// of bf16 gradient, 12 B of fp32 state (master, m, v) and writes the 12 B of
+// state back plus 2 B of bf16 parameter: 2W + 26 bytes, nothing else.  The
+// reduced gradient lives only in registers.  No LDS and no MFMA: the work
+// is an elementwise stream bounded by HBM bandwidth.
 //
 // Arithmetic (CS336 lecture 8 notes, "Code example: ZeRO-1": reduce-scatter
 // with SUM, then the rank-local AdamW update; DDP-to-ZeRO blog 2.1: the
 // gradients are averaged), one IEEE fp32 rounding per operation, no
 // contraction (built with -ffp-contract=off), correctly rounded divide and
-// square root (hipcc's default for fp32):
+// square root:
 //   g   = (((G0 + G1) + G2) + ... + G_{W-1}) / W
 //   m   = b1*m + (1-b1)*g
 //   v   = b2*v + (1-b2)*(g*g)
 //   th  = th*(1-lr*wd) - (lr/bc1) * (m / (sqrt(v)/sqrt(bc2) + eps))
 //   p   = bf16 of th, round to nearest even
 //
-// Grid shape: blockIdx.y is the bucket, blockIdx.x the 2048-element tile of
-// that bucket's slice, so no thread divides to find its bucket and the
-// all-gather position of each element is one multiply-add away.
+// Work decomposition.  One 512-thread workgroup (8 wave64s) owns one tile
+// of ZS_TILE = 8192 elements of one bucket's slice; each thread owns four
+// 4-element units at stride 512 units, so every load or store instruction of
+// a wave covers one contiguous run (1 KiB of fp32, 512 B of bf16) and the
+// whole workgroup sweeps each stream in one 16-32 KiB burst.  With the tiled
+// state the three 32 KiB rows of a tile are adjacent, and with tiled
+// gradients so are the W 16 KiB slice rows; measured on MI355X, that lifts
+// this 2:1 read/write stream from about 5.4 to about 6.4 TB/s.  All loads of
+// a unit are issued before its arithmetic (the W slices in batches of 8), and
+// every access is non-temporal: nothing is reused.
+//
+// Grid: blockIdx.y = bucket, blockIdx.x = tile of that bucket's slice, so no
+// thread divides to find its bucket, and the all-gather position of each
+// element is one multiply-add away.
 
 #include <hip/hip_runtime.h>
 
@@ -33,12 +43,14 @@
 
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;              // 4 waves of 64
-constexpr int kGroup = 8;                  // elements per thread (16 B bf16)
-constexpr int64_t kTile = kThreads * kGroup;
+constexpr int kThreads = 512;              // 8 waves of 64
+constexpr int kUnits = 4;                  // 4-element units per thread
+constexpr int64_t kTile = ZS_TILE;
+static_assert(kTile == (int64_t)kThreads * kUnits * 4, "tile shape");
+constexpr int kBatch = 8;                  // gradient slices loaded together
 constexpr int64_t kMaxGridY = 65535;
 
 struct Consts {
@@ -52,22 +64,40 @@ struct Consts {
     int pow2;                   // W is a power of two
 };
 
-struct StepArgs {
-    const uint16_t* grads;      // [W][gstride], element 0 = launch start
-    int64_t gstride;
-    float* master;              // shard arrays, element 0 = launch start
-    float* m;
-    float* v;
-    uint16_t* pshard;           // nullable
-    uint16_t* flat;             // flat buffer at the launch's first bucket
-    int64_t S;                  // slice numel of a full bucket
-    int64_t S_last;             // slice numel of bucket q_last
-    int64_t B;                  // numel of a full bucket
-    int32_t q_last;             // launch-relative index of the last bucket
-    int32_t rank;
-    int32_t W;
-    Consts c;
+// Where one launch's tiles sit.  Buckets are launch-relative: bucket q
+// (q < q_last, or every q when q_last < 0) is a full bucket with slice S,
+// numel B and TPB tiles; bucket q_last has slice S_last <= S.
+struct Geom {
+    int64_t S, S_last, B, TPB;
+    int32_t q_last, rank;
 };
+
+struct TileRef {
+    int64_t tile;       // launch-relative tile index
+    int64_t e0;         // launch-relative shard element of the tile start
+    int64_t nvalid;     // elements of the tile inside the slice
+    int64_t fpos;       // launch-relative flat position of the tile start
+};
+
+__device__ __forceinline__ bool tile_of(const Geom& g, TileRef& r)
+{
+    const int32_t q = blockIdx.y;
+    const int64_t slice = (q == g.q_last) ? g.S_last : g.S;
+    const int64_t j0 = (int64_t)blockIdx.x * kTile;
+    if (j0 >= slice)
+        return false;
+    r.tile = (int64_t)q * g.TPB + blockIdx.x;
+    r.e0 = (int64_t)q * g.S + j0;
+    r.nvalid = slice - j0 < kTile ? slice - j0 : kTile;
+    r.fpos = (int64_t)q * g.B + (int64_t)g.rank * slice + j0;
+    return true;
+}
+
+// element offset of unit k of this thread inside its tile
+__device__ __forceinline__ int unit_off(int k)
+{
+    return 4 * (k * kThreads + (int)threadIdx.x);
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t u)
 {
@@ -89,138 +119,238 @@ __device__ __forceinline__ uint32_t to_bf16(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ __forceinline__ void accumulate(float (&acc)[kGroup], u32x4 x)
+__device__ __forceinline__ u32x2 ld2(const uint16_t* p)
 {
-    acc[0] = acc[0] + bf16_lo(x.x);
-    acc[1] = acc[1] + bf16_hi(x.x);
-    acc[2] = acc[2] + bf16_lo(x.y);
-    acc[3] = acc[3] + bf16_hi(x.y);
-    acc[4] = acc[4] + bf16_lo(x.z);
-    acc[5] = acc[5] + bf16_hi(x.z);
-    acc[6] = acc[6] + bf16_lo(x.w);
-    acc[7] = acc[7] + bf16_hi(x.w);
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 }
 
-__device__ __forceinline__ u32x4 ld_nt(const uint16_t* p)
-{
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-
-__device__ __forceinline__ f32x4 ld_nt(const float* p)
+__device__ __forceinline__ f32x4 ld4(const float* p)
 {
     return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
 }
 
-__device__ __forceinline__ void st_nt(float* p, f32x4 x)
+__device__ __forceinline__ void st2(uint16_t* p, u32x2 x)
+{
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x2*>(p));
+}
+
+__device__ __forceinline__ void st4(float* p, f32x4 x)
 {
     __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
 }
 
-__device__ __forceinline__ void st_nt(uint16_t* p, u32x4 x)
-{
-    __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
-}
+struct StepArgs {
+    const uint16_t* grads;      // launch base (see zs_step)
+    int64_t gstride;            // slices layout: elements between slices
+    float* state;               // tiled state at the launch's first tile
+    uint16_t* pshard;           // nullable, at the launch's first element
+    uint16_t* flat;             // nullable, at the launch's first bucket
+    Geom g;
+    int32_t W;
+    Consts c;
+};
 
-// Sum of the W gradient slices for 8 consecutive elements, rank order.
-// WT > 0: W known at compile time; WT == 0: runtime W.
-template <int WT>
-__device__ __forceinline__ void reduce_group(const uint16_t* __restrict__ g,
-                                             int64_t stride, int W,
-                                             float (&acc)[kGroup])
+// Slices s0 .. s0+n-1 (n <= NB) of every unit: all loads first, then the
+// adds in rank order.  Slice 0 initialises the sum, so the sign of a zero
+// sum is that of the first addend, as in a left-to-right sum.
+template <int NB>
+__device__ __forceinline__ void reduce_batch(const uint16_t* __restrict__ g0,
+                                             int64_t gs, int s0, int n,
+                                             bool full, int64_t nvalid,
+                                             float (&acc)[kUnits][4])
 {
-    const u32x4 x0 = ld_nt(g);
-    acc[0] = bf16_lo(x0.x);
-    acc[1] = bf16_hi(x0.x);
-    acc[2] = bf16_lo(x0.y);
-    acc[3] = bf16_hi(x0.y);
-    acc[4] = bf16_lo(x0.z);
-    acc[5] = bf16_hi(x0.z);
-    acc[6] = bf16_lo(x0.w);
-    acc[7] = bf16_hi(x0.w);
-    if constexpr (WT > 0 && WT <= 16) {
-        // all loads in flight at once, then the ordered adds
-        u32x4 x[WT > 1 ? WT - 1 : 1];
+    u32x2 x[kUnits][NB];
 #pragma unroll
-        for (int s = 1; s < WT; ++s)
-            x[s - 1] = ld_nt(g + (int64_t)s * stride);
+    for (int k = 0; k < kUnits; ++k) {
+        const int jj = unit_off(k);
+        if (full || jj < nvalid) {
 #pragma unroll
-        for (int s = 1; s < WT; ++s)
-            accumulate(acc, x[s - 1]);
-    } else {
-        // batches of 16 slices keep 64 VGPRs of loads in flight
-        constexpr int kBatch = 16;
-        int s = 1;
-#pragma unroll 1
-        for (; s + kBatch <= W; s += kBatch) {
-            u32x4 x[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u)
-                x[u] = ld_nt(g + (int64_t)(s + u) * stride);
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u)
-                accumulate(acc, x[u]);
+            for (int i = 0; i < NB; ++i)
+                if (i < n)
+                    x[k][i] = ld2(g0 + (int64_t)(s0 + i) * gs + jj);
         }
-#pragma unroll 1
-        for (; s < W; ++s)
-            accumulate(acc, ld_nt(g + (int64_t)s * stride));
+    }
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) {
+        const int jj = unit_off(k);
+        if (!(full || jj < nvalid))
+            continue;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (i >= n)
+                continue;
+            const u32x2 u = x[k][i];
+            if (s0 + i == 0) {
+                acc[k][0] = bf16_lo(u.x);
+                acc[k][1] = bf16_hi(u.x);
+                acc[k][2] = bf16_lo(u.y);
+                acc[k][3] = bf16_hi(u.y);
+            } else {
+                acc[k][0] = acc[k][0] + bf16_lo(u.x);
+                acc[k][1] = acc[k][1] + bf16_hi(u.x);
+                acc[k][2] = acc[k][2] + bf16_lo(u.y);
+                acc[k][3] = acc[k][3] + bf16_hi(u.y);
+            }
+        }
     }
 }
 
+// WT > 0: W known at compile time; WT == 0: runtime W.
 template <int WT>
+__device__ __forceinline__ void reduce(const uint16_t* __restrict__ g0,
+                                       int64_t gs, int W, bool full,
+                                       int64_t nvalid,
+                                       float (&acc)[kUnits][4])
+{
+    if constexpr (WT > 0 && WT <= kBatch) {
+        reduce_batch<WT>(g0, gs, 0, WT, full, nvalid, acc);
+    } else if constexpr (WT > 0) {
+        static_assert(WT % kBatch == 0, "compiled W above 8 must be a "
+                      "multiple of 8");
+#pragma unroll
+        for (int s0 = 0; s0 < WT; s0 += kBatch)
+            reduce_batch<kBatch>(g0, gs, s0, kBatch, full, nvalid, acc);
+    } else {
+#pragma unroll 1
+        for (int s0 = 0; s0 < W; s0 += kBatch) {
+            const int n = W - s0 < kBatch ? W - s0 : kBatch;
+            reduce_batch<kBatch>(g0, gs, s0, n, full, nvalid, acc);
+        }
+    }
+}
+
+template <int WT, bool TILED>
 __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a)
 {
-    const int32_t q = blockIdx.y;
-    const int64_t slice = (q == a.q_last) ? a.S_last : a.S;
-    const int64_t j = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kGroup;
-    if (j >= slice)
+    TileRef r;
+    if (!tile_of(a.g, r))
         return;
-    const int64_t e = (int64_t)q * a.S + j;
+    const int W = WT > 0 ? WT : a.W;
+    const bool full = r.nvalid == kTile;
+    float* st = a.state + r.tile * (3 * kTile);
+    const uint16_t* g0 = TILED ? a.grads + r.tile * (int64_t)W * kTile
+                               : a.grads + r.e0;
+    const int64_t gs = TILED ? kTile : a.gstride;
 
     // fp32 state first: its loads do not depend on the gradients
-    const f32x4 th0 = ld_nt(a.master + e), th1 = ld_nt(a.master + e + 4);
-    const f32x4 m0 = ld_nt(a.m + e), m1 = ld_nt(a.m + e + 4);
-    const f32x4 v0 = ld_nt(a.v + e), v1 = ld_nt(a.v + e + 4);
+    f32x4 th[kUnits], mm[kUnits], vv[kUnits];
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) {
+        const int jj = unit_off(k);
+        if (full || jj < r.nvalid) {
+            th[k] = ld4(st + jj);
+            mm[k] = ld4(st + kTile + jj);
+            vv[k] = ld4(st + 2 * kTile + jj);
+        }
+    }
 
-    float g[kGroup];
-    reduce_group<WT>(a.grads + e, a.gstride, WT > 0 ? WT : a.W, g);
+    float g[kUnits][4];
+    reduce<WT>(g0, gs, W, full, r.nvalid, g);
 
     const Consts c = a.c;
     const bool pow2 = WT > 0 ? ((WT & (WT - 1)) == 0) : (c.pow2 != 0);
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k)
-        g[k] = pow2 ? g[k] * c.invw : g[k] / c.fw;
-
-    float th[kGroup] = {th0.x, th0.y, th0.z, th0.w, th1.x, th1.y, th1.z, th1.w};
-    float mm[kGroup] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-    float vv[kGroup] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint32_t pb[kGroup];
+    for (int k = 0; k < kUnits; ++k) {
+        const int jj = unit_off(k);
+        if (!(full || jj < r.nvalid))
+            continue;
+        float t4[4] = {th[k].x, th[k].y, th[k].z, th[k].w};
+        float m4[4] = {mm[k].x, mm[k].y, mm[k].z, mm[k].w};
+        float v4[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
+        uint32_t pb[4];
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k) {
-        const float mi = (c.b1 * mm[k]) + (c.omb1 * g[k]);
-        const float g2 = g[k] * g[k];
-        const float vi = (c.b2 * vv[k]) + (c.omb2 * g2);
-        const float root = sqrtf(vi);
-        const float den = (root / c.bc2s) + c.eps;
-        const float upd = mi / den;
-        const float t = (th[k] * c.dec) - (c.ss * upd);
-        mm[k] = mi;
-        vv[k] = vi;
-        th[k] = t;
-        pb[k] = to_bf16(t);
+        for (int i = 0; i < 4; ++i) {
+            const float gi = pow2 ? g[k][i] * c.invw : g[k][i] / c.fw;
+            const float mi = (c.b1 * m4[i]) + (c.omb1 * gi);
+            const float g2 = gi * gi;
+            const float vi = (c.b2 * v4[i]) + (c.omb2 * g2);
+            const float root = sqrtf(vi);
+            const float den = (root / c.bc2s) + c.eps;
+            const float upd = mi / den;
+            const float t = (t4[i] * c.dec) - (c.ss * upd);
+            m4[i] = mi;
+            v4[i] = vi;
+            t4[i] = t;
+            pb[i] = to_bf16(t);
+        }
+        st4(st + jj, f32x4{t4[0], t4[1], t4[2], t4[3]});
+        st4(st + kTile + jj, f32x4{m4[0], m4[1], m4[2], m4[3]});
+        st4(st + 2 * kTile + jj, f32x4{v4[0], v4[1], v4[2], v4[3]});
+        const u32x2 p = {pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+        if (a.pshard)
+            st2(a.pshard + r.e0 + jj, p);
+        if (a.flat)
+            st2(a.flat + r.fpos + jj, p);
     }
+}
 
-    st_nt(a.master + e, f32x4{th[0], th[1], th[2], th[3]});
-    st_nt(a.master + e + 4, f32x4{th[4], th[5], th[6], th[7]});
-    st_nt(a.m + e, f32x4{mm[0], mm[1], mm[2], mm[3]});
-    st_nt(a.m + e + 4, f32x4{mm[4], mm[5], mm[6], mm[7]});
-    st_nt(a.v + e, f32x4{vv[0], vv[1], vv[2], vv[3]});
-    st_nt(a.v + e + 4, f32x4{vv[4], vv[5], vv[6], vv[7]});
-    const u32x4 p = {pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16),
-                     pb[4] | (pb[5] << 16), pb[6] | (pb[7] << 16)};
-    if (a.pshard)
-        st_nt(a.pshard + e, p);
-    if (a.flat)
-        st_nt(a.flat + (int64_t)q * a.B + (int64_t)a.rank * slice + j, p);
+// ---- layout conversions ------------------------------------------------------
+
+// plain master/m/v -> tiled state; padding positions written as zero
+__global__ __launch_bounds__(kThreads) void state_pack_kernel(
+    const float* __restrict__ master, const float* __restrict__ m,
+    const float* __restrict__ v, float* __restrict__ state, Geom g)
+{
+    TileRef r;
+    if (!tile_of(g, r))
+        return;
+    float* st = state + r.tile * (3 * kTile);
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) {
+        const int jj = unit_off(k);
+        f32x4 a = z, b = z, c = z;
+        if (jj < r.nvalid) {
+            a = ld4(master + r.e0 + jj);
+            if (m) b = ld4(m + r.e0 + jj);
+            if (v) c = ld4(v + r.e0 + jj);
+        }
+        st4(st + jj, a);
+        st4(st + kTile + jj, b);
+        st4(st + 2 * kTile + jj, c);
+    }
+}
+
+// tiled state -> plain master/m/v (each nullable)
+__global__ __launch_bounds__(kThreads) void state_unpack_kernel(
+    const float* __restrict__ state, float* __restrict__ master,
+    float* __restrict__ m, float* __restrict__ v, Geom g)
+{
+    TileRef r;
+    if (!tile_of(g, r))
+        return;
+    const float* st = state + r.tile * (3 * kTile);
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) {
+        const int jj = unit_off(k);
+        if (jj >= r.nvalid)
+            continue;
+        if (master) st4(master + r.e0 + jj, ld4(st + jj));
+        if (m) st4(m + r.e0 + jj, ld4(st + kTile + jj));
+        if (v) st4(v + r.e0 + jj, ld4(st + 2 * kTile + jj));
+    }
+}
+
+// gradient slices [W][stride] -> tiled [tile][W][kTile]; padding zeroed
+__global__ __launch_bounds__(kThreads) void grads_tile_kernel(
+    const uint16_t* __restrict__ slices, int64_t stride,
+    uint16_t* __restrict__ tiled, int32_t W, Geom g)
+{
+    TileRef r;
+    if (!tile_of(g, r))
+        return;
+    uint16_t* dst = tiled + r.tile * (int64_t)W * kTile;
+    const u32x2 z = {0u, 0u};
+#pragma unroll 1
+    for (int s = 0; s < W; ++s) {
+#pragma unroll
+        for (int k = 0; k < kUnits; ++k) {
+            const int jj = unit_off(k);
+            const u32x2 x = jj < r.nvalid
+                ? ld2(slices + (int64_t)s * stride + r.e0 + jj) : z;
+            st2(dst + (int64_t)s * kTile + jj, x);
+        }
+    }
 }
 
 // ---- pack: shard -> flat all-gather buffer ---------------------------------
@@ -228,25 +358,31 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a)
 struct PackFlatArgs {
     const uint16_t* shard;      // at the launch's first bucket
     uint16_t* flat;             // at the launch's first bucket
-    int64_t S, S_last, B;
-    int32_t q_last;
-    int32_t rank;
+    Geom g;
 };
 
 __global__ __launch_bounds__(kThreads) void pack_flat_kernel(PackFlatArgs a)
 {
-    const int32_t q = blockIdx.y;
-    const int64_t slice = (q == a.q_last) ? a.S_last : a.S;
-    const int64_t j = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kGroup;
-    if (j >= slice)
+    TileRef r;
+    if (!tile_of(a.g, r))
         return;
-    const u32x4 x = ld_nt(a.shard + (int64_t)q * a.S + j);
-    st_nt(a.flat + (int64_t)q * a.B + (int64_t)a.rank * slice + j, x);
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) {
+        const int jj = unit_off(k);
+        if (jj < r.nvalid)
+            st2(a.flat + r.fpos + jj, ld2(a.shard + r.e0 + jj));
+    }
 }
 
 // ---- pack: shard -> per-tensor storage through the chunk table -------------
 
-__global__ __launch_bounds__(kThreads) void pack_chunks_kernel(
+constexpr int kPackThreads = 256;
+constexpr int kPackGroup = 8;
+constexpr int64_t kPackTile = kPackThreads * kPackGroup;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kPackThreads) void pack_chunks_kernel(
     const uint16_t* __restrict__ shard, const zs_chunk* __restrict__ chunks,
     int32_t c0, uint16_t* const* __restrict__ tensors)
 {
@@ -256,15 +392,19 @@ __global__ __launch_bounds__(kThreads) void pack_chunks_kernel(
     uint16_t* dst = tensors[ch.tensor_id] + ch.tensor_off;
     const uint16_t* src = shard + ch.shard_off;
     const int64_t n = ch.numel;
-    const int64_t step = (int64_t)gridDim.x * kTile;
+    const int64_t step = (int64_t)gridDim.x * kPackTile;
     const bool vec = ((reinterpret_cast<uintptr_t>(dst) |
                        reinterpret_cast<uintptr_t>(src)) & 15u) == 0;
-    for (int64_t j = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kGroup;
+    for (int64_t j = ((int64_t)blockIdx.x * kPackThreads + threadIdx.x) *
+                     kPackGroup;
          j < n; j += step) {
-        if (vec && j + kGroup <= n) {
-            st_nt(dst + j, ld_nt(src + j));
+        if (vec && j + kPackGroup <= n) {
+            __builtin_nontemporal_store(
+                __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(src + j)),
+                reinterpret_cast<u32x4*>(dst + j));
         } else {
-            const int64_t end = j + kGroup < n ? j + kGroup : n;
+            const int64_t end = j + kPackGroup < n ? j + kPackGroup : n;
             for (int64_t k = j; k < end; ++k)
                 dst[k] = src[k];
         }
@@ -307,59 +447,116 @@ int check_launch(const char* what)
     return ZS_OK;
 }
 
-template <int WT>
-void launch_step_w(const StepArgs& a, dim3 grid, hipStream_t s)
+int64_t tiles_for(int64_t slice)
 {
-    hipLaunchKernelGGL(step_kernel<WT>, grid, dim3(kThreads), 0, s, a);
+    return (slice + kTile - 1) / kTile;
 }
 
-void launch_step(const StepArgs& a, dim3 grid, hipStream_t s)
+// One launch range of the whole shard: buckets [y0, y0 + ny).  Every bucket
+// before the last is full, so bucket y0 starts at element y0*S of the shard
+// and at tile y0*TPB.
+struct Range {
+    int64_t y0, ny;
+    Geom g;
+};
+
+// Calls fn(range) for each chunk of at most kMaxGridY buckets.
+template <class Fn>
+int for_shard_ranges(const zs_layout* L, Fn fn)
+{
+    const int64_t nb = (int64_t)L->buckets.size();
+    Geom g;
+    g.S = L->buckets[0].slice_numel;
+    g.B = L->buckets[0].numel;
+    g.S_last = L->buckets.back().slice_numel;
+    g.TPB = tiles_for(g.S);
+    g.rank = L->rank;
+    for (int64_t y0 = 0; y0 < nb; y0 += kMaxGridY) {
+        Range r;
+        r.y0 = y0;
+        r.ny = nb - y0 < kMaxGridY ? nb - y0 : kMaxGridY;
+        r.g = g;
+        r.g.q_last = (nb - 1 - y0 < r.ny) ? (int32_t)(nb - 1 - y0) : -1;
+        const int rc = fn(r);
+        if (rc) return rc;
+    }
+    return ZS_OK;
+}
+
+Geom bucket_geom(const zs_layout* L, const zs_bucket& b)
+{
+    Geom g;
+    g.S = b.slice_numel;
+    g.S_last = b.slice_numel;
+    g.B = b.numel;
+    g.TPB = tiles_for(b.slice_numel);
+    g.q_last = 0;
+    g.rank = L->rank;
+    return g;
+}
+
+template <int WT>
+void launch_step_w(const StepArgs& a, bool tiled, dim3 grid, hipStream_t s)
+{
+    if (tiled)
+        hipLaunchKernelGGL((step_kernel<WT, true>), grid, dim3(kThreads), 0,
+                           s, a);
+    else
+        hipLaunchKernelGGL((step_kernel<WT, false>), grid, dim3(kThreads), 0,
+                           s, a);
+}
+
+int launch_step(const StepArgs& a, bool tiled, dim3 grid, hipStream_t s)
 {
     switch (a.W) {
-    case 1: launch_step_w<1>(a, grid, s); break;
-    case 2: launch_step_w<2>(a, grid, s); break;
-    case 4: launch_step_w<4>(a, grid, s); break;
-    case 8: launch_step_w<8>(a, grid, s); break;
-    case 16: launch_step_w<16>(a, grid, s); break;
-    case 32: launch_step_w<32>(a, grid, s); break;
-    case 64: launch_step_w<64>(a, grid, s); break;
-    default: launch_step_w<0>(a, grid, s); break;
+    case 1: launch_step_w<1>(a, tiled, grid, s); break;
+    case 2: launch_step_w<2>(a, tiled, grid, s); break;
+    case 4: launch_step_w<4>(a, tiled, grid, s); break;
+    case 8: launch_step_w<8>(a, tiled, grid, s); break;
+    case 16: launch_step_w<16>(a, tiled, grid, s); break;
+    case 32: launch_step_w<32>(a, tiled, grid, s); break;
+    case 64: launch_step_w<64>(a, tiled, grid, s); break;
+    default: launch_step_w<0>(a, tiled, grid, s); break;
     }
+    return check_launch("step kernel");
 }
 
-// Checks shared by zs_step and zs_bucket_step.  `n` is the number of shard
-// elements the call covers; `len` the gradient elements per slice it reads.
+// Checks shared by zs_step and zs_bucket_step.  `len` is the number of
+// gradient elements per slice the call reads.
 int check_step_args(const zs_layout* L, const uint16_t* grads,
-                    int64_t grad_stride, int64_t len, const float* master,
-                    const float* m, const float* v, const uint16_t* pshard,
+                    int32_t grad_layout, int64_t grad_stride, int64_t len,
+                    const float* state, const uint16_t* pshard,
                     const uint16_t* flat, const zs_adamw* hp, int64_t step)
 {
     using zs::fail;
     if (!hp) return fail(ZS_EINVAL, "hp is NULL");
     if (step < 1) return fail(ZS_EINVAL, "step %lld < 1", (long long)step);
-    if (!grads || !master || !m || !v)
-        return fail(ZS_EINVAL, "grads, master, m and v must be non-NULL");
+    if (grad_layout != ZS_GRADS_SLICES && grad_layout != ZS_GRADS_TILED)
+        return fail(ZS_EINVAL, "unknown grad_layout %d", grad_layout);
+    if (!grads || !state)
+        return fail(ZS_EINVAL, "grads and state must be non-NULL");
     if (!pshard && !flat)
         return fail(ZS_EINVAL, "need param_shard or full_flat");
-    if (!aligned16(grads) || !aligned16(master) || !aligned16(m) ||
-        !aligned16(v) || (pshard && !aligned16(pshard)) ||
-        (flat && !aligned16(flat)))
+    if (!aligned16(grads) || !aligned16(state) ||
+        (pshard && !aligned16(pshard)) || (flat && !aligned16(flat)))
         return fail(ZS_EALIGN, "device pointers must be 16-byte aligned");
-    if (grad_stride % kGroup)
-        return fail(ZS_EALIGN, "grad_stride %lld is not a multiple of 8",
-                    (long long)grad_stride);
-    if (grad_stride < len)
-        return fail(ZS_ERANGE, "grad_stride %lld < %lld elements per slice",
-                    (long long)grad_stride, (long long)len);
-    if (grad_stride > INT64_MAX / 2 / L->world)
-        return fail(ZS_ERANGE, "W * grad_stride overflows");
+    if (grad_layout == ZS_GRADS_SLICES) {
+        if (grad_stride % 8)
+            return fail(ZS_EALIGN, "grad_stride %lld is not a multiple of 8",
+                        (long long)grad_stride);
+        if (grad_stride < len)
+            return fail(ZS_ERANGE, "grad_stride %lld < %lld elements per "
+                        "slice", (long long)grad_stride, (long long)len);
+        if (grad_stride > INT64_MAX / 2 / L->world)
+            return fail(ZS_ERANGE, "W * grad_stride overflows");
+    }
     return ZS_OK;
 }
 
 }  // namespace
 
 extern "C" int zs_step(const zs_layout* L, const uint16_t* grads,
-                       int64_t grad_stride, float* master, float* m, float* v,
+                       int32_t grad_layout, int64_t grad_stride, float* state,
                        uint16_t* param_shard, uint16_t* full_flat,
                        const zs_adamw* hp, int64_t step, void* hip_stream)
 {
@@ -369,42 +566,34 @@ extern "C" int zs_step(const zs_layout* L, const uint16_t* grads,
     if (step < 1) return zs::fail(ZS_EINVAL, "step %lld < 1", (long long)step);
     if (L->shard_numel == 0)
         return ZS_OK;
-    int rc = check_step_args(L, grads, grad_stride, L->shard_numel, master, m,
-                             v, param_shard, full_flat, hp, step);
+    int rc = check_step_args(L, grads, grad_layout, grad_stride,
+                             L->shard_numel, state, param_shard, full_flat,
+                             hp, step);
     if (rc) return rc;
-
-    const int64_t nb = (int64_t)L->buckets.size();
+    const bool tiled = grad_layout == ZS_GRADS_TILED;
     const int32_t W = L->world;
-    StepArgs a;
-    a.gstride = grad_stride;
-    a.S = nb > 1 ? L->bucket_elems / W : L->buckets[0].slice_numel;
-    a.S_last = L->buckets.back().slice_numel;
-    a.B = nb > 1 ? L->bucket_elems : L->buckets[0].numel;
-    a.rank = L->rank;
-    a.W = W;
-    a.c = make_consts(*hp, step, W);
+    const Consts c = make_consts(*hp, step, W);
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const unsigned gx = (unsigned)((a.S + kTile - 1) / kTile);
-    for (int64_t y0 = 0; y0 < nb; y0 += kMaxGridY) {
-        const int64_t ny = nb - y0 < kMaxGridY ? nb - y0 : kMaxGridY;
-        const int64_t e0 = L->buckets[y0].shard_off;   // == y0 * S
-        a.grads = grads + e0;
-        a.master = master + e0;
-        a.m = m + e0;
-        a.v = v + e0;
-        a.pshard = param_shard ? param_shard + e0 : nullptr;
-        a.flat = full_flat ? full_flat + L->buckets[y0].flat_off : nullptr;
-        a.q_last = (nb - 1 - y0 < ny) ? (int32_t)(nb - 1 - y0) : -1;
-        launch_step(a, dim3(gx, (unsigned)ny), s);
-        rc = check_launch("step kernel");
-        if (rc) return rc;
-    }
-    return ZS_OK;
+    return for_shard_ranges(L, [&](const Range& R) {
+        const zs_bucket& b0 = L->buckets[R.y0];
+        StepArgs a;
+        a.grads = tiled ? grads + b0.tile_off * W * kTile
+                        : grads + b0.shard_off;
+        a.gstride = grad_stride;
+        a.state = state + b0.tile_off * 3 * kTile;
+        a.pshard = param_shard ? param_shard + b0.shard_off : nullptr;
+        a.flat = full_flat ? full_flat + b0.flat_off : nullptr;
+        a.g = R.g;
+        a.W = W;
+        a.c = c;
+        return launch_step(a, tiled, dim3((unsigned)R.g.TPB, (unsigned)R.ny),
+                           s);
+    });
 }
 
 extern "C" int zs_bucket_step(const zs_layout* L, int32_t bucket_id,
-                              const uint16_t* grads, int64_t grad_stride,
-                              float* master, float* m, float* v,
+                              const uint16_t* grads, int32_t grad_layout,
+                              int64_t grad_stride, float* state,
                               uint16_t* param_shard, uint16_t* full_flat,
                               const zs_adamw* hp, int64_t step,
                               void* hip_stream)
@@ -415,27 +604,118 @@ extern "C" int zs_bucket_step(const zs_layout* L, int32_t bucket_id,
         return zs::fail(ZS_ERANGE, "bucket_id %d outside [0, %d)", bucket_id,
                         (int)L->buckets.size());
     const zs_bucket& b = L->buckets[bucket_id];
-    int rc = check_step_args(L, grads, grad_stride, b.slice_numel, master, m,
-                             v, param_shard, full_flat, hp, step);
+    int rc = check_step_args(L, grads, grad_layout, grad_stride,
+                             b.slice_numel, state, param_shard, full_flat,
+                             hp, step);
     if (rc) return rc;
     StepArgs a;
     a.grads = grads;
     a.gstride = grad_stride;
-    a.master = master + b.shard_off;
-    a.m = m + b.shard_off;
-    a.v = v + b.shard_off;
+    a.state = state + b.tile_off * 3 * kTile;
     a.pshard = param_shard ? param_shard + b.shard_off : nullptr;
     a.flat = full_flat ? full_flat + b.flat_off : nullptr;
-    a.S = b.slice_numel;
-    a.S_last = b.slice_numel;
-    a.B = b.numel;
-    a.q_last = 0;
-    a.rank = L->rank;
+    a.g = bucket_geom(L, b);
     a.W = L->world;
     a.c = make_consts(*hp, step, L->world);
-    const unsigned gx = (unsigned)((b.slice_numel + kTile - 1) / kTile);
-    launch_step(a, dim3(gx, 1), static_cast<hipStream_t>(hip_stream));
-    return check_launch("bucket step kernel");
+    return launch_step(a, grad_layout == ZS_GRADS_TILED,
+                       dim3((unsigned)a.g.TPB, 1),
+                       static_cast<hipStream_t>(hip_stream));
+}
+
+extern "C" int zs_state_pack(const zs_layout* L, const float* master,
+                             const float* m, const float* v, float* state,
+                             void* hip_stream)
+{
+    using zs::fail;
+    zs::clear_error();
+    if (!L) return fail(ZS_EINVAL, "layout is NULL");
+    if (L->shard_numel == 0) return ZS_OK;
+    if (!master || !state)
+        return fail(ZS_EINVAL, "master and state must be non-NULL");
+    if (!aligned16(master) || !aligned16(state) || (m && !aligned16(m)) ||
+        (v && !aligned16(v)))
+        return fail(ZS_EALIGN, "device pointers must be 16-byte aligned");
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    return for_shard_ranges(L, [&](const Range& R) {
+        const zs_bucket& b0 = L->buckets[R.y0];
+        const int64_t e = b0.shard_off;
+        hipLaunchKernelGGL(state_pack_kernel,
+                           dim3((unsigned)R.g.TPB, (unsigned)R.ny),
+                           dim3(kThreads), 0, s, master + e,
+                           m ? m + e : nullptr, v ? v + e : nullptr,
+                           state + b0.tile_off * 3 * kTile, R.g);
+        return check_launch("state pack kernel");
+    });
+}
+
+extern "C" int zs_state_unpack(const zs_layout* L, const float* state,
+                               float* master, float* m, float* v,
+                               void* hip_stream)
+{
+    using zs::fail;
+    zs::clear_error();
+    if (!L) return fail(ZS_EINVAL, "layout is NULL");
+    if (L->shard_numel == 0) return ZS_OK;
+    if (!state) return fail(ZS_EINVAL, "state is NULL");
+    if (!aligned16(state) || (master && !aligned16(master)) ||
+        (m && !aligned16(m)) || (v && !aligned16(v)))
+        return fail(ZS_EALIGN, "device pointers must be 16-byte aligned");
+    if (!master && !m && !v) return ZS_OK;
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    return for_shard_ranges(L, [&](const Range& R) {
+        const zs_bucket& b0 = L->buckets[R.y0];
+        const int64_t e = b0.shard_off;
+        hipLaunchKernelGGL(state_unpack_kernel,
+                           dim3((unsigned)R.g.TPB, (unsigned)R.ny),
+                           dim3(kThreads), 0, s,
+                           state + b0.tile_off * 3 * kTile,
+                           master ? master + e : nullptr,
+                           m ? m + e : nullptr, v ? v + e : nullptr, R.g);
+        return check_launch("state unpack kernel");
+    });
+}
+
+extern "C" int zs_grads_tile(const zs_layout* L, int32_t bucket_id,
+                             const uint16_t* slices, int64_t stride,
+                             uint16_t* tiled, void* hip_stream)
+{
+    using zs::fail;
+    zs::clear_error();
+    if (!L) return fail(ZS_EINVAL, "layout is NULL");
+    if (bucket_id >= (int32_t)L->buckets.size())
+        return fail(ZS_ERANGE, "bucket_id %d outside [0, %d)", bucket_id,
+                    (int)L->buckets.size());
+    if (L->shard_numel == 0) return ZS_OK;
+    if (!slices || !tiled)
+        return fail(ZS_EINVAL, "slices and tiled must be non-NULL");
+    if (!aligned16(slices) || !aligned16(tiled))
+        return fail(ZS_EALIGN, "device pointers must be 16-byte aligned");
+    if (stride % 8)
+        return fail(ZS_EALIGN, "stride %lld is not a multiple of 8",
+                    (long long)stride);
+    const int32_t W = L->world;
+    const int64_t len = bucket_id < 0 ? L->shard_numel
+                                      : L->buckets[bucket_id].slice_numel;
+    if (stride < len)
+        return fail(ZS_ERANGE, "stride %lld < %lld elements per slice",
+                    (long long)stride, (long long)len);
+    if (stride > INT64_MAX / 2 / W)
+        return fail(ZS_ERANGE, "W * stride overflows");
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (bucket_id >= 0) {
+        const Geom g = bucket_geom(L, L->buckets[bucket_id]);
+        hipLaunchKernelGGL(grads_tile_kernel, dim3((unsigned)g.TPB, 1),
+                           dim3(kThreads), 0, s, slices, stride, tiled, W, g);
+        return check_launch("grads tile kernel");
+    }
+    return for_shard_ranges(L, [&](const Range& R) {
+        const zs_bucket& b0 = L->buckets[R.y0];
+        hipLaunchKernelGGL(grads_tile_kernel,
+                           dim3((unsigned)R.g.TPB, (unsigned)R.ny),
+                           dim3(kThreads), 0, s, slices + b0.shard_off,
+                           stride, tiled + b0.tile_off * W * kTile, W, R.g);
+        return check_launch("grads tile kernel");
+    });
 }
 
 extern "C" int zs_pack(const zs_layout* L, const uint16_t* param_shard,
@@ -465,37 +745,32 @@ extern "C" int zs_pack(const zs_layout* L, const uint16_t* param_shard,
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
 
     if (full_flat) {
-        const int64_t nb = (int64_t)L->buckets.size();
-        PackFlatArgs a;
-        a.S = nb > 1 ? L->bucket_elems / L->world : L->buckets[0].slice_numel;
-        a.S_last = L->buckets.back().slice_numel;
-        a.B = nb > 1 ? L->bucket_elems : L->buckets[0].numel;
-        a.rank = L->rank;
-        const unsigned gx = (unsigned)((a.S + kTile - 1) / kTile);
-        for (int64_t y0 = 0; y0 < nb; y0 += kMaxGridY) {
-            const int64_t ny = nb - y0 < kMaxGridY ? nb - y0 : kMaxGridY;
-            a.shard = param_shard + L->buckets[y0].shard_off;
-            a.flat = full_flat + L->buckets[y0].flat_off;
-            a.q_last = (nb - 1 - y0 < ny) ? (int32_t)(nb - 1 - y0) : -1;
-            hipLaunchKernelGGL(pack_flat_kernel, dim3(gx, (unsigned)ny),
+        const int rc = for_shard_ranges(L, [&](const Range& R) {
+            const zs_bucket& b0 = L->buckets[R.y0];
+            PackFlatArgs a;
+            a.shard = param_shard + b0.shard_off;
+            a.flat = full_flat + b0.flat_off;
+            a.g = R.g;
+            hipLaunchKernelGGL(pack_flat_kernel,
+                               dim3((unsigned)R.g.TPB, (unsigned)R.ny),
                                dim3(kThreads), 0, s, a);
-            const int rc = check_launch("pack flat kernel");
-            if (rc) return rc;
-        }
+            return check_launch("pack flat kernel");
+        });
+        if (rc) return rc;
     }
     if (chunk_mode && n_chunks > 0) {
         int64_t longest = 0;
         for (const zs_chunk& c : L->chunks)
             longest = c.numel > longest ? c.numel : longest;
-        int64_t gx = (longest + kTile - 1) / kTile;
+        int64_t gx = (longest + kPackTile - 1) / kPackTile;
         if (gx > 256) gx = 256;
         for (int32_t c0 = 0; c0 < n_chunks; c0 += (int32_t)kMaxGridY) {
             const int32_t ny = n_chunks - c0 < kMaxGridY ? n_chunks - c0
                                                          : (int32_t)kMaxGridY;
             hipLaunchKernelGGL(pack_chunks_kernel,
                                dim3((unsigned)gx, (unsigned)ny),
-                               dim3(kThreads), 0, s, param_shard, dev_chunks,
-                               c0, dev_tensor_ptrs);
+                               dim3(kPackThreads), 0, s, param_shard,
+                               dev_chunks, c0, dev_tensor_ptrs);
             const int rc = check_launch("pack chunks kernel");
             if (rc) return rc;
         }
