@@ -243,6 +243,22 @@ def test_every_world_size(W, layout):
             c.step(t)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("tiles", [300, 700, 1100])
+def test_tile_split_variants(tiles, layout):
+    """Launches with fewer than 1024 tiles split each tile over 2 or 4
+    workgroups: 300 tiles (4 per tile), 700 (2 per tile), 1100 (1 per
+    tile); one bucket per launch, a ragged last tile."""
+    W = 2
+    n_rank = tiles * TILE - 4096            # the last tile half full
+    numels = [W * n_rank - 1000, 1000]
+    say(f"case split tiles={tiles} {layout}")
+    c = Case(numels, W, 1, cap=0, layout=layout)
+    assert c.lay_o.n_tiles == tiles
+    for t in (1, 2):
+        c.step(t)
+
+
 @pytest.mark.parametrize("W", [3, 8])
 def test_all_ranks_reassemble_to_the_unsharded_step(W):
     """all-reduce = reduce-scatter + all-gather on the GPU: every rank steps

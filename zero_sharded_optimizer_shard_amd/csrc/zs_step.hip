@@ -23,7 +23,10 @@
 // of ZS_TILE = 8192 elements of one bucket's slice; each thread owns four
 // 4-element units at stride 512 units, so every load or store instruction of
 // a wave covers one contiguous run (1 KiB of fp32, 512 B of bf16) and the
-// whole workgroup sweeps each stream in one 16-32 KiB burst.  With the tiled
+// whole workgroup sweeps each stream in one 16-32 KiB burst.  A launch with
+// few tiles (one bucket of a streaming step) splits each tile over P = 2 or
+// 4 workgroups of the same shape, each with 4/P units per thread, so that
+// the grid still covers the 256 CUs.  With the tiled
 // state the three 32 KiB rows of a tile are adjacent, and with tiled
 // gradients so are the W 16 KiB slice rows; measured on MI355X, that lifts
 // this 2:1 read/write stream from about 5.4 to about 6.4 TB/s.  All loads of
@@ -50,6 +53,7 @@ constexpr int kThreads = 512;              // 8 waves of 64
 constexpr int kUnits = 4;                  // 4-element units per thread
 constexpr int64_t kTile = ZS_TILE;
 static_assert(kTile == (int64_t)kThreads * kUnits * 4, "tile shape");
+constexpr int kMinBlocks = 1024;           // below this, split tiles
 constexpr int kBatch = 8;                  // gradient slices loaded together
 constexpr int64_t kMaxGridY = 65535;
 
@@ -79,24 +83,31 @@ struct TileRef {
     int64_t fpos;       // launch-relative flat position of the tile start
 };
 
+// P workgroups per tile (blockIdx.x = tile * P + part); P = 1 for the
+// conversions and the pack.
+template <int P = 1>
 __device__ __forceinline__ bool tile_of(const Geom& g, TileRef& r)
 {
     const int32_t q = blockIdx.y;
     const int64_t slice = (q == g.q_last) ? g.S_last : g.S;
-    const int64_t j0 = (int64_t)blockIdx.x * kTile;
+    const int64_t x = blockIdx.x / P;
+    const int64_t j0 = x * kTile;
     if (j0 >= slice)
         return false;
-    r.tile = (int64_t)q * g.TPB + blockIdx.x;
+    r.tile = (int64_t)q * g.TPB + x;
     r.e0 = (int64_t)q * g.S + j0;
     r.nvalid = slice - j0 < kTile ? slice - j0 : kTile;
     r.fpos = (int64_t)q * g.B + (int64_t)g.rank * slice + j0;
     return true;
 }
 
-// element offset of unit k of this thread inside its tile
+// element offset of unit k of this thread inside its tile, for a workgroup
+// that is part `blockIdx.x % P` of P on the tile
+template <int P = 1>
 __device__ __forceinline__ int unit_off(int k)
 {
-    return 4 * (k * kThreads + (int)threadIdx.x);
+    const int part = (int)(blockIdx.x % P);
+    return part * (int)(kTile / P) + 4 * (k * kThreads + (int)threadIdx.x);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t u)
@@ -153,16 +164,16 @@ struct StepArgs {
 // Slices s0 .. s0+n-1 (n <= NB) of every unit: all loads first, then the
 // adds in rank order.  Slice 0 initialises the sum, so the sign of a zero
 // sum is that of the first addend, as in a left-to-right sum.
-template <int NB>
+template <int NB, int U, int P>
 __device__ __forceinline__ void reduce_batch(const uint16_t* __restrict__ g0,
                                              int64_t gs, int s0, int n,
                                              bool full, int64_t nvalid,
-                                             float (&acc)[kUnits][4])
+                                             float (&acc)[U][4])
 {
-    u32x2 x[kUnits][NB];
+    u32x2 x[U][NB];
 #pragma unroll
-    for (int k = 0; k < kUnits; ++k) {
-        const int jj = unit_off(k);
+    for (int k = 0; k < U; ++k) {
+        const int jj = unit_off<P>(k);
         if (full || jj < nvalid) {
 #pragma unroll
             for (int i = 0; i < NB; ++i)
@@ -171,8 +182,8 @@ __device__ __forceinline__ void reduce_batch(const uint16_t* __restrict__ g0,
         }
     }
 #pragma unroll
-    for (int k = 0; k < kUnits; ++k) {
-        const int jj = unit_off(k);
+    for (int k = 0; k < U; ++k) {
+        const int jj = unit_off<P>(k);
         if (!(full || jj < nvalid))
             continue;
 #pragma unroll
@@ -196,34 +207,36 @@ __device__ __forceinline__ void reduce_batch(const uint16_t* __restrict__ g0,
 }
 
 // WT > 0: W known at compile time; WT == 0: runtime W.
-template <int WT>
+template <int WT, int U, int P>
 __device__ __forceinline__ void reduce(const uint16_t* __restrict__ g0,
                                        int64_t gs, int W, bool full,
-                                       int64_t nvalid,
-                                       float (&acc)[kUnits][4])
+                                       int64_t nvalid, float (&acc)[U][4])
 {
     if constexpr (WT > 0 && WT <= kBatch) {
-        reduce_batch<WT>(g0, gs, 0, WT, full, nvalid, acc);
+        reduce_batch<WT, U, P>(g0, gs, 0, WT, full, nvalid, acc);
     } else if constexpr (WT > 0) {
         static_assert(WT % kBatch == 0, "compiled W above 8 must be a "
                       "multiple of 8");
 #pragma unroll
         for (int s0 = 0; s0 < WT; s0 += kBatch)
-            reduce_batch<kBatch>(g0, gs, s0, kBatch, full, nvalid, acc);
+            reduce_batch<kBatch, U, P>(g0, gs, s0, kBatch, full, nvalid,
+                                       acc);
     } else {
 #pragma unroll 1
         for (int s0 = 0; s0 < W; s0 += kBatch) {
             const int n = W - s0 < kBatch ? W - s0 : kBatch;
-            reduce_batch<kBatch>(g0, gs, s0, n, full, nvalid, acc);
+            reduce_batch<kBatch, U, P>(g0, gs, s0, n, full, nvalid, acc);
         }
     }
 }
 
-template <int WT, bool TILED>
+// P workgroups per tile, each with U = 4/P units per thread
+template <int WT, bool TILED, int P>
 __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a)
 {
+    constexpr int U = kUnits / P;
     TileRef r;
-    if (!tile_of(a.g, r))
+    if (!tile_of<P>(a.g, r))
         return;
     const int W = WT > 0 ? WT : a.W;
     const bool full = r.nvalid == kTile;
@@ -233,10 +246,10 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a)
     const int64_t gs = TILED ? kTile : a.gstride;
 
     // fp32 state first: its loads do not depend on the gradients
-    f32x4 th[kUnits], mm[kUnits], vv[kUnits];
+    f32x4 th[U], mm[U], vv[U];
 #pragma unroll
-    for (int k = 0; k < kUnits; ++k) {
-        const int jj = unit_off(k);
+    for (int k = 0; k < U; ++k) {
+        const int jj = unit_off<P>(k);
         if (full || jj < r.nvalid) {
             th[k] = ld4(st + jj);
             mm[k] = ld4(st + kTile + jj);
@@ -244,14 +257,14 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a)
         }
     }
 
-    float g[kUnits][4];
-    reduce<WT>(g0, gs, W, full, r.nvalid, g);
+    float g[U][4];
+    reduce<WT, U, P>(g0, gs, W, full, r.nvalid, g);
 
     const Consts c = a.c;
     const bool pow2 = WT > 0 ? ((WT & (WT - 1)) == 0) : (c.pow2 != 0);
 #pragma unroll
-    for (int k = 0; k < kUnits; ++k) {
-        const int jj = unit_off(k);
+    for (int k = 0; k < U; ++k) {
+        const int jj = unit_off<P>(k);
         if (!(full || jj < r.nvalid))
             continue;
         float t4[4] = {th[k].x, th[k].y, th[k].z, th[k].w};
@@ -495,15 +508,30 @@ Geom bucket_geom(const zs_layout* L, const zs_bucket& b)
     return g;
 }
 
+template <int WT, int P>
+void launch_step_wp(const StepArgs& a, bool tiled, dim3 grid, hipStream_t s)
+{
+    grid.x *= P;
+    if (tiled)
+        hipLaunchKernelGGL((step_kernel<WT, true, P>), grid, dim3(kThreads),
+                           0, s, a);
+    else
+        hipLaunchKernelGGL((step_kernel<WT, false, P>), grid, dim3(kThreads),
+                           0, s, a);
+}
+
+// grid: one x per tile; tiles are split over 2 or 4 workgroups when the
+// launch has fewer than kMinBlocks tiles
 template <int WT>
 void launch_step_w(const StepArgs& a, bool tiled, dim3 grid, hipStream_t s)
 {
-    if (tiled)
-        hipLaunchKernelGGL((step_kernel<WT, true>), grid, dim3(kThreads), 0,
-                           s, a);
+    const int64_t blocks = (int64_t)grid.x * grid.y;
+    if (blocks >= kMinBlocks)
+        launch_step_wp<WT, 1>(a, tiled, grid, s);
+    else if (2 * blocks >= kMinBlocks)
+        launch_step_wp<WT, 2>(a, tiled, grid, s);
     else
-        hipLaunchKernelGGL((step_kernel<WT, false>), grid, dim3(kThreads), 0,
-                           s, a);
+        launch_step_wp<WT, 4>(a, tiled, grid, s);
 }
 
 int launch_step(const StepArgs& a, bool tiled, dim3 grid, hipStream_t s)
