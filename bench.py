@@ -132,9 +132,9 @@ def time_steps(fn, K, st):
 def stream_main(args, w):
     """ZeRO-2 streaming: the W slices of each 25 MiB bucket arrive one bucket
     at a time, last bucket first (the order backward fills them), into a ring
-    of staging slots on an upload stream; the step stream runs
-    zs_bucket_step on each bucket as soon as it has landed, and the upload
-    stream reuses a slot only after the step that read it.  Arrival is a
+    of 2G staging slots on an upload stream; the step stream runs
+    zs_buckets_step on every G landed buckets, and the upload stream reuses a
+    slot only after the step that read it.  Arrival is a
     host-to-device copy from a pinned pool of 4 distinct buckets (bucket b
     uses pool b mod 4), or a device copy from an HBM pool (--arrival d2d).
     Reported per full step (every bucket once): the wall time, the same
@@ -150,7 +150,7 @@ def stream_main(args, w):
     n_tiles = zs.zs_layout_tiles(lay)
     B = zs.zs_layout_buckets(lay)
     log(f"workload {w.name} streaming: W={W} shard={n} buckets={nb} "
-        f"tiles={n_tiles} arrival={args.arrival} slots={args.slots}")
+        f"tiles={n_tiles} arrival={args.arrival} group={args.group}")
     state = torch.empty(n_tiles * 3 * T, dtype=torch.float32, device="cuda")
     master = torch.empty(n, dtype=torch.float32, device="cuda")
     synth.dev_normal_f32(master, 0, synth.TAG_MASTER, 0, 0, 0, w.master_sigma)
@@ -181,8 +181,10 @@ def stream_main(args, w):
         del pool_d
     else:
         pool = pool_d
+    G = max(1, min(args.group, zs.ZS_MAX_GROUP))
+    slots = 2 * G
     staging = [torch.empty(slot_elems, dtype=torch.bfloat16, device="cuda")
-               for _ in range(args.slots)]
+               for _ in range(slots)]
     torch.cuda.synchronize()
     log("inputs resident")
     up = torch.cuda.Stream()
@@ -192,29 +194,38 @@ def stream_main(args, w):
     t_step = 0
 
     def full_step(do_upload=True, do_step=True):
+        """Every bucket once: arrival k lands in slot k mod 2G; after each G
+        arrivals one zs_buckets_step steps them, on the step stream, once
+        the last of them has landed (the upload stream is in order)."""
         nonlocal t_step
         t_step += 1
-        done = [None] * args.slots
-        for k, b in enumerate(order):
-            slot = k % args.slots
+        done = [None] * slots
+        for g0 in range(0, nb, G):
+            ids = order[g0:g0 + G]
+            sl = [(g0 + i) % slots for i in range(len(ids))]
             landed = None
             if do_upload:
                 with torch.cuda.stream(up):
-                    if done[slot] is not None:
-                        up.wait_event(done[slot])
-                    staging[slot][:cnt[b]].copy_(pool[b % 4][:cnt[b]],
-                                                 non_blocking=True)
+                    waited = set()
+                    for b, k in zip(ids, sl):
+                        ev = done[k]
+                        if ev is not None and id(ev) not in waited:
+                            up.wait_event(ev)
+                            waited.add(id(ev))
+                        staging[k][:cnt[b]].copy_(pool[b % 4][:cnt[b]],
+                                                  non_blocking=True)
                     landed = torch.cuda.Event()
                     landed.record(up)
             if do_step:
                 if landed is not None:
                     st.wait_event(landed)
-                zs.zs_bucket_step(lay, b, staging[slot], state, None, flat,
-                                  grad_layout="tiled", step=t_step,
-                                  stream=st, **HP)
+                zs.zs_buckets_step(lay, ids, [staging[k] for k in sl], state,
+                                   None, flat, grad_layout="tiled",
+                                   step=t_step, stream=st, **HP)
                 ev = torch.cuda.Event()
                 ev.record(st)
-                done[slot] = ev
+                for k in sl:
+                    done[k] = ev
 
     K = min(args.steps, w.steps)            # full steps are long here
 
@@ -263,7 +274,7 @@ def stream_main(args, w):
                    "params_total": sum(w.numels), "shard_params": n,
                    "buckets": nb, "bucket_cap_mb": 25,
                    "bytes_per_param": bpp, "arrival": args.arrival,
-                   "staging_slots": args.slots,
+                   "buckets_per_launch": G, "staging_slots": slots,
                    "grads_layout": "tiled [tile][W][8192]"},
         "roofline": {"bound": "hbm", "achieved": kern_gbs,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -275,7 +286,8 @@ def stream_main(args, w):
                       "exposed_step_ms": wall_ms - up_ms,
                       "arrival_bytes_per_step": arrival_bytes,
                       "arrival_GBps": arrival_bytes / (up_ms * 1e-3) / 1e9,
-                      "per_bucket_kernel_us": kern_ev_ms * 1e3 / nb},
+                      "per_bucket_kernel_us": kern_ev_ms * 1e3 / nb,
+                      "launches_per_step": -(-nb // G)},
     }
     print(json.dumps(out), flush=True)
 
@@ -292,8 +304,9 @@ def main():
     ap.add_argument("--arrival", default="h2d", choices=["h2d", "d2d"],
                     help="streaming mode: buckets arrive from pinned host "
                     "memory (h2d) or from an HBM pool (d2d)")
-    ap.add_argument("--slots", type=int, default=3,
-                    help="streaming mode: staging slots in the ring")
+    ap.add_argument("--group", type=int, default=8,
+                    help="streaming mode: landed buckets stepped per launch "
+                    "(zs_buckets_step); the ring holds 2*group slots")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ceiling", action="store_true",

@@ -215,6 +215,22 @@ int zs_bucket_step(const zs_layout* layout, int32_t bucket_id,
                    uint16_t* full_flat, const zs_adamw* hp, int64_t step,
                    void* hip_stream);
 
+/* Up to ZS_MAX_GROUP buckets in one launch: the bucket steps of the
+ * streaming mode, batched when several buckets have landed, so that launch
+ * and synchronisation costs are paid once per group.  Member i is bucket
+ * bucket_ids[i] (all distinct) with its own staging buffer grads[i], laid
+ * out as zs_bucket_step takes it; bucket_ids and grads are HOST arrays of
+ * count entries, read during the call.  The result equals count
+ * zs_bucket_step calls.  Errors: ZS_EINVAL for count outside
+ * [1, ZS_MAX_GROUP], a repeated bucket or NULL arrays; otherwise as
+ * zs_bucket_step, checked per member. */
+#define ZS_MAX_GROUP 16
+int zs_buckets_step(const zs_layout* layout, int32_t count,
+                    const int32_t* bucket_ids, const uint16_t* const* grads,
+                    int32_t grad_layout, int64_t grad_stride, float* state,
+                    uint16_t* param_shard, uint16_t* full_flat,
+                    const zs_adamw* hp, int64_t step, void* hip_stream);
+
 /* Plain [shard_numel] fp32 master / m / v -> tiled state [n_tiles][3]
  * [ZS_TILE].  m or v may be NULL: that row is set to zero (a fresh
  * optimizer).  Padding positions of the tiles are set to zero.  master must

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     L = zs.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -158,6 +158,23 @@ def test_step_argument_checks_need_no_device():
                             ctypes.byref(hp), 1, None) == -3
     assert L.zs_bucket_step(h, 0, A, 7, shard, A, A, None,
                             ctypes.byref(hp), 1, None) == -1
+    # bucket groups
+    I32, P_ = ctypes.c_int32, ctypes.c_void_p
+    ids = (I32 * 2)(0, 0)
+    ptrs = (P_ * 2)(A, A)
+    one = (I32 * 1)(0)
+
+    def grp(count, i=one, g=ptrs, gs=shard):
+        return L.zs_buckets_step(h, count, i, g, 0, gs, A, A, None,
+                                 ctypes.byref(hp), 1, None)
+    assert grp(0) == -1
+    assert grp(17) == -1
+    assert grp(2, ids) == -1                        # bucket 0 twice
+    assert grp(1, (I32 * 1)(1)) == -3               # tiny has one bucket
+    assert grp(1, None) == -1
+    assert grp(1, one, None) == -1
+    assert grp(1, one, (P_ * 1)(A + 2)) == -2
+    assert grp(1, one, ptrs, shard - 8) == -3
     # layout conversions
     assert L.zs_state_pack(h, None, A, A, A, None) == -1
     assert L.zs_state_pack(h, A, A, A, None, None) == -1

@@ -382,6 +382,70 @@ def test_bucket_steps_in_any_order_equal_the_whole_step(layout):
         assert np.array_equal(got[1], want[1])
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("W,cap,groups", [
+    (8, 25 << 20, [3, 1, 4, 2]),                 # GPT-2-shaped, 10 buckets
+    (4, 4 * 256 * 8, [16, 16, 7, 1, 5]),         # 45 small buckets
+])
+def test_bucket_groups_equal_the_whole_step(W, cap, groups, layout):
+    """zs_buckets_step over groups of buckets in a shuffled order, each
+    bucket from its own staging buffer, equals zs_step bit for bit."""
+    numels = wl.gpt2_small() if W == 8 else [50000, 7, 129, 90000, 40000]
+    lay_o = build_layout(numels, W, W - 1, cap)
+    lay = zs.zs_layout_build(numels, W, W - 1, cap)
+    assert sum(groups) == len(lay_o.buckets)
+    n = lay_o.shard_numel
+    say(f"case groups W={W} buckets={len(lay_o.buckets)} {groups} {layout}")
+    ref = Case(numels, W, W - 1, cap=cap)
+    assert ref.pad                       # the last rank holds the padding
+    state = dev_state(lay, lay_o, 0.02, pad=ref.pad)
+    p = dev_bf16(n)
+    full = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
+    full_t = dev_bf16(lay_o.n_tiles * W * TILE)
+    order = list(range(len(lay_o.buckets)))
+    random.Random(W).shuffle(order)
+    for t in (1, 2):
+        ref.step(t, check=False)
+        S.dev_grads(full, W, n, t, 1e-3, pad=ref.pad)
+        zs.zs_grads_tile(lay, -1, full, n, full_t)
+        k = 0
+        for gsize in groups:
+            ids = order[k:k + gsize]
+            k += gsize
+            stg = []
+            for b_id in ids:
+                b = lay_o.buckets[b_id]
+                if layout == "tiled":
+                    lo = b.tile_off * W * TILE
+                    cnt = -(-b.slice_numel // TILE) * W * TILE
+                    stg.append(full_t[lo:lo + cnt].clone())
+                else:
+                    stg.append(full[:, b.shard_off:b.shard_off
+                                    + b.slice_numel].contiguous())
+            stride = max(lay_o.buckets[b].slice_numel for b in ids)
+            if layout == "slices":
+                # one common stride for the group: pad every staging row
+                padded = []
+                for x in stg:
+                    y = torch.empty((W, stride), dtype=torch.bfloat16,
+                                    device="cuda")
+                    y[:, :x.shape[1]] = x
+                    padded.append(y)
+                stg = padded
+            zs.zs_buckets_step(lay, ids, stg, state, p, None,
+                               grad_layout=layout, grad_stride=stride,
+                               step=t, **HP)
+        torch.cuda.synchronize()
+        slot_idx = tile_slot(lay_o)
+        g3 = npf(state).reshape(-1, 3, TILE)
+        w3 = npf(ref.state).reshape(-1, 3, TILE)
+        for row in range(3):
+            a_ = g3[:, row, :].reshape(-1)[slot_idx]
+            b_ = w3[:, row, :].reshape(-1)[slot_idx]
+            assert np.array_equal(a_.view(np.uint32), b_.view(np.uint32))
+        assert np.array_equal(np16(p), np16(ref.p))
+
+
 def test_pack_flat_and_per_tensor():
     w = wl.presets()["gpt2"]
     for rank in (0, 5, 7):

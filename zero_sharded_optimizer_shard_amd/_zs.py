@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libzs.so")
 ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ERANGE, ZS_ENOMEM, ZS_EDEVICE = \
     0, -1, -2, -3, -4, -5
 ZS_TILE = 8192
+ZS_MAX_GROUP = 16
 ZS_GRADS_SLICES, ZS_GRADS_TILED = 0, 1
 
 
@@ -48,7 +49,8 @@ _lib = None
 EXPORTS = ["zs_layout_build", "zs_layout_info", "zs_layout_tiles",
            "zs_layout_buckets", "zs_layout_chunks",
            "zs_layout_tensor_offsets", "zs_layout_rank", "zs_layout_free",
-           "zs_step", "zs_bucket_step", "zs_state_pack", "zs_state_unpack",
+           "zs_step", "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
+           "zs_state_unpack",
            "zs_grads_tile", "zs_pack", "zs_strerror", "zs_last_error"]
 
 
@@ -76,6 +78,8 @@ def lib():
     L.zs_step.argtypes = [p, p, i32, i64, p, p, p, P(zs_adamw), i64, p]
     L.zs_bucket_step.argtypes = [p, i32, p, i32, i64, p, p, p, P(zs_adamw),
                                  i64, p]
+    L.zs_buckets_step.argtypes = [p, i32, P(i32), P(p), i32, i64, p, p, p,
+                                  P(zs_adamw), i64, p]
     L.zs_state_pack.argtypes = [p, p, p, p, p, p]
     L.zs_state_unpack.argtypes = [p, p, p, p, p, p]
     L.zs_grads_tile.argtypes = [p, i32, p, i64, p, p]
@@ -87,7 +91,8 @@ def lib():
     for name in ("zs_layout_build", "zs_layout_info", "zs_layout_tiles",
                  "zs_layout_buckets", "zs_layout_chunks",
                  "zs_layout_tensor_offsets", "zs_layout_rank", "zs_step",
-                 "zs_bucket_step", "zs_state_pack", "zs_state_unpack",
+                 "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
+                 "zs_state_unpack",
                  "zs_grads_tile", "zs_pack"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -262,6 +267,28 @@ def zs_bucket_step(layout: Layout, bucket_id: int, grads, state,
                                 _bf16(full_flat, "full_flat"),
                                 ctypes.byref(hp), step, _stream(stream)),
            "zs_bucket_step")
+
+
+def zs_buckets_step(layout: Layout, bucket_ids, grads, state,
+                    param_shard=None, full_flat=None, *,
+                    grad_layout="slices", grad_stride: int = 0, lr: float,
+                    beta1: float, beta2: float, eps: float,
+                    weight_decay: float, step: int, stream=None) -> None:
+    """bucket_ids: sequence of bucket ids; grads: one staging tensor per
+    bucket, in the same order."""
+    n = len(bucket_ids)
+    if len(grads) != n:
+        raise ValueError("one staging tensor per bucket")
+    ids = (ctypes.c_int32 * max(n, 1))(*bucket_ids)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[_bf16(g, "grads") for g in grads])
+    hp = _hp(lr, beta1, beta2, eps, weight_decay)
+    _check(lib().zs_buckets_step(layout.handle, n, ids, ptrs,
+                                 _layout_code(grad_layout), grad_stride,
+                                 _f32(state, "state"),
+                                 _bf16(param_shard, "param_shard"),
+                                 _bf16(full_flat, "full_flat"),
+                                 ctypes.byref(hp), step, _stream(stream)),
+           "zs_buckets_step")
 
 
 def zs_state_pack(layout: Layout, master, m, v, state, stream=None) -> None:

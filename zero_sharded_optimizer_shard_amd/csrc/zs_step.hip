@@ -41,6 +41,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "zs_internal.h"
 
@@ -230,27 +231,28 @@ __device__ __forceinline__ void reduce(const uint16_t* __restrict__ g0,
     }
 }
 
-// P workgroups per tile, each with U = 4/P units per thread
-template <int WT, bool TILED, int P>
-__global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a)
+// One tile of the step, with every pointer already at the tile: g0 the
+// first gradient value of slice 0 (tiled: the tile's W rows, gs = ZS_TILE;
+// slices: gs = the slice stride), st the tile's state rows, ps / fl the
+// tile's first bf16 output (each nullable).  This workgroup is part
+// blockIdx.x % P of P on the tile, with U = 4/P units per thread.
+template <int WT, int P>
+__device__ __forceinline__ void step_tile(const uint16_t* __restrict__ g0,
+                                          int64_t gs, float* __restrict__ st,
+                                          uint16_t* __restrict__ ps,
+                                          uint16_t* __restrict__ fl,
+                                          int64_t nvalid, int W,
+                                          const Consts& c)
 {
     constexpr int U = kUnits / P;
-    TileRef r;
-    if (!tile_of<P>(a.g, r))
-        return;
-    const int W = WT > 0 ? WT : a.W;
-    const bool full = r.nvalid == kTile;
-    float* st = a.state + r.tile * (3 * kTile);
-    const uint16_t* g0 = TILED ? a.grads + r.tile * (int64_t)W * kTile
-                               : a.grads + r.e0;
-    const int64_t gs = TILED ? kTile : a.gstride;
+    const bool full = nvalid == kTile;
 
     // fp32 state first: its loads do not depend on the gradients
     f32x4 th[U], mm[U], vv[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         const int jj = unit_off<P>(k);
-        if (full || jj < r.nvalid) {
+        if (full || jj < nvalid) {
             th[k] = ld4(st + jj);
             mm[k] = ld4(st + kTile + jj);
             vv[k] = ld4(st + 2 * kTile + jj);
@@ -258,14 +260,13 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a)
     }
 
     float g[U][4];
-    reduce<WT, U, P>(g0, gs, W, full, r.nvalid, g);
+    reduce<WT, U, P>(g0, gs, W, full, nvalid, g);
 
-    const Consts c = a.c;
     const bool pow2 = WT > 0 ? ((WT & (WT - 1)) == 0) : (c.pow2 != 0);
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         const int jj = unit_off<P>(k);
-        if (!(full || jj < r.nvalid))
+        if (!(full || jj < nvalid))
             continue;
         float t4[4] = {th[k].x, th[k].y, th[k].z, th[k].w};
         float m4[4] = {mm[k].x, mm[k].y, mm[k].z, mm[k].w};
@@ -290,11 +291,63 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a)
         st4(st + kTile + jj, f32x4{m4[0], m4[1], m4[2], m4[3]});
         st4(st + 2 * kTile + jj, f32x4{v4[0], v4[1], v4[2], v4[3]});
         const u32x2 p = {pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
-        if (a.pshard)
-            st2(a.pshard + r.e0 + jj, p);
-        if (a.flat)
-            st2(a.flat + r.fpos + jj, p);
+        if (ps)
+            st2(ps + jj, p);
+        if (fl)
+            st2(fl + jj, p);
     }
+}
+
+// Whole-shard step: blockIdx.y = bucket, blockIdx.x = tile * P + part.
+template <int WT, bool TILED, int P>
+__global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a)
+{
+    TileRef r;
+    if (!tile_of<P>(a.g, r))
+        return;
+    const int W = WT > 0 ? WT : a.W;
+    const uint16_t* g0 = TILED ? a.grads + r.tile * (int64_t)W * kTile
+                               : a.grads + r.e0;
+    step_tile<WT, P>(g0, TILED ? kTile : a.gstride,
+                     a.state + r.tile * (3 * kTile),
+                     a.pshard ? a.pshard + r.e0 : nullptr,
+                     a.flat ? a.flat + r.fpos : nullptr, r.nvalid, W, a.c);
+}
+
+// A group of buckets, each from its own staging buffer: blockIdx.y = member,
+// blockIdx.x = tile * P + part of that member's slice.
+constexpr int kMaxGroup = ZS_MAX_GROUP;
+
+struct GroupMember {
+    const uint16_t* grads;      // this bucket's staging
+    float* state;               // state at the bucket's first tile
+    uint16_t* pshard;           // nullable, at the bucket's first element
+    uint16_t* flat;             // nullable, at this rank's slice of it
+    int64_t slice;              // slice_numel
+};
+
+struct GroupArgs {
+    GroupMember mb[kMaxGroup];
+    int64_t gstride;
+    int32_t W;
+    Consts c;
+};
+
+template <int WT, bool TILED, int P>
+__global__ __launch_bounds__(kThreads) void group_step_kernel(GroupArgs a)
+{
+    const GroupMember& mb = a.mb[blockIdx.y];
+    const int64_t x = blockIdx.x / P;
+    const int64_t j0 = x * kTile;
+    if (j0 >= mb.slice)
+        return;
+    const int W = WT > 0 ? WT : a.W;
+    const int64_t nvalid = mb.slice - j0 < kTile ? mb.slice - j0 : kTile;
+    const uint16_t* g0 = TILED ? mb.grads + x * (int64_t)W * kTile
+                               : mb.grads + j0;
+    step_tile<WT, P>(g0, TILED ? kTile : a.gstride, mb.state + x * 3 * kTile,
+                     mb.pshard ? mb.pshard + j0 : nullptr,
+                     mb.flat ? mb.flat + j0 : nullptr, nvalid, W, a.c);
 }
 
 // ---- layout conversions ------------------------------------------------------
@@ -508,22 +561,32 @@ Geom bucket_geom(const zs_layout* L, const zs_bucket& b)
     return g;
 }
 
-template <int WT, int P>
-void launch_step_wp(const StepArgs& a, bool tiled, dim3 grid, hipStream_t s)
+// Kernel choice: Args = StepArgs (whole shard) or GroupArgs (buckets).
+template <int WT, bool TILED, int P, class Args>
+void launch_kernel(const Args& a, dim3 grid, hipStream_t s)
+{
+    if constexpr (std::is_same<Args, StepArgs>::value)
+        hipLaunchKernelGGL((step_kernel<WT, TILED, P>), grid, dim3(kThreads),
+                           0, s, a);
+    else
+        hipLaunchKernelGGL((group_step_kernel<WT, TILED, P>), grid,
+                           dim3(kThreads), 0, s, a);
+}
+
+template <int WT, int P, class Args>
+void launch_step_wp(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 {
     grid.x *= P;
     if (tiled)
-        hipLaunchKernelGGL((step_kernel<WT, true, P>), grid, dim3(kThreads),
-                           0, s, a);
+        launch_kernel<WT, true, P>(a, grid, s);
     else
-        hipLaunchKernelGGL((step_kernel<WT, false, P>), grid, dim3(kThreads),
-                           0, s, a);
+        launch_kernel<WT, false, P>(a, grid, s);
 }
 
 // grid: one x per tile; tiles are split over 2 or 4 workgroups when the
 // launch has fewer than kMinBlocks tiles
-template <int WT>
-void launch_step_w(const StepArgs& a, bool tiled, dim3 grid, hipStream_t s)
+template <int WT, class Args>
+void launch_step_w(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 {
     const int64_t blocks = (int64_t)grid.x * grid.y;
     if (blocks >= kMinBlocks)
@@ -534,7 +597,8 @@ void launch_step_w(const StepArgs& a, bool tiled, dim3 grid, hipStream_t s)
         launch_step_wp<WT, 4>(a, tiled, grid, s);
 }
 
-int launch_step(const StepArgs& a, bool tiled, dim3 grid, hipStream_t s)
+template <class Args>
+int launch_step(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 {
     switch (a.W) {
     case 1: launch_step_w<1>(a, tiled, grid, s); break;
@@ -619,6 +683,58 @@ extern "C" int zs_step(const zs_layout* L, const uint16_t* grads,
     });
 }
 
+extern "C" int zs_buckets_step(const zs_layout* L, int32_t count,
+                               const int32_t* bucket_ids,
+                               const uint16_t* const* grads,
+                               int32_t grad_layout, int64_t grad_stride,
+                               float* state, uint16_t* param_shard,
+                               uint16_t* full_flat, const zs_adamw* hp,
+                               int64_t step, void* hip_stream)
+{
+    using zs::fail;
+    zs::clear_error();
+    if (!L) return fail(ZS_EINVAL, "layout is NULL");
+    if (count < 1 || count > kMaxGroup)
+        return fail(ZS_EINVAL, "count %d outside [1, %d]", count, kMaxGroup);
+    if (!bucket_ids || !grads)
+        return fail(ZS_EINVAL, "bucket_ids and grads must be non-NULL");
+    const int32_t nb = (int32_t)L->buckets.size();
+    int64_t longest = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const int32_t b = bucket_ids[i];
+        if (b < 0 || b >= nb)
+            return fail(ZS_ERANGE, "bucket_ids[%d] = %d outside [0, %d)", i,
+                        b, nb);
+        for (int32_t k = 0; k < i; ++k)
+            if (bucket_ids[k] == b)
+                return fail(ZS_EINVAL, "bucket %d appears twice", b);
+        const int64_t sl = L->buckets[b].slice_numel;
+        longest = sl > longest ? sl : longest;
+        const int rc = check_step_args(L, grads[i], grad_layout, grad_stride,
+                                       sl, state, param_shard, full_flat, hp,
+                                       step);
+        if (rc) return rc;
+    }
+    GroupArgs a;
+    for (int32_t i = 0; i < count; ++i) {
+        const zs_bucket& b = L->buckets[bucket_ids[i]];
+        GroupMember& mb = a.mb[i];
+        mb.grads = grads[i];
+        mb.state = state + b.tile_off * 3 * kTile;
+        mb.pshard = param_shard ? param_shard + b.shard_off : nullptr;
+        mb.flat = full_flat ? full_flat + b.flat_off +
+                                  (int64_t)L->rank * b.slice_numel
+                            : nullptr;
+        mb.slice = b.slice_numel;
+    }
+    a.gstride = grad_stride;
+    a.W = L->world;
+    a.c = make_consts(*hp, step, L->world);
+    return launch_step(a, grad_layout == ZS_GRADS_TILED,
+                       dim3((unsigned)tiles_for(longest), (unsigned)count),
+                       static_cast<hipStream_t>(hip_stream));
+}
+
 extern "C" int zs_bucket_step(const zs_layout* L, int32_t bucket_id,
                               const uint16_t* grads, int32_t grad_layout,
                               int64_t grad_stride, float* state,
@@ -631,23 +747,9 @@ extern "C" int zs_bucket_step(const zs_layout* L, int32_t bucket_id,
     if (bucket_id < 0 || bucket_id >= (int32_t)L->buckets.size())
         return zs::fail(ZS_ERANGE, "bucket_id %d outside [0, %d)", bucket_id,
                         (int)L->buckets.size());
-    const zs_bucket& b = L->buckets[bucket_id];
-    int rc = check_step_args(L, grads, grad_layout, grad_stride,
-                             b.slice_numel, state, param_shard, full_flat,
-                             hp, step);
-    if (rc) return rc;
-    StepArgs a;
-    a.grads = grads;
-    a.gstride = grad_stride;
-    a.state = state + b.tile_off * 3 * kTile;
-    a.pshard = param_shard ? param_shard + b.shard_off : nullptr;
-    a.flat = full_flat ? full_flat + b.flat_off : nullptr;
-    a.g = bucket_geom(L, b);
-    a.W = L->world;
-    a.c = make_consts(*hp, step, L->world);
-    return launch_step(a, grad_layout == ZS_GRADS_TILED,
-                       dim3((unsigned)a.g.TPB, 1),
-                       static_cast<hipStream_t>(hip_stream));
+    return zs_buckets_step(L, 1, &bucket_id, &grads, grad_layout,
+                           grad_stride, state, param_shard, full_flat, hp,
+                           step, hip_stream);
 }
 
 extern "C" int zs_state_pack(const zs_layout* L, const float* master,
