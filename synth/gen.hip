@@ -182,7 +182,7 @@ extern "C" int synth_copy_dev(void* dst, const void* src, int64_t nbytes,
  * into the flat buffer at the rank-0 position of the bucket. */
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-template <int WT>
+template <int WT, int NB>
 __global__ __launch_bounds__(512) void k_mix_stream(
     const u32x2* __restrict__ grads, u32x4* __restrict__ state,
     u32x2* __restrict__ flat, int Wrt, int64_t S, int64_t S_last, int64_t B,
@@ -211,14 +211,14 @@ __global__ __launch_bounds__(512) void k_mix_stream(
         }
         x[k] = u32x2{0u, 0u};
     }
-    /* slices in batches of 8, all loads of a batch issued before use */
-    for (int s0 = 0; s0 < W; s0 += 8) {
-        u32x2 y[4][8];
+    /* slices in batches of NB, all loads of a batch issued before use */
+    for (int s0 = 0; s0 < W; s0 += NB) {
+        u32x2 y[4][NB];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int u = k * 512 + threadIdx.x;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < NB; ++i)
                 if (4 * u < nv && s0 + i < W)
                     y[k][i] = __builtin_nontemporal_load(
                         g + (int64_t)(s0 + i) * 2048 + u);
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(512) void k_mix_stream(
         for (int k = 0; k < 4; ++k) {
             const int u = k * 512 + threadIdx.x;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < NB; ++i)
                 if (4 * u < nv && s0 + i < W)
                     x[k] ^= y[k][i];
         }
@@ -265,13 +265,22 @@ extern "C" int synth_mix_stream_dev(const void* grads, void* state,
     if (((uintptr_t)grads | (uintptr_t)state | (uintptr_t)flat) & 15u)
         return -2;
     const int64_t tpb = (S + 8191) / 8192;
+    /* the step's shapes: slices 4 at a time up to W = 16, 8 above */
     if (W == 8)
-        hipLaunchKernelGGL(k_mix_stream<8>, dim3((unsigned)tpb, (unsigned)nb),
+        hipLaunchKernelGGL((k_mix_stream<8, 4>),
+                           dim3((unsigned)tpb, (unsigned)nb),
+                           dim3(512), 0, (hipStream_t)stream,
+                           (const u32x2*)grads, (u32x4*)state, (u32x2*)flat,
+                           (int)W, S, S_last, B, tpb, nb - 1);
+    else if (W <= 16)
+        hipLaunchKernelGGL((k_mix_stream<0, 4>),
+                           dim3((unsigned)tpb, (unsigned)nb),
                            dim3(512), 0, (hipStream_t)stream,
                            (const u32x2*)grads, (u32x4*)state, (u32x2*)flat,
                            (int)W, S, S_last, B, tpb, nb - 1);
     else
-        hipLaunchKernelGGL(k_mix_stream<0>, dim3((unsigned)tpb, (unsigned)nb),
+        hipLaunchKernelGGL((k_mix_stream<0, 8>),
+                           dim3((unsigned)tpb, (unsigned)nb),
                            dim3(512), 0, (hipStream_t)stream,
                            (const u32x2*)grads, (u32x4*)state, (u32x2*)flat,
                            (int)W, S, S_last, B, tpb, nb - 1);

@@ -244,16 +244,16 @@ def test_every_world_size(W, layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("tiles", [300, 700, 1100])
-def test_tile_split_variants(tiles, layout):
-    """Launches with fewer than 1024 tiles split each tile over 2 or 4
-    workgroups: 300 tiles (4 per tile), 700 (2 per tile), 1100 (1 per
-    tile); one bucket per launch, a ragged last tile."""
-    W = 2
+@pytest.mark.parametrize("W,tiles", [(2, 300), (2, 1100), (32, 1030),
+                                     (5, 1030)])
+def test_launch_shapes(W, tiles, layout):
+    """Each work shape of the step: fewer than 1024 tiles (four workgroups
+    per tile), 1024 or more at W <= 16, at W >= 32, and the runtime-W
+    kernel; one bucket per launch, a ragged last tile."""
     n_rank = tiles * TILE - 4096            # the last tile half full
     numels = [W * n_rank - 1000, 1000]
-    say(f"case split tiles={tiles} {layout}")
-    c = Case(numels, W, 1, cap=0, layout=layout)
+    say(f"case shape W={W} tiles={tiles} {layout}")
+    c = Case(numels, W, W - 1, cap=0, layout=layout)
     assert c.lay_o.n_tiles == tiles
     for t in (1, 2):
         c.step(t)

@@ -19,23 +19,22 @@
 //   th  = th*(1-lr*wd) - (lr/bc1) * (m / (sqrt(v)/sqrt(bc2) + eps))
 //   p   = bf16 of th, round to nearest even
 //
-// Work decomposition.  One 512-thread workgroup (8 wave64s) owns one tile
-// of ZS_TILE = 8192 elements of one bucket's slice; each thread owns four
-// 4-element units at stride 512 units, so every load or store instruction of
-// a wave covers one contiguous run (1 KiB of fp32, 512 B of bf16) and the
-// whole workgroup sweeps each stream in one 16-32 KiB burst.  A launch with
-// few tiles (one bucket of a streaming step) splits each tile over P = 2 or
-// 4 workgroups of the same shape, each with 4/P units per thread, so that
-// the grid still covers the 256 CUs.  With the tiled
-// state the three 32 KiB rows of a tile are adjacent, and with tiled
-// gradients so are the W 16 KiB slice rows; measured on MI355X, that lifts
-// this 2:1 read/write stream from about 5.4 to about 6.4 TB/s.  All loads of
-// a unit are issued before its arithmetic (the W slices in batches of 8), and
-// every access is non-temporal: nothing is reused.
+// Work decomposition.  The shard is cut into tiles of ZS_TILE = 8192
+// elements of one bucket's slice.  A tile is owned by one 512-thread
+// workgroup (8 wave64s) whose threads each own four 4-element units at
+// stride 512 units, or, in launches of few tiles, by four workgroups of
+// one unit per thread; either way every load or store instruction of a wave
+// covers one contiguous run (1 KiB of fp32, 512 B of bf16) and a tile's
+// rows are swept in 8-32 KiB bursts.  With the tiled state the three 32 KiB
+// rows of a tile are adjacent, and with tiled gradients so are the W 16 KiB
+// slice rows; measured on MI355X, that lifts this 2:1 read/write stream
+// from about 5.4 to about 6.4 TB/s.  All loads of a unit are issued before
+// its arithmetic (the W slices in batches of 4 or 8), and every access is
+// non-temporal: nothing is reused.
 //
-// Grid: blockIdx.y = bucket, blockIdx.x = tile of that bucket's slice, so no
-// thread divides to find its bucket, and the all-gather position of each
-// element is one multiply-add away.
+// Grid: blockIdx.y = bucket, blockIdx.x = tile (times the workgroups per
+// tile) of that bucket's slice, so no thread divides to find its bucket, and
+// the all-gather position of each element is one multiply-add away.
 
 #include <hip/hip_runtime.h>
 
@@ -50,13 +49,25 @@ namespace {
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 512;              // 8 waves of 64
-constexpr int kUnits = 4;                  // 4-element units per thread
 constexpr int64_t kTile = ZS_TILE;
+// the layout conversions and the flat pack: one 512-thread workgroup per
+// tile, four 4-element units per thread
+constexpr int kThreads = 512;
+constexpr int kUnits = 4;
 static_assert(kTile == (int64_t)kThreads * kUnits * 4, "tile shape");
-constexpr int kMinBlocks = 1024;           // below this, split tiles
-constexpr int kBatch = 8;                  // gradient slices loaded together
 constexpr int64_t kMaxGridY = 65535;
+
+// Work shape of the step kernels: NT threads per workgroup, U 4-element
+// units per thread, gradient slices loaded NB at a time; P = ZS_TILE /
+// (4 NT U) workgroups share one tile (consecutive blockIdx.x).
+template <int NT_, int U_, int NB_>
+struct Shape {
+    static constexpr int NT = NT_;
+    static constexpr int U = U_;
+    static constexpr int NB = NB_;
+    static constexpr int P = (int)(kTile / (4 * NT_ * U_));
+    static_assert((int64_t)P * 4 * NT_ * U_ == kTile, "shape must tile");
+};
 
 struct Consts {
     float b1, b2, omb1, omb2;   // beta1, beta2, 1-beta1, 1-beta2
@@ -103,12 +114,12 @@ __device__ __forceinline__ bool tile_of(const Geom& g, TileRef& r)
 }
 
 // element offset of unit k of this thread inside its tile, for a workgroup
-// that is part `blockIdx.x % P` of P on the tile
-template <int P = 1>
+// of NT threads that is part `blockIdx.x % P` of P on the tile
+template <int P = 1, int NT = kThreads>
 __device__ __forceinline__ int unit_off(int k)
 {
     const int part = (int)(blockIdx.x % P);
-    return part * (int)(kTile / P) + 4 * (k * kThreads + (int)threadIdx.x);
+    return part * (int)(kTile / P) + 4 * (k * NT + (int)threadIdx.x);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t u)
@@ -165,16 +176,17 @@ struct StepArgs {
 // Slices s0 .. s0+n-1 (n <= NB) of every unit: all loads first, then the
 // adds in rank order.  Slice 0 initialises the sum, so the sign of a zero
 // sum is that of the first addend, as in a left-to-right sum.
-template <int NB, int U, int P>
+template <int NB, class SH>
 __device__ __forceinline__ void reduce_batch(const uint16_t* __restrict__ g0,
                                              int64_t gs, int s0, int n,
                                              bool full, int64_t nvalid,
-                                             float (&acc)[U][4])
+                                             float (&acc)[SH::U][4])
 {
+    constexpr int U = SH::U;
     u32x2 x[U][NB];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const int jj = unit_off<P>(k);
+        const int jj = unit_off<SH::P, SH::NT>(k);
         if (full || jj < nvalid) {
 #pragma unroll
             for (int i = 0; i < NB; ++i)
@@ -184,7 +196,7 @@ __device__ __forceinline__ void reduce_batch(const uint16_t* __restrict__ g0,
     }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const int jj = unit_off<P>(k);
+        const int jj = unit_off<SH::P, SH::NT>(k);
         if (!(full || jj < nvalid))
             continue;
 #pragma unroll
@@ -208,25 +220,26 @@ __device__ __forceinline__ void reduce_batch(const uint16_t* __restrict__ g0,
 }
 
 // WT > 0: W known at compile time; WT == 0: runtime W.
-template <int WT, int U, int P>
+template <int WT, class SH>
 __device__ __forceinline__ void reduce(const uint16_t* __restrict__ g0,
                                        int64_t gs, int W, bool full,
-                                       int64_t nvalid, float (&acc)[U][4])
+                                       int64_t nvalid,
+                                       float (&acc)[SH::U][4])
 {
-    if constexpr (WT > 0 && WT <= kBatch) {
-        reduce_batch<WT, U, P>(g0, gs, 0, WT, full, nvalid, acc);
+    constexpr int NB = SH::NB;
+    if constexpr (WT > 0 && WT <= NB) {
+        reduce_batch<WT, SH>(g0, gs, 0, WT, full, nvalid, acc);
     } else if constexpr (WT > 0) {
-        static_assert(WT % kBatch == 0, "compiled W above 8 must be a "
-                      "multiple of 8");
+        static_assert(WT % NB == 0, "compiled W must be a multiple of the "
+                      "batch");
 #pragma unroll
-        for (int s0 = 0; s0 < WT; s0 += kBatch)
-            reduce_batch<kBatch, U, P>(g0, gs, s0, kBatch, full, nvalid,
-                                       acc);
+        for (int s0 = 0; s0 < WT; s0 += NB)
+            reduce_batch<NB, SH>(g0, gs, s0, NB, full, nvalid, acc);
     } else {
 #pragma unroll 1
-        for (int s0 = 0; s0 < W; s0 += kBatch) {
-            const int n = W - s0 < kBatch ? W - s0 : kBatch;
-            reduce_batch<kBatch, U, P>(g0, gs, s0, n, full, nvalid, acc);
+        for (int s0 = 0; s0 < W; s0 += NB) {
+            const int n = W - s0 < NB ? W - s0 : NB;
+            reduce_batch<NB, SH>(g0, gs, s0, n, full, nvalid, acc);
         }
     }
 }
@@ -235,8 +248,8 @@ __device__ __forceinline__ void reduce(const uint16_t* __restrict__ g0,
 // first gradient value of slice 0 (tiled: the tile's W rows, gs = ZS_TILE;
 // slices: gs = the slice stride), st the tile's state rows, ps / fl the
 // tile's first bf16 output (each nullable).  This workgroup is part
-// blockIdx.x % P of P on the tile, with U = 4/P units per thread.
-template <int WT, int P>
+// blockIdx.x % P of SH::P on the tile.
+template <int WT, class SH>
 __device__ __forceinline__ void step_tile(const uint16_t* __restrict__ g0,
                                           int64_t gs, float* __restrict__ st,
                                           uint16_t* __restrict__ ps,
@@ -244,14 +257,14 @@ __device__ __forceinline__ void step_tile(const uint16_t* __restrict__ g0,
                                           int64_t nvalid, int W,
                                           const Consts& c)
 {
-    constexpr int U = kUnits / P;
+    constexpr int U = SH::U;
     const bool full = nvalid == kTile;
 
     // fp32 state first: its loads do not depend on the gradients
     f32x4 th[U], mm[U], vv[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const int jj = unit_off<P>(k);
+        const int jj = unit_off<SH::P, SH::NT>(k);
         if (full || jj < nvalid) {
             th[k] = ld4(st + jj);
             mm[k] = ld4(st + kTile + jj);
@@ -260,12 +273,12 @@ __device__ __forceinline__ void step_tile(const uint16_t* __restrict__ g0,
     }
 
     float g[U][4];
-    reduce<WT, U, P>(g0, gs, W, full, nvalid, g);
+    reduce<WT, SH>(g0, gs, W, full, nvalid, g);
 
     const bool pow2 = WT > 0 ? ((WT & (WT - 1)) == 0) : (c.pow2 != 0);
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const int jj = unit_off<P>(k);
+        const int jj = unit_off<SH::P, SH::NT>(k);
         if (!(full || jj < nvalid))
             continue;
         float t4[4] = {th[k].x, th[k].y, th[k].z, th[k].w};
@@ -299,19 +312,19 @@ __device__ __forceinline__ void step_tile(const uint16_t* __restrict__ g0,
 }
 
 // Whole-shard step: blockIdx.y = bucket, blockIdx.x = tile * P + part.
-template <int WT, bool TILED, int P>
-__global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a)
+template <int WT, bool TILED, class SH>
+__global__ __launch_bounds__(SH::NT) void step_kernel(StepArgs a)
 {
     TileRef r;
-    if (!tile_of<P>(a.g, r))
+    if (!tile_of<SH::P>(a.g, r))
         return;
     const int W = WT > 0 ? WT : a.W;
     const uint16_t* g0 = TILED ? a.grads + r.tile * (int64_t)W * kTile
                                : a.grads + r.e0;
-    step_tile<WT, P>(g0, TILED ? kTile : a.gstride,
-                     a.state + r.tile * (3 * kTile),
-                     a.pshard ? a.pshard + r.e0 : nullptr,
-                     a.flat ? a.flat + r.fpos : nullptr, r.nvalid, W, a.c);
+    step_tile<WT, SH>(g0, TILED ? kTile : a.gstride,
+                      a.state + r.tile * (3 * kTile),
+                      a.pshard ? a.pshard + r.e0 : nullptr,
+                      a.flat ? a.flat + r.fpos : nullptr, r.nvalid, W, a.c);
 }
 
 // A group of buckets, each from its own staging buffer: blockIdx.y = member,
@@ -333,11 +346,11 @@ struct GroupArgs {
     Consts c;
 };
 
-template <int WT, bool TILED, int P>
-__global__ __launch_bounds__(kThreads) void group_step_kernel(GroupArgs a)
+template <int WT, bool TILED, class SH>
+__global__ __launch_bounds__(SH::NT) void group_step_kernel(GroupArgs a)
 {
     const GroupMember& mb = a.mb[blockIdx.y];
-    const int64_t x = blockIdx.x / P;
+    const int64_t x = blockIdx.x / SH::P;
     const int64_t j0 = x * kTile;
     if (j0 >= mb.slice)
         return;
@@ -345,9 +358,10 @@ __global__ __launch_bounds__(kThreads) void group_step_kernel(GroupArgs a)
     const int64_t nvalid = mb.slice - j0 < kTile ? mb.slice - j0 : kTile;
     const uint16_t* g0 = TILED ? mb.grads + x * (int64_t)W * kTile
                                : mb.grads + j0;
-    step_tile<WT, P>(g0, TILED ? kTile : a.gstride, mb.state + x * 3 * kTile,
-                     mb.pshard ? mb.pshard + j0 : nullptr,
-                     mb.flat ? mb.flat + j0 : nullptr, nvalid, W, a.c);
+    step_tile<WT, SH>(g0, TILED ? kTile : a.gstride,
+                      mb.state + x * 3 * kTile,
+                      mb.pshard ? mb.pshard + j0 : nullptr,
+                      mb.flat ? mb.flat + j0 : nullptr, nvalid, W, a.c);
 }
 
 // ---- layout conversions ------------------------------------------------------
@@ -562,39 +576,52 @@ Geom bucket_geom(const zs_layout* L, const zs_bucket& b)
 }
 
 // Kernel choice: Args = StepArgs (whole shard) or GroupArgs (buckets).
-template <int WT, bool TILED, int P, class Args>
+template <int WT, bool TILED, class SH, class Args>
 void launch_kernel(const Args& a, dim3 grid, hipStream_t s)
 {
+    grid.x *= SH::P;
     if constexpr (std::is_same<Args, StepArgs>::value)
-        hipLaunchKernelGGL((step_kernel<WT, TILED, P>), grid, dim3(kThreads),
+        hipLaunchKernelGGL((step_kernel<WT, TILED, SH>), grid, dim3(SH::NT),
                            0, s, a);
     else
-        hipLaunchKernelGGL((group_step_kernel<WT, TILED, P>), grid,
-                           dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((group_step_kernel<WT, TILED, SH>), grid,
+                           dim3(SH::NT), 0, s, a);
 }
 
-template <int WT, int P, class Args>
-void launch_step_wp(const Args& a, bool tiled, dim3 grid, hipStream_t s)
+template <int WT, class SH, class Args>
+void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 {
-    grid.x *= P;
     if (tiled)
-        launch_kernel<WT, true, P>(a, grid, s);
+        launch_kernel<WT, true, SH>(a, grid, s);
     else
-        launch_kernel<WT, false, P>(a, grid, s);
+        launch_kernel<WT, false, SH>(a, grid, s);
 }
 
-// grid: one x per tile; tiles are split over 2 or 4 workgroups when the
-// launch has fewer than kMinBlocks tiles
+// Work shapes, chosen by measurement on MI355X (8B-shaped shard at W = 8
+// and 16, 7B-shaped at W = 64, 70B-shaped bucket groups at W = 16):
+//  - Wide: one 512-thread workgroup per tile, 4 units per thread, slices
+//    loaded 4 at a time: 112 VGPRs at W = 8, so two workgroups share a CU;
+//  - Deep (W >= 32, where gradients are most of the bytes): slices loaded
+//    8 at a time, more loads in flight per thread, one workgroup per CU;
+//  - Small (launches of fewer than kSmallLaunch tiles, i.e. bucket groups
+//    of a streaming step): one unit per thread and four workgroups per
+//    tile, so that a few hundred tiles still spread over the 256 CUs.
+using ShapeWide = Shape<512, 4, 4>;
+using ShapeDeep = Shape<512, 4, 8>;
+using ShapeSmall = Shape<512, 1, 4>;
+constexpr int64_t kSmallLaunch = 1024;
+
+// grid: one x per tile (launch_kernel multiplies by the shape's P)
 template <int WT, class Args>
 void launch_step_w(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 {
-    const int64_t blocks = (int64_t)grid.x * grid.y;
-    if (blocks >= kMinBlocks)
-        launch_step_wp<WT, 1>(a, tiled, grid, s);
-    else if (2 * blocks >= kMinBlocks)
-        launch_step_wp<WT, 2>(a, tiled, grid, s);
+    const int64_t tiles = (int64_t)grid.x * grid.y;
+    if (tiles < kSmallLaunch)
+        launch_shape<WT, ShapeSmall>(a, tiled, grid, s);
+    else if constexpr (WT >= 32)
+        launch_shape<WT, ShapeDeep>(a, tiled, grid, s);
     else
-        launch_step_wp<WT, 4>(a, tiled, grid, s);
+        launch_shape<WT, ShapeWide>(a, tiled, grid, s);
 }
 
 template <class Args>
