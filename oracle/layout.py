@@ -163,16 +163,25 @@ def shard_flat_index(lay: Layout) -> List[range]:
             for b in lay.buckets]
 
 
-def tile_slot(lay: Layout) -> np.ndarray:
-    """int64 [shard_numel]: for shard element e, tile * T + position of e
-    in the tiled layouts, T = lay.tile (element j of bucket b's slice sits in
-    tile b.tile_off + j // T at position j % T)."""
+def tile_slot_range(lay: Layout, bucket_id: int, j0: int, k: int):
+    """int64 [k]: tile * T + position, in the tiled layouts (T = lay.tile),
+    of elements j0 .. j0+k-1 of bucket bucket_id's slice: element j sits in
+    tile b.tile_off + j // T at position j % T."""
+    b = lay.buckets[bucket_id]
+    if j0 < 0 or j0 + k > b.slice_numel:
+        raise IndexError("range outside the bucket's slice")
     T = lay.tile
+    j = np.arange(j0, j0 + k, dtype=np.int64)
+    return (b.tile_off + j // T) * T + j % T
+
+
+def tile_slot(lay: Layout) -> np.ndarray:
+    """int64 [shard_numel]: tile * T + position of every shard element in
+    the tiled layouts (see tile_slot_range)."""
     out = np.empty(lay.shard_numel, np.int64)
-    for b in lay.buckets:
-        j = np.arange(b.slice_numel, dtype=np.int64)
+    for b_id, b in enumerate(lay.buckets):
         out[b.shard_off:b.shard_off + b.slice_numel] = \
-            (b.tile_off + j // T) * T + j % T
+            tile_slot_range(lay, b_id, 0, b.slice_numel)
     return out
 
 

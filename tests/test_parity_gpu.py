@@ -21,7 +21,7 @@ import synth
 import zero_sharded_optimizer_shard_amd as zs
 from oracle import step as O
 from oracle.layout import (TILE, build_layout, from_tiled_state, tile_slot,
-                           to_tiled_grads, to_tiled_state)
+                           tile_slot_range, to_tiled_grads, to_tiled_state)
 from oracle.pack import pack_flat, pack_tensors
 from synth import state as S
 from synth import workloads as wl
@@ -586,6 +586,67 @@ def test_full_size_sampled(name):
         other = np16(flat[b.flat_off + b.slice_numel:
                           b.flat_off + b.slice_numel + 4096])
         assert np.all(other == 0x7fc0)
+
+
+def test_streaming_70b_sampled_beyond_2_32():
+    """The Llama-3-70B-shaped W=16 rank-0 shard at full size (4.41e9
+    elements; shard, tile and state offsets beyond 2^32): a group of buckets
+    from the start, the middle and the end of the shard, each from its own
+    tiled staging buffer as the streaming mode gets them, stepped twice by
+    zs_buckets_step; windows at both ends of every stepped slice against
+    the oracle."""
+    w = wl.presets()["llama70b"]
+    lay_o = build_layout(w.numels, w.world, 0)
+    lay = zs.zs_layout_build(w.numels, w.world, 0)
+    n, W, nb = lay_o.shard_numel, w.world, len(lay_o.buckets)
+    assert n > 2 ** 32
+    say(f"case 70b sampled: W={W} shard={n} buckets={nb}")
+    state = dev_f32(lay_o.n_tiles * 3 * TILE)
+    master = dev_f32(n)
+    synth.dev_normal_f32(master, 0, synth.TAG_MASTER, 0, 0, 0,
+                         w.master_sigma)
+    zs.zs_state_pack(lay, master, None, None, state)
+    torch.cuda.synchronize()
+    del master
+    torch.cuda.empty_cache()
+    p = dev_bf16(n)
+    ids = [0, 1, nb // 2, nb - 3, nb - 2, nb - 1]
+    assert lay_o.buckets[nb - 1].shard_off > 2 ** 32
+    smax = max(lay_o.buckets[b].slice_numel for b in ids)
+    tmp = torch.empty((W, smax), dtype=torch.bfloat16, device="cuda")
+    stg = [dev_bf16(-(-smax // TILE) * W * TILE) for _ in ids]
+    st3 = state.view(lay_o.n_tiles, 3, TILE)
+    wins = []
+    for b_id in ids:
+        b = lay_o.buckets[b_id]
+        for j0 in (0, b.slice_numel - 2048):
+            wins.append((b_id, j0, 2048))
+    ref = {x: S.cpu_state(lay_o.buckets[x[0]].shard_off + x[1], x[2],
+                          w.master_sigma) for x in wins}
+    for t in (1, 2):
+        for b_id, buf in zip(ids, stg):
+            b = lay_o.buckets[b_id]
+            for s in range(W):
+                synth.dev_normal_bf16(tmp[s, :b.slice_numel], 0,
+                                      synth.TAG_GRAD, t, s, b.shard_off,
+                                      w.grad_sigma)
+            zs.zs_grads_tile(lay, b_id, tmp, smax, buf)
+        zs.zs_buckets_step(lay, ids, stg, state, p, None,
+                           grad_layout="tiled", step=t, **HP)
+        torch.cuda.synchronize()
+        for (b_id, j0, k) in wins:
+            b = lay_o.buckets[b_id]
+            a = b.shard_off + j0
+            st = ref[(b_id, j0, k)]
+            p16 = O.step(S.cpu_grads(W, a, k, t, w.grad_sigma), *st, OHP, t)
+            sl = torch.from_numpy(tile_slot_range(lay_o, b_id, j0, k)).cuda()
+            ti, pi = sl // TILE, sl % TILE
+            got = [npf(st3[ti, row, pi]) for row in range(3)]
+            assert_parity(
+                dict(master=got[0], m=got[1], v=got[2],
+                     p=np16(p[a:a + k])),
+                dict(master=st[0], m=st[1], v=st[2], p=p16),
+                f"70b t={t} bucket {b_id} window {j0}+{k}")
 
 
 def test_two_runs_are_bit_identical():
