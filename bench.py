@@ -145,6 +145,164 @@ def time_each(fn, K, st):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+def fsdp_units(numels):
+    """FSDP wrapping units of a Llama-shaped list (embed, L x [attn_norm, q,
+    k, v, o, ffn_norm, gate, up, down], final norm, lm_head): the
+    embedding, one unit per block, and final norm + head; as (first tensor,
+    last tensor) pairs."""
+    L = (len(numels) - 3) // 9
+    return ([(0, 0)] + [(1 + 9 * i, 9 + 9 * i) for i in range(L)] +
+            [(len(numels) - 2, len(numels) - 1)])
+
+
+def zero3_main(args, w):
+    """ZeRO-3 / FSDP forward: each rank holds only its bf16 shard of the
+    parameters (the W ranks' shards are W resident buffers here); before a
+    unit runs, zs_gather materialises its full weights into one of two
+    buffers, the next unit's gather runs on a second stream while the
+    current unit computes, and a buffer is reused only after the unit that
+    read it is done (at most two units materialised).  The layer compute is
+    a stand-in: one bf16 GEMM per 2-D weight (F.linear, `--tokens` rows;
+    the embedding as a lookup), not part of the library.  Reported per
+    forward pass: the gathers alone, the compute alone, both pipelined."""
+    import torch
+    import torch.nn.functional as Fn
+    import synth
+    import zero_sharded_optimizer_shard_amd as zs
+
+    W = w.world
+    lay = zs.zs_layout_build(w.numels, W, 0)
+    flat_n, n, nb, nc = zs.zs_layout_info(lay)
+    offs = zs.zs_layout_tensor_offsets(lay, len(w.numels))
+    units = fsdp_units(w.numels)
+    ranges = [(offs[a], offs[b] + w.numels[b]) for a, b in units]
+    biggest = max(hi - lo for lo, hi in ranges)
+    log(f"workload {w.name} ZeRO-3: W={W} shard={n} units={len(units)} "
+        f"largest unit {biggest} elements")
+    shards = []
+    for r in range(W):
+        t = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        synth.dev_normal_bf16(t, 0, synth.TAG_MASTER, 0, r, 0, 0.02)
+        shards.append(t)
+    bufs = [torch.empty(biggest, dtype=torch.bfloat16, device="cuda")
+            for _ in range(2)]
+    d = w.numels[1]                              # hidden size (a norm)
+    x = torch.randn(args.tokens, d, dtype=torch.bfloat16, device="cuda")
+    ids = torch.randint(0, w.numels[0] // d, (args.tokens,), device="cuda")
+    torch.cuda.synchronize()
+    log("shards resident")
+
+    def views(u, buf):
+        a, b = units[u]
+        lo = ranges[u][0]
+        out = []
+        for t in range(a, b + 1):
+            v = buf[offs[t] - lo:offs[t] - lo + w.numels[t]]
+            out.append(v.view(-1, d) if w.numels[t] % d == 0 and
+                       w.numels[t] > d else None)
+        return out
+
+    def compute(u, buf):
+        """Stand-in for the unit's forward: the embedding as a lookup, every
+        other weight (viewed as [rows, d]) applied once to x with F.linear,
+        i.e. 2 * tokens * numel flops per weight; results are dropped."""
+        ws = views(u, buf)
+        if u == 0:
+            Fn.embedding(ids, ws[0])
+            return
+        for wt in ws:
+            if wt is not None:
+                Fn.linear(x, wt)
+
+    gs = torch.cuda.Stream()
+    st = torch.cuda.current_stream()
+    NU = len(units)
+
+    def gathers_alone():
+        for u in range(NU):
+            zs.zs_gather(lay, shards, ranges[u][0], ranges[u][1],
+                         bufs[u % 2], stream=st)
+
+    def compute_alone():
+        for u in range(NU):
+            compute(u, bufs[u % 2])
+
+    def pipelined():
+        ready = [None] * NU
+        used = [None, None]
+
+        def issue(u):
+            with torch.cuda.stream(gs):
+                if used[u % 2] is not None:
+                    gs.wait_event(used[u % 2])
+                zs.zs_gather(lay, shards, ranges[u][0], ranges[u][1],
+                             bufs[u % 2], stream=gs)
+                ev = torch.cuda.Event()
+                ev.record(gs)
+                ready[u] = ev
+        issue(0)
+        for u in range(NU):
+            if u + 1 < NU:
+                issue(u + 1)                     # prefetch the next unit
+            st.wait_event(ready[u])
+            compute(u, bufs[u % 2])
+            ev = torch.cuda.Event()
+            ev.record(st)
+            used[u % 2] = ev
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps, (time.perf_counter() - t0) * 1e3 \
+            / reps
+
+    K = max(1, min(args.steps, 10))
+    g_ms, g_wall = timed(gathers_alone, K)
+    elems = sum(hi - lo for lo, hi in ranges)
+    g_gbs = 4 * elems / (g_ms * 1e-3) / 1e9
+    log(f"gathers alone: {g_ms:.3f} ms per forward ({elems} elements, "
+        f"{g_gbs:.0f} GB/s, {g_gbs / PEAK_HBM_GBS:.1%})")
+    c_ms, _ = timed(compute_alone, K)
+    log(f"stand-in compute alone: {c_ms:.3f} ms per forward")
+    p_ms, p_wall = timed(pipelined, K)
+    log(f"pipelined: {p_ms:.3f} ms per forward, exposed gather "
+        f"{p_ms - c_ms:.3f} ms")
+    out = {
+        "metric": "ZeRO-3 per-layer parameter gather (FSDP forward with "
+                  "prefetch), gathered params/s per GPU",
+        "value": elems / (g_ms * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": 1,
+        "ms_per_step": g_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} parameters, W={W} shards, "
+                               f"ZeRO-3 gather per FSDP unit",
+                   "params_total": sum(w.numels), "fsdp_units": NU,
+                   "bytes_per_param": 4, "tokens": args.tokens},
+        "roofline": {"bound": "hbm", "achieved": g_gbs,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": g_gbs / PEAK_HBM_GBS, "traffic": None},
+        "zero3": {"gathers_alone_ms": g_ms, "compute_alone_ms": c_ms,
+                  "pipelined_ms": p_ms, "exposed_gather_ms": p_ms - c_ms,
+                  "elements_per_forward": elems},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def stream_main(args, w):
     """ZeRO-2 streaming: the W slices of each 25 MiB bucket arrive one bucket
     at a time, last bucket first (the order backward fills them), into a ring
@@ -320,6 +478,11 @@ def main():
     ap.add_argument("--arrival", default="h2d", choices=["h2d", "d2d"],
                     help="streaming mode: buckets arrive from pinned host "
                     "memory (h2d) or from an HBM pool (d2d)")
+    ap.add_argument("--zero3", action="store_true",
+                    help="ZeRO-3 / FSDP mode: per-layer parameter gather "
+                    "(zs_gather) with prefetch, on the workload's layout")
+    ap.add_argument("--tokens", type=int, default=2048,
+                    help="ZeRO-3 mode: tokens of the stand-in layer compute")
     ap.add_argument("--group", type=int, default=8,
                     help="streaming mode: landed buckets stepped per launch "
                     "(zs_buckets_step); the ring holds 2*group slots")
@@ -351,6 +514,8 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     w = wl.presets()[args.workload]
+    if args.zero3:
+        return zero3_main(args, w)
     if w.streaming:
         return stream_main(args, w)
     W = w.world

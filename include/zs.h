@@ -252,6 +252,29 @@ int zs_grads_tile(const zs_layout* layout, int32_t bucket_id,
                   const uint16_t* slices, int64_t stride, uint16_t* tiled,
                   void* hip_stream);
 
+/* ZeRO-3 / FSDP parameter gather (podcast summary, "ZeRO optimizer": a
+ * layer's full weight is all-gathered from the shards right before it is
+ * used, the next layer's gather overlaps the current layer's compute, and
+ * the full weight is dropped afterwards; CS336 notes, "Code example: FSDP").
+ *
+ * Writes flat positions [flat_lo, flat_hi) of the bf16 parameter buffer to
+ * out[0 .. flat_hi - flat_lo), pulling each position from the rank that
+ * owns it: shards is a HOST array of W device pointers, shards[r] = rank
+ * r's bf16 shard [shard_numel] (as zs_step writes it to param_shard; on one
+ * GPU the ranks' shards are W resident buffers).  Use a tensor's flat
+ * offset and numel (zs_layout_tensor_offsets) to gather one tensor or a
+ * run of tensors (a layer); padding positions are copied like the rest.
+ * Any rank's layout works: the bucket table is the same for every rank.
+ *
+ * flat_lo must be a multiple of 8 (tensor starts are); flat_hi is free.
+ * Errors: ZS_EINVAL for NULL pointers or W above ZS_GATHER_MAX_WORLD;
+ * ZS_ERANGE for a range outside [0, flat_numel]; ZS_EALIGN for a pointer
+ * not 16-byte aligned or a misaligned flat_lo.  An empty range is a no-op. */
+#define ZS_GATHER_MAX_WORLD 64
+int zs_gather(const zs_layout* layout, const uint16_t* const* shards,
+              int64_t flat_lo, int64_t flat_hi, uint16_t* out,
+              void* hip_stream);
+
 /* Local part of the all-gather (CS336 notes, "Code example: ZeRO-1": the
  * all-gather concatenates the updated slices in rank order; "Code example:
  * FSDP": per-layer weights are views of the gathered parameters).

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     L = zs.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -186,6 +186,23 @@ def test_step_argument_checks_need_no_device():
     assert L.zs_grads_tile(h, -1, A, shard + 4, A, None) == -2
     assert L.zs_grads_tile(h, 1, A, shard, A, None) == -3
     assert L.zs_grads_tile(h, 0, A + 2, shard, A, None) == -2
+    # gather (ZeRO-3)
+    P_ = ctypes.c_void_p
+    sh = (P_ * 4)(A, A, A, A)
+    flat = zs.zs_layout_info(lay)[0]
+    assert L.zs_gather(h, sh, 0, 0, None, None) == 0        # empty range
+    assert L.zs_gather(h, None, 0, 8, A, None) == -1
+    assert L.zs_gather(h, sh, 0, 8, None, None) == -1
+    assert L.zs_gather(h, (P_ * 4)(A, None, A, A), 0, 8, A, None) == -1
+    assert L.zs_gather(h, (P_ * 4)(A, A + 2, A, A), 0, 8, A, None) == -2
+    assert L.zs_gather(h, sh, 0, 8, A + 4, None) == -2
+    assert L.zs_gather(h, sh, 4, 8, A, None) == -2          # lo % 8
+    assert L.zs_gather(h, sh, -8, 8, A, None) == -3
+    assert L.zs_gather(h, sh, 16, 8, A, None) == -3
+    assert L.zs_gather(h, sh, 0, flat + 1, A, None) == -3
+    big = zs.zs_layout_build([1000], 65, 0)
+    assert L.zs_gather(big.handle, (P_ * 65)(*([A] * 65)), 0, 8, A,
+                       None) == -1
     # pack
     assert L.zs_pack(h, A, None, None, 0, None, None) == -1
     assert L.zs_pack(h, None, A, None, 0, None, None) == -1

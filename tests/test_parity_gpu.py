@@ -22,7 +22,7 @@ import zero_sharded_optimizer_shard_amd as zs
 from oracle import step as O
 from oracle.layout import (TILE, build_layout, from_tiled_state, tile_slot,
                            tile_slot_range, to_tiled_grads, to_tiled_state)
-from oracle.pack import pack_flat, pack_tensors
+from oracle.pack import gather, owner_runs, pack_flat, pack_tensors
 from synth import state as S
 from synth import workloads as wl
 
@@ -647,6 +647,73 @@ def test_streaming_70b_sampled_beyond_2_32():
                      p=np16(p[a:a + k])),
                 dict(master=st[0], m=st[1], v=st[2], p=p16),
                 f"70b t={t} bucket {b_id} window {j0}+{k}")
+
+
+@pytest.mark.parametrize("W,cap", [(1, 25 << 20), (3, 3 * 256 * 37),
+                                   (8, 8 * 256 * 11), (64, 0)])
+def test_gather_matches_the_oracle(W, cap):
+    """zs_gather (ZeRO-3 / FSDP materialisation) against the oracle, bit for
+    bit: the whole flat buffer, every tensor, runs of tensors, random
+    windows with a ragged end; nothing written past the range."""
+    numels = [1000, 70000, 7, 129, 20000, 9000, 3]
+    lay_o = build_layout(numels, W, 0, cap)
+    lay = zs.zs_layout_build(numels, W, 0, cap)
+    n, F = lay_o.shard_numel, lay_o.flat_numel
+    say(f"case gather W={W} cap={cap} flat={F}")
+    host = [synth.cpu_bits16(n, 4, synth.TAG_SENTINEL, 0, r, 0)
+            for r in range(W)]
+    dev = [torch.from_numpy(h.view(np.int16)).cuda() for h in host]
+    out = torch.empty(F + 64, dtype=torch.int16, device="cuda")
+    rng = random.Random(W)
+    offs = lay_o.tensor_flat_off
+    ranges = [(0, F)] + [(o, o + k) for o, k in zip(offs, numels)]
+    ranges += [(offs[1], offs[4] + numels[4]), (offs[2], offs[6] + 3)]
+    for _ in range(6):
+        lo = rng.randrange(0, F) // 8 * 8
+        ranges.append((lo, rng.randrange(lo, F + 1)))
+    for lo, hi in ranges:
+        out.fill_(0x5a5a)
+        zs.zs_gather(lay, dev, lo, hi, out)
+        got = np16(out)
+        assert np.array_equal(got[:hi - lo],
+                              gather(numels, W, host, lo, hi, cap)), (lo, hi)
+        assert np.all(got[hi - lo:] == 0x5a5a), (lo, hi)
+
+
+def test_gather_llama8b_layers_sampled():
+    """Full-size Llama-3-8B-shaped W=8 layout: the embedding, a middle
+    block and the final norm + lm_head gathered from 8 resident shards;
+    sampled windows against the oracle's ownership runs."""
+    w = wl.presets()["llama8b"]
+    lay_o = build_layout(w.numels, w.world, 0)
+    lay = zs.zs_layout_build(w.numels, w.world, 0)
+    n, W = lay_o.shard_numel, w.world
+    say(f"case gather llama8b: W={W} shard={n}")
+    dev = []
+    for r in range(W):
+        t = dev_bf16(n)
+        synth.dev_bits16(t, 5, synth.TAG_SENTINEL, 0, r, 0)
+        dev.append(t)
+    offs, nm = lay_o.tensor_flat_off, w.numels
+    units = [(0, 0), (1 + 9 * 15, 9 + 9 * 15), (len(nm) - 2, len(nm) - 1)]
+    rng = random.Random(8)
+    for t0, t1 in units:
+        lo, hi = offs[t0], offs[t1] + nm[t1]
+        out = dev_bf16(hi - lo + 8)
+        out.view(torch.int16).fill_(0x5a5a)
+        zs.zs_gather(lay, dev, lo, hi, out)
+        torch.cuda.synchronize()
+        wins = [(lo, 4096), (hi - 4096, 4096)] + \
+            [(lo + rng.randrange(0, hi - lo - 65536), 65536)
+             for _ in range(8)]
+        for a, k in wins:
+            want = np.empty(k, np.uint16)
+            for f0, m, r, s0 in owner_runs(lay_o, a, a + k):
+                want[f0 - a:f0 - a + m] = synth.cpu_bits16(
+                    m, 5, synth.TAG_SENTINEL, 0, r, s0)
+            assert np.array_equal(np16(out[a - lo:a - lo + k]), want), \
+                (t0, a, k)
+        assert np.all(np16(out[hi - lo:]) == 0x5a5a)
 
 
 def test_two_runs_are_bit_identical():

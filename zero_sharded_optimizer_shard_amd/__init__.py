@@ -5,18 +5,20 @@ package is its ctypes binding, with the same names.
 """
 
 from ._zs import (EXPORTS, LIB_PATH, ZS_GRADS_SLICES, ZS_GRADS_TILED,
-                  ZS_MAX_GROUP, ZS_TILE, Layout, ZsError, chunks_bytes, lib,
-                  zs_adamw, zs_bucket, zs_bucket_step, zs_buckets_step,
-                  zs_chunk, zs_grads_tile,
+                  ZS_GATHER_MAX_WORLD, ZS_MAX_GROUP, ZS_TILE, Layout,
+                  ZsError, chunks_bytes, lib, zs_adamw, zs_bucket,
+                  zs_bucket_step, zs_buckets_step, zs_chunk, zs_gather,
+                  zs_grads_tile,
                   zs_last_error, zs_layout_buckets, zs_layout_build,
                   zs_layout_chunks, zs_layout_info, zs_layout_rank,
                   zs_layout_tensor_offsets, zs_layout_tiles, zs_pack,
                   zs_state_pack, zs_state_unpack, zs_step, zs_strerror)
 
 __all__ = ["EXPORTS", "LIB_PATH", "ZS_GRADS_SLICES", "ZS_GRADS_TILED",
-           "ZS_MAX_GROUP", "ZS_TILE", "Layout", "ZsError", "chunks_bytes",
-           "lib", "zs_adamw", "zs_bucket", "zs_bucket_step",
-           "zs_buckets_step", "zs_chunk", "zs_grads_tile",
+           "ZS_GATHER_MAX_WORLD", "ZS_MAX_GROUP", "ZS_TILE", "Layout",
+           "ZsError", "chunks_bytes", "lib", "zs_adamw", "zs_bucket",
+           "zs_bucket_step", "zs_buckets_step", "zs_chunk", "zs_gather",
+           "zs_grads_tile",
            "zs_last_error", "zs_layout_buckets", "zs_layout_build",
            "zs_layout_chunks", "zs_layout_info", "zs_layout_rank",
            "zs_layout_tensor_offsets", "zs_layout_tiles", "zs_pack",

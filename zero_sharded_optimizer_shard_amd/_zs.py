@@ -17,6 +17,7 @@ ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ERANGE, ZS_ENOMEM, ZS_EDEVICE = \
     0, -1, -2, -3, -4, -5
 ZS_TILE = 8192
 ZS_MAX_GROUP = 16
+ZS_GATHER_MAX_WORLD = 64
 ZS_GRADS_SLICES, ZS_GRADS_TILED = 0, 1
 
 
@@ -51,7 +52,8 @@ EXPORTS = ["zs_layout_build", "zs_layout_info", "zs_layout_tiles",
            "zs_layout_tensor_offsets", "zs_layout_rank", "zs_layout_free",
            "zs_step", "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
            "zs_state_unpack",
-           "zs_grads_tile", "zs_pack", "zs_strerror", "zs_last_error"]
+           "zs_grads_tile", "zs_gather", "zs_pack", "zs_strerror",
+           "zs_last_error"]
 
 
 def lib():
@@ -83,6 +85,7 @@ def lib():
     L.zs_state_pack.argtypes = [p, p, p, p, p, p]
     L.zs_state_unpack.argtypes = [p, p, p, p, p, p]
     L.zs_grads_tile.argtypes = [p, i32, p, i64, p, p]
+    L.zs_gather.argtypes = [p, P(p), i64, i64, p, p]
     L.zs_pack.argtypes = [p, p, p, p, i32, p, p]
     L.zs_strerror.argtypes = [ctypes.c_int]
     L.zs_strerror.restype = ctypes.c_char_p
@@ -93,7 +96,7 @@ def lib():
                  "zs_layout_tensor_offsets", "zs_layout_rank", "zs_step",
                  "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
                  "zs_state_unpack",
-                 "zs_grads_tile", "zs_pack"):
+                 "zs_grads_tile", "zs_gather", "zs_pack"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -316,6 +319,16 @@ def zs_grads_tile(layout: Layout, bucket_id: int, slices, stride: int,
                                _bf16(slices, "slices"), stride,
                                _bf16(tiled, "tiled"), _stream(stream)),
            "zs_grads_tile")
+
+
+def zs_gather(layout: Layout, shards, flat_lo: int, flat_hi: int, out,
+              stream=None) -> None:
+    """shards: one bf16 shard tensor per rank, in rank order; out: at least
+    flat_hi - flat_lo bf16 elements."""
+    ptrs = (ctypes.c_void_p * max(len(shards), 1))(
+        *[_bf16(t, "shards") for t in shards])
+    _check(lib().zs_gather(layout.handle, ptrs, flat_lo, flat_hi,
+                           _bf16(out, "out"), _stream(stream)), "zs_gather")
 
 
 def zs_pack(layout: Layout, param_shard, full_flat=None, dev_chunks=None,
