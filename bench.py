@@ -145,6 +145,80 @@ def time_each(fn, K, st):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+def bf16_main(args, w):
+    """Pure-bf16 variant (12 B/param: bf16 parameter and gradient, fp32 m and
+    v, no fp32 master): the step reads each parameter from this rank's
+    positions of the flat bf16 buffer, updates it with the same AdamW
+    statements in fp32 and writes the bf16 result back in place.  Tiled
+    gradients, state tiled as [tile][m|v][8192].  2W + 20 bytes per
+    element."""
+    import torch
+    import synth
+    import zero_sharded_optimizer_shard_amd as zs
+    from synth import state as S
+
+    W, T = w.world, zs.ZS_TILE
+    lay = zs.zs_layout_build(w.numels, W, w.rank)
+    flat_n, n, nb, nc = zs.zs_layout_info(lay)
+    n_tiles = zs.zs_layout_tiles(lay)
+    log(f"workload {w.name} pure bf16: W={W} shard={n} buckets={nb}")
+    G = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
+    Gt = torch.empty(n_tiles * W * T, dtype=torch.bfloat16, device="cuda")
+    S.dev_grads(G, W, n, 1, w.grad_sigma)
+    zs.zs_grads_tile(lay, -1, G, n, Gt)
+    del G
+    state = torch.empty(n_tiles * 2 * T, dtype=torch.float32, device="cuda")
+    zs.zs_state_mv_pack(lay, None, None, state)
+    flat = torch.empty(flat_n, dtype=torch.bfloat16, device="cuda")
+    synth.dev_normal_bf16(flat, 0, synth.TAG_MASTER, 0, 0, 0, w.master_sigma)
+    torch.cuda.synchronize()
+    log("inputs resident")
+    st = torch.cuda.current_stream()
+    t = 0
+
+    def one():
+        nonlocal t
+        t += 1
+        zs.zs_step_bf16(lay, Gt, state, flat, params_flat=True,
+                        grad_layout="tiled", step=t, stream=st, **HP)
+
+    for _ in range(args.warmup):
+        one()
+    K = args.steps
+    avg_ms, ms_per_step = time_steps(one, K, st)
+    bpp = 2 * W + 20
+    achieved = bpp * n / (avg_ms * 1e-3) / 1e9
+    log(f"zs_step_bf16: {avg_ms:.3f} ms per launch -> {achieved:.0f} GB/s "
+        f"({achieved / PEAK_HBM_GBS:.1%} of 8 TB/s)")
+    out = {
+        "metric": "pure-bf16 optimizer-step params/s per GPU + achieved HBM "
+                  "GB/s (% of peak)",
+        "value": n / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} rank-0 shard, W={W}, pure bf16",
+                   "params_total": sum(w.numels), "shard_params": n,
+                   "buckets": nb, "bucket_cap_mb": 25,
+                   "bytes_per_param": bpp,
+                   "grads_layout": "tiled [tile][W][8192]",
+                   "state_layout": "tiled [tile][m|v][8192]",
+                   "params": "flat bf16 buffer, in place"},
+        "roofline": {"bound": "hbm", "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+        "kernel_ms": {"avg": avg_ms},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def fsdp_units(numels):
     """FSDP wrapping units of a Llama-shaped list (embed, L x [attn_norm, q,
     k, v, o, ffn_norm, gate, up, down], final norm, lm_head): the
@@ -478,6 +552,9 @@ def main():
     ap.add_argument("--arrival", default="h2d", choices=["h2d", "d2d"],
                     help="streaming mode: buckets arrive from pinned host "
                     "memory (h2d) or from an HBM pool (d2d)")
+    ap.add_argument("--pure-bf16", action="store_true",
+                    help="pure-bf16 step (no fp32 master, 12 B/param): "
+                    "zs_step_bf16 on the flat buffer in place")
     ap.add_argument("--zero3", action="store_true",
                     help="ZeRO-3 / FSDP mode: per-layer parameter gather "
                     "(zs_gather) with prefetch, on the workload's layout")
@@ -516,6 +593,8 @@ def main():
     w = wl.presets()[args.workload]
     if args.zero3:
         return zero3_main(args, w)
+    if args.pure_bf16:
+        return bf16_main(args, w)
     if w.streaming:
         return stream_main(args, w)
     W = w.world

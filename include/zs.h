@@ -243,6 +243,36 @@ int zs_state_pack(const zs_layout* layout, const float* master,
 int zs_state_unpack(const zs_layout* layout, const float* state,
                     float* master, float* m, float* v, void* hip_stream);
 
+/* ---- pure-bf16 variant ----------------------------------------------------
+ *
+ * Training in pure bf16 keeps 12 bytes per parameter: the bf16 parameter,
+ * the bf16 gradient and two fp32 Adam moments, with no fp32 master copy
+ * (CS336 notes, "Core concepts", and the fit table of "Code example:
+ * FSDP", both at 12 bytes per parameter).  The optimizer state is then
+ * tiled as fp32 [n_tiles][2][ZS_TILE]: row 0 = m, row 1 = v. */
+
+/* One pure-bf16 step over the whole shard: the same reduction and AdamW
+ * statements as zs_step, with the parameter read from its bf16 value and
+ * the result rounded back to bf16 (nearest even) in place, so updates under
+ * half a bf16 ulp are lost.  params: the bf16 parameters, read and written
+ * at this rank's positions: params_flat = 0: the bf16 shard [shard_numel];
+ * params_flat = 1: the flat bf16 buffer [flat_numel] (bucket.flat_off +
+ * rank*slice_numel + j), i.e. the all-gather buffer updated in place.
+ * grads, grad_layout, grad_stride, hp, step: as zs_step.  2W + 20 bytes per
+ * element.  Errors as zs_step; ZS_EINVAL for params_flat not 0 or 1. */
+int zs_step_bf16(const zs_layout* layout, const uint16_t* grads,
+                 int32_t grad_layout, int64_t grad_stride, float* state_mv,
+                 uint16_t* params, int32_t params_flat, const zs_adamw* hp,
+                 int64_t step, void* hip_stream);
+
+/* Plain fp32 m / v [shard_numel] -> tiled [n_tiles][2][ZS_TILE] (NULL
+ * rows are set to zero; padding positions to zero), and back (NULL outputs
+ * skipped). */
+int zs_state_mv_pack(const zs_layout* layout, const float* m, const float* v,
+                     float* state_mv, void* hip_stream);
+int zs_state_mv_unpack(const zs_layout* layout, const float* state_mv,
+                       float* m, float* v, void* hip_stream);
+
 /* Gradient slices [W][stride] -> tiled [tiles][W][ZS_TILE]; padding
  * positions of the tiles are set to zero.  bucket_id < 0: the whole shard
  * (stride >= shard_numel, output n_tiles tiles); otherwise bucket

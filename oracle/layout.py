@@ -185,24 +185,35 @@ def tile_slot(lay: Layout) -> np.ndarray:
     return out
 
 
+def to_tiled_rows(lay: Layout, rows) -> np.ndarray:
+    """Plain fp32 arrays [shard_numel], one per row, -> a tiled state
+    [n_tiles * len(rows) * lay.tile]; padding positions 0."""
+    R = len(rows)
+    st = np.zeros((lay.n_tiles, R, lay.tile), np.float32)
+    slot = tile_slot(lay)
+    t, p = slot // lay.tile, slot % lay.tile
+    for k, a in enumerate(rows):
+        st[t, k, p] = a
+    return st.reshape(-1)
+
+
+def from_tiled_rows(lay: Layout, state, n_rows: int):
+    """A tiled state of n_rows rows -> the plain arrays, one per row."""
+    st = np.asarray(state, np.float32).reshape(lay.n_tiles, n_rows, lay.tile)
+    slot = tile_slot(lay)
+    t, p = slot // lay.tile, slot % lay.tile
+    return tuple(st[t, k, p].copy() for k in range(n_rows))
+
+
 def to_tiled_state(lay: Layout, master, m, v) -> np.ndarray:
     """Plain fp32 master/m/v [shard_numel] -> tiled state
     [n_tiles * 3 * lay.tile]; padding positions 0."""
-    st = np.zeros((lay.n_tiles, 3, lay.tile), np.float32)
-    slot = tile_slot(lay)
-    t, p = slot // lay.tile, slot % lay.tile
-    st[t, 0, p] = master
-    st[t, 1, p] = m
-    st[t, 2, p] = v
-    return st.reshape(-1)
+    return to_tiled_rows(lay, [master, m, v])
 
 
 def from_tiled_state(lay: Layout, state):
     """Tiled state -> plain (master, m, v)."""
-    st = np.asarray(state, np.float32).reshape(lay.n_tiles, 3, lay.tile)
-    slot = tile_slot(lay)
-    t, p = slot // lay.tile, slot % lay.tile
-    return st[t, 0, p].copy(), st[t, 1, p].copy(), st[t, 2, p].copy()
+    return from_tiled_rows(lay, state, 3)
 
 
 def to_tiled_grads(lay: Layout, G) -> np.ndarray:

@@ -53,8 +53,11 @@ def lib():
                                    i64]
         L.oracle_step.argtypes = [i32, p, i64, i64, p, p, p, p,
                                   ctypes.POINTER(_HP), i64]
+        L.oracle_step_bf16.argtypes = [i32, p, i64, i64, p, p, p,
+                                       ctypes.POINTER(_HP), i64]
         for f in (L.oracle_constants, L.oracle_bf16_round,
-                  L.oracle_reduce_mean, L.oracle_adamw, L.oracle_step):
+                  L.oracle_reduce_mean, L.oracle_adamw, L.oracle_step,
+                  L.oracle_step_bf16):
             f.restype = None
         _lib = L
     return _lib
@@ -134,3 +137,18 @@ def step(grads: np.ndarray, master: np.ndarray, m: np.ndarray, v: np.ndarray,
     lib().oracle_step(W, _ptr(grads), stride, n, _ptr(master), _ptr(m),
                       _ptr(v), _ptr(p16), ctypes.byref(hp.c()), t)
     return p16
+
+
+def step_bf16(grads: np.ndarray, param: np.ndarray, m: np.ndarray,
+              v: np.ndarray, hp: AdamW, t: int) -> None:
+    """Pure-bf16 step (no fp32 master) over a contiguous run, in place:
+    grads uint16 [W][n], param uint16 [n] (bf16 bits), m and v fp32 [n]."""
+    _check(grads, np.uint16, "grads")
+    _check(param, np.uint16, "param")
+    for a, nm in ((m, "m"), (v, "v")):
+        _check(a, np.float32, nm)
+    W, n = grads.shape
+    if param.size != n or m.size != n or v.size != n:
+        raise ValueError("size mismatch")
+    lib().oracle_step_bf16(W, _ptr(grads), n, n, _ptr(param), _ptr(m),
+                           _ptr(v), ctypes.byref(hp.c()), t)

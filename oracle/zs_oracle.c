@@ -147,3 +147,31 @@ void oracle_step(int32_t W, const uint16_t* grads, int64_t grad_stride,
                   &master[i], &m[i], &v[i],
                   param_bf16 ? &param_bf16[i] : 0, c);
 }
+
+/* Pure-bf16 variant (CS336 lecture 8 notes, "Core concepts" and "Code
+ * example: FSDP": training in pure bf16 keeps 12 bytes per parameter, the
+ * bf16 parameter, the bf16 gradient and the two fp32 Adam moments; there is
+ * no fp32 master copy).  The parameter itself is the bf16 value: the step
+ * reads it, applies the same AdamW statements in fp32 and rounds the result
+ * back to bf16 (nearest even), so updates below half a bf16 ulp are lost.
+ * param is [n] bf16 bits, read and written in place. */
+void oracle_step_bf16(int32_t W, const uint16_t* grads, int64_t grad_stride,
+                      int64_t n, uint16_t* param, float* m, float* v,
+                      const oracle_hp* hp, int64_t t)
+{
+    float c[8];
+    oracle_constants(hp, t, c);
+    for (int64_t i = 0; i < n; ++i) {
+        float g = reduce_one(W, grads, grad_stride, i);
+        float mi = (c[0] * m[i]) + (c[2] * g);
+        float g2 = g * g;
+        float vi = (c[1] * v[i]) + (c[3] * g2);
+        float root = sqrtf(vi);
+        float den = (root / c[5]) + c[7];
+        float upd = mi / den;
+        float th = (bf16_bits_to_float(param[i]) * c[6]) - (c[4] * upd);
+        m[i] = mi;
+        v[i] = vi;
+        param[i] = float_to_bf16_rne(th);
+    }
+}

@@ -20,12 +20,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def header_functions():
     text = open(os.path.join(ROOT, "include", "zs.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(zs_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(zs_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 18
+    assert len(names) == 21
     L = zs.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -186,6 +186,23 @@ def test_step_argument_checks_need_no_device():
     assert L.zs_grads_tile(h, -1, A, shard + 4, A, None) == -2
     assert L.zs_grads_tile(h, 1, A, shard, A, None) == -3
     assert L.zs_grads_tile(h, 0, A + 2, shard, A, None) == -2
+    # pure-bf16 step and its state conversions
+    assert L.zs_step_bf16(h, A, 0, shard, A, A, 0, ctypes.byref(hp), 0,
+                          None) == -1                     # t < 1
+    assert L.zs_step_bf16(h, A, 0, shard, A, A, 2, ctypes.byref(hp), 1,
+                          None) == -1                     # params_flat
+    assert L.zs_step_bf16(h, A, 0, shard, A, None, 0, ctypes.byref(hp), 1,
+                          None) == -1
+    assert L.zs_step_bf16(h, A, 0, shard, None, A, 1, ctypes.byref(hp), 1,
+                          None) == -1
+    assert L.zs_step_bf16(h, A, 0, shard, A + 4, A, 0, ctypes.byref(hp), 1,
+                          None) == -2
+    assert L.zs_step_bf16(h, A, 0, shard - 8, A, A, 0, ctypes.byref(hp), 1,
+                          None) == -3
+    assert L.zs_state_mv_pack(h, A, A, None, None) == -1
+    assert L.zs_state_mv_pack(h, A + 4, A, A, None) == -2
+    assert L.zs_state_mv_unpack(h, None, A, A, None) == -1
+    assert L.zs_state_mv_unpack(h, A, A + 8, None, None) == -2
     # gather (ZeRO-3)
     P_ = ctypes.c_void_p
     sh = (P_ * 4)(A, A, A, A)
@@ -224,3 +241,6 @@ def test_empty_layout_calls_are_noops():
     assert L.zs_state_pack(lay.handle, None, None, None, None, None) == 0
     assert L.zs_state_unpack(lay.handle, None, None, None, None, None) == 0
     assert L.zs_grads_tile(lay.handle, -1, None, 0, None, None) == 0
+    assert L.zs_step_bf16(lay.handle, None, 0, 0, None, None, 0,
+                          ctypes.byref(hp), 1, None) == 0
+    assert L.zs_state_mv_pack(lay.handle, None, None, None, None) == 0

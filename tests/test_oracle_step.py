@@ -347,3 +347,70 @@ def test_constants_first_step():
     # the bias corrections vanish as t grows
     c = O.constants(hp, 10_000)
     assert c[4] == np.float32(hp.lr) and c[5] == np.float32(1.0)
+
+
+# ---- pure-bf16 variant (no fp32 master) ---------------------------------
+
+def bf16_ordinal(bits):
+    b = np.asarray(bits, np.uint16).astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7fff), b)
+
+
+@pytest.mark.parametrize("W", [1, 3, 8])
+def test_bf16_step_is_the_mixed_step_from_the_bf16_value(W):
+    """Each pure-bf16 step equals the (pinned) mixed-precision step whose
+    master starts from the bf16 parameter, rounded back to bf16; the
+    moments are identical.  Checked over several steps with warm moments."""
+    n = 4096
+    hp = hp_f32()
+    p16 = O.bf16_round(master_f32(n))
+    m = synth.cpu_normal_f32(n, 1, synth.TAG_M, 0, 0, 0, 1e-4)
+    v = synth.cpu_normal_f32(n, 1, synth.TAG_V, 0, 0, 0, 1e-8, True)
+    m2, v2 = m.copy(), v.copy()
+    for t in range(1, 6):
+        G = grads_bf16(W, n, t)
+        master = O.bf16_to_f32(p16).copy()
+        want = O.step(G, master, m2, v2, hp, t)
+        O.step_bf16(G, p16, m, v, hp, t)
+        assert np.array_equal(p16, want)
+        assert np.array_equal(m.view(np.uint32), m2.view(np.uint32))
+        assert np.array_equal(v.view(np.uint32), v2.view(np.uint32))
+
+
+def test_bf16_first_step_closed_form():
+    n, W = 8192, 4
+    hp = hp_f32()
+    G = grads_bf16(W, n, 1)
+    p0 = O.bf16_round(master_f32(n))
+    p = p0.copy()
+    O.step_bf16(G, p, np.zeros(n, np.float32), np.zeros(n, np.float32), hp,
+                1)
+    g = O.reduce_mean(G).astype(np.float64)
+    th0 = O.bf16_to_f32(p0).astype(np.float64)
+    lr, wd, eps = hp.lr, hp.weight_decay, hp.eps
+    ref = th0 * (1 - lr * wd) - lr * g / (np.abs(g) + eps)
+    # the fp32 value is within a few roundings of ref, so its bf16 rounding
+    # is ref's bf16 rounding or a neighbour
+    refb = O.bf16_round(ref.astype(np.float32))
+    assert np.abs(bf16_ordinal(p) - bf16_ordinal(refb)).max() <= 1
+
+
+def test_bf16_zero_lr_keeps_the_parameter_and_small_updates_vanish():
+    n, W = 2048, 2
+    G = grads_bf16(W, n, 1)
+    p0 = O.bf16_round(master_f32(n))
+    p = p0.copy()
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    O.step_bf16(G, p, m, v, hp_f32(lr=0.0), 1)
+    assert np.array_equal(p, p0) and np.any(m != 0)
+    # parameters of 1.0: an Adam step of 1e-5 is below half an ulp of bf16
+    # (2^-8 at 1.0), so with no decay the parameter never moves, step after
+    # step; an fp32 master would have moved by about 3e-5 after 3 steps
+    one = np.full(n, 0x3f80, np.uint16)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    for t in (1, 2, 3):
+        O.step_bf16(grads_bf16(W, n, t), one, m, v,
+                    hp_f32(lr=1e-5, weight_decay=0.0), t)
+    assert np.all(one == 0x3f80)

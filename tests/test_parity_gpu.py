@@ -20,8 +20,9 @@ import torch
 import synth
 import zero_sharded_optimizer_shard_amd as zs
 from oracle import step as O
-from oracle.layout import (TILE, build_layout, from_tiled_state, tile_slot,
-                           tile_slot_range, to_tiled_grads, to_tiled_state)
+from oracle.layout import (TILE, build_layout, from_tiled_rows,
+                           from_tiled_state, tile_slot, tile_slot_range,
+                           to_tiled_grads, to_tiled_rows, to_tiled_state)
 from oracle.pack import gather, owner_runs, pack_flat, pack_tensors
 from synth import state as S
 from synth import workloads as wl
@@ -714,6 +715,134 @@ def test_gather_llama8b_layers_sampled():
             assert np.array_equal(np16(out[a - lo:a - lo + k]), want), \
                 (t0, a, k)
         assert np.all(np16(out[hi - lo:]) == 0x5a5a)
+
+
+@pytest.mark.parametrize("flat_params", [False, True])
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("W", [1, 3, 8, 16, 64])
+def test_pure_bf16_step(W, layout, flat_params):
+    """zs_step_bf16 (no fp32 master, 12 B/param) against the oracle, bit for
+    bit, three steps with warm moments; parameters as the bf16 shard or in
+    place in the flat buffer (other ranks' positions untouched)."""
+    rng = random.Random(100 + W)
+    numels = [rng.choice([7, 129, 1000, 4096, 33333, 65536])
+              for _ in range(9)]
+    cap = W * 256 * rng.choice([3, 17, 40])
+    rank = W - 1
+    lay_o = build_layout(numels, W, rank, cap)
+    lay = zs.zs_layout_build(numels, W, rank, cap)
+    n, F = lay_o.shard_numel, lay_o.flat_numel
+    pad = S.padding_runs(n, lay_o.chunks)
+    say(f"case bf16 W={W} {layout} flat={flat_params}")
+    om, omm, ov = S.cpu_state(0, n, 0.02, W, pad, (1e-4, 1e-8))
+    p16 = O.bf16_round(om)
+    m_d, v_d = (torch.from_numpy(x.copy()).cuda() for x in (omm, ov))
+    state = dev_f32(lay_o.n_tiles * 2 * TILE)
+    state.fill_(float("nan"))
+    zs.zs_state_mv_pack(lay, m_d, v_d, state)
+    assert np.array_equal(npf(state), to_tiled_rows(lay_o, [omm, ov]))
+    if flat_params:
+        sentinel = synth.cpu_bits16(F, 7, synth.TAG_SENTINEL, 0, 0, 0)
+        host_flat = sentinel.copy()
+        pack_flat(lay_o, p16, host_flat)
+        params = torch.from_numpy(host_flat.view(np.int16)).cuda()
+    else:
+        params = torch.from_numpy(p16.view(np.int16).copy()).cuda()
+    G = torch.empty((W, n + 8), dtype=torch.bfloat16, device="cuda")
+    Gt = dev_bf16(lay_o.n_tiles * W * TILE)
+    for t in (1, 2, 3):
+        S.dev_grads(G, W, n, t, 1e-3, W, pad)
+        if layout == "tiled":
+            zs.zs_grads_tile(lay, -1, G, n + 8, Gt)
+            zs.zs_step_bf16(lay, Gt, state, params, params_flat=flat_params,
+                            grad_layout="tiled", step=t, **HP)
+        else:
+            zs.zs_step_bf16(lay, G, state, params, params_flat=flat_params,
+                            grad_stride=n + 8, step=t, **HP)
+        O.step_bf16(S.cpu_grads(W, 0, n, t, 1e-3, W, pad), p16, omm, ov,
+                    OHP, t)
+        torch.cuda.synchronize()
+        m_g, v_g = from_tiled_rows(lay_o, npf(state), 2)
+        if flat_params:
+            want = sentinel.copy()
+            pack_flat(lay_o, p16, want)
+            got_p = np16(params)
+        else:
+            want, got_p = p16, np16(params)
+        assert np.array_equal(got_p, want), f"params t={t}"
+        assert np.array_equal(m_g.view(np.uint32), omm.view(np.uint32))
+        assert np.array_equal(v_g.view(np.uint32), ov.view(np.uint32))
+    outs = [dev_f32(n), dev_f32(n)]
+    zs.zs_state_mv_unpack(lay, state, *outs)
+    assert np.array_equal(npf(outs[0]), omm)
+    assert np.array_equal(npf(outs[1]), ov)
+
+
+def test_pure_bf16_llama8b_flat_sampled():
+    """Full-size Llama-3-8B-shaped W=8 rank-0 shard, pure bf16, tiled
+    gradients, parameters updated in place in the flat buffer; sampled
+    windows against the oracle after each of two steps."""
+    w = wl.presets()["llama8b"]
+    lay_o = build_layout(w.numels, w.world, 0)
+    lay = zs.zs_layout_build(w.numels, w.world, 0)
+    n, W = lay_o.shard_numel, w.world
+    say(f"case bf16 full-size llama8b: W={W} shard={n}")
+    state = dev_f32(lay_o.n_tiles * 2 * TILE)
+    zs.zs_state_mv_pack(lay, None, None, state)
+    master = dev_f32(n)
+    synth.dev_normal_f32(master, 0, synth.TAG_MASTER, 0, 0, 0,
+                         w.master_sigma)
+    shard16 = dev_bf16(n)
+    flat = dev_bf16(lay_o.flat_numel)
+    flat.view(torch.int16).fill_(0x7fc0)
+    # the initial bf16 parameters: the master rounded on the host, per window
+    wins = sample_windows(lay_o, n_random=8)
+    G = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
+    Gt = dev_bf16(lay_o.n_tiles * W * TILE)
+    # round the device master to bf16 through the oracle's rule, window by
+    # window, and place the whole shard with the pack (its own parity test)
+    host_master = npf(master)
+    del master
+    shard16.copy_(torch.from_numpy(O.bf16_round(host_master).view(np.int16)
+                                   ).view(torch.bfloat16).cuda())
+    zs.zs_pack(lay, shard16, flat)
+    ref = {}
+    for a, k in wins:
+        ref[(a, k)] = [O.bf16_round(host_master[a:a + k]),
+                       np.zeros(k, np.float32), np.zeros(k, np.float32)]
+    del host_master
+    for t in (1, 2):
+        S.dev_grads(G, W, n, t, w.grad_sigma)
+        zs.zs_grads_tile(lay, -1, G, n, Gt)
+        zs.zs_step_bf16(lay, Gt, state, flat, params_flat=True,
+                        grad_layout="tiled", step=t, **HP)
+        torch.cuda.synchronize()
+        st2 = state.view(lay_o.n_tiles, 2, TILE)
+        slot = None
+        for (a, k), (p16, mm, vv) in ref.items():
+            O.step_bf16(S.cpu_grads(W, a, k, t, w.grad_sigma), p16, mm, vv,
+                        OHP, t)
+            got_p = np.empty(k, np.uint16)
+            for b in lay_o.buckets:
+                lo, hi = max(a, b.shard_off), min(a + k, b.shard_off
+                                                  + b.slice_numel)
+                if hi > lo:
+                    f0 = b.flat_off + (lo - b.shard_off)
+                    got_p[lo - a:hi - a] = np16(flat[f0:f0 + hi - lo])
+            assert np.array_equal(got_p, p16), f"t={t} window {a}+{k}"
+            sl = []
+            for b_id, b in enumerate(lay_o.buckets):
+                lo, hi = max(a, b.shard_off), min(a + k, b.shard_off
+                                                  + b.slice_numel)
+                if hi > lo:
+                    sl.append(tile_slot_range(lay_o, b_id, lo - b.shard_off,
+                                              hi - lo))
+            slot = torch.from_numpy(np.concatenate(sl)).cuda()
+            ti, pi = slot // TILE, slot % TILE
+            assert np.array_equal(npf(st2[ti, 0, pi]).view(np.uint32),
+                                  mm.view(np.uint32))
+            assert np.array_equal(npf(st2[ti, 1, pi]).view(np.uint32),
+                                  vv.view(np.uint32))
 
 
 def test_two_runs_are_bit_identical():

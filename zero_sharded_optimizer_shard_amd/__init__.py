@@ -12,7 +12,8 @@ from ._zs import (EXPORTS, LIB_PATH, ZS_GRADS_SLICES, ZS_GRADS_TILED,
                   zs_last_error, zs_layout_buckets, zs_layout_build,
                   zs_layout_chunks, zs_layout_info, zs_layout_rank,
                   zs_layout_tensor_offsets, zs_layout_tiles, zs_pack,
-                  zs_state_pack, zs_state_unpack, zs_step, zs_strerror)
+                  zs_state_mv_pack, zs_state_mv_unpack, zs_state_pack,
+                  zs_state_unpack, zs_step, zs_step_bf16, zs_strerror)
 
 __all__ = ["EXPORTS", "LIB_PATH", "ZS_GRADS_SLICES", "ZS_GRADS_TILED",
            "ZS_GATHER_MAX_WORLD", "ZS_MAX_GROUP", "ZS_TILE", "Layout",
@@ -22,4 +23,5 @@ __all__ = ["EXPORTS", "LIB_PATH", "ZS_GRADS_SLICES", "ZS_GRADS_TILED",
            "zs_last_error", "zs_layout_buckets", "zs_layout_build",
            "zs_layout_chunks", "zs_layout_info", "zs_layout_rank",
            "zs_layout_tensor_offsets", "zs_layout_tiles", "zs_pack",
-           "zs_state_pack", "zs_state_unpack", "zs_step", "zs_strerror"]
+           "zs_state_mv_pack", "zs_state_mv_unpack", "zs_state_pack",
+           "zs_state_unpack", "zs_step", "zs_step_bf16", "zs_strerror"]

@@ -52,7 +52,8 @@ EXPORTS = ["zs_layout_build", "zs_layout_info", "zs_layout_tiles",
            "zs_layout_tensor_offsets", "zs_layout_rank", "zs_layout_free",
            "zs_step", "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
            "zs_state_unpack",
-           "zs_grads_tile", "zs_gather", "zs_pack", "zs_strerror",
+           "zs_grads_tile", "zs_gather", "zs_pack", "zs_step_bf16",
+           "zs_state_mv_pack", "zs_state_mv_unpack", "zs_strerror",
            "zs_last_error"]
 
 
@@ -86,6 +87,10 @@ def lib():
     L.zs_state_unpack.argtypes = [p, p, p, p, p, p]
     L.zs_grads_tile.argtypes = [p, i32, p, i64, p, p]
     L.zs_gather.argtypes = [p, P(p), i64, i64, p, p]
+    L.zs_step_bf16.argtypes = [p, p, i32, i64, p, p, i32, P(zs_adamw), i64,
+                               p]
+    L.zs_state_mv_pack.argtypes = [p, p, p, p, p]
+    L.zs_state_mv_unpack.argtypes = [p, p, p, p, p]
     L.zs_pack.argtypes = [p, p, p, p, i32, p, p]
     L.zs_strerror.argtypes = [ctypes.c_int]
     L.zs_strerror.restype = ctypes.c_char_p
@@ -96,7 +101,8 @@ def lib():
                  "zs_layout_tensor_offsets", "zs_layout_rank", "zs_step",
                  "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
                  "zs_state_unpack",
-                 "zs_grads_tile", "zs_gather", "zs_pack"):
+                 "zs_grads_tile", "zs_gather", "zs_pack", "zs_step_bf16",
+                 "zs_state_mv_pack", "zs_state_mv_unpack"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -319,6 +325,39 @@ def zs_grads_tile(layout: Layout, bucket_id: int, slices, stride: int,
                                _bf16(slices, "slices"), stride,
                                _bf16(tiled, "tiled"), _stream(stream)),
            "zs_grads_tile")
+
+
+def zs_step_bf16(layout: Layout, grads, state_mv, params, *,
+                 params_flat: bool = False, grad_layout="slices",
+                 grad_stride: int = 0, lr: float, beta1: float, beta2: float,
+                 eps: float, weight_decay: float, step: int,
+                 stream=None) -> None:
+    """Pure-bf16 step: params (bf16 shard, or the flat buffer when
+    params_flat) updated in place; state_mv tiled [tiles][2][ZS_TILE]."""
+    hp = _hp(lr, beta1, beta2, eps, weight_decay)
+    _check(lib().zs_step_bf16(layout.handle, _bf16(grads, "grads"),
+                              _layout_code(grad_layout), grad_stride,
+                              _f32(state_mv, "state_mv"),
+                              _bf16(params, "params"), int(params_flat),
+                              ctypes.byref(hp), step, _stream(stream)),
+           "zs_step_bf16")
+
+
+def zs_state_mv_pack(layout: Layout, m, v, state_mv, stream=None) -> None:
+    _check(lib().zs_state_mv_pack(layout.handle,
+                                  None if m is None else _f32(m, "m"),
+                                  None if v is None else _f32(v, "v"),
+                                  _f32(state_mv, "state_mv"),
+                                  _stream(stream)), "zs_state_mv_pack")
+
+
+def zs_state_mv_unpack(layout: Layout, state_mv, m=None, v=None,
+                       stream=None) -> None:
+    _check(lib().zs_state_mv_unpack(layout.handle,
+                                    _f32(state_mv, "state_mv"),
+                                    None if m is None else _f32(m, "m"),
+                                    None if v is None else _f32(v, "v"),
+                                    _stream(stream)), "zs_state_mv_unpack")
 
 
 def zs_gather(layout: Layout, shards, flat_lo: int, flat_hi: int, out,

@@ -40,6 +40,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 #include <type_traits>
 
 #include "zs_internal.h"
@@ -249,7 +250,11 @@ __device__ __forceinline__ void reduce(const uint16_t* __restrict__ g0,
 // slices: gs = the slice stride), st the tile's state rows, ps / fl the
 // tile's first bf16 output (each nullable).  This workgroup is part
 // blockIdx.x % P of SH::P on the tile.
-template <int WT, class SH>
+//
+// PURE (the pure-bf16 variant, no fp32 master): the state tile holds only
+// the rows m and v, and the parameter is the bf16 value itself, read from
+// and written back to ps if it is given, else fl.
+template <int WT, class SH, bool PURE = false>
 __device__ __forceinline__ void step_tile(const uint16_t* __restrict__ g0,
                                           int64_t gs, float* __restrict__ st,
                                           uint16_t* __restrict__ ps,
@@ -260,15 +265,23 @@ __device__ __forceinline__ void step_tile(const uint16_t* __restrict__ g0,
     constexpr int U = SH::U;
     const bool full = nvalid == kTile;
 
-    // fp32 state first: its loads do not depend on the gradients
+    // state first: its loads do not depend on the gradients
+    uint16_t* const pp = PURE ? (ps ? ps : fl) : nullptr;
+    constexpr int kM = PURE ? 0 : 1;        // row of m; v follows
     f32x4 th[U], mm[U], vv[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         const int jj = unit_off<SH::P, SH::NT>(k);
         if (full || jj < nvalid) {
-            th[k] = ld4(st + jj);
-            mm[k] = ld4(st + kTile + jj);
-            vv[k] = ld4(st + 2 * kTile + jj);
+            if constexpr (PURE) {
+                const u32x2 q = ld2(pp + jj);
+                th[k] = f32x4{bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y),
+                              bf16_hi(q.y)};
+            } else {
+                th[k] = ld4(st + jj);
+            }
+            mm[k] = ld4(st + kM * kTile + jj);
+            vv[k] = ld4(st + (kM + 1) * kTile + jj);
         }
     }
 
@@ -300,19 +313,24 @@ __device__ __forceinline__ void step_tile(const uint16_t* __restrict__ g0,
             t4[i] = t;
             pb[i] = to_bf16(t);
         }
-        st4(st + jj, f32x4{t4[0], t4[1], t4[2], t4[3]});
-        st4(st + kTile + jj, f32x4{m4[0], m4[1], m4[2], m4[3]});
-        st4(st + 2 * kTile + jj, f32x4{v4[0], v4[1], v4[2], v4[3]});
+        if constexpr (!PURE)
+            st4(st + jj, f32x4{t4[0], t4[1], t4[2], t4[3]});
+        st4(st + kM * kTile + jj, f32x4{m4[0], m4[1], m4[2], m4[3]});
+        st4(st + (kM + 1) * kTile + jj, f32x4{v4[0], v4[1], v4[2], v4[3]});
         const u32x2 p = {pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
-        if (ps)
-            st2(ps + jj, p);
-        if (fl)
-            st2(fl + jj, p);
+        if constexpr (PURE) {
+            st2(pp + jj, p);
+        } else {
+            if (ps)
+                st2(ps + jj, p);
+            if (fl)
+                st2(fl + jj, p);
+        }
     }
 }
 
 // Whole-shard step: blockIdx.y = bucket, blockIdx.x = tile * P + part.
-template <int WT, bool TILED, class SH>
+template <int WT, bool TILED, class SH, bool PURE>
 __global__ __launch_bounds__(SH::NT) void step_kernel(StepArgs a)
 {
     TileRef r;
@@ -321,8 +339,8 @@ __global__ __launch_bounds__(SH::NT) void step_kernel(StepArgs a)
     const int W = WT > 0 ? WT : a.W;
     const uint16_t* g0 = TILED ? a.grads + r.tile * (int64_t)W * kTile
                                : a.grads + r.e0;
-    step_tile<WT, SH>(g0, TILED ? kTile : a.gstride,
-                      a.state + r.tile * (3 * kTile),
+    step_tile<WT, SH, PURE>(g0, TILED ? kTile : a.gstride,
+                      a.state + r.tile * ((PURE ? 2 : 3) * kTile),
                       a.pshard ? a.pshard + r.e0 : nullptr,
                       a.flat ? a.flat + r.fpos : nullptr, r.nvalid, W, a.c);
 }
@@ -366,48 +384,54 @@ __global__ __launch_bounds__(SH::NT) void group_step_kernel(GroupArgs a)
 
 // ---- layout conversions ------------------------------------------------------
 
-// plain master/m/v -> tiled state; padding positions written as zero
+// Up to three plain fp32 arrays, one per row of a tiled state of ROWS rows
+// (3: master, m, v; 2: m, v).
+struct Rows {
+    const float* in[3];         // pack: sources, NULL = zeros
+    float* out[3];              // unpack: destinations, NULL = skipped
+};
+
+// plain rows -> tiled state; padding positions written as zero
+template <int ROWS>
 __global__ __launch_bounds__(kThreads) void state_pack_kernel(
-    const float* __restrict__ master, const float* __restrict__ m,
-    const float* __restrict__ v, float* __restrict__ state, Geom g)
+    Rows rw, float* __restrict__ state, Geom g)
 {
     TileRef r;
     if (!tile_of(g, r))
         return;
-    float* st = state + r.tile * (3 * kTile);
+    float* st = state + r.tile * (ROWS * kTile);
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kUnits; ++k) {
         const int jj = unit_off(k);
-        f32x4 a = z, b = z, c = z;
-        if (jj < r.nvalid) {
-            a = ld4(master + r.e0 + jj);
-            if (m) b = ld4(m + r.e0 + jj);
-            if (v) c = ld4(v + r.e0 + jj);
+#pragma unroll
+        for (int row = 0; row < ROWS; ++row) {
+            f32x4 x = z;
+            if (jj < r.nvalid && rw.in[row])
+                x = ld4(rw.in[row] + r.e0 + jj);
+            st4(st + row * kTile + jj, x);
         }
-        st4(st + jj, a);
-        st4(st + kTile + jj, b);
-        st4(st + 2 * kTile + jj, c);
     }
 }
 
-// tiled state -> plain master/m/v (each nullable)
+// tiled state -> plain rows (each nullable)
+template <int ROWS>
 __global__ __launch_bounds__(kThreads) void state_unpack_kernel(
-    const float* __restrict__ state, float* __restrict__ master,
-    float* __restrict__ m, float* __restrict__ v, Geom g)
+    const float* __restrict__ state, Rows rw, Geom g)
 {
     TileRef r;
     if (!tile_of(g, r))
         return;
-    const float* st = state + r.tile * (3 * kTile);
+    const float* st = state + r.tile * (ROWS * kTile);
 #pragma unroll
     for (int k = 0; k < kUnits; ++k) {
         const int jj = unit_off(k);
         if (jj >= r.nvalid)
             continue;
-        if (master) st4(master + r.e0 + jj, ld4(st + jj));
-        if (m) st4(m + r.e0 + jj, ld4(st + kTile + jj));
-        if (v) st4(v + r.e0 + jj, ld4(st + 2 * kTile + jj));
+#pragma unroll
+        for (int row = 0; row < ROWS; ++row)
+            if (rw.out[row])
+                st4(rw.out[row] + r.e0 + jj, ld4(st + row * kTile + jj));
     }
 }
 
@@ -576,25 +600,25 @@ Geom bucket_geom(const zs_layout* L, const zs_bucket& b)
 }
 
 // Kernel choice: Args = StepArgs (whole shard) or GroupArgs (buckets).
-template <int WT, bool TILED, class SH, class Args>
+template <int WT, bool TILED, class SH, bool PURE, class Args>
 void launch_kernel(const Args& a, dim3 grid, hipStream_t s)
 {
     grid.x *= SH::P;
     if constexpr (std::is_same<Args, StepArgs>::value)
-        hipLaunchKernelGGL((step_kernel<WT, TILED, SH>), grid, dim3(SH::NT),
-                           0, s, a);
+        hipLaunchKernelGGL((step_kernel<WT, TILED, SH, PURE>), grid,
+                           dim3(SH::NT), 0, s, a);
     else
         hipLaunchKernelGGL((group_step_kernel<WT, TILED, SH>), grid,
                            dim3(SH::NT), 0, s, a);
 }
 
-template <int WT, class SH, class Args>
+template <int WT, class SH, bool PURE, class Args>
 void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 {
     if (tiled)
-        launch_kernel<WT, true, SH>(a, grid, s);
+        launch_kernel<WT, true, SH, PURE>(a, grid, s);
     else
-        launch_kernel<WT, false, SH>(a, grid, s);
+        launch_kernel<WT, false, SH, PURE>(a, grid, s);
 }
 
 // Work shapes, chosen by measurement on MI355X (8B-shaped shard at W = 8
@@ -612,30 +636,30 @@ using ShapeSmall = Shape<512, 1, 4>;
 constexpr int64_t kSmallLaunch = 1024;
 
 // grid: one x per tile (launch_kernel multiplies by the shape's P)
-template <int WT, class Args>
+template <int WT, bool PURE, class Args>
 void launch_step_w(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 {
     const int64_t tiles = (int64_t)grid.x * grid.y;
     if (tiles < kSmallLaunch)
-        launch_shape<WT, ShapeSmall>(a, tiled, grid, s);
+        launch_shape<WT, ShapeSmall, PURE>(a, tiled, grid, s);
     else if constexpr (WT >= 32)
-        launch_shape<WT, ShapeDeep>(a, tiled, grid, s);
+        launch_shape<WT, ShapeDeep, PURE>(a, tiled, grid, s);
     else
-        launch_shape<WT, ShapeWide>(a, tiled, grid, s);
+        launch_shape<WT, ShapeWide, PURE>(a, tiled, grid, s);
 }
 
-template <class Args>
+template <bool PURE = false, class Args>
 int launch_step(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 {
     switch (a.W) {
-    case 1: launch_step_w<1>(a, tiled, grid, s); break;
-    case 2: launch_step_w<2>(a, tiled, grid, s); break;
-    case 4: launch_step_w<4>(a, tiled, grid, s); break;
-    case 8: launch_step_w<8>(a, tiled, grid, s); break;
-    case 16: launch_step_w<16>(a, tiled, grid, s); break;
-    case 32: launch_step_w<32>(a, tiled, grid, s); break;
-    case 64: launch_step_w<64>(a, tiled, grid, s); break;
-    default: launch_step_w<0>(a, tiled, grid, s); break;
+    case 1: launch_step_w<1, PURE>(a, tiled, grid, s); break;
+    case 2: launch_step_w<2, PURE>(a, tiled, grid, s); break;
+    case 4: launch_step_w<4, PURE>(a, tiled, grid, s); break;
+    case 8: launch_step_w<8, PURE>(a, tiled, grid, s); break;
+    case 16: launch_step_w<16, PURE>(a, tiled, grid, s); break;
+    case 32: launch_step_w<32, PURE>(a, tiled, grid, s); break;
+    case 64: launch_step_w<64, PURE>(a, tiled, grid, s); break;
+    default: launch_step_w<0, PURE>(a, tiled, grid, s); break;
     }
     return check_launch("step kernel");
 }
@@ -779,6 +803,47 @@ extern "C" int zs_bucket_step(const zs_layout* L, int32_t bucket_id,
                            step, hip_stream);
 }
 
+namespace {
+
+// Pack (unpack) ROWS plain arrays into (out of) a tiled state.
+template <int ROWS>
+int convert_state(const zs_layout* L, bool pack, const float* const* in,
+                  float* const* out, float* state_w, const float* state_r,
+                  void* hip_stream)
+{
+    Rows base{};
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    return for_shard_ranges(L, [&](const Range& R) {
+        const zs_bucket& b0 = L->buckets[R.y0];
+        const int64_t e = b0.shard_off;
+        Rows rw = base;
+        for (int row = 0; row < ROWS; ++row) {
+            rw.in[row] = (pack && in[row]) ? in[row] + e : nullptr;
+            rw.out[row] = (!pack && out[row]) ? out[row] + e : nullptr;
+        }
+        const dim3 grid((unsigned)R.g.TPB, (unsigned)R.ny);
+        const int64_t t0 = b0.tile_off * ROWS * kTile;
+        if (pack)
+            hipLaunchKernelGGL(state_pack_kernel<ROWS>, grid, dim3(kThreads),
+                               0, s, rw, state_w + t0, R.g);
+        else
+            hipLaunchKernelGGL(state_unpack_kernel<ROWS>, grid,
+                               dim3(kThreads), 0, s, state_r + t0, rw, R.g);
+        return check_launch(pack ? "state pack kernel"
+                                 : "state unpack kernel");
+    });
+}
+
+bool all_aligned16(std::initializer_list<const void*> ps)
+{
+    for (const void* p : ps)
+        if (p && !aligned16(p))
+            return false;
+    return true;
+}
+
+}  // namespace
+
 extern "C" int zs_state_pack(const zs_layout* L, const float* master,
                              const float* m, const float* v, float* state,
                              void* hip_stream)
@@ -789,20 +854,11 @@ extern "C" int zs_state_pack(const zs_layout* L, const float* master,
     if (L->shard_numel == 0) return ZS_OK;
     if (!master || !state)
         return fail(ZS_EINVAL, "master and state must be non-NULL");
-    if (!aligned16(master) || !aligned16(state) || (m && !aligned16(m)) ||
-        (v && !aligned16(v)))
+    if (!all_aligned16({master, m, v, state}))
         return fail(ZS_EALIGN, "device pointers must be 16-byte aligned");
-    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    return for_shard_ranges(L, [&](const Range& R) {
-        const zs_bucket& b0 = L->buckets[R.y0];
-        const int64_t e = b0.shard_off;
-        hipLaunchKernelGGL(state_pack_kernel,
-                           dim3((unsigned)R.g.TPB, (unsigned)R.ny),
-                           dim3(kThreads), 0, s, master + e,
-                           m ? m + e : nullptr, v ? v + e : nullptr,
-                           state + b0.tile_off * 3 * kTile, R.g);
-        return check_launch("state pack kernel");
-    });
+    const float* in[3] = {master, m, v};
+    return convert_state<3>(L, true, in, nullptr, state, nullptr,
+                            hip_stream);
 }
 
 extern "C" int zs_state_unpack(const zs_layout* L, const float* state,
@@ -814,21 +870,85 @@ extern "C" int zs_state_unpack(const zs_layout* L, const float* state,
     if (!L) return fail(ZS_EINVAL, "layout is NULL");
     if (L->shard_numel == 0) return ZS_OK;
     if (!state) return fail(ZS_EINVAL, "state is NULL");
-    if (!aligned16(state) || (master && !aligned16(master)) ||
-        (m && !aligned16(m)) || (v && !aligned16(v)))
+    if (!all_aligned16({state, master, m, v}))
         return fail(ZS_EALIGN, "device pointers must be 16-byte aligned");
     if (!master && !m && !v) return ZS_OK;
+    float* out[3] = {master, m, v};
+    return convert_state<3>(L, false, nullptr, out, nullptr, state,
+                            hip_stream);
+}
+
+extern "C" int zs_state_mv_pack(const zs_layout* L, const float* m,
+                                const float* v, float* state_mv,
+                                void* hip_stream)
+{
+    using zs::fail;
+    zs::clear_error();
+    if (!L) return fail(ZS_EINVAL, "layout is NULL");
+    if (L->shard_numel == 0) return ZS_OK;
+    if (!state_mv) return fail(ZS_EINVAL, "state_mv is NULL");
+    if (!all_aligned16({m, v, state_mv}))
+        return fail(ZS_EALIGN, "device pointers must be 16-byte aligned");
+    const float* in[3] = {m, v, nullptr};
+    return convert_state<2>(L, true, in, nullptr, state_mv, nullptr,
+                            hip_stream);
+}
+
+extern "C" int zs_state_mv_unpack(const zs_layout* L, const float* state_mv,
+                                  float* m, float* v, void* hip_stream)
+{
+    using zs::fail;
+    zs::clear_error();
+    if (!L) return fail(ZS_EINVAL, "layout is NULL");
+    if (L->shard_numel == 0) return ZS_OK;
+    if (!state_mv) return fail(ZS_EINVAL, "state_mv is NULL");
+    if (!all_aligned16({state_mv, m, v}))
+        return fail(ZS_EALIGN, "device pointers must be 16-byte aligned");
+    if (!m && !v) return ZS_OK;
+    float* out[3] = {m, v, nullptr};
+    return convert_state<2>(L, false, nullptr, out, nullptr, state_mv,
+                            hip_stream);
+}
+
+extern "C" int zs_step_bf16(const zs_layout* L, const uint16_t* grads,
+                            int32_t grad_layout, int64_t grad_stride,
+                            float* state_mv, uint16_t* params,
+                            int32_t params_flat, const zs_adamw* hp,
+                            int64_t step, void* hip_stream)
+{
+    using zs::fail;
+    zs::clear_error();
+    if (!L) return fail(ZS_EINVAL, "layout is NULL");
+    if (!hp) return fail(ZS_EINVAL, "hp is NULL");
+    if (step < 1) return fail(ZS_EINVAL, "step %lld < 1", (long long)step);
+    if (params_flat != 0 && params_flat != 1)
+        return fail(ZS_EINVAL, "params_flat must be 0 or 1");
+    if (L->shard_numel == 0)
+        return ZS_OK;
+    uint16_t* pshard = params_flat ? nullptr : params;
+    uint16_t* flat = params_flat ? params : nullptr;
+    int rc = check_step_args(L, grads, grad_layout, grad_stride,
+                             L->shard_numel, state_mv, pshard, flat, hp,
+                             step);
+    if (rc) return rc;
+    const bool tiled = grad_layout == ZS_GRADS_TILED;
+    const int32_t W = L->world;
+    const Consts c = make_consts(*hp, step, W);
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
     return for_shard_ranges(L, [&](const Range& R) {
         const zs_bucket& b0 = L->buckets[R.y0];
-        const int64_t e = b0.shard_off;
-        hipLaunchKernelGGL(state_unpack_kernel,
-                           dim3((unsigned)R.g.TPB, (unsigned)R.ny),
-                           dim3(kThreads), 0, s,
-                           state + b0.tile_off * 3 * kTile,
-                           master ? master + e : nullptr,
-                           m ? m + e : nullptr, v ? v + e : nullptr, R.g);
-        return check_launch("state unpack kernel");
+        StepArgs a;
+        a.grads = tiled ? grads + b0.tile_off * W * kTile
+                        : grads + b0.shard_off;
+        a.gstride = grad_stride;
+        a.state = state_mv + b0.tile_off * 2 * kTile;
+        a.pshard = pshard ? pshard + b0.shard_off : nullptr;
+        a.flat = flat ? flat + b0.flat_off : nullptr;
+        a.g = R.g;
+        a.W = W;
+        a.c = c;
+        return launch_step<true>(a, tiled,
+                                 dim3((unsigned)R.g.TPB, (unsigned)R.ny), s);
     });
 }
 
