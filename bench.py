@@ -219,6 +219,73 @@ def bf16_main(args, w):
     print(json.dumps(out), flush=True)
 
 
+def accumulate_main(args, w):
+    """Gradient accumulation over K micro-batches on the full flat bf16
+    gradient buffer of the workload (what backward produces on every rank
+    before the bucketed reduce-scatter): the first call starts the fp32
+    accumulator, K - 2 calls add, the last adds, divides by K and writes
+    the bf16 bucket in place over the last micro-batch's gradient.  Bytes
+    per element per cycle: 6 + 10 (K - 2) + 8."""
+    import torch
+    import synth
+    import zero_sharded_optimizer_shard_amd as zs
+
+    K = args.accumulate
+    if K < 2:
+        raise SystemExit("--accumulate needs K >= 2")
+    lay = zs.zs_layout_build(w.numels, w.world, w.rank)
+    flat_n = zs.zs_layout_info(lay)[0]
+    log(f"workload {w.name} gradient accumulation: {flat_n} elements, "
+        f"{K} micro-batches")
+    grads = [torch.empty(flat_n, dtype=torch.bfloat16, device="cuda")
+             for _ in range(2)]
+    for j, g in enumerate(grads):
+        synth.dev_normal_bf16(g, 0, synth.TAG_GRAD, j, 0, 0, w.grad_sigma)
+    acc = torch.empty(flat_n, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+
+    def cycle():
+        zs.zs_accumulate(zs.ZS_ACC_FIRST, acc, grads[0], stream=st)
+        for j in range(1, K - 1):
+            zs.zs_accumulate(zs.ZS_ACC_ADD, acc, grads[j % 2], stream=st)
+        zs.zs_accumulate(zs.ZS_ACC_LAST, acc, grads[1], grads[1], k=K,
+                         stream=st)
+
+    for _ in range(args.warmup):
+        cycle()
+    R = max(1, min(args.steps, 10))
+    avg_ms, wall_ms = time_steps(cycle, R, st)
+    bpe = 6 + 10 * (K - 2) + 8
+    gbs = bpe * flat_n / (avg_ms * 1e-3) / 1e9
+    log(f"accumulation cycle: {avg_ms:.3f} ms -> {gbs:.0f} GB/s "
+        f"({gbs / PEAK_HBM_GBS:.1%} of 8 TB/s)")
+    out = {
+        "metric": "gradient accumulation, micro-batch gradients per second "
+                  "per GPU (elements)",
+        "value": K * flat_n / (wall_ms * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": R,
+        "warmup": args.warmup,
+        "ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} flat gradient buffer, {K} "
+                               f"micro-batches",
+                   "elements": flat_n, "micro_batches": K,
+                   "bytes_per_element_per_cycle": bpe},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                     "traffic": None},
+        "kernel_ms": {"avg": avg_ms},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def fsdp_units(numels):
     """FSDP wrapping units of a Llama-shaped list (embed, L x [attn_norm, q,
     k, v, o, ffn_norm, gate, up, down], final norm, lm_head): the
@@ -555,6 +622,9 @@ def main():
     ap.add_argument("--pure-bf16", action="store_true",
                     help="pure-bf16 step (no fp32 master, 12 B/param): "
                     "zs_step_bf16 on the flat buffer in place")
+    ap.add_argument("--accumulate", type=int, default=0, metavar="K",
+                    help="gradient accumulation over K micro-batches "
+                    "(zs_accumulate) on the workload's flat gradient buffer")
     ap.add_argument("--zero3", action="store_true",
                     help="ZeRO-3 / FSDP mode: per-layer parameter gather "
                     "(zs_gather) with prefetch, on the workload's layout")
@@ -595,6 +665,8 @@ def main():
         return zero3_main(args, w)
     if args.pure_bf16:
         return bf16_main(args, w)
+    if args.accumulate:
+        return accumulate_main(args, w)
     if w.streaming:
         return stream_main(args, w)
     W = w.world

@@ -243,6 +243,28 @@ int zs_state_pack(const zs_layout* layout, const float* master,
 int zs_state_unpack(const zs_layout* layout, const float* state,
                     float* master, float* m, float* v, void* hip_stream);
 
+/* ---- gradient accumulation -------------------------------------------------
+ *
+ * The step before the path: the global batch is split into k micro-batches
+ * whose gradients are added up one after another before one optimizer step
+ * (podcast summary, "Motivation" and the glossary; DDP-to-ZeRO blog 3.3,
+ * gradient_accumulation_steps).  Per element, over the bf16 gradients
+ * g_0 .. g_{k-1} of the k micro-batches, in order:
+ *   ZS_ACC_FIRST  acc = f32(g_0)
+ *   ZS_ACC_ADD    acc = acc + f32(g_j)            (j = 1 .. k-2)
+ *   ZS_ACC_LAST   out = bf16((acc + f32(g_{k-1})) / k), nearest even
+ * so out is the bf16 mean of the micro-batch gradients, summed in fp32 in
+ * order: the local gradient bucket the reduce-scatter sends.  acc: fp32
+ * [n] accumulator (not written by ZS_ACC_LAST); grad: bf16 [n]; out: bf16
+ * [n] (ZS_ACC_LAST only, may alias grad).  n: a multiple of 4; acc
+ * 16-byte aligned, grad and out 8-byte aligned; k >= 2 for ZS_ACC_LAST.
+ * Errors: ZS_EINVAL (mode, pointers, k), ZS_EALIGN (alignment, n). */
+#define ZS_ACC_FIRST 0
+#define ZS_ACC_ADD   1
+#define ZS_ACC_LAST  2
+int zs_accumulate(int32_t mode, float* acc, const uint16_t* grad,
+                  uint16_t* out, int64_t n, int32_t k, void* hip_stream);
+
 /* ---- pure-bf16 variant ----------------------------------------------------
  *
  * Training in pure bf16 keeps 12 bytes per parameter: the bf16 parameter,

@@ -55,9 +55,10 @@ def lib():
                                   ctypes.POINTER(_HP), i64]
         L.oracle_step_bf16.argtypes = [i32, p, i64, i64, p, p, p,
                                        ctypes.POINTER(_HP), i64]
+        L.oracle_accumulate.argtypes = [i32, p, i64, i64, p]
         for f in (L.oracle_constants, L.oracle_bf16_round,
                   L.oracle_reduce_mean, L.oracle_adamw, L.oracle_step,
-                  L.oracle_step_bf16):
+                  L.oracle_step_bf16, L.oracle_accumulate):
             f.restype = None
         _lib = L
     return _lib
@@ -152,3 +153,13 @@ def step_bf16(grads: np.ndarray, param: np.ndarray, m: np.ndarray,
         raise ValueError("size mismatch")
     lib().oracle_step_bf16(W, _ptr(grads), n, n, _ptr(param), _ptr(m),
                            _ptr(v), ctypes.byref(hp.c()), t)
+
+
+def accumulate(grads: np.ndarray) -> np.ndarray:
+    """Gradient accumulation: uint16 [k][n] micro-batch gradients (bf16
+    bits) -> the bf16 bits of their fp32 mean, summed in order."""
+    _check(grads, np.uint16, "grads")
+    k, n = grads.shape
+    out = np.empty(n, np.uint16)
+    lib().oracle_accumulate(k, _ptr(grads), n, n, _ptr(out))
+    return out

@@ -175,3 +175,23 @@ void oracle_step_bf16(int32_t W, const uint16_t* grads, int64_t grad_stride,
         param[i] = float_to_bf16_rne(th);
     }
 }
+
+/* Gradient accumulation into the local gradient bucket (podcast summary of
+ * "Training at thousands of GPUs", sections "Motivation" and the glossary:
+ * the global batch is split into micro-batches whose gradients are added up
+ * one after another before a single optimizer step; DDP-to-ZeRO blog 3.3:
+ * gradient_accumulation_steps).  The k micro-batch bf16 gradients of one
+ * element are summed in fp32 in micro-batch order, starting from the first,
+ * then divided by k (the mean over the micro-batches) and rounded to bf16
+ * to nearest even: that bf16 bucket is what the reduce-scatter sends.
+ * grads is [k][stride] bf16 bits; out is [n]. */
+void oracle_accumulate(int32_t k, const uint16_t* grads, int64_t stride,
+                       int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float acc = bf16_bits_to_float(grads[i]);
+        for (int32_t j = 1; j < k; ++j)
+            acc = acc + bf16_bits_to_float(grads[(int64_t)j * stride + i]);
+        out[i] = float_to_bf16_rne(acc / (float)k);
+    }
+}

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     L = zs.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -203,6 +203,17 @@ def test_step_argument_checks_need_no_device():
     assert L.zs_state_mv_pack(h, A + 4, A, A, None) == -2
     assert L.zs_state_mv_unpack(h, None, A, A, None) == -1
     assert L.zs_state_mv_unpack(h, A, A + 8, None, None) == -2
+    # gradient accumulation
+    assert L.zs_accumulate(3, A, A, A, 16, 2, None) == -1        # mode
+    assert L.zs_accumulate(2, A, A, A, 16, 1, None) == -1        # k < 2
+    assert L.zs_accumulate(0, A, A, None, 18, 2, None) == -2     # n % 4
+    assert L.zs_accumulate(0, None, A, None, 16, 2, None) == -1
+    assert L.zs_accumulate(2, A, A, None, 16, 2, None) == -1     # out
+    assert L.zs_accumulate(1, A + 8, A, None, 16, 2, None) == -2
+    assert L.zs_accumulate(2, A, A, A + 2, 16, 2, None) == -2
+    assert L.zs_accumulate(2, A + 8, A, A + 8, 16, 2, None) == -2  # acc
+    assert L.zs_accumulate(1, A, A + 4, None, 16, 2, None) == -2
+    assert L.zs_accumulate(0, None, None, None, 0, 2, None) == 0  # empty
     # gather (ZeRO-3)
     P_ = ctypes.c_void_p
     sh = (P_ * 4)(A, A, A, A)

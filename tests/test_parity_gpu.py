@@ -845,6 +845,29 @@ def test_pure_bf16_llama8b_flat_sampled():
                                   vv.view(np.uint32))
 
 
+@pytest.mark.parametrize("k", [2, 3, 4, 8])
+def test_gradient_accumulation(k):
+    """zs_accumulate over k micro-batches against the oracle, bit for bit;
+    a length that ends inside a chunk; the last call writing over the
+    last micro-batch's gradient (out aliasing grad); acc untouched by it."""
+    n = 4096 * 5 + 12
+    say(f"case accumulate k={k} n={n}")
+    G = np.stack([synth.cpu_normal_bf16(n, k, synth.TAG_GRAD, j, 0, 0, 1.0)
+                  for j in range(k)])
+    G[0, :4] = [0x7fc0, 0xff80, 0x0001, 0x8000]     # NaN, -Inf, denormal, -0
+    want = O.accumulate(G)
+    dG = torch.from_numpy(G.view(np.int16)).cuda()
+    acc = dev_f32(n)
+    zs.zs_accumulate(zs.ZS_ACC_FIRST, acc, dG[0])
+    for j in range(1, k - 1):
+        zs.zs_accumulate(zs.ZS_ACC_ADD, acc, dG[j])
+    before = acc.clone()
+    zs.zs_accumulate(zs.ZS_ACC_LAST, acc, dG[k - 1], dG[k - 1], k=k)
+    torch.cuda.synchronize()
+    assert np.array_equal(np16(dG[k - 1]), want)
+    assert torch.equal(acc.view(torch.int32), before.view(torch.int32))
+
+
 def test_two_runs_are_bit_identical():
     w = wl.presets()["tiny"]
     outs = []

@@ -18,6 +18,7 @@ ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ERANGE, ZS_ENOMEM, ZS_EDEVICE = \
 ZS_TILE = 8192
 ZS_MAX_GROUP = 16
 ZS_GATHER_MAX_WORLD = 64
+ZS_ACC_FIRST, ZS_ACC_ADD, ZS_ACC_LAST = 0, 1, 2
 ZS_GRADS_SLICES, ZS_GRADS_TILED = 0, 1
 
 
@@ -53,8 +54,8 @@ EXPORTS = ["zs_layout_build", "zs_layout_info", "zs_layout_tiles",
            "zs_step", "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
            "zs_state_unpack",
            "zs_grads_tile", "zs_gather", "zs_pack", "zs_step_bf16",
-           "zs_state_mv_pack", "zs_state_mv_unpack", "zs_strerror",
-           "zs_last_error"]
+           "zs_state_mv_pack", "zs_state_mv_unpack", "zs_accumulate",
+           "zs_strerror", "zs_last_error"]
 
 
 def lib():
@@ -91,6 +92,7 @@ def lib():
                                p]
     L.zs_state_mv_pack.argtypes = [p, p, p, p, p]
     L.zs_state_mv_unpack.argtypes = [p, p, p, p, p]
+    L.zs_accumulate.argtypes = [i32, p, p, p, i64, i32, p]
     L.zs_pack.argtypes = [p, p, p, p, i32, p, p]
     L.zs_strerror.argtypes = [ctypes.c_int]
     L.zs_strerror.restype = ctypes.c_char_p
@@ -102,7 +104,8 @@ def lib():
                  "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
                  "zs_state_unpack",
                  "zs_grads_tile", "zs_gather", "zs_pack", "zs_step_bf16",
-                 "zs_state_mv_pack", "zs_state_mv_unpack"):
+                 "zs_state_mv_pack", "zs_state_mv_unpack",
+                 "zs_accumulate"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -358,6 +361,16 @@ def zs_state_mv_unpack(layout: Layout, state_mv, m=None, v=None,
                                     None if m is None else _f32(m, "m"),
                                     None if v is None else _f32(v, "v"),
                                     _stream(stream)), "zs_state_mv_unpack")
+
+
+def zs_accumulate(mode: int, acc, grad, out=None, k: int = 0,
+                  stream=None) -> None:
+    """One micro-batch of gradient accumulation (ZS_ACC_FIRST / _ADD /
+    _LAST); acc fp32, grad and out bf16, all of the same length."""
+    n = grad.numel()
+    _check(lib().zs_accumulate(mode, _f32(acc, "acc"), _bf16(grad, "grad"),
+                               _bf16(out, "out"), n, k, _stream(stream)),
+           "zs_accumulate")
 
 
 def zs_gather(layout: Layout, shards, flat_lo: int, flat_hi: int, out,

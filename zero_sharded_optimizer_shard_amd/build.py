@@ -17,7 +17,8 @@ LIB = os.path.join(PKG, "libzs.so")
 
 SOURCES = [os.path.join(CSRC, "zs_layout.cpp"),
            os.path.join(CSRC, "zs_step.hip"),
-           os.path.join(CSRC, "zs_gather.hip")]
+           os.path.join(CSRC, "zs_gather.hip"),
+           os.path.join(CSRC, "zs_accum.hip")]
 
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
