@@ -245,12 +245,12 @@ def test_every_world_size(W, layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("W,tiles", [(2, 300), (2, 1100), (32, 1030),
-                                     (5, 1030)])
+@pytest.mark.parametrize("W,tiles", [(2, 300), (2, 4200), (32, 4100),
+                                     (5, 4100), (5, 1100)])
 def test_launch_shapes(W, tiles, layout):
-    """Each work shape of the step: fewer than 1024 tiles (four workgroups
-    per tile), 1024 or more at W <= 16, at W >= 32, and the runtime-W
-    kernel; one bucket per launch, a ragged last tile."""
+    """Each work shape of the step: fewer than 4096 tiles (four workgroups
+    per tile), 4096 or more at W <= 16, at W >= 32, and the runtime-W
+    kernel on both sides; one bucket per launch, a ragged last tile."""
     n_rank = tiles * TILE - 4096            # the last tile half full
     numels = [W * n_rank - 1000, 1000]
     say(f"case shape W={W} tiles={tiles} {layout}")

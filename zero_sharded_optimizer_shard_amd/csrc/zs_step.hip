@@ -627,13 +627,16 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 //    loaded 4 at a time: 112 VGPRs at W = 8, so two workgroups share a CU;
 //  - Deep (W >= 32, where gradients are most of the bytes): slices loaded
 //    8 at a time, more loads in flight per thread, one workgroup per CU;
-//  - Small (launches of fewer than kSmallLaunch tiles, i.e. bucket groups
-//    of a streaming step): one unit per thread and four workgroups per
-//    tile, so that a few hundred tiles still spread over the 256 CUs.
+//  - Small (launches of fewer than kSmallLaunch tiles: bucket groups of a
+//    streaming step, GPT-2-sized shards): one unit per thread and four
+//    workgroups per tile, so that a few hundred or thousand tiles still
+//    spread evenly over the 256 CUs with a short tail (GPT-2-shaped W = 8
+//    shard, 1899 tiles: 81 % vs 75 % with Wide; at 122 K tiles the two
+//    are equal).
 using ShapeWide = Shape<512, 4, 4>;
 using ShapeDeep = Shape<512, 4, 8>;
 using ShapeSmall = Shape<512, 1, 4>;
-constexpr int64_t kSmallLaunch = 1024;
+constexpr int64_t kSmallLaunch = 4096;
 
 // grid: one x per tile (launch_kernel multiplies by the shape's P)
 template <int WT, bool PURE, class Args>
