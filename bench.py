@@ -625,6 +625,10 @@ def main():
     ap.add_argument("--accumulate", type=int, default=0, metavar="K",
                     help="gradient accumulation over K micro-batches "
                     "(zs_accumulate) on the workload's flat gradient buffer")
+    ap.add_argument("--whole-tensors", action="store_true",
+                    help="whole-tensor shard assignment "
+                    "(zs_layout_build_tensors): every tensor on one rank, "
+                    "same step kernel over the rank's owned tensors")
     ap.add_argument("--zero3", action="store_true",
                     help="ZeRO-3 / FSDP mode: per-layer parameter gather "
                     "(zs_gather) with prefetch, on the workload's layout")
@@ -670,10 +674,13 @@ def main():
     if w.streaming:
         return stream_main(args, w)
     W = w.world
-    lay = zs.zs_layout_build(w.numels, W, w.rank)
+    if args.whole_tensors:
+        lay = zs.zs_layout_build_tensors(w.numels, W, w.rank)
+    else:
+        lay = zs.zs_layout_build(w.numels, W, w.rank)
     flat_n, n, nb, nc = zs.zs_layout_info(lay)
     log(f"workload {w.name}: W={W} shard={n} flat={flat_n} buckets={nb} "
-        f"chunks={nc}")
+        f"chunks={nc}{' (whole tensors)' if args.whole_tensors else ''}")
 
     n_tiles = zs.zs_layout_tiles(lay)
     T = zs.ZS_TILE
@@ -755,15 +762,28 @@ def main():
         extra["unfused_ms"] = dict(step=e[0].elapsed_time(e[1]),
                                    pack=e[1].elapsed_time(e[2]))
         del p
-    if args.ceiling:
+    if args.ceiling and not args.whole_tensors:
         gbs, cms = ceiling(Gt, state, flat, lay, W, n)
         extra["same_mix_ceiling"] = dict(GBps=gbs, ms=cms,
                                          frac_of_peak=gbs / PEAK_HBM_GBS)
         log(f"same-mix ceiling: {gbs:.0f} GB/s ({cms:.3f} ms)")
 
-    traffic = traffic_record(args.workload)
+    traffic = None if args.whole_tensors else traffic_record(args.workload)
+    config = {"workload": f"{w.name} rank-0 shard, W={W}",
+              "params_total": sum(w.numels), "shard_params": n,
+              "buckets": nb, "bucket_cap_mb": 25,
+              "bytes_per_param": bpp,
+              "grads_layout": "tiled [tile][W][8192]",
+              "state_layout": "tiled [tile][master|m|v][8192]"}
+    if args.whole_tensors:
+        config.update(workload=f"{w.name} rank-0 shard, W={W}, whole-tensor "
+                      "assignment", assignment="whole tensors, longest "
+                      "first to the least-loaded rank", owned_tensors=nb)
+        del config["bucket_cap_mb"]
     out = {
-        "metric": METRIC,
+        "metric": METRIC if not args.whole_tensors else
+        "whole-tensor-assignment optimizer-step params/s per GPU + achieved "
+        "HBM GB/s (% of peak)",
         "value": n / (ms_per_step * 1e-3),
         "unit": "params/s",
         "n_gpus": 1,
@@ -775,12 +795,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{w.name} rank-0 shard, W={W}",
-                   "params_total": sum(w.numels), "shard_params": n,
-                   "buckets": nb, "bucket_cap_mb": 25,
-                   "bytes_per_param": bpp,
-                   "grads_layout": "tiled [tile][W][8192]",
-                   "state_layout": "tiled [tile][master|m|v][8192]"},
+        "config": config,
         "roofline": {"bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},

@@ -113,6 +113,37 @@ int zs_layout_build(const int64_t* tensor_numel, int32_t n_tensors,
                     int32_t world, int32_t rank, int64_t bucket_cap_bytes,
                     int32_t align_bytes, zs_layout** out);
 
+/* Whole-tensor shard assignment (podcast summary, "ZeRO optimizer": an
+ * optimizer that needs whole tensors, such as Muon, cannot work on
+ * flattened slices, so the shards are assigned at whole-tensor granularity,
+ * as FSDP2 keeps whole tensors per rank).
+ *
+ * Every tensor belongs entirely to one rank, assigned greedily longest
+ * first: in order of decreasing padded size (numel rounded up to
+ * align_bytes/2 elements; ties by list index), each tensor goes to the rank
+ * with the least padded load so far (ties to the lowest rank).  Rank
+ * `rank`'s shard is its tensors in list order, each padded; each owned
+ * non-empty tensor is one bucket {flat_off = the tensor's flat offset,
+ * numel = slice_numel = its padded size, shard_off, tile_off} whose whole
+ * extent is this rank's slice, and one chunk.  The flat buffer is the same
+ * aligned flattening as zs_layout_build, rounded up to align_bytes/2
+ * elements; the padded tensors partition it.  The gradient exchange becomes
+ * a reduce of each tensor to its owner (the W source ranks' gradients of
+ * the owned tensors arrive as the [W][...] slices of this shard) and the
+ * all-gather a broadcast from the owner: zs_step, zs_step_bf16, the bucket
+ * steps, the conversions, zs_pack and zs_gather all accept such a layout.
+ * Errors as zs_layout_build. */
+int zs_layout_build_tensors(const int64_t* tensor_numel, int32_t n_tensors,
+                            int32_t world, int32_t rank, int32_t align_bytes,
+                            zs_layout** out);
+
+/* Whole-tensor layouts only: owner rank of every tensor and the tensor's
+ * offset in its owner's shard, into caller memory of `cap` entries each.
+ * Returns the tensor count, ZS_ERANGE if cap is short, ZS_EINVAL for a
+ * flat-mode layout. */
+int zs_layout_owners(const zs_layout* layout, int32_t* owner,
+                     int64_t* owner_shard_off, int32_t cap);
+
 /* Sizes: flat buffer elements (padding included), this rank's shard
  * elements, bucket count, this rank's chunk count.  Null outputs skipped. */
 int zs_layout_info(const zs_layout* layout, int64_t* flat_numel,

@@ -82,6 +82,11 @@ class Layout:
     tile: int = TILE
     buckets: List[Bucket] = field(default_factory=list)
     chunks: List[Chunk] = field(default_factory=list)
+    # whole-tensor mode: the owner rank of every tensor and its offset in
+    # the owner's shard (empty lists in the flat mode)
+    whole_tensors: bool = False
+    owner: List[int] = field(default_factory=list)
+    owner_shard_off: List[int] = field(default_factory=list)
 
 
 class LayoutError(ValueError):
@@ -226,3 +231,71 @@ def to_tiled_grads(lay: Layout, G) -> np.ndarray:
     for s in range(W):
         out[t, s, p] = G[s]
     return out.reshape(-1)
+
+
+def build_tensor_layout(tensor_numel: Sequence[int], world: int, rank: int,
+                        align_bytes: int = 256,
+                        tile: int = TILE) -> Layout:
+    """Whole-tensor shard assignment (podcast summary of "Training at
+    thousands of GPUs", section "ZeRO optimizer": an optimizer that needs
+    whole tensors, such as Muon, cannot work on flattened slices; the
+    shards are assigned at whole-tensor granularity, as FSDP2 keeps whole
+    tensors per rank).
+
+    Reading: every tensor belongs entirely to one rank.  Tensors are
+    assigned greedily, longest first: in order of decreasing padded size
+    (ties by list index), each goes to the rank with the least padded load
+    so far (ties to the lowest rank).  A rank's shard is its tensors in list
+    order, each padded to the alignment unit; one bucket per owned non-empty
+    tensor, whose whole extent is this rank's slice, at the tensor's flat
+    offset.  The flat buffer is the same aligned flattening as the flat
+    mode, rounded up to the alignment unit; the padded tensors partition
+    it."""
+    if world < 1 or not (0 <= rank < world):
+        raise LayoutError("need world >= 1 and 0 <= rank < world")
+    if align_bytes < 16 or align_bytes % 16:
+        raise LayoutError("align_bytes must be a positive multiple of 16")
+    for n in tensor_numel:
+        if n < 0:
+            raise LayoutError("negative tensor numel")
+    align = align_bytes // 2
+    starts = []
+    pos = 0
+    for n in tensor_numel:
+        pos = _roundup(pos, align)
+        starts.append(pos)
+        pos += n
+    flat_numel = _roundup(pos, align)
+    padded = [_roundup(n, align) for n in tensor_numel]
+
+    # greedy assignment, longest first
+    order = sorted(range(len(tensor_numel)), key=lambda t: (-padded[t], t))
+    load = [0] * world
+    owner = [0] * len(tensor_numel)
+    for t in order:
+        r = min(range(world), key=lambda q: (load[q], q))
+        owner[t] = r
+        load[r] += padded[t]
+    # shard offsets inside each owner's shard, in list order
+    fill = [0] * world
+    owner_off = [0] * len(tensor_numel)
+    for t in range(len(tensor_numel)):
+        owner_off[t] = fill[owner[t]]
+        fill[owner[t]] += padded[t]
+
+    buckets, chunks = [], []
+    tiles = 0
+    for t in range(len(tensor_numel)):
+        if owner[t] != rank or tensor_numel[t] == 0:
+            continue
+        b_id = len(buckets)
+        buckets.append(Bucket(starts[t], padded[t], padded[t], owner_off[t],
+                              tiles))
+        chunks.append(Chunk(t, b_id, 0, tensor_numel[t], owner_off[t]))
+        tiles += _roundup(padded[t], tile) // tile
+    return Layout(world=world, rank=rank, align_elems=align, bucket_elems=0,
+                  tensor_numel=list(tensor_numel), tensor_flat_off=starts,
+                  flat_numel=flat_numel, shard_numel=fill[rank],
+                  n_tiles=tiles, tile=tile, buckets=buckets, chunks=chunks,
+                  whole_tensors=True, owner=owner,
+                  owner_shard_off=owner_off)

@@ -15,13 +15,15 @@ from __future__ import annotations
 
 import numpy as np
 
-from .layout import Layout, build_layout
+from .layout import Layout, build_layout, build_tensor_layout
 
 
 def pack_flat(lay: Layout, shard: np.ndarray, full_flat: np.ndarray) -> None:
-    """Write the rank's shard into its positions of the flat buffer."""
+    """Write the rank's shard into its positions of the flat buffer (in the
+    whole-tensor mode, each owned tensor at its flat offset)."""
     for b in lay.buckets:
-        dst = b.flat_off + lay.rank * b.slice_numel
+        dst = b.flat_off + (0 if lay.whole_tensors
+                            else lay.rank * b.slice_numel)
         full_flat[dst:dst + b.slice_numel] = \
             shard[b.shard_off:b.shard_off + b.slice_numel]
 
@@ -47,6 +49,20 @@ def gather(tensor_numel, world: int, shards, flat_lo: int, flat_hi: int,
     its flat positions; the layer is a window of it."""
     lays = [build_layout(tensor_numel, world, r, bucket_cap_bytes,
                          align_bytes) for r in range(world)]
+    return _gather(lays, shards, flat_lo, flat_hi)
+
+
+def gather_tensors(tensor_numel, world: int, shards, flat_lo: int,
+                   flat_hi: int, align_bytes: int = 256) -> np.ndarray:
+    """The gather of the whole-tensor mode: every tensor comes whole from
+    its owner's shard (a broadcast from the owner instead of an all-gather
+    of slices)."""
+    lays = [build_tensor_layout(tensor_numel, world, r, align_bytes)
+            for r in range(world)]
+    return _gather(lays, shards, flat_lo, flat_hi)
+
+
+def _gather(lays, shards, flat_lo, flat_hi):
     full = np.zeros(lays[0].flat_numel, np.asarray(shards[0]).dtype)
     for lay, sh in zip(lays, shards):
         pack_flat(lay, np.asarray(sh), full)

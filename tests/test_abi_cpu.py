@@ -11,7 +11,7 @@ import re
 import pytest
 
 import zero_sharded_optimizer_shard_amd as zs
-from oracle.layout import LayoutError, build_layout
+from oracle.layout import LayoutError, build_layout, build_tensor_layout
 from synth import workloads as wl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 22
+    assert len(names) == 24
     L = zs.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -82,6 +82,80 @@ def test_layout_matches_oracle_workloads(name):
     w = wl.presets()[name]
     for rank in sorted({0, 1 % w.world, w.world - 1}):
         same(w.numels, w.world, rank, 25 << 20, 256)
+
+
+def same_tensors(numels, world, rank, align):
+    try:
+        o = build_tensor_layout(numels, world, rank, align)
+    except LayoutError:
+        with pytest.raises(zs.ZsError) as ei:
+            zs.zs_layout_build_tensors(numels, world, rank, align)
+        assert ei.value.code == -1
+        return
+    lay = zs.zs_layout_build_tensors(numels, world, rank, align)
+    assert tables(lay, len(numels)) == oracle_tables(o)
+    assert zs.zs_layout_owners(lay, len(numels)) == (o.owner,
+                                                     o.owner_shard_off)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_tensor_layout_matches_oracle_random(seed):
+    rng = random.Random(5000 + seed)
+    numels = [rng.choice([0, 1, 7, 128, 129, 1000, 4096, 50257, 70000])
+              for _ in range(rng.randint(0, 14))]
+    world = rng.choice([1, 2, 3, 5, 8, 16, 64])
+    align = rng.choice([16, 256, 4096])
+    for rank in sorted({0, world - 1, rng.randrange(world)}):
+        same_tensors(numels, world, rank, align)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2", "llama8b", "dense7b",
+                                  "llama70b"])
+def test_tensor_layout_matches_oracle_workloads(name):
+    w = wl.presets()[name]
+    for rank in sorted({0, 1 % w.world, w.world - 1}):
+        same_tensors(w.numels, w.world, rank, 256)
+
+
+def test_tensor_layout_errors():
+    L = zs.lib()
+    out = ctypes.c_void_p()
+    arr = (ctypes.c_int64 * 2)(10, 20)
+    assert L.zs_layout_build_tensors(arr, 2, 4, 1, 256, None) == -1
+    assert L.zs_layout_build_tensors(arr, 2, 4, 4, 256,
+                                     ctypes.byref(out)) == -1
+    assert L.zs_layout_build_tensors(arr, 2, 4, 1, 100,
+                                     ctypes.byref(out)) == -1
+    big = (ctypes.c_int64 * 2)(2 ** 62, 2 ** 62)
+    assert L.zs_layout_build_tensors(big, 2, 4, 1, 256,
+                                     ctypes.byref(out)) == -3
+    flat = zs.zs_layout_build([10, 20], 4, 0)
+    o = (ctypes.c_int32 * 2)()
+    f = (ctypes.c_int64 * 2)()
+    assert L.zs_layout_owners(flat.handle, o, f, 2) == -1   # flat mode
+    t = zs.zs_layout_build_tensors([10, 20, 30], 4, 0)
+    assert L.zs_layout_owners(t.handle, o, f, 2) == -3      # short
+
+
+def test_launch_size_limits():
+    """A bucket slice (a whole tensor in the whole-tensor mode) beyond
+    2^23 - 1 tiles of 8192 elements would need a launch of 2^32 work-items
+    or more: both builders refuse it; one tile less is accepted."""
+    tile = 8192
+    lim = (2 ** 23 - 1) * tile
+    cap = 1 << 62
+    lay = zs.zs_layout_build([lim], 1, 0, cap)
+    assert zs.zs_layout_info(lay)[1] == lim
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_layout_build([lim + tile], 1, 0, cap)
+    assert e.value.code == -3
+    # per rank: W = 2 halves the slice
+    zs.zs_layout_build([2 * lim], 2, 1, cap)
+    lay = zs.zs_layout_build_tensors([lim, 5, lim], 2, 1)
+    assert zs.zs_layout_info(lay)[1] == lim
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_layout_build_tensors([7, lim + 1], 2, 0)
+    assert e.value.code == -3
 
 
 def test_layout_errors():
@@ -214,6 +288,9 @@ def test_step_argument_checks_need_no_device():
     assert L.zs_accumulate(2, A + 8, A, A + 8, 16, 2, None) == -2  # acc
     assert L.zs_accumulate(1, A, A + 4, None, 16, 2, None) == -2
     assert L.zs_accumulate(0, None, None, None, 0, 2, None) == 0  # empty
+    # one launch holds fewer than 2^32 work-items: 512 threads x 4 elements
+    big = (2 ** 32 // 512) * 2048
+    assert L.zs_accumulate(0, A, A, None, big, 2, None) == -3
     # gather (ZeRO-3)
     P_ = ctypes.c_void_p
     sh = (P_ * 4)(A, A, A, A)

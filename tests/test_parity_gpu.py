@@ -20,10 +20,12 @@ import torch
 import synth
 import zero_sharded_optimizer_shard_amd as zs
 from oracle import step as O
-from oracle.layout import (TILE, build_layout, from_tiled_rows,
-                           from_tiled_state, tile_slot, tile_slot_range,
-                           to_tiled_grads, to_tiled_rows, to_tiled_state)
-from oracle.pack import gather, owner_runs, pack_flat, pack_tensors
+from oracle.layout import (TILE, build_layout, build_tensor_layout,
+                           from_tiled_rows, from_tiled_state, tile_slot,
+                           tile_slot_range, to_tiled_grads, to_tiled_rows,
+                           to_tiled_state)
+from oracle.pack import (gather, gather_tensors, owner_runs, pack_flat,
+                         pack_tensors)
 from synth import state as S
 from synth import workloads as wl
 
@@ -84,9 +86,14 @@ class Case:
     """One rank's step on the GPU and on the oracle, full arrays."""
 
     def __init__(self, numels, W, rank, cap=25 << 20, align=256, sigma=1e-3,
-                 stride_pad=0, warm=None, seed=0, layout="slices"):
-        self.lay_o = build_layout(numels, W, rank, cap, align)
-        self.lay = zs.zs_layout_build(numels, W, rank, cap, align)
+                 stride_pad=0, warm=None, seed=0, layout="slices",
+                 tensors=False):
+        if tensors:                         # whole-tensor shard assignment
+            self.lay_o = build_tensor_layout(numels, W, rank, align)
+            self.lay = zs.zs_layout_build_tensors(numels, W, rank, align)
+        else:
+            self.lay_o = build_layout(numels, W, rank, cap, align)
+            self.lay = zs.zs_layout_build(numels, W, rank, cap, align)
         self.W, self.rank, self.sigma, self.seed = W, rank, sigma, seed
         self.layout = layout
         n = self.n = self.lay_o.shard_numel
@@ -866,6 +873,188 @@ def test_gradient_accumulation(k):
     torch.cuda.synchronize()
     assert np.array_equal(np16(dG[k - 1]), want)
     assert torch.equal(acc.view(torch.int32), before.view(torch.int32))
+
+
+TENSOR_LIST = [1000, 70000, 7, 129, 20000, 9000, 3, 65536, 300000, 512]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("W", [1, 3, 8])
+def test_whole_tensor_step(W, layout):
+    """Whole-tensor shard assignment: every rank's step over its own
+    tensors, bf16 result into the flat buffer at the tensors' offsets;
+    against the oracle on the oracle's whole-tensor layout, bit for bit;
+    other positions of the flat buffer untouched."""
+    for rank in sorted({0, W - 1}):
+        say(f"case whole-tensor W={W} rank={rank} {layout}")
+        c = Case(TENSOR_LIST, W, rank, layout=layout, tensors=True,
+                 warm=(1e-4, 1e-8), seed=W, stride_pad=8)
+        F = c.lay_o.flat_numel
+        flat = dev_bf16(F)
+        synth.dev_bits16(flat, 3, synth.TAG_SENTINEL, 0, rank, 0)
+        want = synth.cpu_bits16(F, 3, synth.TAG_SENTINEL, 0, rank, 0)
+        for t in (1, 2, 3):
+            c.step(t, full_flat=flat)
+        torch.cuda.synchronize()
+        pack_flat(c.lay_o, c.op, want)
+        assert np.array_equal(np16(flat), want)
+
+
+def test_whole_tensor_pure_bf16_and_pack():
+    W = 3
+    for rank in range(W):
+        lay_o = build_tensor_layout(TENSOR_LIST, W, rank)
+        lay = zs.zs_layout_build_tensors(TENSOR_LIST, W, rank)
+        n, F = lay_o.shard_numel, lay_o.flat_numel
+        say(f"case whole-tensor bf16 rank={rank} shard={n}")
+        pad = S.padding_runs(n, lay_o.chunks)
+        om, omm, ov = S.cpu_state(0, n, 0.02, 1, pad, (1e-4, 1e-8))
+        p16 = O.bf16_round(om)
+        state = dev_f32(lay_o.n_tiles * 2 * TILE)
+        zs.zs_state_mv_pack(lay, torch.from_numpy(omm.copy()).cuda(),
+                            torch.from_numpy(ov.copy()).cuda(), state)
+        host_flat = synth.cpu_bits16(F, 8, synth.TAG_SENTINEL, 0, 0, 0)
+        pack_flat(lay_o, p16, host_flat)
+        flat = torch.from_numpy(host_flat.view(np.int16)).cuda()
+        G = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
+        for t in (1, 2):
+            S.dev_grads(G, W, n, t, 1e-3, 1, pad)
+            zs.zs_step_bf16(lay, G, state, flat, params_flat=True,
+                            grad_stride=n, step=t, **HP)
+            O.step_bf16(S.cpu_grads(W, 0, n, t, 1e-3, 1, pad), p16, omm, ov,
+                        OHP, t)
+        torch.cuda.synchronize()
+        want = synth.cpu_bits16(F, 8, synth.TAG_SENTINEL, 0, 0, 0)
+        pack_flat(lay_o, p16, want)
+        assert np.array_equal(np16(flat), want)
+        m_g, v_g = from_tiled_rows(lay_o, npf(state), 2)
+        assert np.array_equal(m_g, omm) and np.array_equal(v_g, ov)
+        # zs_pack: flat positions and per-tensor storage
+        shard = torch.from_numpy(p16.view(np.int16).copy()).cuda()
+        out = dev_bf16(F)
+        out.view(torch.int16).fill_(0x5a5a)
+        tensors = [dev_bf16(k) for k in TENSOR_LIST]
+        for x in tensors:
+            x.view(torch.int16).fill_(0x1111)
+        ptrs = torch.tensor([x.data_ptr() for x in tensors],
+                            dtype=torch.int64, device="cuda")
+        chunks = zs.zs_layout_chunks(lay)
+        raw = np.frombuffer(zs.chunks_bytes(chunks), np.uint8).copy()
+        zs.zs_pack(lay, shard, out, torch.from_numpy(raw).cuda(),
+                   len(chunks), ptrs)
+        torch.cuda.synchronize()
+        want = np.full(F, 0x5a5a, np.uint16)
+        pack_flat(lay_o, p16, want)
+        assert np.array_equal(np16(out), want)
+        ref_t = [np.full(k, 0x1111, np.uint16) for k in TENSOR_LIST]
+        pack_tensors(lay_o, p16, ref_t)
+        for x, r_ in zip(tensors, ref_t):
+            assert np.array_equal(np16(x), r_)
+
+
+@pytest.mark.parametrize("W", [3, 8])
+def test_whole_tensor_ranks_reassemble_to_the_unsharded_step(W):
+    """The all-reduce equivalence with whole tensors: every rank steps its
+    own tensors into one shared flat buffer; it equals the oracle's step on
+    the whole mean gradient, bit for bit."""
+    lay0 = build_tensor_layout(TENSOR_LIST, W, 0)
+    F = lay0.flat_numel
+    pad = np.ones(F, bool)
+    for s0, k in zip(lay0.tensor_flat_off, TENSOR_LIST):
+        pad[s0:s0 + k] = False
+    fullG = [np.zeros((W, F), np.uint16) for _ in range(2)]
+    for t in (1, 2):
+        for s_ in range(W):
+            fullG[t - 1][s_] = synth.cpu_normal_bf16(F, 0, synth.TAG_GRAD, t,
+                                                     s_, 0, 1e-3)
+        fullG[t - 1][:, pad] = 0
+    full_master = synth.cpu_normal_f32(F, 0, synth.TAG_MASTER, 0, 0, 0, 0.02)
+    full_master[pad] = 0
+    flat = dev_bf16(F)
+    flat.view(torch.int16).fill_(0x7fc0)
+    for r in range(W):
+        say(f"case whole-tensor all-ranks W={W} rank={r}")
+        lay_o = build_tensor_layout(TENSOR_LIST, W, r)
+        lay = zs.zs_layout_build_tensors(TENSOR_LIST, W, r)
+        if lay_o.shard_numel == 0:
+            continue
+        idx = np.concatenate([np.arange(b.flat_off, b.flat_off + b.numel)
+                              for b in lay_o.buckets])
+        n = idx.size
+        master = torch.from_numpy(full_master[idx].copy()).cuda()
+        state = dev_f32(lay_o.n_tiles * 3 * TILE)
+        zs.zs_state_pack(lay, master, None, None, state)
+        for t in (1, 2):
+            G = torch.from_numpy(np.ascontiguousarray(
+                fullG[t - 1][:, idx]).view(np.int16)).cuda()
+            zs.zs_step(lay, G, state, None, flat, grad_stride=n, step=t,
+                       **HP)
+        torch.cuda.synchronize()
+    om = full_master.copy()
+    omm = np.zeros(F, np.float32)
+    ov = np.zeros(F, np.float32)
+    for t in (1, 2):
+        acc = O.bf16_to_f32(fullG[t - 1][0]).copy()
+        for s_ in range(1, W):
+            acc = acc + O.bf16_to_f32(fullG[t - 1][s_])
+        p16 = O.adamw(acc / np.float32(W), om, omm, ov, OHP, t)
+    assert np.array_equal(np16(flat), p16)
+
+
+def test_whole_tensor_bucket_groups_and_gather():
+    """Per-tensor bucket steps in groups (shuffled) equal the whole step;
+    zs_gather of the whole-tensor layout against the oracle (each tensor
+    whole from its owner)."""
+    W = 3
+    rank = 1
+    ref = Case(TENSOR_LIST, W, rank, tensors=True, layout="tiled")
+    lay, lay_o = ref.lay, ref.lay_o
+    n = lay_o.shard_numel
+    state = dev_state(lay, lay_o, 0.02, pad=ref.pad)
+    full = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
+    full_t = dev_bf16(lay_o.n_tiles * W * TILE)
+    order = list(range(len(lay_o.buckets)))
+    random.Random(4).shuffle(order)
+    p_out = dev_bf16(n)
+    for t in (1, 2):
+        ref.step(t, check=False)
+        S.dev_grads(full, W, n, t, 1e-3, 0, ref.pad)
+        zs.zs_grads_tile(lay, -1, full, n, full_t)
+        for g0 in range(0, len(order), 2):
+            ids = order[g0:g0 + 2]
+            stg = []
+            for b_id in ids:
+                b = lay_o.buckets[b_id]
+                lo = b.tile_off * W * TILE
+                stg.append(full_t[lo:lo + -(-b.slice_numel // TILE) * W
+                                  * TILE].clone())
+            zs.zs_buckets_step(lay, ids, stg, state, p_out, None,
+                               grad_layout="tiled", step=t, **HP)
+    torch.cuda.synchronize()
+    slot_idx = tile_slot(lay_o)
+    g3 = npf(state).reshape(-1, 3, TILE)
+    w3 = npf(ref.state).reshape(-1, 3, TILE)
+    for row in range(3):
+        assert np.array_equal(g3[:, row, :].reshape(-1)[slot_idx].view(
+            np.uint32), w3[:, row, :].reshape(-1)[slot_idx].view(np.uint32))
+    assert np.array_equal(np16(p_out), np16(ref.p))
+    # gather from the three ranks' shards
+    lays = [build_tensor_layout(TENSOR_LIST, W, r) for r in range(W)]
+    host = [synth.cpu_bits16(l_.shard_numel, 6, synth.TAG_SENTINEL, 0, r, 0)
+            for r, l_ in enumerate(lays)]
+    dev = [torch.from_numpy(h.view(np.int16)).cuda() if h.size else
+           dev_bf16(8) for h in host]
+    F = lays[0].flat_numel
+    offs = lays[0].tensor_flat_off
+    out = torch.empty(F + 64, dtype=torch.int16, device="cuda")
+    for lo, hi in [(0, F), (offs[1], offs[5] + 9000), (offs[3], offs[3] + 7),
+                   (offs[8], F - 5)]:
+        out.fill_(0x5a5a)
+        zs.zs_gather(lay, dev, lo, hi, out)
+        got = np16(out)
+        assert np.array_equal(got[:hi - lo],
+                              gather_tensors(TENSOR_LIST, W, host, lo, hi))
+        assert np.all(got[hi - lo:] == 0x5a5a)
 
 
 def test_two_runs_are_bit_identical():

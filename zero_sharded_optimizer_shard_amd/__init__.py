@@ -10,8 +10,8 @@ from ._zs import (EXPORTS, LIB_PATH, ZS_ACC_ADD, ZS_ACC_FIRST, ZS_ACC_LAST,
                   zs_accumulate, zs_adamw, zs_bucket, zs_bucket_step,
                   zs_buckets_step, zs_chunk, zs_gather, zs_grads_tile,
                   zs_last_error, zs_layout_buckets, zs_layout_build,
-                  zs_layout_chunks, zs_layout_info, zs_layout_rank,
-                  zs_layout_tensor_offsets, zs_layout_tiles, zs_pack,
+                  zs_layout_build_tensors, zs_layout_chunks, zs_layout_info, zs_layout_owners,
+                  zs_layout_rank, zs_layout_tensor_offsets, zs_layout_tiles, zs_pack,
                   zs_state_mv_pack, zs_state_mv_unpack, zs_state_pack,
                   zs_state_unpack, zs_step, zs_step_bf16, zs_strerror)
 
@@ -21,7 +21,7 @@ __all__ = ["EXPORTS", "LIB_PATH", "ZS_ACC_ADD", "ZS_ACC_FIRST", "ZS_ACC_LAST",
            "lib", "zs_accumulate", "zs_adamw", "zs_bucket", "zs_bucket_step",
            "zs_buckets_step", "zs_chunk", "zs_gather", "zs_grads_tile",
            "zs_last_error", "zs_layout_buckets", "zs_layout_build",
-           "zs_layout_chunks", "zs_layout_info", "zs_layout_rank",
+           "zs_layout_build_tensors", "zs_layout_chunks", "zs_layout_info", "zs_layout_owners", "zs_layout_rank",
            "zs_layout_tensor_offsets", "zs_layout_tiles", "zs_pack",
            "zs_state_mv_pack", "zs_state_mv_unpack", "zs_state_pack",
            "zs_state_unpack", "zs_step", "zs_step_bf16", "zs_strerror"]

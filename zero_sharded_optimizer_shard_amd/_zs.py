@@ -48,7 +48,8 @@ class zs_adamw(ctypes.Structure):
 
 _lib = None
 
-EXPORTS = ["zs_layout_build", "zs_layout_info", "zs_layout_tiles",
+EXPORTS = ["zs_layout_build", "zs_layout_build_tensors", "zs_layout_owners",
+           "zs_layout_info", "zs_layout_tiles",
            "zs_layout_buckets", "zs_layout_chunks",
            "zs_layout_tensor_offsets", "zs_layout_rank", "zs_layout_free",
            "zs_step", "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
@@ -72,6 +73,8 @@ def lib():
     P = ctypes.POINTER
     L.zs_layout_build.argtypes = [P(i64), i32, i32, i32, i64, i32, P(p)]
     L.zs_layout_info.argtypes = [p, P(i64), P(i64), P(i32), P(i32)]
+    L.zs_layout_build_tensors.argtypes = [P(i64), i32, i32, i32, i32, P(p)]
+    L.zs_layout_owners.argtypes = [p, P(i32), P(i64), i32]
     L.zs_layout_tiles.argtypes = [p, P(i64)]
     L.zs_layout_buckets.argtypes = [p, P(zs_bucket), i32]
     L.zs_layout_chunks.argtypes = [p, P(zs_chunk), i32]
@@ -98,7 +101,8 @@ def lib():
     L.zs_strerror.restype = ctypes.c_char_p
     L.zs_last_error.argtypes = []
     L.zs_last_error.restype = ctypes.c_char_p
-    for name in ("zs_layout_build", "zs_layout_info", "zs_layout_tiles",
+    for name in ("zs_layout_build", "zs_layout_build_tensors",
+                 "zs_layout_owners", "zs_layout_info", "zs_layout_tiles",
                  "zs_layout_buckets", "zs_layout_chunks",
                  "zs_layout_tensor_offsets", "zs_layout_rank", "zs_step",
                  "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
@@ -152,6 +156,27 @@ def zs_layout_build(tensor_numel: Sequence[int], world: int, rank: int,
                                  align_bytes, ctypes.byref(out)),
            "zs_layout_build")
     return Layout(out.value)
+
+
+def zs_layout_build_tensors(tensor_numel: Sequence[int], world: int,
+                            rank: int, align_bytes: int = 256) -> Layout:
+    """Whole-tensor shard assignment (see include/zs.h)."""
+    n = len(tensor_numel)
+    arr = (ctypes.c_int64 * max(n, 1))(*tensor_numel)
+    out = ctypes.c_void_p()
+    _check(lib().zs_layout_build_tensors(arr, n, world, rank, align_bytes,
+                                         ctypes.byref(out)),
+           "zs_layout_build_tensors")
+    return Layout(out.value)
+
+
+def zs_layout_owners(layout: Layout, n_tensors: int):
+    """(owner rank per tensor, offset in the owner's shard per tensor)."""
+    o = (ctypes.c_int32 * max(n_tensors, 1))()
+    off = (ctypes.c_int64 * max(n_tensors, 1))()
+    n = _check(lib().zs_layout_owners(layout.handle, o, off, n_tensors),
+               "zs_layout_owners")
+    return list(o[:n]), list(off[:n])
 
 
 def zs_layout_info(layout: Layout):

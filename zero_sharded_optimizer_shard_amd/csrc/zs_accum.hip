@@ -134,7 +134,10 @@ extern "C" int zs_accumulate(int32_t mode, float* acc, const uint16_t* grad,
     a.invk = k > 0 ? (float)(1.0 / (double)k) : 0.f;
     a.pow2 = k > 0 && (k & (k - 1)) == 0;
     const int64_t blocks = (n + kChunk - 1) / kChunk;
-    if (blocks > 0x7fffffff) return fail(ZS_ERANGE, "n too large");
+    // one launch: fewer than 2^32 work-items along x
+    if (blocks > (((int64_t)1 << 32) - 1) / kThreads)
+        return fail(ZS_ERANGE, "n %lld too large for one launch",
+                    (long long)n);
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
     switch (mode) {
     case ZS_ACC_FIRST:

@@ -18,7 +18,8 @@
 // shards are W resident buffers; on a node they would be peer-mapped shards
 // of the other GPUs read over xGMI.  2 B read + 2 B written per element,
 // 16-byte non-temporal accesses except at a ragged end; bounded by HBM
-// bandwidth.
+// bandwidth.  Whole-tensor layouts take each tensor whole from its owner
+// (gather_tensors below).
 
 #include <hip/hip_runtime.h>
 
@@ -81,6 +82,101 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a)
         dst[t] = src[t];
 }
 
+// Whole-tensor layouts: every tensor comes whole from its owner's shard
+// (a broadcast from the owner in place of an all-gather of slices); the
+// padded tensors partition the flat buffer, so [lo, hi) is a list of
+// contiguous copies, up to kMaxSegs per launch.
+constexpr int kMaxSegs = 16;
+// chunks per launch: kThreads work-items each stay below 2^32
+constexpr int64_t kMaxLaunchChunks = ((int64_t(1) << 32) - 1) / kThreads;
+
+struct CopySeg {
+    const uint16_t* src;
+    uint16_t* dst;
+    int64_t n;
+};
+
+struct CopyArgs {
+    CopySeg s[kMaxSegs];
+    int64_t start[kMaxSegs + 1];    // prefix of the segments' chunk counts
+    int count;
+};
+
+__global__ __launch_bounds__(kThreads) void copy_segments_kernel(CopyArgs a)
+{
+    // blockIdx.x runs over the segments' chunks, in segment order
+    const int64_t t = blockIdx.x;
+    int i = 0;
+    while (i + 1 < a.count && a.start[i + 1] <= t)
+        ++i;
+    const CopySeg& sg = a.s[i];
+    const int64_t c0 = (t - a.start[i]) * kChunk;
+    if (c0 >= sg.n)
+        return;
+    const int64_t n = sg.n - c0 < kChunk ? sg.n - c0 : kChunk;
+    const uint16_t* src = sg.src + c0;     // both 16-byte aligned
+    uint16_t* dst = sg.dst + c0;
+    const int64_t nvec = n / kVec;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int64_t v = (int64_t)k * kThreads + threadIdx.x;
+        if (v < nvec)
+            __builtin_nontemporal_store(
+                __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(src) + v),
+                reinterpret_cast<u32x4*>(dst) + v);
+    }
+    const int64_t j = nvec * kVec + threadIdx.x;
+    if (j < n)
+        dst[j] = src[j];
+}
+
+int gather_tensors(const zs_layout* L, const uint16_t* const* shards,
+                   int64_t lo, int64_t hi, uint16_t* out, hipStream_t s)
+{
+    const int64_t A = L->align_elems;
+    const int32_t nt = (int32_t)L->tensor_numel.size();
+    CopyArgs a;
+    int cnt = 0;
+    a.start[0] = 0;
+    auto flush = [&]() -> int {
+        if (cnt == 0) return ZS_OK;
+        a.count = cnt;
+        hipLaunchKernelGGL(copy_segments_kernel,
+                           dim3((unsigned)a.start[cnt], 1), dim3(kThreads),
+                           0, s, a);
+        cnt = 0;
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return zs::fail(ZS_EDEVICE, "gather kernel: %s",
+                            hipGetErrorString(err));
+        return ZS_OK;
+    };
+    for (int32_t t = 0; t < nt; ++t) {
+        const int64_t n = L->tensor_numel[t];
+        if (n == 0) continue;
+        const int64_t t0 = L->tensor_off[t];
+        const int64_t t1 = t0 + (n + A - 1) / A * A;     // padded extent
+        const int64_t x0 = t0 > lo ? t0 : lo, x1 = t1 < hi ? t1 : hi;
+        if (x1 <= x0) continue;
+        const int64_t nc = (x1 - x0 + kChunk - 1) / kChunk;
+        if (cnt > 0 && a.start[cnt] + nc > kMaxLaunchChunks) {
+            const int rc = flush();
+            if (rc) return rc;
+        }
+        a.s[cnt].src = shards[L->owner[t]] + L->owner_shard_off[t] +
+                       (x0 - t0);
+        a.s[cnt].dst = out + (x0 - lo);
+        a.s[cnt].n = x1 - x0;
+        a.start[cnt + 1] = a.start[cnt] + nc;
+        if (++cnt == kMaxSegs) {
+            const int rc = flush();
+            if (rc) return rc;
+        }
+    }
+    return flush();
+}
+
 }  // namespace
 
 extern "C" int zs_gather(const zs_layout* L, const uint16_t* const* shards,
@@ -114,6 +210,9 @@ extern "C" int zs_gather(const zs_layout* L, const uint16_t* const* shards,
     }
     if (reinterpret_cast<uintptr_t>(out) & 15u)
         return fail(ZS_EALIGN, "out not 16-byte aligned");
+    if (L->whole_tensors)
+        return gather_tensors(L, shards, flat_lo, flat_hi, out,
+                              static_cast<hipStream_t>(hip_stream));
     const int64_t nb = (int64_t)L->buckets.size();
     a.out = out;
     a.lo = flat_lo;

@@ -20,7 +20,26 @@ struct zs_layout {
     std::vector<int64_t> tensor_off;
     std::vector<zs_bucket> buckets;
     std::vector<zs_chunk> chunks;
+    // whole-tensor mode: every tensor belongs to one rank; each owned tensor
+    // is one bucket whose whole extent is this rank's slice
+    bool whole_tensors = false;
+    std::vector<int32_t> owner;            // per tensor
+    std::vector<int64_t> owner_shard_off;  // per tensor, in the owner's shard
 };
+
+// Most tiles one kernel launch covers: launches put one 512-thread
+// workgroup per tile along x, and HIP allows fewer than 2^32 work-items
+// there.  A bucket slice (a whole tensor in the whole-tensor mode) is at
+// most this many tiles, 68.7 G elements; group launches end a group early
+// rather than pass it.
+constexpr int64_t kMaxLaunchTiles = (int64_t(1) << 23) - 1;
+
+// Flat position of this rank's slice of bucket b.
+inline int64_t slice_flat_pos(const zs_layout* L, const zs_bucket& b)
+{
+    return b.flat_off + (L->whole_tensors ? 0 : (int64_t)L->rank *
+                                                    b.slice_numel);
+}
 
 namespace zs {
 

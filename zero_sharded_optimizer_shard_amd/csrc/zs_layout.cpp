@@ -5,8 +5,10 @@
 // parallelism" and "ZeRO optimizer"; DDP-to-ZeRO blog sections 2.1 and 3.3)
 // and the reduce-scatter ownership of the CS336 lecture 8 ZeRO-1 example.
 
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <numeric>
 #include <limits>
 #include <new>
 #include <string>
@@ -143,6 +145,12 @@ extern "C" int zs_layout_build(const int64_t* tensor_numel, int32_t n_tensors,
             b.flat_off = off;
             b.numel = rest < full ? rest : full;
             b.slice_numel = b.numel / world;
+            if ((b.slice_numel + ZS_TILE - 1) / ZS_TILE > kMaxLaunchTiles) {
+                delete L;
+                return fail(ZS_ERANGE, "bucket slice of %lld elements above "
+                            "%lld tiles", (long long)b.slice_numel,
+                            (long long)kMaxLaunchTiles);
+            }
             b.shard_off = shard;
             b.tile_off = tiles;
             L->buckets.push_back(b);
@@ -195,6 +203,138 @@ extern "C" int zs_layout_build(const int64_t* tensor_numel, int32_t n_tensors,
     }
     *out = L;
     return ZS_OK;
+}
+
+// Whole-tensor mode (the rule is stated with zs_layout_build_tensors in
+// include/zs.h): longest-first greedy assignment of whole tensors to ranks.
+extern "C" int zs_layout_build_tensors(const int64_t* tensor_numel,
+                                       int32_t n_tensors, int32_t world,
+                                       int32_t rank, int32_t align_bytes,
+                                       zs_layout** out)
+{
+    using zs::fail;
+    zs::clear_error();
+    if (!out) return fail(ZS_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (n_tensors < 0) return fail(ZS_EINVAL, "n_tensors < 0");
+    if (n_tensors > 0 && !tensor_numel)
+        return fail(ZS_EINVAL, "tensor_numel is NULL");
+    if (world < 1) return fail(ZS_EINVAL, "world %d < 1", world);
+    if (rank < 0 || rank >= world)
+        return fail(ZS_EINVAL, "rank %d outside [0, %d)", rank, world);
+    if (align_bytes < 16 || align_bytes % 16)
+        return fail(ZS_EINVAL, "align_bytes %d is not a positive multiple "
+                    "of 16", align_bytes);
+    zs_layout* L = new (std::nothrow) zs_layout;
+    if (!L) return fail(ZS_ENOMEM, "host allocation");
+    try {
+        L->world = world;
+        L->rank = rank;
+        L->whole_tensors = true;
+        L->align_elems = align_bytes / 2;
+        const int64_t A = L->align_elems;
+        L->tensor_numel.assign(tensor_numel, tensor_numel + n_tensors);
+        L->tensor_off.resize(n_tensors);
+        std::vector<int64_t> padded(n_tensors);
+        int64_t pos = 0;
+        for (int32_t k = 0; k < n_tensors; ++k) {
+            const int64_t n = tensor_numel[k];
+            if (n < 0) {
+                delete L;
+                return fail(ZS_EINVAL, "tensor %d has numel %lld < 0", k,
+                            (long long)n);
+            }
+            int64_t start, end;
+            if (!roundup_ok(pos, A, &start) || !add_ok(start, n, &end) ||
+                !roundup_ok(n, A, &padded[k])) {
+                delete L;
+                return fail(ZS_ERANGE, "flat size overflows int64");
+            }
+            L->tensor_off[k] = start;
+            pos = end;
+        }
+        if (!roundup_ok(pos, A, &L->flat_numel)) {
+            delete L;
+            return fail(ZS_ERANGE, "flat size overflows int64");
+        }
+        // longest first (ties: lower index), each to the least-loaded rank
+        // (ties: lower rank)
+        std::vector<int32_t> order(n_tensors);
+        std::iota(order.begin(), order.end(), 0);
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int32_t a, int32_t b) {
+                             return padded[a] > padded[b];
+                         });
+        std::vector<int64_t> load(world, 0);
+        L->owner.assign(n_tensors, 0);
+        for (int32_t t : order) {
+            if ((padded[t] + ZS_TILE - 1) / ZS_TILE > kMaxLaunchTiles) {
+                delete L;
+                return fail(ZS_ERANGE, "tensor %d of %lld elements above "
+                            "%lld tiles", t, (long long)padded[t],
+                            (long long)kMaxLaunchTiles);
+            }
+            int32_t r = 0;
+            for (int32_t q = 1; q < world; ++q)
+                if (load[q] < load[r]) r = q;
+            L->owner[t] = r;
+            load[r] += padded[t];
+        }
+        std::vector<int64_t> fill(world, 0);
+        L->owner_shard_off.assign(n_tensors, 0);
+        int64_t tiles = 0;
+        for (int32_t t = 0; t < n_tensors; ++t) {
+            const int32_t r = L->owner[t];
+            L->owner_shard_off[t] = fill[r];
+            fill[r] += padded[t];
+            if (r != rank || tensor_numel[t] == 0) continue;
+            zs_bucket b;
+            b.flat_off = L->tensor_off[t];
+            b.numel = padded[t];
+            b.slice_numel = padded[t];
+            b.shard_off = L->owner_shard_off[t];
+            b.tile_off = tiles;
+            tiles += (padded[t] + ZS_TILE - 1) / ZS_TILE;
+            zs_chunk c;
+            c.tensor_id = t;
+            c.bucket_id = (int32_t)L->buckets.size();
+            c.tensor_off = 0;
+            c.numel = tensor_numel[t];
+            c.shard_off = b.shard_off;
+            L->buckets.push_back(b);
+            L->chunks.push_back(c);
+        }
+        L->shard_numel = fill[rank];
+        L->n_tiles = tiles;
+        L->bucket_elems = 0;
+    } catch (const std::bad_alloc&) {
+        delete L;
+        return fail(ZS_ENOMEM, "host allocation");
+    }
+    *out = L;
+    return ZS_OK;
+}
+
+extern "C" int zs_layout_owners(const zs_layout* L, int32_t* owner,
+                                int64_t* owner_shard_off, int32_t cap)
+{
+    using zs::fail;
+    zs::clear_error();
+    if (!L) return fail(ZS_EINVAL, "layout is NULL");
+    if (!L->whole_tensors)
+        return fail(ZS_EINVAL, "not a whole-tensor layout");
+    const int64_t n = (int64_t)L->owner.size();
+    if (cap < 0 || (cap > 0 && (!owner || !owner_shard_off)))
+        return fail(ZS_EINVAL, "bad output buffers");
+    if (cap < n)
+        return fail(ZS_ERANGE, "capacity %d < %lld tensors", cap,
+                    (long long)n);
+    if (n) {
+        std::memcpy(owner, L->owner.data(), (size_t)n * sizeof(int32_t));
+        std::memcpy(owner_shard_off, L->owner_shard_off.data(),
+                    (size_t)n * sizeof(int64_t));
+    }
+    return (int)n;
 }
 
 extern "C" int zs_layout_info(const zs_layout* L, int64_t* flat_numel,

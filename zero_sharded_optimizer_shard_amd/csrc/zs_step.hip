@@ -42,6 +42,7 @@
 #include <cstdint>
 #include <initializer_list>
 #include <type_traits>
+#include <vector>
 
 #include "zs_internal.h"
 
@@ -122,6 +123,53 @@ __device__ __forceinline__ int unit_off(int k)
     const int part = (int)(blockIdx.x % P);
     return part * (int)(kTile / P) + 4 * (k * NT + (int)threadIdx.x);
 }
+
+// Tile locators of the layout conversions and the flat pack.  GeomLoc:
+// the regular buckets of the flat mode (blockIdx.y = bucket); SegLoc: up to
+// kMaxGroup explicit segments (blockIdx.y = segment), e.g. the owned tensors
+// of the whole-tensor mode; positions are then absolute.
+constexpr int kMaxGroup = ZS_MAX_GROUP;
+
+struct Seg {
+    int64_t shard_off, tile_off, fpos, slice;
+};
+
+struct GeomLoc {
+    Geom g;
+    __device__ bool operator()(TileRef& r) const { return tile_of(g, r); }
+};
+
+// Member i of a group launch owns the launch's tiles [start[i], start[i+1])
+// (blockIdx.x runs over the group's tiles); a short scalar scan finds it.
+__device__ __forceinline__ int member_of(const int64_t* start, int count,
+                                         int64_t t)
+{
+    int i = 0;
+    while (i + 1 < count && start[i + 1] <= t)
+        ++i;
+    return i;
+}
+
+struct SegLoc {
+    Seg s[kMaxGroup];
+    int64_t start[kMaxGroup + 1];
+    int count;
+    __device__ bool operator()(TileRef& r) const
+    {
+        const int64_t t = blockIdx.x;
+        const int i = member_of(start, count, t);
+        const Seg& sg = s[i];
+        const int64_t x = t - start[i];
+        const int64_t j0 = x * kTile;
+        if (j0 >= sg.slice)
+            return false;
+        r.tile = sg.tile_off + x;
+        r.e0 = sg.shard_off + j0;
+        r.nvalid = sg.slice - j0 < kTile ? sg.slice - j0 : kTile;
+        r.fpos = sg.fpos + j0;
+        return true;
+    }
+};
 
 __device__ __forceinline__ float bf16_lo(uint32_t u)
 {
@@ -345,30 +393,36 @@ __global__ __launch_bounds__(SH::NT) void step_kernel(StepArgs a)
                       a.flat ? a.flat + r.fpos : nullptr, r.nvalid, W, a.c);
 }
 
-// A group of buckets, each from its own staging buffer: blockIdx.y = member,
-// blockIdx.x = tile * P + part of that member's slice.
-constexpr int kMaxGroup = ZS_MAX_GROUP;
+// A group of buckets, each from its own staging buffer: blockIdx.x runs
+// over the members' tiles (times P), in member order.
 
 struct GroupMember {
     const uint16_t* grads;      // this bucket's staging
     float* state;               // state at the bucket's first tile
     uint16_t* pshard;           // nullable, at the bucket's first element
     uint16_t* flat;             // nullable, at this rank's slice of it
+                                // (pure: exactly one of pshard, flat)
     int64_t slice;              // slice_numel
 };
 
 struct GroupArgs {
     GroupMember mb[kMaxGroup];
+    int64_t start[kMaxGroup + 1];   // prefix of the members' tile counts
+    int32_t count;
     int64_t gstride;
     int32_t W;
     Consts c;
 };
 
-template <int WT, bool TILED, class SH>
+template <int WT, bool TILED, class SH, bool PURE>
 __global__ __launch_bounds__(SH::NT) void group_step_kernel(GroupArgs a)
 {
-    const GroupMember& mb = a.mb[blockIdx.y];
-    const int64_t x = blockIdx.x / SH::P;
+    // blockIdx.x = (group tile) * P + part; the group tile belongs to one
+    // member, as its tile x
+    const int64_t t = blockIdx.x / SH::P;
+    const int i = member_of(a.start, a.count, t);
+    const GroupMember& mb = a.mb[i];
+    const int64_t x = t - a.start[i];
     const int64_t j0 = x * kTile;
     if (j0 >= mb.slice)
         return;
@@ -376,8 +430,8 @@ __global__ __launch_bounds__(SH::NT) void group_step_kernel(GroupArgs a)
     const int64_t nvalid = mb.slice - j0 < kTile ? mb.slice - j0 : kTile;
     const uint16_t* g0 = TILED ? mb.grads + x * (int64_t)W * kTile
                                : mb.grads + j0;
-    step_tile<WT, SH>(g0, TILED ? kTile : a.gstride,
-                      mb.state + x * 3 * kTile,
+    step_tile<WT, SH, PURE>(g0, TILED ? kTile : a.gstride,
+                      mb.state + x * (PURE ? 2 : 3) * kTile,
                       mb.pshard ? mb.pshard + j0 : nullptr,
                       mb.flat ? mb.flat + j0 : nullptr, nvalid, W, a.c);
 }
@@ -392,12 +446,12 @@ struct Rows {
 };
 
 // plain rows -> tiled state; padding positions written as zero
-template <int ROWS>
+template <int ROWS, class Loc>
 __global__ __launch_bounds__(kThreads) void state_pack_kernel(
-    Rows rw, float* __restrict__ state, Geom g)
+    Rows rw, float* __restrict__ state, Loc loc)
 {
     TileRef r;
-    if (!tile_of(g, r))
+    if (!loc(r))
         return;
     float* st = state + r.tile * (ROWS * kTile);
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -415,12 +469,12 @@ __global__ __launch_bounds__(kThreads) void state_pack_kernel(
 }
 
 // tiled state -> plain rows (each nullable)
-template <int ROWS>
+template <int ROWS, class Loc>
 __global__ __launch_bounds__(kThreads) void state_unpack_kernel(
-    const float* __restrict__ state, Rows rw, Geom g)
+    const float* __restrict__ state, Rows rw, Loc loc)
 {
     TileRef r;
-    if (!tile_of(g, r))
+    if (!loc(r))
         return;
     const float* st = state + r.tile * (ROWS * kTile);
 #pragma unroll
@@ -436,12 +490,13 @@ __global__ __launch_bounds__(kThreads) void state_unpack_kernel(
 }
 
 // gradient slices [W][stride] -> tiled [tile][W][kTile]; padding zeroed
+template <class Loc>
 __global__ __launch_bounds__(kThreads) void grads_tile_kernel(
     const uint16_t* __restrict__ slices, int64_t stride,
-    uint16_t* __restrict__ tiled, int32_t W, Geom g)
+    uint16_t* __restrict__ tiled, int32_t W, Loc loc)
 {
     TileRef r;
-    if (!tile_of(g, r))
+    if (!loc(r))
         return;
     uint16_t* dst = tiled + r.tile * (int64_t)W * kTile;
     const u32x2 z = {0u, 0u};
@@ -459,22 +514,19 @@ __global__ __launch_bounds__(kThreads) void grads_tile_kernel(
 
 // ---- pack: shard -> flat all-gather buffer ---------------------------------
 
-struct PackFlatArgs {
-    const uint16_t* shard;      // at the launch's first bucket
-    uint16_t* flat;             // at the launch's first bucket
-    Geom g;
-};
-
-__global__ __launch_bounds__(kThreads) void pack_flat_kernel(PackFlatArgs a)
+template <class Loc>
+__global__ __launch_bounds__(kThreads) void pack_flat_kernel(
+    const uint16_t* __restrict__ shard, uint16_t* __restrict__ flat,
+    Loc loc)
 {
     TileRef r;
-    if (!tile_of(a.g, r))
+    if (!loc(r))
         return;
 #pragma unroll
     for (int k = 0; k < kUnits; ++k) {
         const int jj = unit_off(k);
         if (jj < r.nvalid)
-            st2(a.flat + r.fpos + jj, ld2(a.shard + r.e0 + jj));
+            st2(flat + r.fpos + jj, ld2(shard + r.e0 + jj));
     }
 }
 
@@ -587,6 +639,44 @@ int for_shard_ranges(const zs_layout* L, Fn fn)
     return ZS_OK;
 }
 
+// Calls fn(loc, grid, shard_base, tile_base, flat_base) for every launch
+// that covers the whole shard: regular bucket ranges in the flat mode
+// (positions relative to the bases), groups of up to kMaxGroup owned
+// tensors in the whole-tensor mode (absolute positions, zero bases, a 1-D
+// grid over the group's tiles).
+template <class Fn>
+int for_launches(const zs_layout* L, Fn fn)
+{
+    if (!L->whole_tensors)
+        return for_shard_ranges(L, [&](const Range& R) {
+            const zs_bucket& b0 = L->buckets[R.y0];
+            GeomLoc loc;
+            loc.g = R.g;
+            return fn(loc, dim3((unsigned)R.g.TPB, (unsigned)R.ny),
+                      b0.shard_off, b0.tile_off, b0.flat_off);
+        });
+    const int64_t nb = (int64_t)L->buckets.size();
+    for (int64_t g0 = 0; g0 < nb;) {
+        SegLoc loc;
+        int cnt = 0;
+        loc.start[0] = 0;
+        for (; cnt < kMaxGroup && g0 + cnt < nb; ++cnt) {
+            const zs_bucket& b = L->buckets[g0 + cnt];
+            const int64_t nt = tiles_for(b.slice_numel);
+            if (cnt > 0 && loc.start[cnt] + nt > kMaxLaunchTiles)
+                break;
+            loc.s[cnt] = Seg{b.shard_off, b.tile_off, slice_flat_pos(L, b),
+                             b.slice_numel};
+            loc.start[cnt + 1] = loc.start[cnt] + nt;
+        }
+        loc.count = cnt;
+        g0 += cnt;
+        const int rc = fn(loc, dim3((unsigned)loc.start[cnt], 1), 0, 0, 0);
+        if (rc) return rc;
+    }
+    return ZS_OK;
+}
+
 Geom bucket_geom(const zs_layout* L, const zs_bucket& b)
 {
     Geom g;
@@ -608,7 +698,7 @@ void launch_kernel(const Args& a, dim3 grid, hipStream_t s)
         hipLaunchKernelGGL((step_kernel<WT, TILED, SH, PURE>), grid,
                            dim3(SH::NT), 0, s, a);
     else
-        hipLaunchKernelGGL((group_step_kernel<WT, TILED, SH>), grid,
+        hipLaunchKernelGGL((group_step_kernel<WT, TILED, SH, PURE>), grid,
                            dim3(SH::NT), 0, s, a);
 }
 
@@ -701,6 +791,88 @@ int check_step_args(const zs_layout* L, const uint16_t* grads,
 
 }  // namespace
 
+namespace {
+
+// Group launches over `count` buckets of the layout (ids[i]), each member's
+// gradients at grads_of(i) (a bucket's staging, or its part of whole-shard
+// gradients); state / pshard / flat are whole-shard bases.  PURE: state is
+// the two-row [m|v] state and pshard / flat is the in-out parameter.
+template <bool PURE, class GradsOf>
+int launch_groups(const zs_layout* L, int32_t count, const int32_t* ids,
+                  GradsOf grads_of, bool tiled, int64_t grad_stride,
+                  float* state, uint16_t* pshard, uint16_t* flat,
+                  const Consts& c, hipStream_t s)
+{
+    constexpr int kRows = PURE ? 2 : 3;
+    for (int32_t g0 = 0; g0 < count;) {
+        GroupArgs a;
+        int32_t cnt = 0;
+        a.start[0] = 0;
+        for (; cnt < kMaxGroup && g0 + cnt < count; ++cnt) {
+            const zs_bucket& b = L->buckets[ids[g0 + cnt]];
+            const int64_t nt = tiles_for(b.slice_numel);
+            if (cnt > 0 && a.start[cnt] + nt > kMaxLaunchTiles)
+                break;
+            GroupMember& mb = a.mb[cnt];
+            mb.grads = grads_of(g0 + cnt);
+            mb.state = state + b.tile_off * kRows * kTile;
+            mb.pshard = pshard ? pshard + b.shard_off : nullptr;
+            mb.flat = flat ? flat + slice_flat_pos(L, b) : nullptr;
+            mb.slice = b.slice_numel;
+            a.start[cnt + 1] = a.start[cnt] + nt;
+        }
+        a.count = cnt;
+        g0 += cnt;
+        a.gstride = grad_stride;
+        a.W = L->world;
+        a.c = c;
+        const int rc = launch_step<PURE>(
+            a, tiled, dim3((unsigned)a.start[cnt], 1), s);
+        if (rc) return rc;
+    }
+    return ZS_OK;
+}
+
+// Whole-shard step, flat or whole-tensor layout.
+template <bool PURE>
+int shard_step(const zs_layout* L, const uint16_t* grads, bool tiled,
+               int64_t grad_stride, float* state, uint16_t* pshard,
+               uint16_t* flat, const Consts& c, hipStream_t s)
+{
+    constexpr int kRows = PURE ? 2 : 3;
+    const int32_t W = L->world;
+    if (L->whole_tensors) {
+        const int32_t nb = (int32_t)L->buckets.size();
+        std::vector<int32_t> ids(nb);
+        for (int32_t i = 0; i < nb; ++i) ids[i] = i;
+        return launch_groups<PURE>(
+            L, nb, ids.data(),
+            [&](int32_t i) {
+                const zs_bucket& b = L->buckets[i];
+                return tiled ? grads + b.tile_off * W * kTile
+                             : grads + b.shard_off;
+            },
+            tiled, grad_stride, state, pshard, flat, c, s);
+    }
+    return for_shard_ranges(L, [&](const Range& R) {
+        const zs_bucket& b0 = L->buckets[R.y0];
+        StepArgs a;
+        a.grads = tiled ? grads + b0.tile_off * W * kTile
+                        : grads + b0.shard_off;
+        a.gstride = grad_stride;
+        a.state = state + b0.tile_off * kRows * kTile;
+        a.pshard = pshard ? pshard + b0.shard_off : nullptr;
+        a.flat = flat ? flat + b0.flat_off : nullptr;
+        a.g = R.g;
+        a.W = W;
+        a.c = c;
+        return launch_step<PURE>(a, tiled,
+                                 dim3((unsigned)R.g.TPB, (unsigned)R.ny), s);
+    });
+}
+
+}  // namespace
+
 extern "C" int zs_step(const zs_layout* L, const uint16_t* grads,
                        int32_t grad_layout, int64_t grad_stride, float* state,
                        uint16_t* param_shard, uint16_t* full_flat,
@@ -716,25 +888,10 @@ extern "C" int zs_step(const zs_layout* L, const uint16_t* grads,
                              L->shard_numel, state, param_shard, full_flat,
                              hp, step);
     if (rc) return rc;
-    const bool tiled = grad_layout == ZS_GRADS_TILED;
-    const int32_t W = L->world;
-    const Consts c = make_consts(*hp, step, W);
-    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    return for_shard_ranges(L, [&](const Range& R) {
-        const zs_bucket& b0 = L->buckets[R.y0];
-        StepArgs a;
-        a.grads = tiled ? grads + b0.tile_off * W * kTile
-                        : grads + b0.shard_off;
-        a.gstride = grad_stride;
-        a.state = state + b0.tile_off * 3 * kTile;
-        a.pshard = param_shard ? param_shard + b0.shard_off : nullptr;
-        a.flat = full_flat ? full_flat + b0.flat_off : nullptr;
-        a.g = R.g;
-        a.W = W;
-        a.c = c;
-        return launch_step(a, tiled, dim3((unsigned)R.g.TPB, (unsigned)R.ny),
-                           s);
-    });
+    return shard_step<false>(L, grads, grad_layout == ZS_GRADS_TILED,
+                             grad_stride, state, param_shard, full_flat,
+                             make_consts(*hp, step, L->world),
+                             static_cast<hipStream_t>(hip_stream));
 }
 
 extern "C" int zs_buckets_step(const zs_layout* L, int32_t count,
@@ -753,7 +910,6 @@ extern "C" int zs_buckets_step(const zs_layout* L, int32_t count,
     if (!bucket_ids || !grads)
         return fail(ZS_EINVAL, "bucket_ids and grads must be non-NULL");
     const int32_t nb = (int32_t)L->buckets.size();
-    int64_t longest = 0;
     for (int32_t i = 0; i < count; ++i) {
         const int32_t b = bucket_ids[i];
         if (b < 0 || b >= nb)
@@ -762,31 +918,16 @@ extern "C" int zs_buckets_step(const zs_layout* L, int32_t count,
         for (int32_t k = 0; k < i; ++k)
             if (bucket_ids[k] == b)
                 return fail(ZS_EINVAL, "bucket %d appears twice", b);
-        const int64_t sl = L->buckets[b].slice_numel;
-        longest = sl > longest ? sl : longest;
         const int rc = check_step_args(L, grads[i], grad_layout, grad_stride,
-                                       sl, state, param_shard, full_flat, hp,
-                                       step);
+                                       L->buckets[b].slice_numel, state,
+                                       param_shard, full_flat, hp, step);
         if (rc) return rc;
     }
-    GroupArgs a;
-    for (int32_t i = 0; i < count; ++i) {
-        const zs_bucket& b = L->buckets[bucket_ids[i]];
-        GroupMember& mb = a.mb[i];
-        mb.grads = grads[i];
-        mb.state = state + b.tile_off * 3 * kTile;
-        mb.pshard = param_shard ? param_shard + b.shard_off : nullptr;
-        mb.flat = full_flat ? full_flat + b.flat_off +
-                                  (int64_t)L->rank * b.slice_numel
-                            : nullptr;
-        mb.slice = b.slice_numel;
-    }
-    a.gstride = grad_stride;
-    a.W = L->world;
-    a.c = make_consts(*hp, step, L->world);
-    return launch_step(a, grad_layout == ZS_GRADS_TILED,
-                       dim3((unsigned)tiles_for(longest), (unsigned)count),
-                       static_cast<hipStream_t>(hip_stream));
+    return launch_groups<false>(
+        L, count, bucket_ids, [&](int32_t i) { return grads[i]; },
+        grad_layout == ZS_GRADS_TILED, grad_stride, state, param_shard,
+        full_flat, make_consts(*hp, step, L->world),
+        static_cast<hipStream_t>(hip_stream));
 }
 
 extern "C" int zs_bucket_step(const zs_layout* L, int32_t bucket_id,
@@ -814,24 +955,22 @@ int convert_state(const zs_layout* L, bool pack, const float* const* in,
                   float* const* out, float* state_w, const float* state_r,
                   void* hip_stream)
 {
-    Rows base{};
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    return for_shard_ranges(L, [&](const Range& R) {
-        const zs_bucket& b0 = L->buckets[R.y0];
-        const int64_t e = b0.shard_off;
-        Rows rw = base;
+    return for_launches(L, [&](const auto& loc, dim3 grid, int64_t e,
+                               int64_t t, int64_t) {
+        Rows rw{};
         for (int row = 0; row < ROWS; ++row) {
             rw.in[row] = (pack && in[row]) ? in[row] + e : nullptr;
             rw.out[row] = (!pack && out[row]) ? out[row] + e : nullptr;
         }
-        const dim3 grid((unsigned)R.g.TPB, (unsigned)R.ny);
-        const int64_t t0 = b0.tile_off * ROWS * kTile;
+        using Loc = std::decay_t<decltype(loc)>;
+        const int64_t t0 = t * ROWS * kTile;
         if (pack)
-            hipLaunchKernelGGL(state_pack_kernel<ROWS>, grid, dim3(kThreads),
-                               0, s, rw, state_w + t0, R.g);
+            hipLaunchKernelGGL((state_pack_kernel<ROWS, Loc>), grid,
+                               dim3(kThreads), 0, s, rw, state_w + t0, loc);
         else
-            hipLaunchKernelGGL(state_unpack_kernel<ROWS>, grid,
-                               dim3(kThreads), 0, s, state_r + t0, rw, R.g);
+            hipLaunchKernelGGL((state_unpack_kernel<ROWS, Loc>), grid,
+                               dim3(kThreads), 0, s, state_r + t0, rw, loc);
         return check_launch(pack ? "state pack kernel"
                                  : "state unpack kernel");
     });
@@ -934,25 +1073,10 @@ extern "C" int zs_step_bf16(const zs_layout* L, const uint16_t* grads,
                              L->shard_numel, state_mv, pshard, flat, hp,
                              step);
     if (rc) return rc;
-    const bool tiled = grad_layout == ZS_GRADS_TILED;
-    const int32_t W = L->world;
-    const Consts c = make_consts(*hp, step, W);
-    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    return for_shard_ranges(L, [&](const Range& R) {
-        const zs_bucket& b0 = L->buckets[R.y0];
-        StepArgs a;
-        a.grads = tiled ? grads + b0.tile_off * W * kTile
-                        : grads + b0.shard_off;
-        a.gstride = grad_stride;
-        a.state = state_mv + b0.tile_off * 2 * kTile;
-        a.pshard = pshard ? pshard + b0.shard_off : nullptr;
-        a.flat = flat ? flat + b0.flat_off : nullptr;
-        a.g = R.g;
-        a.W = W;
-        a.c = c;
-        return launch_step<true>(a, tiled,
-                                 dim3((unsigned)R.g.TPB, (unsigned)R.ny), s);
-    });
+    return shard_step<true>(L, grads, grad_layout == ZS_GRADS_TILED,
+                            grad_stride, state_mv, pshard, flat,
+                            make_consts(*hp, step, L->world),
+                            static_cast<hipStream_t>(hip_stream));
 }
 
 extern "C" int zs_grads_tile(const zs_layout* L, int32_t bucket_id,
@@ -983,17 +1107,19 @@ extern "C" int zs_grads_tile(const zs_layout* L, int32_t bucket_id,
         return fail(ZS_ERANGE, "W * stride overflows");
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
     if (bucket_id >= 0) {
-        const Geom g = bucket_geom(L, L->buckets[bucket_id]);
-        hipLaunchKernelGGL(grads_tile_kernel, dim3((unsigned)g.TPB, 1),
-                           dim3(kThreads), 0, s, slices, stride, tiled, W, g);
+        // one bucket's staging: positions relative to the bucket
+        GeomLoc loc;
+        loc.g = bucket_geom(L, L->buckets[bucket_id]);
+        hipLaunchKernelGGL(grads_tile_kernel<GeomLoc>,
+                           dim3((unsigned)loc.g.TPB, 1), dim3(kThreads), 0,
+                           s, slices, stride, tiled, W, loc);
         return check_launch("grads tile kernel");
     }
-    return for_shard_ranges(L, [&](const Range& R) {
-        const zs_bucket& b0 = L->buckets[R.y0];
-        hipLaunchKernelGGL(grads_tile_kernel,
-                           dim3((unsigned)R.g.TPB, (unsigned)R.ny),
-                           dim3(kThreads), 0, s, slices + b0.shard_off,
-                           stride, tiled + b0.tile_off * W * kTile, W, R.g);
+    return for_launches(L, [&](const auto& loc, dim3 grid, int64_t e,
+                               int64_t t, int64_t) {
+        using Loc = std::decay_t<decltype(loc)>;
+        hipLaunchKernelGGL(grads_tile_kernel<Loc>, grid, dim3(kThreads), 0, s,
+                           slices + e, stride, tiled + t * W * kTile, W, loc);
         return check_launch("grads tile kernel");
     });
 }
@@ -1025,15 +1151,11 @@ extern "C" int zs_pack(const zs_layout* L, const uint16_t* param_shard,
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
 
     if (full_flat) {
-        const int rc = for_shard_ranges(L, [&](const Range& R) {
-            const zs_bucket& b0 = L->buckets[R.y0];
-            PackFlatArgs a;
-            a.shard = param_shard + b0.shard_off;
-            a.flat = full_flat + b0.flat_off;
-            a.g = R.g;
-            hipLaunchKernelGGL(pack_flat_kernel,
-                               dim3((unsigned)R.g.TPB, (unsigned)R.ny),
-                               dim3(kThreads), 0, s, a);
+        const int rc = for_launches(L, [&](const auto& loc, dim3 grid,
+                                           int64_t e, int64_t, int64_t f) {
+            using Loc = std::decay_t<decltype(loc)>;
+            hipLaunchKernelGGL(pack_flat_kernel<Loc>, grid, dim3(kThreads),
+                               0, s, param_shard + e, full_flat + f, loc);
             return check_launch("pack flat kernel");
         });
         if (rc) return rc;
