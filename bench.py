@@ -64,6 +64,81 @@ def traffic_record(workload: str):
     return rec.get("bytes_per_launch")
 
 
+def read_counter_csv(path: str, counter: str):
+    """(kernel name, value) per dispatch from a rocprofv3 counter-collection
+    CSV, in dispatch order."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                             float(r["Counter_Value"])))
+    rows.sort()
+    return [(k, v) for _, k, v in rows]
+
+
+def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int) -> dict:
+    """HBM bytes per launch of the headline step from two rocprofv3 --pmc
+    runs of `bench.py --copy-calibration` (FETCH_SIZE, then WRITE_SIZE, KiB
+    per dispatch), each scaled by what the same counter reads for the
+    calibration copy of 4 GiB; written to profiles/traffic_llama8b.json with
+    the current kernel source hash."""
+    fetch = read_counter_csv(fetch_csv, "FETCH_SIZE")
+    write = read_counter_csv(write_csv, "WRITE_SIZE")
+    copy_bytes = 4 << 30
+
+    def pick(rows, pred):
+        return [v for k, v in rows if pred(k)]
+
+    is_copy = lambda k: "k_copy16" in k
+    tiled = lambda k: (k.startswith("void (anonymous namespace)::step_kernel<"
+                                    f"{W}, true,") and "true>" not in k)
+    plain = lambda k: (k.startswith("void (anonymous namespace)::step_kernel<"
+                                    f"{W}, false,") and "true>" not in k)
+    cf, cw = pick(fetch, is_copy), pick(write, is_copy)
+    if len(cf) != 1 or len(cw) != 1:
+        raise SystemExit("record-traffic: expected one calibration copy per "
+                         "run")
+    rs = copy_bytes / 1024 / cf[0]
+    ws = copy_bytes / 1024 / cw[0]
+    tf, tw = pick(fetch, tiled), pick(write, tiled)
+    pf, pw = pick(fetch, plain), pick(write, plain)
+    if not tf or not tw:
+        raise SystemExit("record-traffic: no tiled step dispatches found")
+    avg = lambda x: sum(x) / len(x)
+    rd = avg(tf) * 1024 * rs
+    wr = avg(tw) * 1024 * ws
+    alg = (2 * W + 26) * n
+    rec = {
+        "kernel": f"step_kernel<{W}, true, Shape<512, 4, 4> > (zs_step, "
+                  "tiled gradients, tiled state, flat output)",
+        "workload": f"llama8b rank-0 shard, W={W}, {n:,} elements",
+        "source_sha256_16": source_hash(),
+        "copy_calibration": {"bytes_read": copy_bytes,
+                             "bytes_written": copy_bytes,
+                             "FETCH_SIZE_KiB": cf[0], "WRITE_SIZE_KiB": cw[0],
+                             "read_scale": rs, "write_scale": ws},
+        "FETCH_SIZE_KiB_per_launch": tf,
+        "WRITE_SIZE_KiB_per_launch": tw,
+        "bytes_read_per_launch": rd,
+        "bytes_written_per_launch": wr,
+        "bytes_per_launch": rd + wr,
+        "algorithmic_bytes_per_launch": alg,
+        "ratio_to_algorithmic": (rd + wr) / alg,
+    }
+    if pf and pw:
+        prd, pwr = avg(pf) * 1024 * rs, avg(pw) * 1024 * ws
+        rec["plain_slices"] = {"bytes_read_per_launch": prd,
+                               "bytes_written_per_launch": pwr,
+                               "ratio_to_algorithmic": (prd + pwr) / alg}
+    with open(os.path.join(ROOT, "profiles", "traffic_llama8b.json"),
+              "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
 def cpu_baseline(W, seconds: float):
     """The oracle as it stands, single-threaded, on a bounded sample of the
     same workload: a 2^22-element window of the shard, stepped repeatedly
@@ -646,7 +721,23 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="launch one plain 4 GiB device copy before the "
                     "steps (the reference dispatch for rocprofv3 counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV",
+                                                          "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 --pmc counter CSVs of "
+                    "a --copy-calibration run into profiles/"
+                    "traffic_llama8b.json")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        import zero_sharded_optimizer_shard_amd as zs
+        from synth import workloads as wl
+        w = wl.presets()["llama8b"]
+        n = zs.zs_layout_info(zs.zs_layout_build(w.numels, w.world,
+                                                 w.rank))[1]
+        rec = record_traffic(*args.record_traffic, n, w.world)
+        print(json.dumps({k: rec[k] for k in
+                          ("bytes_per_launch", "ratio_to_algorithmic")}))
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus "
