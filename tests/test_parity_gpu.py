@@ -735,12 +735,31 @@ def test_pure_bf16_step(W, layout, flat_params):
     numels = [rng.choice([7, 129, 1000, 4096, 33333, 65536])
               for _ in range(9)]
     cap = W * 256 * rng.choice([3, 17, 40])
-    rank = W - 1
+    say(f"case bf16 W={W} {layout} flat={flat_params}")
+    run_pure_bf16(numels, W, W - 1, cap, layout, flat_params, (1, 2, 3))
+
+
+@pytest.mark.parametrize("W,tiles", [(2, 300), (2, 4200), (8, 4100),
+                                     (5, 4100), (32, 4100)])
+def test_pure_bf16_launch_shapes(W, tiles):
+    """Each work shape of the pure-bf16 step: fewer than 4096 tiles, 4096 or
+    more at W < 32 (its own shape), at W >= 32, and the runtime-W kernel;
+    one bucket, a ragged last tile, parameters in place in the flat
+    buffer, tiled gradients; bit for bit against the oracle."""
+    n_rank = tiles * TILE - 4096            # the last tile half full
+    numels = [W * n_rank - 1000, 1000]
+    say(f"case bf16 shape W={W} tiles={tiles}")
+    lay_o = run_pure_bf16(numels, W, W - 1, 0, "tiled", True, (1, 2))
+    assert lay_o.n_tiles == tiles
+
+
+def run_pure_bf16(numels, W, rank, cap, layout, flat_params, steps):
+    """zs_step_bf16 on rank `rank`'s shard for the given steps, checked
+    after each against the oracle, bit for bit; returns the oracle layout."""
     lay_o = build_layout(numels, W, rank, cap)
     lay = zs.zs_layout_build(numels, W, rank, cap)
     n, F = lay_o.shard_numel, lay_o.flat_numel
     pad = S.padding_runs(n, lay_o.chunks)
-    say(f"case bf16 W={W} {layout} flat={flat_params}")
     om, omm, ov = S.cpu_state(0, n, 0.02, W, pad, (1e-4, 1e-8))
     p16 = O.bf16_round(om)
     m_d, v_d = (torch.from_numpy(x.copy()).cuda() for x in (omm, ov))
@@ -757,7 +776,7 @@ def test_pure_bf16_step(W, layout, flat_params):
         params = torch.from_numpy(p16.view(np.int16).copy()).cuda()
     G = torch.empty((W, n + 8), dtype=torch.bfloat16, device="cuda")
     Gt = dev_bf16(lay_o.n_tiles * W * TILE)
-    for t in (1, 2, 3):
+    for t in steps:
         S.dev_grads(G, W, n, t, 1e-3, W, pad)
         if layout == "tiled":
             zs.zs_grads_tile(lay, -1, G, n + 8, Gt)
@@ -783,6 +802,7 @@ def test_pure_bf16_step(W, layout, flat_params):
     zs.zs_state_mv_unpack(lay, state, *outs)
     assert np.array_equal(npf(outs[0]), omm)
     assert np.array_equal(npf(outs[1]), ov)
+    return lay_o
 
 
 def test_pure_bf16_llama8b_flat_sampled():

@@ -722,10 +722,15 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 //    workgroups per tile, so that a few hundred or thousand tiles still
 //    spread evenly over the 256 CUs with a short tail (GPT-2-shaped W = 8
 //    shard, 1899 tiles: 81 % vs 75 % with Wide; at 122 K tiles the two
-//    are equal).
+//    are equal);
+//  - PureWide (the pure-bf16 step at W < 32, where the state is two rows):
+//    256-thread workgroups, two per tile, 4 units per thread: 80-81 % vs
+//    78-79 % with Wide at W = 4, 8 and 16 on the 8B-shaped shard (at
+//    W = 64 Deep stays ahead).
 using ShapeWide = Shape<512, 4, 4>;
 using ShapeDeep = Shape<512, 4, 8>;
 using ShapeSmall = Shape<512, 1, 4>;
+using ShapePureWide = Shape<256, 4, 4>;
 constexpr int64_t kSmallLaunch = 4096;
 
 // grid: one x per tile (launch_kernel multiplies by the shape's P)
@@ -737,6 +742,8 @@ void launch_step_w(const Args& a, bool tiled, dim3 grid, hipStream_t s)
         launch_shape<WT, ShapeSmall, PURE>(a, tiled, grid, s);
     else if constexpr (WT >= 32)
         launch_shape<WT, ShapeDeep, PURE>(a, tiled, grid, s);
+    else if constexpr (PURE)
+        launch_shape<WT, ShapePureWide, PURE>(a, tiled, grid, s);
     else
         launch_shape<WT, ShapeWide, PURE>(a, tiled, grid, s);
 }
