@@ -27,7 +27,6 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -40,26 +39,35 @@ HP = dict(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
 PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E, 8 TB/s
 METRIC = ("optimizer-step params/s per GPU + achieved HBM GB/s (% of peak), "
           "8B W=8 shard")
-STEP_SRC = os.path.join(ROOT, "zero_sharded_optimizer_shard_amd", "csrc",
-                        "zs_step.hip")
+KERNELS = os.path.join(ROOT, "zero_sharded_optimizer_shard_amd",
+                       "libzs.kernels.json")
+# the kernel whose HBM counters the roofline's traffic figure comes from
+HEADLINE_KERNEL = ("_ZN12_GLOBAL__N_111step_kernelILi8ELb1ENS_5ShapeILi512ELi4E"
+                   "Li4EEELb0EEEvNS_8StepArgsE")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
-    return hashlib.sha256(open(STEP_SRC, "rb").read()).hexdigest()[:16]
+def kernel_digest(symbol: str):
+    """sha256 prefix of the kernel's machine code in the built libzs.so
+    (the build writes them beside the library), or None."""
+    if not os.path.exists(KERNELS):
+        return None
+    return json.load(open(KERNELS)).get(symbol)
 
 
 def traffic_record(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
-    only if it was taken on the current kernel source."""
+    only if the counters were taken on the kernel now built (same machine
+    code)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256_16") != source_hash():
+    now = kernel_digest(rec.get("kernel_symbol", ""))
+    if now is None or rec.get("kernel_sha256_16") != now:
         return None
     return rec.get("bytes_per_launch")
 
@@ -83,7 +91,8 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int) -> dict:
     runs of `bench.py --copy-calibration` (FETCH_SIZE, then WRITE_SIZE, KiB
     per dispatch), each scaled by what the same counter reads for the
     calibration copy of 4 GiB; written to profiles/traffic_llama8b.json with
-    the current kernel source hash."""
+    the digest of the kernel's machine code in the current build (the
+    counters must have been taken on that build)."""
     fetch = read_counter_csv(fetch_csv, "FETCH_SIZE")
     write = read_counter_csv(write_csv, "WRITE_SIZE")
     copy_bytes = 4 << 30
@@ -114,7 +123,8 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int) -> dict:
         "kernel": f"step_kernel<{W}, true, Shape<512, 4, 4> > (zs_step, "
                   "tiled gradients, tiled state, flat output)",
         "workload": f"llama8b rank-0 shard, W={W}, {n:,} elements",
-        "source_sha256_16": source_hash(),
+        "kernel_symbol": HEADLINE_KERNEL,
+        "kernel_sha256_16": kernel_digest(HEADLINE_KERNEL),
         "copy_calibration": {"bytes_read": copy_bytes,
                              "bytes_written": copy_bytes,
                              "FETCH_SIZE_KiB": cf[0], "WRITE_SIZE_KiB": cw[0],

@@ -332,3 +332,16 @@ def test_empty_layout_calls_are_noops():
     assert L.zs_step_bf16(lay.handle, None, 0, 0, None, None, 0,
                           ctypes.byref(hp), 1, None) == 0
     assert L.zs_state_mv_pack(lay.handle, None, None, None, None) == 0
+
+
+def test_build_records_kernel_digests():
+    """The build lists a digest of every kernel's machine code beside the
+    library; the benchmark's traffic figure is tied to the headline step
+    kernel's entry, so that entry must exist under its mangled name."""
+    import json
+    import bench
+    from zero_sharded_optimizer_shard_amd import build as B
+    digests = json.load(open(B.KERNELS))
+    assert bench.HEADLINE_KERNEL in digests
+    assert all(len(v) == 16 for v in digests.values())
+    assert any("gather_kernel" in k for k in digests)

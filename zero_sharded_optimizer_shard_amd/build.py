@@ -6,14 +6,21 @@ fp32 divide and square root, IEEE denormals (no flush), and packed fp32
 instructions disabled.
 """
 
+import hashlib
+import json
 import os
+import re
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libzs.so")
+# sha256 prefix of every kernel's machine code in LIB, written by build()
+KERNELS = os.path.join(PKG, "libzs.kernels.json")
+LLVM = "/opt/rocm/llvm/bin"
 
 SOURCES = [os.path.join(CSRC, "zs_layout.cpp"),
            os.path.join(CSRC, "zs_step.hip"),
@@ -41,7 +48,62 @@ def build(verbose: bool = False, extra=()) -> str:
     if verbose and msg.strip():
         print(msg)
     os.replace(LIB + ".tmp", LIB)
+    with open(KERNELS, "w") as f:
+        json.dump(kernel_digests(LIB), f, indent=0, sort_keys=True)
     return LIB
+
+
+def _tool(name, *args) -> str:
+    return subprocess.run([os.path.join(LLVM, name), *args], check=True,
+                          capture_output=True, text=True).stdout
+
+
+def kernel_digests(lib: str) -> dict:
+    """{mangled kernel name: sha256 prefix of its machine code} for the
+    gfx950 code object embedded in `lib` (a library built here).  Identical
+    bytes mean an identical kernel, whatever else changed in the sources;
+    measurements tied to one kernel (its HBM counters) stay valid while its
+    digest does."""
+    out = {}
+    with tempfile.TemporaryDirectory() as d:
+        fat = os.path.join(d, "fat.bin")
+        _tool("llvm-objcopy", f"--dump-section=.hip_fatbin={fat}", lib,
+              os.path.join(d, "rest.so"))
+        # one offload bundle per source file with device code
+        blob = open(fat, "rb").read()
+        magic = b"__CLANG_OFFLOAD_BUNDLE__"
+        starts = [m.start() for m in re.finditer(re.escape(magic), blob)]
+        for i, a in enumerate(starts):
+            part = os.path.join(d, f"b{i}.bin")
+            co = os.path.join(d, f"b{i}.elf")
+            end = starts[i + 1] if i + 1 < len(starts) else len(blob)
+            with open(part, "wb") as f:
+                f.write(blob[a:end])
+            _tool("clang-offload-bundler", "--unbundle", "--type=o",
+                  f"--input={part}", f"--output={co}",
+                  "--targets=hipv4-amdgcn-amd-amdhsa--gfx950")
+            out.update(_elf_kernel_digests(co))
+    return out
+
+
+def _elf_kernel_digests(co: str) -> dict:
+    data = open(co, "rb").read()
+    text = None
+    for line in _tool("llvm-readelf", "-S", "-W", co).splitlines():
+        m = re.search(r"\]\s+\.text\s+PROGBITS\s+([0-9a-f]+)\s+"
+                      r"([0-9a-f]+)", line)
+        if m:
+            text = (int(m.group(1), 16), int(m.group(2), 16))
+    out = {}
+    if text is None:
+        return out
+    for line in _tool("llvm-readelf", "-s", "-W", co).splitlines():
+        f = line.split()
+        if len(f) >= 8 and f[3] == "FUNC" and f[2] != "0":
+            off = int(f[1], 16) - text[0] + text[1]
+            code = data[off:off + int(f[2])]
+            out[f[7]] = hashlib.sha256(code).hexdigest()[:16]
+    return out
 
 
 if __name__ == "__main__":
