@@ -719,7 +719,7 @@ def main():
                     "(zs_gather) with prefetch, on the workload's layout")
     ap.add_argument("--tokens", type=int, default=2048,
                     help="ZeRO-3 mode: tokens of the stand-in layer compute")
-    ap.add_argument("--group", type=int, default=8,
+    ap.add_argument("--group", type=int, default=16,
                     help="streaming mode: landed buckets stepped per launch "
                     "(zs_buckets_step); the ring holds 2*group slots")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
