@@ -149,34 +149,75 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int) -> dict:
     return rec
 
 
-def cpu_baseline(W, seconds: float):
-    """The oracle as it stands, single-threaded, on a bounded sample of the
-    same workload: a 2^22-element window of the shard, stepped repeatedly
-    until `seconds` have passed."""
+def cpu_baseline(W, seconds: float, threads: int = 1):
+    """The oracle as it stands on a bounded sample of the same workload:
+    each of `threads` host threads steps its own 2^22-element window of the
+    shard (windows one after another) with the single-threaded C oracle,
+    repeatedly until `seconds` have passed; the oracle call holds no Python
+    lock, so the threads run on separate cores."""
+    import threading
     from oracle import step as O
     from synth import state as S
     n = 1 << 22
-    G = S.cpu_grads(W, 0, n, 1, 1e-4)
-    master, m, v = S.cpu_state(0, n, 0.02)
     hp = O.AdamW(**HP)
-    reps = 0
+    data = [(S.cpu_grads(W, k * n, n, 1, 1e-4),
+             *S.cpu_state(k * n, n, 0.02)) for k in range(threads)]
+    reps = [0] * threads
+    start = threading.Barrier(threads + 1)
+    t_end = [0.0]
+
+    def work(k):
+        G, master, m, v = data[k]
+        start.wait()
+        while True:
+            O.step(G, master, m, v, hp, reps[k] + 1)
+            reps[k] += 1
+            if time.perf_counter() >= t_end[0]:
+                break
+
+    ts = [threading.Thread(target=work, args=(k,)) for k in range(threads)]
+    for t in ts:
+        t.start()
     t0 = time.perf_counter()
-    while True:
-        O.step(G, master, m, v, hp, reps + 1)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return dict(value=n * reps / el, unit="params/s", cores=1, kind="oracle",
-                sample=f"{reps} steps over a {n}-element window of the rank-0 "
-                       f"shard (W={W}), single-threaded C oracle, "
+    t_end[0] = t0 + seconds
+    start.wait()
+    for t in ts:
+        t.join()
+    el = time.perf_counter() - t0
+    what = ("single-threaded C oracle" if threads == 1 else
+            f"the single-threaded C oracle in {threads} host threads, one "
+            f"window each")
+    return dict(value=n * sum(reps) / el, unit="params/s", cores=threads,
+                kind="oracle",
+                sample=f"{sum(reps)} steps over {threads} x {n}-element "
+                       f"windows of the rank-0 shard (W={W}), {what}, "
                        f"{el:.1f} s")
 
 
+def host_cores() -> int:
+    """Cores this process may use, capped at 16 (one GPU's share of the
+    host on a shared node)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _time_launches(fn, reps, st):
+    import torch
+    for _ in range(2):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(st)
+    for _ in range(reps):
+        fn()
+    ev[1].record(st)
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / reps
+
+
 def ceiling(Gt, state, flat, lay, W, n, reps=10):
-    """The step's exact access pattern (tiled gradients and state, flat
-    output), no arithmetic: the achievable bandwidth for this read/write
-    mix on this device."""
+    """Achievable bandwidths on this device: the step's exact access
+    pattern (tiled gradients and state, flat output) with XORs in place of
+    the arithmetic, a read-only stream over the tiled gradients, and a
+    plain 4 GiB copy."""
     import torch
     import synth
     import zero_sharded_optimizer_shard_amd as zs
@@ -185,16 +226,24 @@ def ceiling(Gt, state, flat, lay, W, n, reps=10):
     b0 = buckets[0]
     args = (Gt, state, flat, W, b0.slice_numel, buckets[-1].slice_numel,
             b0.numel, len(buckets), st)
-    for _ in range(2):
-        synth.dev_mix_stream(*args)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record(st)
-    for _ in range(reps):
-        synth.dev_mix_stream(*args)
-    ev[1].record(st)
-    torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / reps
-    return (2 * W + 26) * n / (ms * 1e-3) / 1e9, ms
+    ms = _time_launches(lambda: synth.dev_mix_stream(*args), reps, st)
+    out = {"same_mix": dict(GBps=(2 * W + 26) * n / (ms * 1e-3) / 1e9,
+                            ms=ms)}
+    nb = Gt.numel() * 2 // 16 * 16
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    ms = _time_launches(lambda: synth.dev_read(Gt, nb, sink, stream=st),
+                        reps, st)
+    out["read_only"] = dict(GBps=nb / (ms * 1e-3) / 1e9, ms=ms, bytes=nb)
+    cb = 4 << 30
+    src = torch.empty(cb // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    ms = _time_launches(lambda: synth.dev_copy(dst, src, cb, stream=st),
+                        reps, st)
+    out["copy"] = dict(GBps=2 * cb / (ms * 1e-3) / 1e9, ms=ms, bytes=2 * cb)
+    del src, dst
+    for v in out.values():
+        v["frac_of_peak"] = v["GBps"] / PEAK_HBM_GBS
+    return out
 
 
 def time_steps(fn, K, st):
@@ -832,11 +881,13 @@ def main():
     log(f"zs_step (tiled): {avg_ms:.3f} ms per launch, {K} back to back "
         f"-> {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.1%} of 8 TB/s)")
     each = time_each(step_tiled, K, st)
+    med = sorted(each)[K // 2] if K % 2 else sum(sorted(each)[K // 2 - 1:
+                                                             K // 2 + 1]) / 2
     log(f"  with events around each launch: avg {sum(each) / K:.3f} ms, "
-        f"min {min(each):.3f}, max {max(each):.3f}")
+        f"median {med:.3f}, min {min(each):.3f}, max {max(each):.3f}")
 
-    extra = {"per_launch_events_ms": dict(avg=sum(each) / K, min=min(each),
-                                          max=max(each))}
+    extra = {"per_launch_events_ms": dict(avg=sum(each) / K, median=med,
+                                          min=min(each), max=max(each))}
     for _ in range(2):
         step_slices()
     sl_avg, _ = time_steps(step_slices, K, st)
@@ -864,10 +915,14 @@ def main():
                                    pack=e[1].elapsed_time(e[2]))
         del p
     if args.ceiling and not args.whole_tensors:
-        gbs, cms = ceiling(Gt, state, flat, lay, W, n)
-        extra["same_mix_ceiling"] = dict(GBps=gbs, ms=cms,
-                                         frac_of_peak=gbs / PEAK_HBM_GBS)
-        log(f"same-mix ceiling: {gbs:.0f} GB/s ({cms:.3f} ms)")
+        c = ceiling(Gt, state, flat, lay, W, n)
+        c["step_frac_of_same_mix"] = achieved / c["same_mix"]["GBps"]
+        extra["ceilings"] = c
+        log(f"ceilings: same mix {c['same_mix']['GBps']:.0f} GB/s "
+            f"({c['same_mix']['ms']:.3f} ms), read-only "
+            f"{c['read_only']['GBps']:.0f} GB/s, copy "
+            f"{c['copy']['GBps']:.0f} GB/s; the step runs at "
+            f"{c['step_frac_of_same_mix']:.1%} of the same-mix ceiling")
 
     traffic = None if args.whole_tensors else traffic_record(args.workload)
     config = {"workload": f"{w.name} rank-0 shard, W={W}",
@@ -909,6 +964,11 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
+        nc = host_cores()
+        if nc > 1:
+            log(f"timing the CPU oracle on {nc} cores ...")
+            out["cpu_baseline_all_cores"] = cpu_baseline(W, args.cpu_seconds,
+                                                         nc)
     print(json.dumps(out), flush=True)
 
 

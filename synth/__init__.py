@@ -60,10 +60,11 @@ def _dev_lib():
                                             ctypes.c_double, p]
         L.synth_bits16_dev.argtypes = [p, i64, u64, u64, u64, u64, i64, p]
         L.synth_copy_dev.argtypes = [p, p, i64, p]
+        L.synth_read_dev.argtypes = [p, i64, p, p]
         L.synth_mix_stream_dev.argtypes = [p, p, p, i32, i64, i64, i64,
                                            i32, p]
         for f in (L.synth_normal_f32_dev, L.synth_normal_bf16_dev,
-                  L.synth_bits16_dev, L.synth_copy_dev,
+                  L.synth_bits16_dev, L.synth_copy_dev, L.synth_read_dev,
                   L.synth_mix_stream_dev):
             f.restype = ctypes.c_int
         _dev = L
@@ -136,6 +137,12 @@ def dev_bits16(t, seed, tag, step, src, index_base, stream=None):
 def dev_copy(dst, src, nbytes, stream=None):
     _ok(_dev_lib().synth_copy_dev(dst.data_ptr(), src.data_ptr(), nbytes,
                                   _stream_handle(stream)), "synth_copy_dev")
+
+
+def dev_read(src, nbytes, sink, stream=None):
+    """Read nbytes of src (the read-only ceiling); sink: >= 16 bytes."""
+    _ok(_dev_lib().synth_read_dev(src.data_ptr(), nbytes, sink.data_ptr(),
+                                  _stream_handle(stream)), "synth_read_dev")
 
 
 def dev_mix_stream(grads_tiled, state, flat, W, S, S_last, B, nb,

@@ -174,6 +174,42 @@ extern "C" int synth_copy_dev(void* dst, const void* src, int64_t nbytes,
     return finish();
 }
 
+/* Read-only stream: four 16-byte non-temporal loads per thread (each wave
+ * instruction one contiguous 1 KiB run), XORed together; a thread writes
+ * only if its XOR hits one fixed 128-bit pattern, which keeps the loads
+ * alive and, on random data, writes nothing. */
+__global__ __launch_bounds__(256) void k_read16(const u32x4* __restrict__ src,
+                                                int64_t n16,
+                                                u32x4* __restrict__ sink)
+{
+    const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t i = base + k * 256;
+        if (i < n16)
+            acc ^= __builtin_nontemporal_load(&src[i]);
+    }
+    if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u && acc.z == 0xf39cc060u &&
+        acc.w == 0x5ced0f2du)
+        sink[0] = acc;
+}
+
+extern "C" int synth_read_dev(const void* src, int64_t nbytes, void* sink,
+                              void* stream)
+{
+    if (nbytes < 0 || (nbytes % 16) || (nbytes && (!src || !sink))) return -1;
+    if (((uintptr_t)src | (uintptr_t)sink) & 15u) return -2;
+    int64_t n16 = nbytes / 16;
+    if (n16 == 0) return 0;
+    int64_t blocks = (n16 + 1023) / 1024;
+    if (blocks > 0x7fffffff) return -3;
+    hipLaunchKernelGGL(k_read16, dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, (const u32x4*)src, n16,
+                       (u32x4*)sink);
+    return finish();
+}
+
 /* The step's access pattern with integer XORs in place of the arithmetic:
  * one 512-thread workgroup per 8192-element tile of a bucket slice, four
  * 4-element units per thread at stride 512 units; reads W tiled gradient

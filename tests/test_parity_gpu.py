@@ -522,10 +522,12 @@ def test_nan_is_local_and_padding_stays_zero(layout):
         assert not np16(p)[s0:e0].any()
 
 
-def sample_windows(lay_o, per_bucket=2048, n_random=16, span=1 << 16,
-                   seed=0):
-    """Shard windows: both ends of every bucket slice, both sides of every
-    chunk boundary, and random spans."""
+def sample_windows(lay_o, per_bucket=4096, chunk_side=512, n_even=64,
+                   even_span=1 << 20, n_random=8, span=1 << 16, seed=0):
+    """Shard windows (the step is elementwise, so each window checks on its
+    own): the first and last per_bucket elements of every bucket slice,
+    chunk_side elements on both sides of every chunk boundary, n_even
+    evenly spaced windows of even_span elements, and random spans."""
     n = lay_o.shard_numel
     wins = []
     for b in lay_o.buckets:
@@ -534,8 +536,11 @@ def sample_windows(lay_o, per_bucket=2048, n_random=16, span=1 << 16,
         wins.append((max(b.shard_off, e - per_bucket), min(per_bucket,
                                                            b.slice_numel)))
     for c in lay_o.chunks:
-        a = max(0, c.shard_off - 256) // 8 * 8
-        wins.append((a, min(512, n - a)))
+        a = max(0, c.shard_off - chunk_side) // 8 * 8
+        wins.append((a, min(2 * chunk_side, n - a)))
+    for i in range(n_even):
+        a = (n - even_span) * i // max(1, n_even - 1) // 8 * 8
+        wins.append((max(0, a), min(even_span, n)))
     rng = random.Random(seed)
     for _ in range(n_random):
         a = rng.randrange(0, max(1, n - span)) // 8 * 8
@@ -559,7 +564,8 @@ def test_full_size_sampled(name):
     Gt = dev_bf16(lay_o.n_tiles * W * TILE)
     flat = dev_bf16(lay_o.flat_numel)
     flat.view(torch.int16).fill_(0x7fc0)
-    wins = sample_windows(lay_o)
+    # W = 64 makes each window 8 times dearer to generate on the host
+    wins = sample_windows(lay_o, n_even=64 if W <= 8 else 16)
     ref = [S.cpu_state(a, k, w.master_sigma) for a, k in wins]
     slot = tile_slot(lay_o)
     st3 = state.view(lay_o.n_tiles, 3, TILE)
