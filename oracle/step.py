@@ -13,7 +13,10 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libzs_oracle.so")
+_DEFAULT_LIB = os.path.join(_HERE, "libzs_oracle.so")
+# ZS_ORACLE_LIB names another build of zs_oracle.c to load instead; the
+# mutation test uses it to run the pins against planted mistakes.
+_LIB_PATH = os.environ.get("ZS_ORACLE_LIB") or _DEFAULT_LIB
 _lib = None
 
 
@@ -42,6 +45,8 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
+            if _LIB_PATH != _DEFAULT_LIB:
+                raise FileNotFoundError(_LIB_PATH)
             from . import build as _b
             _b.build()
         L = ctypes.CDLL(_LIB_PATH)

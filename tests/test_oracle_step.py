@@ -249,6 +249,24 @@ def test_reduce_mean_is_fixed_order_sum():
     assert np.array_equal(O.reduce_mean(G), acc / np.float32(W))
 
 
+def test_reduce_order_is_rank_order():
+    """Where fp32 rounding makes the order visible: 2^-24 is half an ulp of
+    1.0, so 1 + 2^-24 + 2^-24 is 1 left to right (each addition ties to the
+    even 1.0), while 2^-24 + 2^-24 + 1 is exactly 1 + 2^-23.  Slices are
+    summed in rank order 0, 1, ..., W-1, starting from slice 0."""
+    one, tiny = 0x3F80, 0x3380          # bf16 bits of 1.0 and 2^-24
+    G = np.array([[one, tiny, tiny, one],
+                  [tiny, tiny, one, tiny],
+                  [tiny, one, tiny, tiny]], np.uint16)
+    got = O.reduce_mean(G)
+    third = np.float32(1) / np.float32(3)
+    big = np.float32(1 + 2 ** -23) / np.float32(3)
+    # element 0: 1, t, t -> 1; element 1: t, t, 1 -> 1 + 2^-23;
+    # element 2: t, 1, t -> t + 1 = 1, + t = 1; element 3: 1, t, t -> 1
+    assert got.tolist() == [third, big, third, third]
+    assert third != big
+
+
 def test_step_is_reduce_then_adamw():
     W, n = 3, 3000
     hp = hp_f32()

@@ -267,6 +267,53 @@ def test_launch_shapes(W, tiles, layout):
         c.step(t)
 
 
+@pytest.mark.parametrize("W,tiles,layout", [
+    (3, 10, "tiled"), (8, 10, "slices"), (8, 4100, "tiled"),
+    (5, 4100, "tiled"), (32, 4100, "tiled"), (64, 300, "tiled"),
+    (64, 300, "slices")])
+def test_sum_order_is_rank_order(W, tiles, layout):
+    """Gradients where fp32 rounding exposes the order of the sum: every
+    element's W slices hold one 1.0 at a position that varies with the
+    element and 2^-24 everywhere else (half an ulp of 1.0, so each one
+    added after the 1.0 ties back to it, while the ones before it add up
+    exactly).  Every work shape, compiled and runtime W; bit for bit
+    against the oracle, whose order is pinned on the same values."""
+    n_rank = tiles * TILE - 4096            # the last tile half full
+    numels = [W * n_rank]
+    lay_o = build_layout(numels, W, W - 1, 0)
+    lay = zs.zs_layout_build(numels, W, W - 1, 0)
+    n = lay_o.shard_numel
+    assert lay_o.n_tiles == tiles
+    say(f"case sum order W={W} tiles={tiles} {layout}")
+    i = np.arange(n, dtype=np.int64)
+    pos = (i * 7 + i // 13) % W
+    G = np.full((W, n), 0x3380, np.uint16)
+    G[pos, i] = 0x3F80
+    state = dev_state(lay, lay_o, 0.02)
+    om, omm, ov = read_state(lay_o, state)
+    Gd = torch.from_numpy(G.view(np.int16)).cuda()
+    if layout == "tiled":
+        Gt = dev_bf16(lay_o.n_tiles * W * TILE)
+        zs.zs_grads_tile(lay, -1, Gd, n, Gt)
+    p = dev_bf16(n)
+    if layout == "tiled":
+        zs.zs_step(lay, Gt, state, p, None, grad_layout="tiled", step=1,
+                   **HP)
+    else:
+        zs.zs_step(lay, Gd, state, p, None, grad_stride=n, step=1, **HP)
+    p16 = O.step(G, om, omm, ov, OHP, 1)
+    torch.cuda.synchronize()
+    gm, m1, v1 = read_state(lay_o, state)
+    assert np.array_equal(gm.view(np.uint32), om.view(np.uint32))
+    assert np.array_equal(m1.view(np.uint32), omm.view(np.uint32))
+    assert np.array_equal(v1.view(np.uint32), ov.view(np.uint32))
+    assert np.array_equal(np16(p), p16)
+    # the order is visible in these values: the gradient means differ
+    # between elements whose 1.0 sits at different positions
+    g = O.reduce_mean(np.ascontiguousarray(G[:, :2 * W]))
+    assert len(set(g.tolist())) > 1
+
+
 @pytest.mark.parametrize("W", [3, 8])
 def test_all_ranks_reassemble_to_the_unsharded_step(W):
     """all-reduce = reduce-scatter + all-gather on the GPU: every rank steps
