@@ -314,6 +314,40 @@ def test_sum_order_is_rank_order(W, tiles, layout):
     assert len(set(g.tolist())) > 1
 
 
+@pytest.mark.parametrize("W,tiles", [(8, 4100), (5, 4100), (32, 4100),
+                                     (64, 300)])
+def test_pure_bf16_sum_order_is_rank_order(W, tiles):
+    """The same order-exposing gradients through the pure-bf16 step's work
+    shapes (its own 256-thread shape at W < 32, Deep, Small); parameter
+    shard, bit for bit against the oracle."""
+    n_rank = tiles * TILE - 4096
+    numels = [W * n_rank]
+    lay_o = build_layout(numels, W, W - 1, 0)
+    lay = zs.zs_layout_build(numels, W, W - 1, 0)
+    n = lay_o.shard_numel
+    say(f"case bf16 sum order W={W} tiles={tiles}")
+    i = np.arange(n, dtype=np.int64)
+    G = np.full((W, n), 0x3380, np.uint16)
+    G[(i * 7 + i // 13) % W, i] = 0x3F80
+    om, omm, ov = S.cpu_state(0, n, 0.02, W, (), (1e-4, 1e-8))
+    p16 = O.bf16_round(om)
+    m_d, v_d = (torch.from_numpy(x.copy()).cuda() for x in (omm, ov))
+    state = dev_f32(lay_o.n_tiles * 2 * TILE)
+    zs.zs_state_mv_pack(lay, m_d, v_d, state)
+    params = torch.from_numpy(p16.view(np.int16).copy()).cuda()
+    Gt = dev_bf16(lay_o.n_tiles * W * TILE)
+    zs.zs_grads_tile(lay, -1, torch.from_numpy(G.view(np.int16)).cuda(), n,
+                     Gt)
+    zs.zs_step_bf16(lay, Gt, state, params, params_flat=False,
+                    grad_layout="tiled", step=1, **HP)
+    O.step_bf16(G, p16, omm, ov, OHP, 1)
+    torch.cuda.synchronize()
+    m_g, v_g = from_tiled_rows(lay_o, npf(state), 2)
+    assert np.array_equal(np16(params), p16)
+    assert np.array_equal(m_g.view(np.uint32), omm.view(np.uint32))
+    assert np.array_equal(v_g.view(np.uint32), ov.view(np.uint32))
+
+
 @pytest.mark.parametrize("W", [3, 8])
 def test_all_ranks_reassemble_to_the_unsharded_step(W):
     """all-reduce = reduce-scatter + all-gather on the GPU: every rank steps
