@@ -82,6 +82,28 @@ def test_equal_tensors_go_one_per_rank_in_order():
         assert lay.owner == list(range(W))
 
 
+@pytest.mark.parametrize("numels,owners", [
+    # all pad to 128: list order, loads tie to the lowest rank
+    # (ordering by raw size would give 1, 0, 1)
+    ([1, 128, 100], [0, 1, 0]),
+    # all pad to 256 (raw order 250, 200, 129 would give 1, 0, 1)
+    ([129, 200, 250], [0, 1, 0]),
+    # pads 256, 256, 128, 128: loads 256 | 256, then 384 | 256, so the last
+    # tensor goes to rank 1 (raw loads 129 | 200 would send it to rank 0)
+    ([129, 200, 1, 1], [0, 1, 0, 1]),
+])
+def test_padding_decides_the_assignment(numels, owners):
+    """Worked by hand from the rule, W = 2: sizes and loads are the sizes
+    padded to the 128-element unit."""
+    lays = [build_tensor_layout(numels, 2, r) for r in range(2)]
+    assert lays[0].owner == owners
+    for r in range(2):
+        assert [c.tensor_id for c in lays[r].chunks] == \
+            [t for t in range(len(numels)) if owners[t] == r]
+        assert lays[r].shard_numel == sum(pad(n) for t, n in
+                                          enumerate(numels) if owners[t] == r)
+
+
 def test_one_rank_is_the_flat_single_bucket():
     numels = wl.tiny() + [7, 129, 70000]
     t = build_tensor_layout(numels, 1, 0)
