@@ -913,7 +913,28 @@ def main():
         torch.cuda.synchronize()
         extra["unfused_ms"] = dict(step=e[0].elapsed_time(e[1]),
                                    pack=e[1].elapsed_time(e[2]))
-        del p
+        # the per-tensor pack: this rank's chunks scattered into separate
+        # per-tensor buffers through the device chunk table
+        import numpy as np
+        tensors = [torch.empty(k, dtype=torch.bfloat16, device="cuda")
+                   for k in w.numels]
+        ptrs = torch.tensor([t_.data_ptr() for t_ in tensors],
+                            dtype=torch.int64, device="cuda")
+        chunks = zs.zs_layout_chunks(lay)
+        dch = torch.from_numpy(np.frombuffer(zs.chunks_bytes(chunks),
+                                             np.uint8).copy()).cuda()
+        ms = _time_launches(lambda: zs.zs_pack(lay, p, None, dch, len(chunks),
+                                               ptrs, stream=st), K, st)
+        extra["unfused_ms"]["pack_chunks"] = ms
+        extra["pack_GBps"] = dict(
+            flat=4 * n / (extra["unfused_ms"]["pack"] * 1e-3) / 1e9,
+            chunks=4 * n / (ms * 1e-3) / 1e9)
+        log(f"unfused: step {extra['unfused_ms']['step']:.3f} ms, pack to "
+            f"flat {extra['unfused_ms']['pack']:.3f} ms "
+            f"({extra['pack_GBps']['flat']:.0f} GB/s), pack to "
+            f"{len(w.numels)} tensors {ms:.3f} ms "
+            f"({extra['pack_GBps']['chunks']:.0f} GB/s)")
+        del p, tensors
     if args.ceiling and not args.whole_tensors:
         c = ceiling(Gt, state, flat, lay, W, n)
         c["step_frac_of_same_mix"] = achieved / c["same_mix"]["GBps"]
