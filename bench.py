@@ -923,6 +923,8 @@ def main():
         chunks = zs.zs_layout_chunks(lay)
         dch = torch.from_numpy(np.frombuffer(zs.chunks_bytes(chunks),
                                              np.uint8).copy()).cuda()
+        extra["unfused_ms"]["pack"] = _time_launches(
+            lambda: zs.zs_pack(lay, p, flat, stream=st), K, st)
         ms = _time_launches(lambda: zs.zs_pack(lay, p, None, dch, len(chunks),
                                                ptrs, stream=st), K, st)
         extra["unfused_ms"]["pack_chunks"] = ms
