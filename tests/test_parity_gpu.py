@@ -685,11 +685,13 @@ def test_full_size_sampled(name):
 
 def test_streaming_70b_sampled_beyond_2_32():
     """The Llama-3-70B-shaped W=16 rank-0 shard at full size (4.41e9
-    elements; shard, tile and state offsets beyond 2^32): a group of buckets
-    from the start, the middle and the end of the shard, each from its own
-    tiled staging buffer as the streaming mode gets them, stepped twice by
-    zs_buckets_step; windows at both ends of every stepped slice against
-    the oracle."""
+    elements; shard, tile, state and flat offsets beyond 2^32), in the
+    launch configuration the streaming benchmark times: a group of 16
+    buckets (from the start, the thirds, the middle and the end of the
+    shard), each from its own tiled staging buffer, stepped twice by one
+    zs_buckets_step call that writes the bf16 result into the 141 GB flat
+    buffer (and the shard); windows at both ends of every stepped slice
+    against the oracle."""
     w = wl.presets()["llama70b"]
     lay_o = build_layout(w.numels, w.world, 0)
     lay = zs.zs_layout_build(w.numels, w.world, 0)
@@ -705,7 +707,11 @@ def test_streaming_70b_sampled_beyond_2_32():
     del master
     torch.cuda.empty_cache()
     p = dev_bf16(n)
-    ids = [0, 1, nb // 2, nb - 3, nb - 2, nb - 1]
+    flat = dev_bf16(lay_o.flat_numel)
+    ids = [0, 1, 2, 3, nb // 3, nb // 3 + 1, nb // 2, nb // 2 + 1,
+           2 * nb // 3, 2 * nb // 3 + 1, nb - 6, nb - 5, nb - 4, nb - 3,
+           nb - 2, nb - 1]
+    assert len(set(ids)) == zs.ZS_MAX_GROUP == 16
     assert lay_o.buckets[nb - 1].shard_off > 2 ** 32
     smax = max(lay_o.buckets[b].slice_numel for b in ids)
     tmp = torch.empty((W, smax), dtype=torch.bfloat16, device="cuda")
@@ -726,7 +732,7 @@ def test_streaming_70b_sampled_beyond_2_32():
                                       synth.TAG_GRAD, t, s, b.shard_off,
                                       w.grad_sigma)
             zs.zs_grads_tile(lay, b_id, tmp, smax, buf)
-        zs.zs_buckets_step(lay, ids, stg, state, p, None,
+        zs.zs_buckets_step(lay, ids, stg, state, p, flat,
                            grad_layout="tiled", step=t, **HP)
         torch.cuda.synchronize()
         for (b_id, j0, k) in wins:
@@ -742,6 +748,8 @@ def test_streaming_70b_sampled_beyond_2_32():
                      p=np16(p[a:a + k])),
                 dict(master=st[0], m=st[1], v=st[2], p=p16),
                 f"70b t={t} bucket {b_id} window {j0}+{k}")
+            f0 = b.flat_off + j0                # rank 0's slice position
+            assert np.array_equal(np16(flat[f0:f0 + k]), p16)
 
 
 @pytest.mark.parametrize("W,cap", [(1, 25 << 20), (3, 3 * 256 * 37),
