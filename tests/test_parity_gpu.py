@@ -629,17 +629,25 @@ def sample_windows(lay_o, per_bucket=4096, chunk_side=512, n_even=64,
     return wins
 
 
-@pytest.mark.parametrize("name", ["llama8b", "dense7b"])
-def test_full_size_sampled(name):
+@pytest.mark.parametrize("name,tensors", [("llama8b", False),
+                                          ("dense7b", False),
+                                          ("llama8b", True)])
+def test_full_size_sampled(name, tensors):
     """The full Llama-3-8B-shaped (W=8) and 7B-shaped (W=64) rank-0 shards,
     in the launch configuration the benchmark times (tiled gradients, tiled
-    state, bf16 result straight into the flat all-gather buffer); sampled
-    windows against the oracle after each step."""
+    state, bf16 result straight into the flat all-gather buffer), in the
+    flat layout and (8B) the whole-tensor assignment; sampled windows
+    against the oracle after each step."""
     w = wl.presets()[name]
-    lay_o = build_layout(w.numels, w.world, 0)
-    lay = zs.zs_layout_build(w.numels, w.world, 0)
+    if tensors:
+        lay_o = build_tensor_layout(w.numels, w.world, 0)
+        lay = zs.zs_layout_build_tensors(w.numels, w.world, 0)
+    else:
+        lay_o = build_layout(w.numels, w.world, 0)
+        lay = zs.zs_layout_build(w.numels, w.world, 0)
     n, W = lay_o.shard_numel, w.world
-    say(f"case full-size {name}: W={W} shard={n}")
+    say(f"case full-size {name}{' whole tensors' if tensors else ''}: "
+        f"W={W} shard={n}")
     state = dev_state(lay, lay_o, w.master_sigma)
     G = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
     Gt = dev_bf16(lay_o.n_tiles * W * TILE)
@@ -676,11 +684,15 @@ def test_full_size_sampled(name):
                 dict(master=got[0], m=got[1], v=got[2], p=got_p),
                 dict(master=st[0], m=st[1], v=st[2], p=p16),
                 f"{name} t={t} window {a}+{k}")
-    # rank 0 writes nothing outside its slices
-    for b in lay_o.buckets[:3] + lay_o.buckets[-2:]:
-        other = np16(flat[b.flat_off + b.slice_numel:
-                          b.flat_off + b.slice_numel + 4096])
-        assert np.all(other == 0x7fc0)
+    # rank 0 writes nothing outside its slices (its tensors)
+    if tensors:
+        others = [t for t, r in enumerate(lay_o.owner) if r != 0]
+        spots = [lay_o.tensor_flat_off[t] for t in others[:3] + others[-2:]]
+    else:
+        spots = [b.flat_off + b.slice_numel
+                 for b in lay_o.buckets[:3] + lay_o.buckets[-2:]]
+    for f0 in spots:
+        assert np.all(np16(flat[f0:f0 + 4096]) == 0x7fc0), f0
 
 
 def test_streaming_70b_sampled_beyond_2_32():
@@ -988,6 +1000,36 @@ def test_gradient_accumulation(k):
     torch.cuda.synchronize()
     assert np.array_equal(np16(dG[k - 1]), want)
     assert torch.equal(acc.view(torch.int32), before.view(torch.int32))
+
+
+def test_gradient_accumulation_llama8b_flat_sampled():
+    """The benchmark's accumulation workload at full size: the Llama-3-8B-
+    shaped flat gradient buffer (8.03e9 elements, offsets beyond 2^32),
+    three micro-batches (first, add, last written over the last gradient);
+    sampled windows at both ends, around 2^32 and 3 * 2^31 and at random
+    against the oracle, bit for bit."""
+    w = wl.presets()["llama8b"]
+    n = build_layout(w.numels, w.world, 0).flat_numel
+    k = 3
+    say(f"case accumulate full-size llama8b: n={n} k={k}")
+    G = [dev_bf16(n) for _ in range(k)]
+    for j, g in enumerate(G):
+        synth.dev_normal_bf16(g, 0, synth.TAG_GRAD, j, 0, 0, w.grad_sigma)
+    acc = dev_f32(n)
+    zs.zs_accumulate(zs.ZS_ACC_FIRST, acc, G[0])
+    zs.zs_accumulate(zs.ZS_ACC_ADD, acc, G[1])
+    zs.zs_accumulate(zs.ZS_ACC_LAST, acc, G[2], G[2], k=k)
+    torch.cuda.synchronize()
+    rng = random.Random(11)
+    wins = [(0, 8192), (n - 8192, 8192), (2 ** 32 - 4096, 8192),
+            (3 * 2 ** 31 - 4096, 8192)]
+    assert all(a + m <= n for a, m in wins)
+    wins += [(rng.randrange(0, n - 65536) // 8 * 8, 65536) for _ in range(8)]
+    for a, m in wins:
+        Gh = np.stack([synth.cpu_normal_bf16(m, 0, synth.TAG_GRAD, j, 0, a,
+                                             w.grad_sigma)
+                       for j in range(k)])
+        assert np.array_equal(np16(G[k - 1][a:a + m]), O.accumulate(Gh)), a
 
 
 TENSOR_LIST = [1000, 70000, 7, 129, 20000, 9000, 3, 65536, 300000, 512]
