@@ -234,7 +234,7 @@ def test_gpt2_thirteen_steps_and_flat_output(layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 7, 8, 16, 32, 64])
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 7, 8, 16, 32, 64, 100, 128])
 def test_every_world_size(W, layout):
     """Each compiled world size and the runtime-W kernel, several buckets, a
     ragged last bucket, slices that are not whole tiles, a staging stride
@@ -833,7 +833,7 @@ def test_gather_llama8b_layers_sampled():
 
 @pytest.mark.parametrize("flat_params", [False, True])
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("W", [1, 3, 8, 16, 64])
+@pytest.mark.parametrize("W", [1, 3, 8, 16, 64, 100])
 def test_pure_bf16_step(W, layout, flat_params):
     """zs_step_bf16 (no fp32 master, 12 B/param) against the oracle, bit for
     bit, three steps with warm moments; parameters as the bf16 shard or in
