@@ -23,7 +23,8 @@
 // elements of one bucket's slice.  A tile is owned by one 512-thread
 // workgroup (8 wave64s) whose threads each own four 4-element units at
 // stride 512 units, or, in launches of few tiles, by four workgroups of
-// one unit per thread; either way every load or store instruction of a wave
+// one unit per thread (the pure-bf16 step: two 256-thread workgroups of
+// four units); either way every load or store instruction of a wave
 // covers one contiguous run (1 KiB of fp32, 512 B of bf16) and a tile's
 // rows are swept in 8-32 KiB bursts.  With the tiled state the three 32 KiB
 // rows of a tile are adjacent, and with tiled gradients so are the W 16 KiB
@@ -32,9 +33,12 @@
 // its arithmetic (the W slices in batches of 4 or 8), and every access is
 // non-temporal: nothing is reused.
 //
-// Grid: blockIdx.y = bucket, blockIdx.x = tile (times the workgroups per
-// tile) of that bucket's slice, so no thread divides to find its bucket, and
-// the all-gather position of each element is one multiply-add away.
+// Grid of the whole-shard step: blockIdx.y = bucket, blockIdx.x = tile
+// (times the workgroups per tile) of that bucket's slice, so no thread
+// divides to find its bucket, and the all-gather position of each element
+// is one multiply-add away.  Bucket groups (the streaming step, and the
+// whole-tensor layout's owned tensors) run a 1-D grid over their members'
+// tiles, the member found from a prefix table in the kernel arguments.
 
 #include <hip/hip_runtime.h>
 
