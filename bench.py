@@ -149,6 +149,21 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int) -> dict:
     return rec
 
 
+def copy_calibration():
+    """One plain 4 GiB device copy (synth's k_copy16): the reference
+    dispatch that scales rocprofv3's FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+    import synth
+    nbytes = 4 << 30
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    synth.dev_copy(dst, src, nbytes)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    log(f"copy calibration: {nbytes} bytes read and written")
+
+
 def cpu_baseline(W, seconds: float, threads: int = 1):
     """The oracle as it stands on a bounded sample of the same workload:
     each of `threads` host threads steps its own 2^22-element window of the
@@ -815,6 +830,8 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     w = wl.presets()[args.workload]
+    if args.copy_calibration:
+        copy_calibration()
     if args.zero3:
         return zero3_main(args, w)
     if args.pure_bf16:
@@ -863,14 +880,6 @@ def main():
         zs.zs_step(lay, G, state, None, flat, grad_layout="slices",
                    grad_stride=n, step=t, stream=st, **HP)
 
-    if args.copy_calibration:
-        nbytes = 4 << 30
-        src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
-        dst = torch.empty_like(src)
-        synth.dev_copy(dst, src, nbytes, stream=st)
-        torch.cuda.synchronize()
-        del src, dst
-        log(f"copy calibration: {nbytes} bytes read and written")
     for _ in range(args.warmup):
         step_tiled()
     torch.cuda.synchronize()
