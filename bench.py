@@ -596,8 +596,9 @@ def zero3_main(args, w):
 def stream_main(args, w):
     """ZeRO-2 streaming: the W slices of each 25 MiB bucket arrive one bucket
     at a time, last bucket first (the order backward fills them), into a ring
-    of 2G staging slots on an upload stream; the step stream runs
-    zs_buckets_step on every G landed buckets, and the upload stream reuses a
+    of 2G staging slots on an upload stream; zs_buckets_step runs on every G
+    landed buckets, the groups taking the step streams in turn (so that one
+    launch's tail overlaps the next launch), and the upload stream reuses a
     slot only after the step that read it.  Arrival is a
     host-to-device copy from a pinned pool of 4 distinct buckets (bucket b
     uses pool b mod 4), or a device copy from an HBM pool (--arrival d2d).
@@ -652,7 +653,10 @@ def stream_main(args, w):
     torch.cuda.synchronize()
     log("inputs resident")
     up = torch.cuda.Stream()
-    st = torch.cuda.Stream()
+    # groups go to the step streams in turn, so that one group's tail
+    # overlaps the next group's start (groups touch disjoint buckets)
+    sts = [torch.cuda.Stream() for _ in range(max(1, args.step_streams))]
+    st = sts[0]
     order = list(range(nb))[::-1]
     cnt = [-(-B[b].slice_numel // T) * W * T for b in range(nb)]
     t_step = 0
@@ -665,6 +669,7 @@ def stream_main(args, w):
         t_step += 1
         done = [None] * slots
         for g0 in range(0, nb, G):
+            gst = sts[(g0 // G) % len(sts)]
             ids = order[g0:g0 + G]
             sl = [(g0 + i) % slots for i in range(len(ids))]
             landed = None
@@ -682,12 +687,12 @@ def stream_main(args, w):
                     landed.record(up)
             if do_step:
                 if landed is not None:
-                    st.wait_event(landed)
+                    gst.wait_event(landed)
                 zs.zs_buckets_step(lay, ids, [staging[k] for k in sl], state,
                                    None, flat, grad_layout="tiled",
-                                   step=t_step, stream=st, **HP)
+                                   step=t_step, stream=gst, **HP)
                 ev = torch.cuda.Event()
-                ev.record(st)
+                ev.record(gst)
                 for k in sl:
                     done[k] = ev
 
@@ -705,10 +710,18 @@ def stream_main(args, w):
     torch.cuda.synchronize()
     e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
     e0.record(st)
-    kern_ms = timed(do_upload=False)
+    for s_ in sts[1:]:                      # nothing starts before e0
+        s_.wait_event(e0)
+    for _ in range(K):
+        full_step(do_upload=False)
+    for s_ in sts[1:]:                      # e1 after every stream's work
+        ev = torch.cuda.Event()
+        ev.record(s_)
+        st.wait_event(ev)
     e1.record(st)
     torch.cuda.synchronize()
     kern_ev_ms = e0.elapsed_time(e1) / K
+    kern_ms = timed(do_upload=False)
     log(f"bucket steps alone: {kern_ms:.2f} ms per full step "
         f"(events {kern_ev_ms:.2f} ms)")
     up_ms = timed(do_step=False)
@@ -739,6 +752,7 @@ def stream_main(args, w):
                    "buckets": nb, "bucket_cap_mb": 25,
                    "bytes_per_param": bpp, "arrival": args.arrival,
                    "buckets_per_launch": G, "staging_slots": slots,
+                   "step_streams": len(sts),
                    "grads_layout": "tiled [tile][W][8192]"},
         "roofline": {"bound": "hbm", "achieved": kern_gbs,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -786,6 +800,9 @@ def main():
     ap.add_argument("--group", type=int, default=16,
                     help="streaming mode: landed buckets stepped per launch "
                     "(zs_buckets_step); the ring holds 2*group slots")
+    ap.add_argument("--step-streams", type=int, default=2,
+                    help="streaming mode: step streams the landed groups "
+                    "are spread over, in turn")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ceiling", action="store_true",
