@@ -379,6 +379,55 @@ int zs_pack(const zs_layout* layout, const uint16_t* param_shard,
             int32_t n_chunks, uint16_t* const* dev_tensor_ptrs,
             void* hip_stream);
 
+/* ---- ZeRO-2 streaming engine ----------------------------------------------
+ *
+ * Steps each bucket as soon as its gradients have arrived, while later
+ * buckets are still being produced (podcast summary, "Data parallelism" and
+ * "ZeRO optimizer": per-bucket reduce-scatter overlapped with backward;
+ * DDP-to-ZeRO blog 3.3: overlap_comm).  A host object that schedules work
+ * on caller streams; it allocates no device memory (only HIP events).
+ *
+ * zs_stream_create: `slots` is a ring of n_slots caller-owned device staging
+ * buffers (n_slots >= group, 16-byte aligned) of slot_elems bf16 elements
+ * each, at least the tiled size of every bucket (ceil(slice_numel /
+ * ZS_TILE) * world * ZS_TILE); 2 * group slots let a group's copies run
+ * while the previous group steps.  upload_stream carries the copies;
+ * step_streams (1..8 of them, an array read during the call) take the
+ * group launches in turn.  group: buckets per zs_buckets_step launch,
+ * 1..ZS_MAX_GROUP.  The layout must outlive the engine.
+ * zs_stream_step_begin: opens one optimizer step t (>= 1) on the tiled
+ * state and the outputs (param_shard and/or full_flat, as zs_step).
+ * zs_stream_arrive: bucket bucket_id's gradients have arrived at src, in
+ * the tiled staging form of zs_bucket_step ([tiles][world][ZS_TILE] bf16,
+ * as zs_grads_tile writes it for that bucket), in device memory or in
+ * pinned host memory.  The engine copies them into the next slot on the
+ * upload stream (after the step that last read the slot), and when `group`
+ * buckets are pending it launches zs_buckets_step on the next step stream,
+ * ordered after the copies.  src must stay valid until the copy has run.
+ * Each bucket arrives at most once per step, in any order.
+ * zs_stream_step_end: steps the pending partial group and closes the step.
+ * Returns the number of buckets stepped in the step (>= 0) or an error.
+ * The work is then queued on the caller's streams; synchronise them (or
+ * wait on an event recorded on each step stream) before reading results.
+ * Errors: ZS_EINVAL (NULL arguments, counts, a step not open or already
+ * open, a bucket arriving twice), ZS_EALIGN, ZS_ERANGE (bucket id, slot too
+ * small), ZS_EDEVICE (a HIP call failed), and those of zs_buckets_step.
+ * After an error the step's results are undefined; end the step.  One host
+ * thread at a time per engine. */
+typedef struct zs_stream zs_stream;
+int zs_stream_create(const zs_layout* layout, int32_t group,
+                     uint16_t* const* slots, int32_t n_slots,
+                     int64_t slot_elems, void* upload_stream,
+                     void* const* step_streams, int32_t n_step_streams,
+                     zs_stream** out);
+int zs_stream_step_begin(zs_stream* stream, float* state,
+                         uint16_t* param_shard, uint16_t* full_flat,
+                         const zs_adamw* hp, int64_t step);
+int zs_stream_arrive(zs_stream* stream, int32_t bucket_id,
+                     const uint16_t* src);
+int zs_stream_step_end(zs_stream* stream);
+void zs_stream_free(zs_stream* stream);
+
 /* ---- errors --------------------------------------------------------------- */
 
 /* Static text of a ZS_E* code. */

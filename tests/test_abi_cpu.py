@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 24
+    assert len(names) == 29
     L = zs.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -345,3 +345,42 @@ def test_build_records_kernel_digests():
     assert bench.HEADLINE_KERNEL in digests
     assert all(len(v) == 16 for v in digests.values())
     assert any("gather_kernel" in k for k in digests)
+
+
+def test_stream_engine_argument_checks_need_no_device():
+    """zs_stream_create and the step calls reject bad arguments before any
+    HIP call."""
+    L = zs.lib()
+    P_ = ctypes.c_void_p
+    A = 1 << 20                      # a 16-byte aligned stand-in address
+    lay = zs.zs_layout_build(wl.tiny(), 4, 0)
+    h = lay.handle
+    tile_elems = 279040 // 8192 + 1
+    need = tile_elems * 4 * 8192     # the one bucket's tiled size
+    slots = (P_ * 4)(A, A, A, A)
+    sts = (P_ * 2)(None, None)
+    out = P_()
+
+    def create(lay_h=h, group=2, sl=slots, n=4, elems=need, ss=sts, k=2,
+               o=ctypes.byref(out)):
+        return L.zs_stream_create(lay_h, group, sl, n, elems, None, ss, k, o)
+
+    assert create(lay_h=None) == -1
+    assert create(group=0) == -1
+    assert create(group=zs.ZS_MAX_GROUP + 1) == -1
+    assert create(n=1) == -1                         # n_slots < group
+    assert create(sl=None) == -1
+    assert create(sl=(P_ * 4)(A, None, A, A)) == -1
+    assert create(sl=(P_ * 4)(A, A + 2, A, A)) == -2
+    assert create(elems=need - 1) == -3              # slot too small
+    assert create(k=0) == -1
+    assert create(k=9) == -1
+    assert create(ss=None) == -1
+    assert create(o=None) == -1
+    assert out.value is None
+    hp = zs.zs_adamw(3e-4, 0.9, 0.95, 1e-8, 0.1)
+    assert L.zs_stream_step_begin(None, A, A, None, ctypes.byref(hp), 1) \
+        == -1
+    assert L.zs_stream_arrive(None, 0, A) == -1
+    assert L.zs_stream_step_end(None) == -1
+    L.zs_stream_free(None)                           # no-op

@@ -1032,6 +1032,64 @@ def test_gradient_accumulation_llama8b_flat_sampled():
         assert np.array_equal(np16(G[k - 1][a:a + m]), O.accumulate(Gh)), a
 
 
+@pytest.mark.parametrize("arrival", ["device", "pinned host"])
+def test_stream_engine_equals_the_whole_step(arrival):
+    """The streaming engine (zs_stream_*): a rank's buckets arrive one by
+    one in a shuffled order, from device or pinned host memory, into a ring
+    of 2 x 3 staging slots; groups of 3 alternate over two step streams;
+    two steps; the state, the shard and the flat buffer equal zs_step on
+    the whole shard bit for bit.  A bucket arriving twice is refused."""
+    W, rank = 4, 1
+    numels = [5000, 7, 129, 70000, 300, 2047, 40000, 9000]
+    cap = W * 256 * 9
+    lay_o = build_layout(numels, W, rank, cap)
+    lay = zs.zs_layout_build(numels, W, rank, cap)
+    n, nb, F = lay_o.shard_numel, len(lay_o.buckets), lay_o.flat_numel
+    assert nb > 7
+    say(f"case stream engine W={W} buckets={nb} arrival={arrival}")
+    ref_state = dev_state(lay, lay_o, 0.02, warm=(1e-4, 1e-8))
+    state = ref_state.clone()
+    flat_ref, flat = dev_bf16(F), dev_bf16(F)
+    for f in (flat_ref, flat):
+        synth.dev_bits16(f, 4, synth.TAG_SENTINEL, 0, 0, 0)
+    p_ref, p = dev_bf16(n), dev_bf16(n)
+    G = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
+    Gt = dev_bf16(lay_o.n_tiles * W * TILE)
+    tiles = [-(-b.slice_numel // TILE) for b in lay_o.buckets]
+    pool = [dev_bf16(k * W * TILE) for k in tiles]
+    slots = [dev_bf16(max(tiles) * W * TILE) for _ in range(6)]
+    up = torch.cuda.Stream()
+    sts = [torch.cuda.Stream(), torch.cuda.Stream()]
+    eng = zs.zs_stream_create(lay, 3, slots, up, sts)
+    order = list(range(nb))[::-1]
+    random.Random(3).shuffle(order)
+    for t in (1, 2):
+        S.dev_grads(G, W, n, t, 1e-3)
+        zs.zs_grads_tile(lay, -1, G, n, Gt)
+        for b_id, b in enumerate(lay_o.buckets):
+            sl = G[:, b.shard_off:b.shard_off + b.slice_numel].contiguous()
+            zs.zs_grads_tile(lay, b_id, sl, b.slice_numel, pool[b_id])
+        zs.zs_step(lay, Gt, ref_state, p_ref, flat_ref, grad_layout="tiled",
+                   step=t, **HP)
+        src = pool if arrival == "device" else \
+            [x.cpu().pin_memory() for x in pool]
+        torch.cuda.synchronize()        # inputs ready before the engine
+        zs.zs_stream_step_begin(eng, state, p, flat, step=t, **HP)
+        for b_id in order:
+            zs.zs_stream_arrive(eng, b_id, src[b_id])
+        if t == 2:
+            with pytest.raises(zs.ZsError) as e:
+                zs.zs_stream_arrive(eng, order[0], src[order[0]])
+            assert e.value.code == -1
+        assert zs.zs_stream_step_end(eng) == nb
+        torch.cuda.synchronize()
+        assert torch.equal(state.view(torch.int32),
+                           ref_state.view(torch.int32)), t
+        assert torch.equal(p.view(torch.int16), p_ref.view(torch.int16))
+        assert torch.equal(flat.view(torch.int16), flat_ref.view(torch.int16))
+    zs.zs_stream_free(eng)
+
+
 TENSOR_LIST = [1000, 70000, 7, 129, 20000, 9000, 3, 65536, 300000, 512]
 
 

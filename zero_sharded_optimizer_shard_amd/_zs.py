@@ -56,6 +56,8 @@ EXPORTS = ["zs_layout_build", "zs_layout_build_tensors", "zs_layout_owners",
            "zs_state_unpack",
            "zs_grads_tile", "zs_gather", "zs_pack", "zs_step_bf16",
            "zs_state_mv_pack", "zs_state_mv_unpack", "zs_accumulate",
+           "zs_stream_create", "zs_stream_step_begin", "zs_stream_arrive",
+           "zs_stream_step_end", "zs_stream_free",
            "zs_strerror", "zs_last_error"]
 
 
@@ -97,6 +99,13 @@ def lib():
     L.zs_state_mv_unpack.argtypes = [p, p, p, p, p]
     L.zs_accumulate.argtypes = [i32, p, p, p, i64, i32, p]
     L.zs_pack.argtypes = [p, p, p, p, i32, p, p]
+    L.zs_stream_create.argtypes = [p, i32, P(p), i32, i64, p, P(p), i32,
+                                   P(p)]
+    L.zs_stream_step_begin.argtypes = [p, p, p, p, P(zs_adamw), i64]
+    L.zs_stream_arrive.argtypes = [p, i32, p]
+    L.zs_stream_step_end.argtypes = [p]
+    L.zs_stream_free.argtypes = [p]
+    L.zs_stream_free.restype = None
     L.zs_strerror.argtypes = [ctypes.c_int]
     L.zs_strerror.restype = ctypes.c_char_p
     L.zs_last_error.argtypes = []
@@ -109,7 +118,8 @@ def lib():
                  "zs_state_unpack",
                  "zs_grads_tile", "zs_gather", "zs_pack", "zs_step_bf16",
                  "zs_state_mv_pack", "zs_state_mv_unpack",
-                 "zs_accumulate"):
+                 "zs_accumulate", "zs_stream_create", "zs_stream_step_begin",
+                 "zs_stream_arrive", "zs_stream_step_end"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -416,3 +426,78 @@ def zs_pack(layout: Layout, param_shard, full_flat=None, dev_chunks=None,
                          _bf16(full_flat, "full_flat"), _ptr(dev_chunks),
                          n_chunks, _ptr(dev_tensor_ptrs), _stream(stream)),
            "zs_pack")
+
+
+# ---- ZeRO-2 streaming engine -------------------------------------------------
+
+class Stream:
+    """Owning handle of a zs_stream* (see include/zs.h).  Keeps the layout,
+    the staging slots and the streams it was given alive."""
+
+    def __init__(self, handle: int, keep):
+        self._h = ctypes.c_void_p(handle)
+        self._keep = keep
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None and self._h.value and _lib:
+            _lib.zs_stream_free(self._h)
+            self._h = None
+
+
+def zs_stream_create(layout: Layout, group: int, slots, upload_stream,
+                     step_streams) -> Stream:
+    """slots: device bf16 staging tensors (the ring); upload_stream and
+    step_streams: torch streams."""
+    n = len(slots)
+    arr = (ctypes.c_void_p * max(n, 1))(*[_bf16(t, "slots") for t in slots])
+    k = len(step_streams)
+    ss = (ctypes.c_void_p * max(k, 1))(*[t.cuda_stream for t in step_streams])
+    elems = min(t.numel() for t in slots) if n else 0
+    out = ctypes.c_void_p()
+    _check(lib().zs_stream_create(layout.handle, group, arr, n, elems,
+                                  ctypes.c_void_p(upload_stream.cuda_stream),
+                                  ss, k, ctypes.byref(out)),
+           "zs_stream_create")
+    return Stream(out.value, (layout, list(slots), upload_stream,
+                              list(step_streams)))
+
+
+def zs_stream_step_begin(stream: Stream, state, param_shard=None,
+                         full_flat=None, *, lr: float, beta1: float,
+                         beta2: float, eps: float, weight_decay: float,
+                         step: int) -> None:
+    hp = _hp(lr, beta1, beta2, eps, weight_decay)
+    _check(lib().zs_stream_step_begin(stream.handle, _f32(state, "state"),
+                                      _bf16(param_shard, "param_shard"),
+                                      _bf16(full_flat, "full_flat"),
+                                      ctypes.byref(hp), step),
+           "zs_stream_step_begin")
+
+
+def zs_stream_arrive(stream: Stream, bucket_id: int, src) -> None:
+    """src: the bucket's tiled gradients, a device tensor or a pinned host
+    tensor (2-byte elements, contiguous)."""
+    if src.element_size() != 2 or not src.is_contiguous():
+        raise TypeError("src: need a contiguous 2-byte tensor")
+    if not (src.is_cuda or src.is_pinned()):
+        raise ValueError("src: need device or pinned host memory")
+    _check(lib().zs_stream_arrive(stream.handle, bucket_id,
+                                  ctypes.c_void_p(src.data_ptr())),
+           "zs_stream_arrive")
+
+
+def zs_stream_step_end(stream: Stream) -> int:
+    """Steps the pending partial group; returns the buckets stepped in the
+    step."""
+    return _check(lib().zs_stream_step_end(stream.handle),
+                  "zs_stream_step_end")
+
+
+def zs_stream_free(stream: Stream) -> None:
+    if stream._h is not None and stream._h.value:
+        lib().zs_stream_free(stream._h)
+        stream._h = None

@@ -1,0 +1,248 @@
+// ZeRO-2 streaming engine: the host-side scheduler that steps each bucket
+// as soon as its gradients have arrived.
+//
+// ZeRO-2 keeps only this rank's share of the gradients: the reduce-scatter
+// runs per bucket while backward is still producing the next buckets, and
+// the optimizer work of a bucket can start once its slices are here
+// (podcast summary of "Training at thousands of GPUs", sections "Data
+// parallelism" and "ZeRO optimizer": buckets of bucket_cap_mb, overlap of
+// communication and computation; DDP-to-ZeRO blog 3.3: overlap_comm).
+//
+// The engine owns no device memory.  The caller gives it a ring of staging
+// slots (device buffers), an upload stream and one or more step streams.
+// Each arriving bucket (its W tiled gradient slices, in device or pinned
+// host memory) is copied into the next slot on the upload stream, after the
+// step that last read that slot; every `group` arrivals become one
+// zs_buckets_step launch on the next step stream in turn, ordered after the
+// copies by an event.  Spreading groups over several step streams lets one
+// launch's tail overlap the next launch (groups touch disjoint buckets).
+// HIP events are the only resources it creates.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "zs_internal.h"
+
+struct zs_stream {
+    const zs_layout* L = nullptr;
+    int32_t group = 1;
+    std::vector<uint16_t*> slots;
+    int64_t slot_elems = 0;
+    hipStream_t up = nullptr;
+    std::vector<hipStream_t> steps;
+    std::vector<hipEvent_t> landed;   // per slot: its copy is done
+    std::vector<hipEvent_t> freed;    // per slot: the step that read it is done
+    std::vector<char> used;           // per slot: freed has been recorded
+    // the step in progress
+    bool open = false;
+    float* state = nullptr;
+    uint16_t* pshard = nullptr;
+    uint16_t* flat = nullptr;
+    zs_adamw hp{};
+    int64_t t = 0;
+    std::vector<char> arrived;        // per bucket
+    int32_t cursor = 0;               // next slot of the ring
+    int64_t launches = 0;             // group launches so far (all steps)
+    int32_t stepped = 0;              // buckets stepped in this step
+    std::vector<int32_t> pend_ids, pend_slots;
+};
+
+namespace {
+
+using zs::fail;
+
+int64_t bucket_elems(const zs_layout* L, int32_t b)
+{
+    const int64_t tiles = (L->buckets[b].slice_numel + ZS_TILE - 1) / ZS_TILE;
+    return tiles * L->world * ZS_TILE;
+}
+
+int hip_fail(hipError_t e, const char* what)
+{
+    return fail(ZS_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+void destroy(zs_stream* S)
+{
+    for (hipEvent_t e : S->landed)
+        if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : S->freed)
+        if (e) (void)hipEventDestroy(e);
+    delete S;
+}
+
+// One zs_buckets_step over the pending arrivals, on the next step stream.
+int launch_pending(zs_stream* S)
+{
+    const int32_t cnt = (int32_t)S->pend_ids.size();
+    if (cnt == 0)
+        return ZS_OK;
+    hipStream_t s = S->steps[S->launches % (int64_t)S->steps.size()];
+    // the upload stream is in order: the last copy's event covers them all
+    hipError_t e = hipStreamWaitEvent(s, S->landed[S->pend_slots.back()], 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    const uint16_t* grads[ZS_MAX_GROUP];
+    for (int32_t i = 0; i < cnt; ++i)
+        grads[i] = S->slots[S->pend_slots[i]];
+    const int rc = zs_buckets_step(S->L, cnt, S->pend_ids.data(), grads,
+                                   ZS_GRADS_TILED, 0, S->state, S->pshard,
+                                   S->flat, &S->hp, S->t, s);
+    if (rc) return rc;
+    for (int32_t k : S->pend_slots) {
+        e = hipEventRecord(S->freed[k], s);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+        S->used[k] = 1;
+    }
+    ++S->launches;
+    S->stepped += cnt;
+    S->pend_ids.clear();
+    S->pend_slots.clear();
+    return ZS_OK;
+}
+
+}  // namespace
+
+extern "C" int zs_stream_create(const zs_layout* L, int32_t group,
+                                uint16_t* const* slots, int32_t n_slots,
+                                int64_t slot_elems, void* upload_stream,
+                                void* const* step_streams,
+                                int32_t n_step_streams, zs_stream** out)
+{
+    zs::clear_error();
+    if (!out) return fail(ZS_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!L) return fail(ZS_EINVAL, "layout is NULL");
+    if (group < 1 || group > ZS_MAX_GROUP)
+        return fail(ZS_EINVAL, "group %d outside [1, %d]", group,
+                    ZS_MAX_GROUP);
+    if (n_slots < group)
+        return fail(ZS_EINVAL, "n_slots %d < group %d", n_slots, group);
+    if (!slots) return fail(ZS_EINVAL, "slots is NULL");
+    for (int32_t k = 0; k < n_slots; ++k) {
+        if (!slots[k]) return fail(ZS_EINVAL, "slots[%d] is NULL", k);
+        if (reinterpret_cast<uintptr_t>(slots[k]) & 15u)
+            return fail(ZS_EALIGN, "slots[%d] not 16-byte aligned", k);
+    }
+    if (n_step_streams < 1 || n_step_streams > 8)
+        return fail(ZS_EINVAL, "n_step_streams %d outside [1, 8]",
+                    n_step_streams);
+    if (!step_streams) return fail(ZS_EINVAL, "step_streams is NULL");
+    const int32_t nb = (int32_t)L->buckets.size();
+    for (int32_t b = 0; b < nb; ++b)
+        if (bucket_elems(L, b) > slot_elems)
+            return fail(ZS_ERANGE, "slot_elems %lld < %lld elements of "
+                        "bucket %d's tiled gradients", (long long)slot_elems,
+                        (long long)bucket_elems(L, b), b);
+    zs_stream* S = new (std::nothrow) zs_stream;
+    if (!S) return fail(ZS_ENOMEM, "host allocation");
+    try {
+        S->L = L;
+        S->group = group;
+        S->slots.assign(slots, slots + n_slots);
+        S->slot_elems = slot_elems;
+        S->up = static_cast<hipStream_t>(upload_stream);
+        for (int32_t i = 0; i < n_step_streams; ++i)
+            S->steps.push_back(static_cast<hipStream_t>(step_streams[i]));
+        S->landed.assign(n_slots, nullptr);
+        S->freed.assign(n_slots, nullptr);
+        S->used.assign(n_slots, 0);
+        S->arrived.assign(nb, 0);
+        S->pend_ids.reserve(group);
+        S->pend_slots.reserve(group);
+    } catch (const std::bad_alloc&) {
+        delete S;
+        return fail(ZS_ENOMEM, "host allocation");
+    }
+    for (int32_t k = 0; k < n_slots; ++k) {
+        hipError_t e = hipEventCreateWithFlags(&S->landed[k],
+                                               hipEventDisableTiming);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&S->freed[k], hipEventDisableTiming);
+        if (e != hipSuccess) {
+            destroy(S);
+            return hip_fail(e, "hipEventCreateWithFlags");
+        }
+    }
+    *out = S;
+    return ZS_OK;
+}
+
+extern "C" int zs_stream_step_begin(zs_stream* S, float* state,
+                                    uint16_t* param_shard,
+                                    uint16_t* full_flat, const zs_adamw* hp,
+                                    int64_t step)
+{
+    zs::clear_error();
+    if (!S) return fail(ZS_EINVAL, "stream is NULL");
+    if (S->open) return fail(ZS_EINVAL, "a step is already open");
+    if (!hp) return fail(ZS_EINVAL, "hp is NULL");
+    if (step < 1) return fail(ZS_EINVAL, "step %lld < 1", (long long)step);
+    if (!state) return fail(ZS_EINVAL, "state is NULL");
+    if (!param_shard && !full_flat)
+        return fail(ZS_EINVAL, "need param_shard or full_flat");
+    S->state = state;
+    S->pshard = param_shard;
+    S->flat = full_flat;
+    S->hp = *hp;
+    S->t = step;
+    S->stepped = 0;
+    S->pend_ids.clear();
+    S->pend_slots.clear();
+    for (char& a : S->arrived) a = 0;
+    S->open = true;
+    return ZS_OK;
+}
+
+extern "C" int zs_stream_arrive(zs_stream* S, int32_t bucket_id,
+                                const uint16_t* src)
+{
+    zs::clear_error();
+    if (!S) return fail(ZS_EINVAL, "stream is NULL");
+    if (!S->open) return fail(ZS_EINVAL, "no step is open");
+    const int32_t nb = (int32_t)S->L->buckets.size();
+    if (bucket_id < 0 || bucket_id >= nb)
+        return fail(ZS_ERANGE, "bucket_id %d outside [0, %d)", bucket_id,
+                    nb);
+    if (S->arrived[bucket_id])
+        return fail(ZS_EINVAL, "bucket %d arrived twice in one step",
+                    bucket_id);
+    if (!src) return fail(ZS_EINVAL, "src is NULL");
+    const int32_t k = S->cursor;
+    S->cursor = (S->cursor + 1) % (int32_t)S->slots.size();
+    hipError_t e = hipSuccess;
+    if (S->used[k]) {
+        e = hipStreamWaitEvent(S->up, S->freed[k], 0);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    }
+    e = hipMemcpyAsync(S->slots[k], src,
+                       (size_t)bucket_elems(S->L, bucket_id) * 2,
+                       hipMemcpyDefault, S->up);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    e = hipEventRecord(S->landed[k], S->up);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    S->arrived[bucket_id] = 1;
+    S->pend_ids.push_back(bucket_id);
+    S->pend_slots.push_back(k);
+    if ((int32_t)S->pend_ids.size() == S->group)
+        return launch_pending(S);
+    return ZS_OK;
+}
+
+extern "C" int zs_stream_step_end(zs_stream* S)
+{
+    zs::clear_error();
+    if (!S) return fail(ZS_EINVAL, "stream is NULL");
+    if (!S->open) return fail(ZS_EINVAL, "no step is open");
+    S->open = false;
+    const int rc = launch_pending(S);
+    if (rc) return rc;
+    return S->stepped;
+}
+
+extern "C" void zs_stream_free(zs_stream* S)
+{
+    if (S) destroy(S);
+}
