@@ -1032,21 +1032,30 @@ def test_gradient_accumulation_llama8b_flat_sampled():
         assert np.array_equal(np16(G[k - 1][a:a + m]), O.accumulate(Gh)), a
 
 
-@pytest.mark.parametrize("arrival", ["device", "pinned host"])
-def test_stream_engine_equals_the_whole_step(arrival):
-    """The streaming engine (zs_stream_*): a rank's buckets arrive one by
-    one in a shuffled order, from device or pinned host memory, into a ring
-    of 2 x 3 staging slots; groups of 3 alternate over two step streams;
-    two steps; the state, the shard and the flat buffer equal zs_step on
-    the whole shard bit for bit.  A bucket arriving twice is refused."""
+@pytest.mark.parametrize("arrival,tensors", [("device", False),
+                                             ("pinned host", False),
+                                             ("device", True)])
+def test_stream_engine_equals_the_whole_step(arrival, tensors):
+    """The streaming engine (zs_stream_*): a rank's buckets (owned tensors
+    in the whole-tensor layout) arrive one by one in a shuffled order, from
+    device or pinned host memory, into a ring of 2 x 3 staging slots;
+    groups of 3 alternate over two step streams; two steps; the state, the
+    shard and the flat buffer equal zs_step on the whole shard bit for bit.
+    A bucket arriving twice is refused."""
     W, rank = 4, 1
     numels = [5000, 7, 129, 70000, 300, 2047, 40000, 9000]
-    cap = W * 256 * 9
-    lay_o = build_layout(numels, W, rank, cap)
-    lay = zs.zs_layout_build(numels, W, rank, cap)
+    if tensors:
+        numels = numels + TENSOR_LIST + [333, 4444, 55555, 6]
+        lay_o = build_tensor_layout(numels, W, rank)
+        lay = zs.zs_layout_build_tensors(numels, W, rank)
+    else:
+        cap = W * 256 * 9
+        lay_o = build_layout(numels, W, rank, cap)
+        lay = zs.zs_layout_build(numels, W, rank, cap)
     n, nb, F = lay_o.shard_numel, len(lay_o.buckets), lay_o.flat_numel
-    assert nb > 7
-    say(f"case stream engine W={W} buckets={nb} arrival={arrival}")
+    assert nb > 4
+    say(f"case stream engine W={W} buckets={nb} arrival={arrival} "
+        f"tensors={tensors}")
     ref_state = dev_state(lay, lay_o, 0.02, warm=(1e-4, 1e-8))
     state = ref_state.clone()
     flat_ref, flat = dev_bf16(F), dev_bf16(F)
