@@ -379,6 +379,43 @@ int zs_pack(const zs_layout* layout, const uint16_t* param_shard,
             int32_t n_chunks, uint16_t* const* dev_tensor_ptrs,
             void* hip_stream);
 
+/* ---- ZeRO-3 / FSDP prefetch -----------------------------------------------
+ *
+ * Schedules the per-unit parameter gathers of ZeRO-3 / FSDP: a unit's full
+ * weights are gathered right before it runs, the next unit's gather
+ * overlaps the current unit's compute, and a unit's buffer is reused once
+ * its compute is done (podcast summary, "ZeRO optimizer"; CS336 lecture 8
+ * notes, "Code example: FSDP").  A host object on caller streams; it
+ * allocates no device memory (only HIP events).
+ *
+ * zs_prefetch_create: shards[world] (device, read through zs_gather; the
+ * array is copied), a ring of n_buffers caller-owned device unit buffers
+ * (1..64, 16-byte aligned) of buffer_elems bf16 elements each, and the
+ * gather stream.  The layout and the shards must outlive the object.
+ * zs_prefetch_issue: gathers flat range [flat_lo, flat_hi) (as zs_gather)
+ * into the next buffer of the ring on the gather stream, after the compute
+ * that last released that buffer; *slot receives the buffer index.
+ * zs_prefetch_acquire: makes compute_stream wait for that gather; *buffer
+ * (may be NULL) receives the buffer's address.
+ * zs_prefetch_release: compute_stream's use of the buffer ends here (an
+ * event on it), so a later issue may overwrite the buffer.
+ * A buffer goes issue -> acquire -> release -> issue ...; calls out of
+ * that order fail with ZS_EINVAL (the next buffer is not released yet, or
+ * the slot is not issued / acquired).  Errors also: ZS_ERANGE (range above
+ * buffer_elems, slot index), those of zs_gather, ZS_EDEVICE. */
+typedef struct zs_prefetch zs_prefetch;
+int zs_prefetch_create(const zs_layout* layout, const uint16_t* const* shards,
+                       uint16_t* const* buffers, int32_t n_buffers,
+                       int64_t buffer_elems, void* gather_stream,
+                       zs_prefetch** out);
+int zs_prefetch_issue(zs_prefetch* prefetch, int64_t flat_lo,
+                      int64_t flat_hi, int32_t* slot);
+int zs_prefetch_acquire(zs_prefetch* prefetch, int32_t slot,
+                        void* compute_stream, uint16_t** buffer);
+int zs_prefetch_release(zs_prefetch* prefetch, int32_t slot,
+                        void* compute_stream);
+void zs_prefetch_free(zs_prefetch* prefetch);
+
 /* ---- ZeRO-2 streaming engine ----------------------------------------------
  *
  * Steps each bucket as soon as its gradients have arrived, while later

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 29
+    assert len(names) == 34
     L = zs.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -384,3 +384,39 @@ def test_stream_engine_argument_checks_need_no_device():
     assert L.zs_stream_arrive(None, 0, A) == -1
     assert L.zs_stream_step_end(None) == -1
     L.zs_stream_free(None)                           # no-op
+
+
+def test_prefetch_argument_checks_need_no_device():
+    """zs_prefetch_create and the slot calls reject bad arguments before
+    any HIP call."""
+    L = zs.lib()
+    P_ = ctypes.c_void_p
+    A = 1 << 20
+    lay = zs.zs_layout_build(wl.tiny(), 4, 0)
+    h = lay.handle
+    shards = (P_ * 4)(A, A, A, A)
+    bufs = (P_ * 2)(A, A)
+    out = P_()
+
+    def create(lay_h=h, sh=shards, bu=bufs, n=2, elems=1 << 16,
+               o=ctypes.byref(out)):
+        return L.zs_prefetch_create(lay_h, sh, bu, n, elems, None, o)
+
+    assert create(lay_h=None) == -1
+    assert create(sh=None) == -1
+    assert create(bu=None) == -1
+    assert create(n=0) == -1
+    assert create(n=65) == -1
+    assert create(elems=-1) == -1
+    assert create(sh=(P_ * 4)(A, A, None, A)) == -1
+    assert create(bu=(P_ * 2)(A, None)) == -1
+    assert create(bu=(P_ * 2)(A, A + 4)) == -2
+    assert create(o=None) == -1
+    big = zs.zs_layout_build([1000], 65, 0)
+    assert create(lay_h=big.handle, sh=(P_ * 65)(*([A] * 65))) == -1
+    assert out.value is None
+    slot = ctypes.c_int32()
+    assert L.zs_prefetch_issue(None, 0, 8, ctypes.byref(slot)) == -1
+    assert L.zs_prefetch_acquire(None, 0, None, None) == -1
+    assert L.zs_prefetch_release(None, 0, None) == -1
+    L.zs_prefetch_free(None)

@@ -1099,6 +1099,74 @@ def test_stream_engine_equals_the_whole_step(arrival, tensors):
     zs.zs_stream_free(eng)
 
 
+@pytest.mark.parametrize("tensors", [False, True])
+def test_prefetch_pipeline_matches_the_oracle(tensors):
+    """The ZeRO-3 prefetch object (zs_prefetch_*) driven as an FSDP forward:
+    each unit (here every tensor, plus two multi-tensor spans) is issued
+    one unit ahead into a ring of two buffers; a compute stream acquires
+    it, copies it out and releases it; every copy equals the oracle's
+    gather.  Out-of-order calls are refused."""
+    W = 4
+    numels = TENSOR_LIST + [5000, 7, 129, 70000]
+    if tensors:
+        lays = [build_tensor_layout(numels, W, r) for r in range(W)]
+        lay = zs.zs_layout_build_tensors(numels, W, 0)
+    else:
+        cap = W * 256 * 37
+        lays = [build_layout(numels, W, r, cap) for r in range(W)]
+        lay = zs.zs_layout_build(numels, W, 0, cap)
+    lay_o = lays[0]
+    F = lay_o.flat_numel
+    say(f"case prefetch W={W} tensors={tensors}")
+    shards_h = [synth.cpu_bits16(l.shard_numel, 6, synth.TAG_SENTINEL, 0, r,
+                                 0) for r, l in enumerate(lays)]
+    shards = [torch.from_numpy(x.view(np.int16)).cuda() for x in shards_h]
+    if tensors:
+        full = gather_tensors(numels, W, shards_h, 0, F)
+    else:
+        full = np.zeros(F, np.uint16)
+        for l, sh in zip(lays, shards_h):
+            pack_flat(l, sh, full)
+    offs = lay_o.tensor_flat_off
+    units = [(o, o + k) for o, k in zip(offs, numels)]
+    units += [(offs[1], offs[5] + numels[5]), (offs[0], F)]
+    units = [(lo // 8 * 8, hi) for lo, hi in units]
+    biggest = max(hi - lo for lo, hi in units)
+    bufs = [dev_bf16(biggest) for _ in range(2)]
+    gs, cs = torch.cuda.Stream(), torch.cuda.Stream()
+    pf = zs.zs_prefetch_create(lay, shards, bufs, gs)
+    outs = [dev_bf16(hi - lo) for lo, hi in units]
+    torch.cuda.synchronize()
+    slots = [zs.zs_prefetch_issue(pf, *units[0])]
+    for u, (lo, hi) in enumerate(units):
+        if u + 1 < len(units):
+            slots.append(zs.zs_prefetch_issue(pf, *units[u + 1]))
+        buf = zs.zs_prefetch_acquire(pf, slots[u], cs)
+        with torch.cuda.stream(cs):
+            outs[u].copy_(buf[:hi - lo])
+        zs.zs_prefetch_release(pf, slots[u], cs)
+    torch.cuda.synchronize()
+    for (lo, hi), o in zip(units, outs):
+        assert np.array_equal(np16(o), full[lo:hi]), (lo, hi)
+    # out of order: two buffers, both issued, a third issue must wait
+    a = zs.zs_prefetch_issue(pf, *units[0])
+    b_ = zs.zs_prefetch_issue(pf, *units[1])
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_prefetch_issue(pf, *units[2])
+    assert e.value.code == -1
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_prefetch_release(pf, a, cs)            # not acquired
+    assert e.value.code == -1
+    for sl in (a, b_):
+        zs.zs_prefetch_acquire(pf, sl, cs)
+        zs.zs_prefetch_release(pf, sl, cs)
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_prefetch_issue(pf, 0, biggest + 8)     # above the buffers
+    assert e.value.code == -3
+    torch.cuda.synchronize()
+    zs.zs_prefetch_free(pf)
+
+
 TENSOR_LIST = [1000, 70000, 7, 129, 20000, 9000, 3, 65536, 300000, 512]
 
 

@@ -58,6 +58,8 @@ EXPORTS = ["zs_layout_build", "zs_layout_build_tensors", "zs_layout_owners",
            "zs_state_mv_pack", "zs_state_mv_unpack", "zs_accumulate",
            "zs_stream_create", "zs_stream_step_begin", "zs_stream_arrive",
            "zs_stream_step_end", "zs_stream_free",
+           "zs_prefetch_create", "zs_prefetch_issue", "zs_prefetch_acquire",
+           "zs_prefetch_release", "zs_prefetch_free",
            "zs_strerror", "zs_last_error"]
 
 
@@ -106,6 +108,12 @@ def lib():
     L.zs_stream_step_end.argtypes = [p]
     L.zs_stream_free.argtypes = [p]
     L.zs_stream_free.restype = None
+    L.zs_prefetch_create.argtypes = [p, P(p), P(p), i32, i64, p, P(p)]
+    L.zs_prefetch_issue.argtypes = [p, i64, i64, P(i32)]
+    L.zs_prefetch_acquire.argtypes = [p, i32, p, P(p)]
+    L.zs_prefetch_release.argtypes = [p, i32, p]
+    L.zs_prefetch_free.argtypes = [p]
+    L.zs_prefetch_free.restype = None
     L.zs_strerror.argtypes = [ctypes.c_int]
     L.zs_strerror.restype = ctypes.c_char_p
     L.zs_last_error.argtypes = []
@@ -119,7 +127,9 @@ def lib():
                  "zs_grads_tile", "zs_gather", "zs_pack", "zs_step_bf16",
                  "zs_state_mv_pack", "zs_state_mv_unpack",
                  "zs_accumulate", "zs_stream_create", "zs_stream_step_begin",
-                 "zs_stream_arrive", "zs_stream_step_end"):
+                 "zs_stream_arrive", "zs_stream_step_end",
+                 "zs_prefetch_create", "zs_prefetch_issue",
+                 "zs_prefetch_acquire", "zs_prefetch_release"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -501,3 +511,71 @@ def zs_stream_free(stream: Stream) -> None:
     if stream._h is not None and stream._h.value:
         lib().zs_stream_free(stream._h)
         stream._h = None
+
+
+# ---- ZeRO-3 / FSDP prefetch -----------------------------------------------------
+
+class Prefetch:
+    """Owning handle of a zs_prefetch* (see include/zs.h).  Keeps the
+    layout, shards, buffers and gather stream it was given alive."""
+
+    def __init__(self, handle: int, keep):
+        self._h = ctypes.c_void_p(handle)
+        self._keep = keep
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None and self._h.value and _lib:
+            _lib.zs_prefetch_free(self._h)
+            self._h = None
+
+
+def zs_prefetch_create(layout: Layout, shards, buffers,
+                       gather_stream) -> Prefetch:
+    """shards: the world's device bf16 shards; buffers: device bf16 unit
+    buffers (the ring); gather_stream: a torch stream."""
+    sh = (ctypes.c_void_p * max(len(shards), 1))(
+        *[_bf16(t, "shards") for t in shards])
+    n = len(buffers)
+    bu = (ctypes.c_void_p * max(n, 1))(*[_bf16(t, "buffers") for t in buffers])
+    elems = min(t.numel() for t in buffers) if n else 0
+    out = ctypes.c_void_p()
+    _check(lib().zs_prefetch_create(layout.handle, sh, bu, n, elems,
+                                    ctypes.c_void_p(gather_stream.cuda_stream),
+                                    ctypes.byref(out)),
+           "zs_prefetch_create")
+    return Prefetch(out.value, (layout, list(shards), list(buffers),
+                                gather_stream))
+
+
+def zs_prefetch_issue(prefetch: Prefetch, flat_lo: int, flat_hi: int) -> int:
+    """Gathers [flat_lo, flat_hi) into the next buffer; returns its slot."""
+    slot = ctypes.c_int32()
+    _check(lib().zs_prefetch_issue(prefetch.handle, flat_lo, flat_hi,
+                                   ctypes.byref(slot)), "zs_prefetch_issue")
+    return slot.value
+
+
+def zs_prefetch_acquire(prefetch: Prefetch, slot: int, compute_stream=None):
+    """Orders compute_stream after the slot's gather; returns the buffer
+    tensor the slot stands for."""
+    _check(lib().zs_prefetch_acquire(prefetch.handle, slot,
+                                     _stream(compute_stream), None),
+           "zs_prefetch_acquire")
+    return prefetch._keep[2][slot]
+
+
+def zs_prefetch_release(prefetch: Prefetch, slot: int,
+                        compute_stream=None) -> None:
+    _check(lib().zs_prefetch_release(prefetch.handle, slot,
+                                     _stream(compute_stream)),
+           "zs_prefetch_release")
+
+
+def zs_prefetch_free(prefetch: Prefetch) -> None:
+    if prefetch._h is not None and prefetch._h.value:
+        lib().zs_prefetch_free(prefetch._h)
+        prefetch._h = None
