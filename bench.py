@@ -517,28 +517,20 @@ def zero3_main(args, w):
         for u in range(NU):
             compute(u, bufs[u % 2])
 
-    def pipelined():
-        ready = [None] * NU
-        used = [None, None]
+    pf = zs.zs_prefetch_create(lay, shards, bufs, gs)
 
-        def issue(u):
-            with torch.cuda.stream(gs):
-                if used[u % 2] is not None:
-                    gs.wait_event(used[u % 2])
-                zs.zs_gather(lay, shards, ranges[u][0], ranges[u][1],
-                             bufs[u % 2], stream=gs)
-                ev = torch.cuda.Event()
-                ev.record(gs)
-                ready[u] = ev
-        issue(0)
+    def pipelined():
+        """The library's prefetch object: unit u + 1 is gathered on the
+        gather stream while unit u computes; a buffer is reused after the
+        compute that read it."""
+        gs.wait_stream(st)          # nothing before the timing event
+        slots = [zs.zs_prefetch_issue(pf, *ranges[0])]
         for u in range(NU):
             if u + 1 < NU:
-                issue(u + 1)                     # prefetch the next unit
-            st.wait_event(ready[u])
-            compute(u, bufs[u % 2])
-            ev = torch.cuda.Event()
-            ev.record(st)
-            used[u % 2] = ev
+                slots.append(zs.zs_prefetch_issue(pf, *ranges[u + 1]))
+            buf = zs.zs_prefetch_acquire(pf, slots[u], st)
+            compute(u, buf)
+            zs.zs_prefetch_release(pf, slots[u], st)
 
     def timed(fn, reps):
         fn()
