@@ -993,6 +993,10 @@ def main():
               "params_total": sum(w.numels), "shard_params": n,
               "buckets": nb, "bucket_cap_mb": 25,
               "bytes_per_param": bpp,
+              # bytes one step touches, against MI355X's 256 MB Infinity
+              # Cache: a smaller working set would be served from cache
+              "working_set_bytes": bpp * n,
+              "cache_resident": bpp * n < (256 << 20),
               "grads_layout": "tiled [tile][W][8192]",
               "state_layout": "tiled [tile][master|m|v][8192]"}
     if args.whole_tensors:
