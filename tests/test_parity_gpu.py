@@ -1099,6 +1099,107 @@ def test_stream_engine_equals_the_whole_step(arrival, tensors):
     zs.zs_stream_free(eng)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_stream_engine_random_configs(seed):
+    """The streaming engine under seeded random configurations: group 1..16,
+    a ring from the minimum (n_slots = group) to group + 5 slots, 1..3 step
+    streams, random layouts and arrival orders, three steps (slots and
+    launch events reused across steps); state and flat output equal zs_step
+    on the whole shard bit for bit after every step."""
+    rng = random.Random(900 + seed)
+    W = rng.choice([2, 3, 4, 8])
+    numels = [rng.choice([7, 129, 1000, 4096, 9000, 33333, 70000])
+              for _ in range(rng.randint(3, 12))]
+    cap = W * 256 * rng.choice([1, 2, 5, 13])
+    rank = rng.randrange(W)
+    lay_o = build_layout(numels, W, rank, cap)
+    lay = zs.zs_layout_build(numels, W, rank, cap)
+    n, nb, F = lay_o.shard_numel, len(lay_o.buckets), lay_o.flat_numel
+    group = rng.randint(1, min(16, nb))
+    n_slots = group + rng.choice([0, 0, 1, group, 5])
+    n_streams = rng.randint(1, 3)
+    say(f"case engine seed={seed} W={W} buckets={nb} group={group} "
+        f"slots={n_slots} streams={n_streams}")
+    ref_state = dev_state(lay, lay_o, 0.02, warm=(1e-4, 1e-8))
+    state = ref_state.clone()
+    flat_ref, flat = dev_bf16(F), dev_bf16(F)
+    for f in (flat_ref, flat):
+        synth.dev_bits16(f, 4, synth.TAG_SENTINEL, 0, 0, 0)
+    G = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
+    Gt = dev_bf16(lay_o.n_tiles * W * TILE)
+    tiles = [-(-b.slice_numel // TILE) for b in lay_o.buckets]
+    pool = [dev_bf16(k * W * TILE) for k in tiles]
+    slots = [dev_bf16(max(tiles) * W * TILE) for _ in range(n_slots)]
+    up = torch.cuda.Stream()
+    sts = [torch.cuda.Stream() for _ in range(n_streams)]
+    eng = zs.zs_stream_create(lay, group, slots, up, sts)
+    for t in (1, 2, 3):
+        S.dev_grads(G, W, n, t, 1e-3)
+        zs.zs_grads_tile(lay, -1, G, n, Gt)
+        for b_id, b in enumerate(lay_o.buckets):
+            sl = G[:, b.shard_off:b.shard_off + b.slice_numel].contiguous()
+            zs.zs_grads_tile(lay, b_id, sl, b.slice_numel, pool[b_id])
+        zs.zs_step(lay, Gt, ref_state, None, flat_ref, grad_layout="tiled",
+                   step=t, **HP)
+        torch.cuda.synchronize()
+        order = list(range(nb))
+        rng.shuffle(order)
+        zs.zs_stream_step_begin(eng, state, None, flat, step=t, **HP)
+        for b_id in order:
+            zs.zs_stream_arrive(eng, b_id, pool[b_id])
+        assert zs.zs_stream_step_end(eng) == nb
+        torch.cuda.synchronize()
+        assert torch.equal(state.view(torch.int32),
+                           ref_state.view(torch.int32)), t
+        assert torch.equal(flat.view(torch.int16), flat_ref.view(torch.int16))
+    zs.zs_stream_free(eng)
+
+
+def test_stream_engine_full_buckets_minimal_ring():
+    """Slot reuse under load: 40 full 25 MiB buckets at W = 16 (the 70B
+    workload's bucket shape) through the smallest ring (4 slots, groups of
+    4, two step streams), so every slot is overwritten as soon as the
+    launch that read it is done; two steps equal zs_step bit for bit."""
+    W = 16
+    numels = [40 * 16 * 819200]
+    lay_o = build_layout(numels, W, 3)
+    lay = zs.zs_layout_build(numels, W, 3)
+    n, nb, F = lay_o.shard_numel, len(lay_o.buckets), lay_o.flat_numel
+    assert nb == 40 and lay_o.buckets[0].slice_numel == 819200
+    say(f"case engine full buckets W={W} buckets={nb}")
+    ref_state = dev_state(lay, lay_o, 0.02)
+    state = ref_state.clone()
+    flat_ref, flat = dev_bf16(F), dev_bf16(F)
+    flat_ref.zero_()
+    flat.zero_()
+    G = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
+    Gt = dev_bf16(lay_o.n_tiles * W * TILE)
+    per = 100 * W * TILE                       # 100 tiles per bucket slice
+    slots = [dev_bf16(per) for _ in range(4)]
+    up = torch.cuda.Stream()
+    sts = [torch.cuda.Stream(), torch.cuda.Stream()]
+    eng = zs.zs_stream_create(lay, 4, slots, up, sts)
+    for t in (1, 2):
+        S.dev_grads(G, W, n, t, 1e-3)
+        zs.zs_grads_tile(lay, -1, G, n, Gt)
+        zs.zs_step(lay, Gt, ref_state, None, flat_ref, grad_layout="tiled",
+                   step=t, **HP)
+        torch.cuda.synchronize()
+        zs.zs_stream_step_begin(eng, state, None, flat, step=t, **HP)
+        for b_id in reversed(range(nb)):
+            # bucket b's tiled gradients are Gt's tiles of that bucket
+            b = lay_o.buckets[b_id]
+            zs.zs_stream_arrive(eng, b_id,
+                                Gt[b.tile_off * W * TILE:
+                                   (b.tile_off + 100) * W * TILE])
+        assert zs.zs_stream_step_end(eng) == nb
+        torch.cuda.synchronize()
+        assert torch.equal(state.view(torch.int32),
+                           ref_state.view(torch.int32)), t
+        assert torch.equal(flat.view(torch.int16), flat_ref.view(torch.int16))
+    zs.zs_stream_free(eng)
+
+
 @pytest.mark.parametrize("tensors", [False, True])
 def test_prefetch_pipeline_matches_the_oracle(tensors):
     """The ZeRO-3 prefetch object (zs_prefetch_*) driven as an FSDP forward:
