@@ -110,20 +110,21 @@ class Case:
         self.om, self.omm, self.ov = S.cpu_state(0, n, 0.02, seed, self.pad,
                                                  warm)
 
-    def step(self, t, full_flat=None, check=True, exact=True):
+    def step(self, t, full_flat=None, check=True, exact=True, hp=None):
+        hp = HP if hp is None else hp
         S.dev_grads(self.G, self.W, self.n, t, self.sigma, self.seed,
                     self.pad)
         if self.layout == "tiled":
             zs.zs_grads_tile(self.lay, -1, self.G, self.stride, self.Gt)
             zs.zs_step(self.lay, self.Gt, self.state, self.p, full_flat,
-                       grad_layout="tiled", step=t, **HP)
+                       grad_layout="tiled", step=t, **hp)
         else:
             zs.zs_step(self.lay, self.G, self.state, self.p, full_flat,
                        grad_layout="slices", grad_stride=self.stride, step=t,
-                       **HP)
+                       **hp)
         Gc = S.cpu_grads(self.W, 0, self.n, t, self.sigma, self.seed,
                          self.pad)
-        p16 = O.step(Gc, self.om, self.omm, self.ov, OHP, t)
+        p16 = O.step(Gc, self.om, self.omm, self.ov, O.AdamW(**hp), t)
         self.op = p16
         if check:
             torch.cuda.synchronize()
@@ -249,6 +250,34 @@ def test_every_world_size(W, layout):
                  warm=(1e-4, 1e-8), seed=W, layout=layout)
         for t in (1, 2, 3):
             c.step(t)
+
+
+HP_CASES = [
+    ("lr 0", dict(HP, lr=0.0), (1, 2)),
+    ("betas 0", dict(HP, beta1=0.0, beta2=0.0), (1, 2, 3)),
+    ("no decay", dict(HP, weight_decay=0.0), (1, 2)),
+    ("eps 1", dict(HP, eps=1.0), (1, 2)),
+    ("large lr and decay", dict(HP, lr=1e-2, weight_decay=1.0), (1, 2)),
+    ("late steps", HP, (1, 1000, 100000)),
+    ("betas 0.999", dict(HP, beta1=0.999, beta2=0.999), (1, 7)),
+]
+
+
+@pytest.mark.parametrize("name,hp,steps", HP_CASES,
+                         ids=[c[0] for c in HP_CASES])
+def test_hyperparameter_edge_cases(name, hp, steps):
+    """Degenerate and extreme hyper-parameters (lr = 0, betas 0 and 0.999,
+    no decay, eps 1, large lr and decay, step counts up to 1e5 where the
+    bias corrections reach 1) through the compiled-W and runtime-W kernels,
+    bit for bit against the oracle."""
+    for W in (8, 5):
+        rng = random.Random(W)
+        numels = [rng.choice([7, 129, 1000, 4096, 33333]) for _ in range(6)]
+        say(f"case hp {name} W={W}")
+        c = Case(numels, W, W - 1, cap=W * 256 * 17, warm=(1e-4, 1e-8),
+                 seed=W, layout="tiled")
+        for t in steps:
+            c.step(t, hp=hp)
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
