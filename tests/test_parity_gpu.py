@@ -252,6 +252,48 @@ def test_every_world_size(W, layout):
             c.step(t)
 
 
+@pytest.mark.parametrize("seed", range(40))
+def test_random_configurations(seed):
+    """Seeded random points of the whole parameter space: W from 1 to 128,
+    any rank, tensor sizes around every alignment and tile boundary,
+    alignment 16 B to 4 KiB, bucket caps from one unit up (or one bucket),
+    the flat or whole-tensor layout, tiled or plain gradients with a padded
+    stride, the mixed-precision or pure-bf16 step, cold or warm moments;
+    two steps, bit for bit against the oracle."""
+    rng = random.Random(4242 + seed)
+    W = rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 24, 32, 48, 64, 100,
+                    128])
+    numels = [rng.choice([1, 7, 8, 127, 128, 129, 1000, 4095, 4096, 8191,
+                          8193, 33333, 65536, 70001])
+              for _ in range(rng.randint(1, 14))]
+    tensors = rng.random() < 0.3
+    align = rng.choice([16, 64, 256, 4096])
+    cap = rng.choice([0, W * align * rng.randint(1, 40)])
+    rank = rng.randrange(W)
+    layout = rng.choice(LAYOUTS)
+    pure = rng.random() < 0.3
+    say(f"case random seed={seed} W={W} rank={rank} tensors={tensors} "
+        f"align={align} cap={cap} {layout} pure={pure}")
+    lay_o = (build_tensor_layout(numels, W, rank, align) if tensors
+             else build_layout(numels, W, rank, cap, align))
+    if lay_o.shard_numel == 0:          # a rank that owns nothing
+        lay = (zs.zs_layout_build_tensors(numels, W, rank, align) if tensors
+               else zs.zs_layout_build(numels, W, rank, cap, align))
+        zs.zs_step(lay, dev_bf16(8), dev_f32(8), dev_bf16(8), None,
+                   grad_layout=layout, grad_stride=8, step=1, **HP)
+        return
+    if pure:
+        run_pure_bf16(numels, W, rank, cap, layout, rng.random() < 0.5,
+                      (1, 2), tensors=tensors, align=align)
+    else:
+        c = Case(numels, W, rank, cap=cap, align=align,
+                 stride_pad=rng.choice([0, 8, 24]),
+                 warm=rng.choice([None, (1e-4, 1e-8)]), seed=seed,
+                 layout=layout, tensors=tensors)
+        for t in (1, 2):
+            c.step(t)
+
+
 HP_CASES = [
     ("lr 0", dict(HP, lr=0.0), (1, 2)),
     ("betas 0", dict(HP, beta1=0.0, beta2=0.0), (1, 2, 3)),
@@ -889,11 +931,17 @@ def test_pure_bf16_launch_shapes(W, tiles):
     assert lay_o.n_tiles == tiles
 
 
-def run_pure_bf16(numels, W, rank, cap, layout, flat_params, steps):
+def run_pure_bf16(numels, W, rank, cap, layout, flat_params, steps,
+                  tensors=False, align=256):
     """zs_step_bf16 on rank `rank`'s shard for the given steps, checked
-    after each against the oracle, bit for bit; returns the oracle layout."""
-    lay_o = build_layout(numels, W, rank, cap)
-    lay = zs.zs_layout_build(numels, W, rank, cap)
+    after each against the oracle, bit for bit; returns the oracle layout.
+    tensors: the whole-tensor assignment instead of the flat layout."""
+    if tensors:
+        lay_o = build_tensor_layout(numels, W, rank, align)
+        lay = zs.zs_layout_build_tensors(numels, W, rank, align)
+    else:
+        lay_o = build_layout(numels, W, rank, cap, align)
+        lay = zs.zs_layout_build(numels, W, rank, cap, align)
     n, F = lay_o.shard_numel, lay_o.flat_numel
     pad = S.padding_runs(n, lay_o.chunks)
     om, omm, ov = S.cpu_state(0, n, 0.02, W, pad, (1e-4, 1e-8))
