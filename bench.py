@@ -334,14 +334,14 @@ def bf16_main(args, w):
     flat_n, n, nb, nc = zs.zs_layout_info(lay)
     n_tiles = zs.zs_layout_tiles(lay)
     log(f"workload {w.name} pure bf16: W={W} shard={n} buckets={nb}")
+    Gt, state, flat = arena_views([(n_tiles * W * T, torch.bfloat16),
+                                   (n_tiles * 2 * T, torch.float32),
+                                   (flat_n, torch.bfloat16)])
     G = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
-    Gt = torch.empty(n_tiles * W * T, dtype=torch.bfloat16, device="cuda")
     S.dev_grads(G, W, n, 1, w.grad_sigma)
     zs.zs_grads_tile(lay, -1, G, n, Gt)
     del G
-    state = torch.empty(n_tiles * 2 * T, dtype=torch.float32, device="cuda")
     zs.zs_state_mv_pack(lay, None, None, state)
-    flat = torch.empty(flat_n, dtype=torch.bfloat16, device="cuda")
     synth.dev_normal_bf16(flat, 0, synth.TAG_MASTER, 0, 0, 0, w.master_sigma)
     torch.cuda.synchronize()
     log("inputs resident")
@@ -382,7 +382,8 @@ def bf16_main(args, w):
                    "bytes_per_param": bpp,
                    "grads_layout": "tiled [tile][W][8192]",
                    "state_layout": "tiled [tile][m|v][8192]",
-                   "params": "flat bf16 buffer, in place"},
+                   "params": "flat bf16 buffer, in place",
+                   "allocation": "one arena: tiled gradients, state, flat"},
         "roofline": {"bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": None},
