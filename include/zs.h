@@ -401,8 +401,9 @@ int zs_pack(const zs_layout* layout, const uint16_t* param_shard,
  * event on it), so a later issue may overwrite the buffer.
  * A buffer goes issue -> acquire -> release -> issue ...; calls out of
  * that order fail with ZS_EINVAL (the next buffer is not released yet, or
- * the slot is not issued / acquired).  Errors also: ZS_ERANGE (range above
- * buffer_elems, slot index), those of zs_gather, ZS_EDEVICE. */
+ * the slot is not issued / acquired).  Errors also: ZS_ERANGE (range
+ * outside [0, flat_numel] or longer than buffer_elems, slot index), those
+ * of zs_gather, ZS_EDEVICE. */
 typedef struct zs_prefetch zs_prefetch;
 int zs_prefetch_create(const zs_layout* layout, const uint16_t* const* shards,
                        uint16_t* const* buffers, int32_t n_buffers,
@@ -449,8 +450,11 @@ void zs_prefetch_free(zs_prefetch* prefetch);
  * Errors: ZS_EINVAL (NULL arguments, counts, a step not open or already
  * open, a bucket arriving twice), ZS_EALIGN, ZS_ERANGE (bucket id, slot too
  * small), ZS_EDEVICE (a HIP call failed), and those of zs_buckets_step.
- * After an error the step's results are undefined; end the step.  One host
- * thread at a time per engine. */
+ * An argument error has no effect and the step stays usable.  A failed
+ * copy or launch abandons the step: its pending group is dropped, later
+ * arrivals are refused, and zs_stream_step_end closes it and returns
+ * ZS_EINVAL; the step's results are then undefined.  One host thread at a
+ * time per engine. */
 typedef struct zs_stream zs_stream;
 int zs_stream_create(const zs_layout* layout, int32_t group,
                      uint16_t* const* slots, int32_t n_slots,

@@ -133,7 +133,7 @@ extern "C" int zs_accumulate(int32_t mode, float* acc, const uint16_t* grad,
     a.fk = (float)k;
     a.invk = k > 0 ? (float)(1.0 / (double)k) : 0.f;
     a.pow2 = k > 0 && (k & (k - 1)) == 0;
-    const int64_t blocks = (n + kChunk - 1) / kChunk;
+    const int64_t blocks = n / kChunk + (n % kChunk != 0);
     // one launch: fewer than 2^32 work-items along x
     if (blocks > (((int64_t)1 << 32) - 1) / kThreads)
         return fail(ZS_ERANGE, "n %lld too large for one launch",

@@ -6,6 +6,7 @@
 // and the reduce-scatter ownership of the CS336 lecture 8 ZeRO-1 example.
 
 #include <algorithm>
+#include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <numeric>

@@ -134,6 +134,10 @@ extern "C" int zs_prefetch_issue(zs_prefetch* P, int64_t flat_lo,
     zs::clear_error();
     if (!P) return fail(ZS_EINVAL, "prefetch is NULL");
     if (!slot) return fail(ZS_EINVAL, "slot is NULL");
+    if (flat_lo < 0 || flat_hi < flat_lo || flat_hi > P->L->flat_numel)
+        return fail(ZS_ERANGE, "range [%lld, %lld) outside [0, %lld]",
+                    (long long)flat_lo, (long long)flat_hi,
+                    (long long)P->L->flat_numel);
     if (flat_hi - flat_lo > P->buffer_elems)
         return fail(ZS_ERANGE, "range of %lld elements above the buffers' "
                     "%lld", (long long)(flat_hi - flat_lo),

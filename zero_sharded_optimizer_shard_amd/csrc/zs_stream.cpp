@@ -49,6 +49,7 @@ struct zs_stream {
                                       // launches the upload stream waited on
     // the step in progress
     bool open = false;
+    bool failed = false;              // a launch or a copy of it failed
     float* state = nullptr;
     uint16_t* pshard = nullptr;
     uint16_t* flat = nullptr;
@@ -76,6 +77,21 @@ int hip_fail(hipError_t e, const char* what)
     return fail(ZS_EDEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+bool aligned16(const void* p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// A device call of the step failed: the step is abandoned (its pending group
+// dropped) and later arrivals are refused until step_end closes it.
+int abandon(zs_stream* S, int rc)
+{
+    S->failed = true;
+    S->pend_ids.clear();
+    S->pend_slots.clear();
+    return rc;
+}
+
 void destroy(zs_stream* S)
 {
     if (S->landed) (void)hipEventDestroy(S->landed);
@@ -90,23 +106,27 @@ int launch_pending(zs_stream* S)
     const int32_t cnt = (int32_t)S->pend_ids.size();
     if (cnt == 0)
         return ZS_OK;
+    if (cnt > ZS_MAX_GROUP)
+        return abandon(S, fail(ZS_EINVAL, "%d pending buckets above %d", cnt,
+                               ZS_MAX_GROUP));
     const int64_t g = S->launches;
     hipStream_t s = S->steps[g % (int64_t)S->steps.size()];
     // the upload stream is in order: one record after the last copy covers
     // the whole group
     hipError_t e = hipEventRecord(S->landed, S->up);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if (e != hipSuccess) return abandon(S, hip_fail(e, "hipEventRecord"));
     e = hipStreamWaitEvent(s, S->landed, 0);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    if (e != hipSuccess)
+        return abandon(S, hip_fail(e, "hipStreamWaitEvent"));
     const uint16_t* grads[ZS_MAX_GROUP];
     for (int32_t i = 0; i < cnt; ++i)
         grads[i] = S->slots[S->pend_slots[i]];
     const int rc = zs_buckets_step(S->L, cnt, S->pend_ids.data(), grads,
                                    ZS_GRADS_TILED, 0, S->state, S->pshard,
                                    S->flat, &S->hp, S->t, s);
-    if (rc) return rc;
+    if (rc) return abandon(S, rc);
     e = hipEventRecord(S->done[g % (int64_t)S->done.size()], s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if (e != hipSuccess) return abandon(S, hip_fail(e, "hipEventRecord"));
     for (int32_t k : S->pend_slots)
         S->reader[k] = g;
     ++S->launches;
@@ -193,6 +213,9 @@ extern "C" int zs_stream_step_begin(zs_stream* S, float* state,
     if (!state) return fail(ZS_EINVAL, "state is NULL");
     if (!param_shard && !full_flat)
         return fail(ZS_EINVAL, "need param_shard or full_flat");
+    if (!aligned16(state) || (param_shard && !aligned16(param_shard)) ||
+        (full_flat && !aligned16(full_flat)))
+        return fail(ZS_EALIGN, "device pointers must be 16-byte aligned");
     S->state = state;
     S->pshard = param_shard;
     S->flat = full_flat;
@@ -202,6 +225,7 @@ extern "C" int zs_stream_step_begin(zs_stream* S, float* state,
     S->pend_ids.clear();
     S->pend_slots.clear();
     for (char& a : S->arrived) a = 0;
+    S->failed = false;
     S->open = true;
     return ZS_OK;
 }
@@ -212,6 +236,9 @@ extern "C" int zs_stream_arrive(zs_stream* S, int32_t bucket_id,
     zs::clear_error();
     if (!S) return fail(ZS_EINVAL, "stream is NULL");
     if (!S->open) return fail(ZS_EINVAL, "no step is open");
+    if (S->failed)
+        return fail(ZS_EINVAL, "an earlier call of this step failed: end "
+                    "the step");
     const int32_t nb = (int32_t)S->L->buckets.size();
     if (bucket_id < 0 || bucket_id >= nb)
         return fail(ZS_ERANGE, "bucket_id %d outside [0, %d)", bucket_id,
@@ -231,14 +258,15 @@ extern "C" int zs_stream_arrive(zs_stream* S, int32_t bucket_id,
         if (S->waited[j] < r) {
             e = hipStreamWaitEvent(S->up,
                                    S->done[r % (int64_t)S->done.size()], 0);
-            if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+            if (e != hipSuccess)
+                return abandon(S, hip_fail(e, "hipStreamWaitEvent"));
             S->waited[j] = r;
         }
     }
     e = hipMemcpyAsync(S->slots[k], src,
                        (size_t)bucket_elems(S->L, bucket_id) * 2,
                        hipMemcpyDefault, S->up);
-    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    if (e != hipSuccess) return abandon(S, hip_fail(e, "hipMemcpyAsync"));
     S->arrived[bucket_id] = 1;
     S->pend_ids.push_back(bucket_id);
     S->pend_slots.push_back(k);
@@ -253,6 +281,9 @@ extern "C" int zs_stream_step_end(zs_stream* S)
     if (!S) return fail(ZS_EINVAL, "stream is NULL");
     if (!S->open) return fail(ZS_EINVAL, "no step is open");
     S->open = false;
+    if (S->failed)
+        return fail(ZS_EINVAL, "the step was abandoned after an earlier "
+                    "error; it is now closed");
     const int rc = launch_pending(S);
     if (rc) return rc;
     return S->stepped;
