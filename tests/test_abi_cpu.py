@@ -291,6 +291,8 @@ def test_step_argument_checks_need_no_device():
     # one launch holds fewer than 2^32 work-items: 512 threads x 4 elements
     big = (2 ** 32 // 512) * 2048
     assert L.zs_accumulate(0, A, A, None, big, 2, None) == -3
+    # the largest n the type holds: refused, with no overflow on the way
+    assert L.zs_accumulate(0, A, A, None, 2 ** 63 - 4, 2, None) == -3
     # gather (ZeRO-3)
     P_ = ctypes.c_void_p
     sh = (P_ * 4)(A, A, A, A)
@@ -420,3 +422,72 @@ def test_prefetch_argument_checks_need_no_device():
     assert L.zs_prefetch_acquire(None, 0, None, None) == -1
     assert L.zs_prefetch_release(None, 0, None) == -1
     L.zs_prefetch_free(None)
+
+
+def test_bindings_refuse_buffers_shorter_than_the_layout():
+    """The kernels address every buffer by the layout's sizes alone, so the
+    Python bindings refuse a tensor shorter than the layout needs before
+    any device access; a tensor of exactly the needed size passes that
+    check (and, being host memory here, is then refused as not a device
+    tensor)."""
+    import torch
+    W = 4
+    lay = zs.zs_layout_build(wl.tiny(), W, 0)
+    F, n, nt, _, buckets = lay.sizes()
+    T = zs.ZS_TILE
+    b0 = buckets[0]
+    t0 = -(-b0.slice_numel // T)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+              step=1)
+
+    def bf(k):
+        return torch.zeros(k, dtype=torch.bfloat16)
+
+    def f32(k):
+        return torch.zeros(k, dtype=torch.float32)
+
+    def check(call, sizes):
+        """call(**buffers) with each buffer in turn one element short."""
+        with pytest.raises(ValueError, match="expected a device tensor"):
+            call(**{k: mk(v) for k, (mk, v) in sizes.items()})
+        for short in sizes:
+            bufs = {k: mk(v - (k == short)) for k, (mk, v) in sizes.items()}
+            with pytest.raises(ValueError, match="the layout needs") as e:
+                call(**bufs)
+            assert str(e.value).startswith(short), (short, str(e.value))
+
+    check(lambda grads, state, param_shard, full_flat: zs.zs_step(
+        lay, grads, state, param_shard, full_flat, grad_layout="tiled",
+        **hp), dict(grads=(bf, nt * W * T), state=(f32, nt * 3 * T),
+                    param_shard=(bf, n), full_flat=(bf, F)))
+    stride = n + 8
+    check(lambda grads, state, param_shard: zs.zs_step(
+        lay, grads, state, param_shard, None, grad_layout="slices",
+        grad_stride=stride, **hp),
+        dict(grads=(bf, (W - 1) * stride + n), state=(f32, nt * 3 * T),
+             param_shard=(bf, n)))
+    check(lambda grads, state, full_flat: zs.zs_buckets_step(
+        lay, [0], [grads], state, None, full_flat, grad_layout="tiled",
+        **hp), dict(grads=(bf, t0 * W * T), state=(f32, nt * 3 * T),
+                    full_flat=(bf, F)))
+    check(lambda grads, state_mv, params: zs.zs_step_bf16(
+        lay, grads, state_mv, params, params_flat=True, grad_layout="tiled",
+        **hp), dict(grads=(bf, nt * W * T), state_mv=(f32, nt * 2 * T),
+                    params=(bf, F)))
+    check(lambda master, m, v, state: zs.zs_state_pack(
+        lay, master, m, v, state),
+        dict(master=(f32, n), m=(f32, n), v=(f32, n),
+             state=(f32, nt * 3 * T)))
+    check(lambda state_mv, m, v: zs.zs_state_mv_unpack(lay, state_mv, m, v),
+          dict(state_mv=(f32, nt * 2 * T), m=(f32, n), v=(f32, n)))
+    check(lambda slices, tiled: zs.zs_grads_tile(lay, -1, slices, stride,
+                                                 tiled),
+          dict(slices=(bf, (W - 1) * stride + n), tiled=(bf, nt * W * T)))
+    check(lambda param_shard, full_flat: zs.zs_pack(lay, param_shard,
+                                                    full_flat),
+          dict(param_shard=(bf, n), full_flat=(bf, F)))
+    check(lambda out: zs.zs_gather(lay, [bf(n)] * W, 8, 1000, out),
+          dict(out=(bf, 992)))
+    check(lambda acc, out: zs.zs_accumulate(zs.ZS_ACC_LAST, acc, bf(4096),
+                                            out, k=2),
+          dict(acc=(f32, 4096), out=(bf, 4096)))

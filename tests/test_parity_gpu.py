@@ -1147,6 +1147,13 @@ def test_stream_engine_equals_the_whole_step(arrival, tensors):
     up = torch.cuda.Stream()
     sts = [torch.cuda.Stream(), torch.cuda.Stream()]
     eng = zs.zs_stream_create(lay, 3, slots, up, sts)
+    wide = torch.empty(state.numel() + 4, dtype=torch.float32,
+                       device="cuda")
+    with pytest.raises(zs.ZsError) as e:             # misaligned state
+        zs.zs_stream_step_begin(eng, wide[1:], p, flat, step=1, **HP)
+    assert e.value.code == -2
+    with pytest.raises(ValueError):                  # state too short
+        zs.zs_stream_step_begin(eng, state[:-4], p, flat, step=1, **HP)
     order = list(range(nb))[::-1]
     random.Random(3).shuffle(order)
     for t in (1, 2):
@@ -1341,7 +1348,21 @@ def test_prefetch_pipeline_matches_the_oracle(tensors):
     with pytest.raises(zs.ZsError) as e:
         zs.zs_prefetch_issue(pf, 0, biggest + 8)     # above the buffers
     assert e.value.code == -3
+    # ranges outside the flat buffer, including ones whose length does not
+    # fit in 64 bits, are refused before anything is queued
+    for lo, hi in ((-8, 8), (16, 8), (F // 8 * 8, F + 8),
+                   (-(1 << 62), 1 << 62)):
+        with pytest.raises(zs.ZsError) as e:
+            zs.zs_prefetch_issue(pf, lo, hi)
+        assert e.value.code == -3, (lo, hi)
+    lo, hi = units[0]
+    sl = zs.zs_prefetch_issue(pf, lo, hi)            # still usable
+    buf = zs.zs_prefetch_acquire(pf, sl, cs)
+    with torch.cuda.stream(cs):
+        outs[0].copy_(buf[:hi - lo])
+    zs.zs_prefetch_release(pf, sl, cs)
     torch.cuda.synchronize()
+    assert np.array_equal(np16(outs[0]), full[lo:hi])
     zs.zs_prefetch_free(pf)
 
 

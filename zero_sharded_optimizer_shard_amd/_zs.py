@@ -155,10 +155,20 @@ class Layout:
 
     def __init__(self, handle: int):
         self._h = ctypes.c_void_p(handle)
+        self._sizes = None
 
     @property
     def handle(self):
         return self._h
+
+    def sizes(self):
+        """(flat_numel, shard_numel, n_tiles, world, buckets), read from
+        the library once; the bindings check tensor sizes against them."""
+        if self._sizes is None:
+            f, n = zs_layout_info(self)[:2]
+            self._sizes = (f, n, zs_layout_tiles(self),
+                           zs_layout_rank(self)[0], zs_layout_buckets(self))
+        return self._sizes
 
     def __del__(self):
         if getattr(self, "_h", None) is not None and self._h.value and _lib:
@@ -276,6 +286,40 @@ def _f32(t, name):
     return _ptr(t)
 
 
+def _need(t, numel: int, name: str) -> None:
+    """The kernels address a buffer by the layout's sizes alone: refuse a
+    tensor shorter than that here, before any device access."""
+    if t is not None and numel > 0 and t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, the layout needs "
+                         f"at least {numel}")
+
+
+def _tiles(slice_numel: int) -> int:
+    return -(-slice_numel // ZS_TILE)
+
+
+def _grads_need(W: int, tiles: int, slice_numel: int, code: int,
+                stride: int) -> int:
+    """Elements a gradient buffer must hold: [tiles][W][ZS_TILE] tiled, or
+    W rows of `slice_numel` at `stride` (a stride below the slice length is
+    the library's to refuse)."""
+    if code == ZS_GRADS_TILED:
+        return tiles * W * ZS_TILE
+    return (W - 1) * max(stride, 0) + slice_numel
+
+
+def _step_need(layout: Layout, grads, code: int, stride: int, state, rows,
+               param_shard, full_flat, names=("state", "param_shard",
+                                              "full_flat")) -> None:
+    f, n, nt, W, _ = layout.sizes()
+    if n == 0:
+        return
+    _need(grads, _grads_need(W, nt, n, code, stride), "grads")
+    _need(state, nt * rows * ZS_TILE, names[0])
+    _need(param_shard, n, names[1])
+    _need(full_flat, f, names[2])
+
+
 def _stream(stream):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -302,6 +346,8 @@ def zs_step(layout: Layout, grads, state, param_shard=None, full_flat=None,
     """grads: [W][grad_stride] slices (grad_layout "slices") or
     [n_tiles][W][ZS_TILE] ("tiled"); state: tiled fp32 state."""
     hp = _hp(lr, beta1, beta2, eps, weight_decay)
+    _step_need(layout, grads, _layout_code(grad_layout), grad_stride, state,
+               3, param_shard, full_flat)
     _check(lib().zs_step(layout.handle, _bf16(grads, "grads"),
                          _layout_code(grad_layout), grad_stride,
                          _f32(state, "state"),
@@ -316,6 +362,8 @@ def zs_bucket_step(layout: Layout, bucket_id: int, grads, state,
                    beta1: float, beta2: float, eps: float,
                    weight_decay: float, step: int, stream=None) -> None:
     hp = _hp(lr, beta1, beta2, eps, weight_decay)
+    _buckets_need(layout, [bucket_id], [grads], _layout_code(grad_layout),
+                  grad_stride, state, param_shard, full_flat)
     _check(lib().zs_bucket_step(layout.handle, bucket_id,
                                 _bf16(grads, "grads"),
                                 _layout_code(grad_layout), grad_stride,
@@ -324,6 +372,16 @@ def zs_bucket_step(layout: Layout, bucket_id: int, grads, state,
                                 _bf16(full_flat, "full_flat"),
                                 ctypes.byref(hp), step, _stream(stream)),
            "zs_bucket_step")
+
+
+def _buckets_need(layout: Layout, bucket_ids, grads, code: int, stride: int,
+                  state, param_shard, full_flat) -> None:
+    f, n, nt, W, buckets = layout.sizes()
+    for b, g in zip(bucket_ids, grads):
+        if 0 <= b < len(buckets):       # other ids: the library's to refuse
+            sl = buckets[b].slice_numel
+            _need(g, _grads_need(W, _tiles(sl), sl, code, stride), "grads")
+    _step_need(layout, None, code, stride, state, 3, param_shard, full_flat)
 
 
 def zs_buckets_step(layout: Layout, bucket_ids, grads, state,
@@ -336,6 +394,8 @@ def zs_buckets_step(layout: Layout, bucket_ids, grads, state,
     n = len(bucket_ids)
     if len(grads) != n:
         raise ValueError("one staging tensor per bucket")
+    _buckets_need(layout, bucket_ids, grads, _layout_code(grad_layout),
+                  grad_stride, state, param_shard, full_flat)
     ids = (ctypes.c_int32 * max(n, 1))(*bucket_ids)
     ptrs = (ctypes.c_void_p * max(n, 1))(*[_bf16(g, "grads") for g in grads])
     hp = _hp(lr, beta1, beta2, eps, weight_decay)
@@ -350,6 +410,7 @@ def zs_buckets_step(layout: Layout, bucket_ids, grads, state,
 
 def zs_state_pack(layout: Layout, master, m, v, state, stream=None) -> None:
     """Plain master/m/v (m, v may be None: zeros) -> tiled state."""
+    _state_need(layout, state, 3, master=master, m=m, v=v)
     _check(lib().zs_state_pack(layout.handle, _f32(master, "master"),
                                None if m is None else _f32(m, "m"),
                                None if v is None else _f32(v, "v"),
@@ -357,8 +418,18 @@ def zs_state_pack(layout: Layout, master, m, v, state, stream=None) -> None:
            "zs_state_pack")
 
 
+def _state_need(layout: Layout, state, rows: int, **plain) -> None:
+    f, n, nt, W, _ = layout.sizes()
+    if n == 0:
+        return
+    _need(state, nt * rows * ZS_TILE, "state" if rows == 3 else "state_mv")
+    for name, t in plain.items():
+        _need(t, n, name)
+
+
 def zs_state_unpack(layout: Layout, state, master=None, m=None, v=None,
                     stream=None) -> None:
+    _state_need(layout, state, 3, master=master, m=m, v=v)
     _check(lib().zs_state_unpack(layout.handle, _f32(state, "state"),
                                  None if master is None
                                  else _f32(master, "master"),
@@ -369,6 +440,18 @@ def zs_state_unpack(layout: Layout, state, master=None, m=None, v=None,
 
 def zs_grads_tile(layout: Layout, bucket_id: int, slices, stride: int,
                   tiled, stream=None) -> None:
+    f, n, nt, W, buckets = layout.sizes()
+    if bucket_id < 0:
+        sl, tiles = n, nt
+    elif bucket_id < len(buckets):
+        sl = buckets[bucket_id].slice_numel
+        tiles = _tiles(sl)
+    else:
+        sl = tiles = 0                  # the library refuses the id
+    if n:
+        _need(slices, _grads_need(W, tiles, sl, ZS_GRADS_SLICES, stride),
+              "slices")
+        _need(tiled, tiles * W * ZS_TILE, "tiled")
     _check(lib().zs_grads_tile(layout.handle, bucket_id,
                                _bf16(slices, "slices"), stride,
                                _bf16(tiled, "tiled"), _stream(stream)),
@@ -383,6 +466,10 @@ def zs_step_bf16(layout: Layout, grads, state_mv, params, *,
     """Pure-bf16 step: params (bf16 shard, or the flat buffer when
     params_flat) updated in place; state_mv tiled [tiles][2][ZS_TILE]."""
     hp = _hp(lr, beta1, beta2, eps, weight_decay)
+    _step_need(layout, grads, _layout_code(grad_layout), grad_stride,
+               state_mv, 2, None if params_flat else params,
+               params if params_flat else None,
+               ("state_mv", "params", "params"))
     _check(lib().zs_step_bf16(layout.handle, _bf16(grads, "grads"),
                               _layout_code(grad_layout), grad_stride,
                               _f32(state_mv, "state_mv"),
@@ -392,6 +479,7 @@ def zs_step_bf16(layout: Layout, grads, state_mv, params, *,
 
 
 def zs_state_mv_pack(layout: Layout, m, v, state_mv, stream=None) -> None:
+    _state_need(layout, state_mv, 2, m=m, v=v)
     _check(lib().zs_state_mv_pack(layout.handle,
                                   None if m is None else _f32(m, "m"),
                                   None if v is None else _f32(v, "v"),
@@ -401,6 +489,7 @@ def zs_state_mv_pack(layout: Layout, m, v, state_mv, stream=None) -> None:
 
 def zs_state_mv_unpack(layout: Layout, state_mv, m=None, v=None,
                        stream=None) -> None:
+    _state_need(layout, state_mv, 2, m=m, v=v)
     _check(lib().zs_state_mv_unpack(layout.handle,
                                     _f32(state_mv, "state_mv"),
                                     None if m is None else _f32(m, "m"),
@@ -413,6 +502,8 @@ def zs_accumulate(mode: int, acc, grad, out=None, k: int = 0,
     """One micro-batch of gradient accumulation (ZS_ACC_FIRST / _ADD /
     _LAST); acc fp32, grad and out bf16, all of the same length."""
     n = grad.numel()
+    _need(acc, n, "acc")
+    _need(out, n, "out")
     _check(lib().zs_accumulate(mode, _f32(acc, "acc"), _bf16(grad, "grad"),
                                _bf16(out, "out"), n, k, _stream(stream)),
            "zs_accumulate")
@@ -422,6 +513,7 @@ def zs_gather(layout: Layout, shards, flat_lo: int, flat_hi: int, out,
               stream=None) -> None:
     """shards: one bf16 shard tensor per rank, in rank order; out: at least
     flat_hi - flat_lo bf16 elements."""
+    _need(out, flat_hi - flat_lo, "out")
     ptrs = (ctypes.c_void_p * max(len(shards), 1))(
         *[_bf16(t, "shards") for t in shards])
     _check(lib().zs_gather(layout.handle, ptrs, flat_lo, flat_hi,
@@ -432,6 +524,10 @@ def zs_pack(layout: Layout, param_shard, full_flat=None, dev_chunks=None,
             n_chunks: int = 0, dev_tensor_ptrs=None, stream=None) -> None:
     """dev_chunks: device tensor holding chunks_bytes(); dev_tensor_ptrs:
     device int64 tensor of per-tensor data pointers."""
+    f, n = layout.sizes()[:2]
+    if n:
+        _need(param_shard, n, "param_shard")
+        _need(full_flat, f, "full_flat")
     _check(lib().zs_pack(layout.handle, _bf16(param_shard, "param_shard"),
                          _bf16(full_flat, "full_flat"), _ptr(dev_chunks),
                          n_chunks, _ptr(dev_tensor_ptrs), _stream(stream)),
@@ -481,6 +577,8 @@ def zs_stream_step_begin(stream: Stream, state, param_shard=None,
                          beta2: float, eps: float, weight_decay: float,
                          step: int) -> None:
     hp = _hp(lr, beta1, beta2, eps, weight_decay)
+    _step_need(stream._keep[0], None, ZS_GRADS_TILED, 0, state, 3,
+               param_shard, full_flat)
     _check(lib().zs_stream_step_begin(stream.handle, _f32(state, "state"),
                                       _bf16(param_shard, "param_shard"),
                                       _bf16(full_flat, "full_flat"),
@@ -495,6 +593,10 @@ def zs_stream_arrive(stream: Stream, bucket_id: int, src) -> None:
         raise TypeError("src: need a contiguous 2-byte tensor")
     if not (src.is_cuda or src.is_pinned()):
         raise ValueError("src: need device or pinned host memory")
+    f, n, nt, W, buckets = stream._keep[0].sizes()
+    if 0 <= bucket_id < len(buckets):   # other ids: the library's to refuse
+        _need(src, _tiles(buckets[bucket_id].slice_numel) * W * ZS_TILE,
+              "src")
     _check(lib().zs_stream_arrive(stream.handle, bucket_id,
                                   ctypes.c_void_p(src.data_ptr())),
            "zs_stream_arrive")
