@@ -1391,6 +1391,46 @@ def test_whole_tensor_step(W, layout):
         assert np.array_equal(np16(flat), want)
 
 
+# 75 tensors of ragged sizes (tile-boundary sizes among them): at W = 1 one
+# rank owns all 75, at W = 2 about 37 and at W = 3 about 25, against 32
+# members per launch (three, two and one launches of the whole-shard step)
+_many = random.Random(11)
+MANY_TENSORS = [_many.choice([1, 7, 129, 4000, 8191, 8192, 8193, 16385,
+                              20000]) + k % 5 for k in range(75)]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("W", [1, 2, 3])
+def test_whole_tensor_step_many_tensors(W, layout):
+    """Whole-tensor assignment with more owned tensors than one launch takes:
+    the step, the state conversions and the flat output split over several
+    launches, bit for bit against the oracle; positions of other ranks'
+    tensors in the flat buffer untouched; zs_state_unpack returns the
+    oracle's master, m and v."""
+    rank = W - 1
+    say(f"case whole-tensor many W={W} rank={rank} {layout}")
+    c = Case(MANY_TENSORS, W, rank, layout=layout, tensors=True,
+             warm=(1e-4, 1e-8), seed=3 + W, stride_pad=8)
+    assert len(c.lay_o.buckets) > (32 if W < 3 else 16)
+    F = c.lay_o.flat_numel
+    flat = dev_bf16(F)
+    synth.dev_bits16(flat, 5, synth.TAG_SENTINEL, 0, rank, 0)
+    want = synth.cpu_bits16(F, 5, synth.TAG_SENTINEL, 0, rank, 0)
+    for t in (1, 2):
+        c.step(t, full_flat=flat)
+    torch.cuda.synchronize()
+    pack_flat(c.lay_o, c.op, want)
+    assert np.array_equal(np16(flat), want)
+    n = c.n
+    outs = [dev_f32(n) for _ in range(3)]
+    for o in outs:
+        o.fill_(float("nan"))
+    zs.zs_state_unpack(c.lay, c.state, *outs)
+    torch.cuda.synchronize()
+    for got, ref in zip(outs, (c.om, c.omm, c.ov)):
+        assert np.array_equal(npf(got).view(np.uint32), ref.view(np.uint32))
+
+
 def test_whole_tensor_pure_bf16_and_pack():
     W = 3
     for rank in range(W):

@@ -131,9 +131,16 @@ __device__ __forceinline__ int unit_off(int k)
 
 // Tile locators of the layout conversions and the flat pack.  GeomLoc:
 // the regular buckets of the flat mode (blockIdx.y = bucket); SegLoc: up to
-// kMaxGroup explicit segments (blockIdx.y = segment), e.g. the owned tensors
-// of the whole-tensor mode; positions are then absolute.
+// kMaxMembers explicit segments (a 1-D grid over their tiles), e.g. the
+// owned tensors of the whole-tensor mode; positions are then absolute.
+//
+// kMaxGroup: buckets per zs_buckets_step call (the public limit).
+// kMaxMembers: members per launch, held in the kernel arguments; whole-shard
+// steps of the whole-tensor mode pack up to this many owned tensors into one
+// launch (the Llama-3-8B-shaped list gives a rank 22 of them at W = 8).
 constexpr int kMaxGroup = ZS_MAX_GROUP;
+constexpr int kMaxMembers = 32;
+static_assert(kMaxMembers >= kMaxGroup, "a call's group fits one launch");
 
 struct Seg {
     int64_t shard_off, tile_off, fpos, slice;
@@ -145,19 +152,26 @@ struct GeomLoc {
 };
 
 // Member i of a group launch owns the launch's tiles [start[i], start[i+1])
-// (blockIdx.x runs over the group's tiles); a short scalar scan finds it.
+// (blockIdx.x runs over the group's tiles, start[0] = 0); a binary search
+// over the prefix table, wave-uniform scalar loads of the kernel arguments,
+// finds it: the largest i < count with start[i] <= t.
 __device__ __forceinline__ int member_of(const int64_t* start, int count,
                                          int64_t t)
 {
-    int i = 0;
-    while (i + 1 < count && start[i + 1] <= t)
-        ++i;
-    return i;
+    int lo = 0, hi = count - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (start[mid] <= t)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
 }
 
 struct SegLoc {
-    Seg s[kMaxGroup];
-    int64_t start[kMaxGroup + 1];
+    Seg s[kMaxMembers];
+    int64_t start[kMaxMembers + 1];
     int count;
     __device__ bool operator()(TileRef& r) const
     {
@@ -411,13 +425,16 @@ struct GroupMember {
 };
 
 struct GroupArgs {
-    GroupMember mb[kMaxGroup];
-    int64_t start[kMaxGroup + 1];   // prefix of the members' tile counts
+    GroupMember mb[kMaxMembers];
+    int64_t start[kMaxMembers + 1]; // prefix of the members' tile counts
     int32_t count;
     int64_t gstride;
     int32_t W;
     Consts c;
 };
+// kernel arguments are limited to 4 KiB
+static_assert(sizeof(GroupArgs) <= 4096 && sizeof(SegLoc) <= 2048,
+              "group tables must fit the kernel arguments");
 
 template <int WT, bool TILED, class SH, bool PURE>
 __global__ __launch_bounds__(SH::NT) void group_step_kernel(GroupArgs a)
@@ -692,7 +709,7 @@ int for_shard_ranges(const zs_layout* L, Fn fn)
 
 // Calls fn(loc, grid, shard_base, tile_base, flat_base) for every launch
 // that covers the whole shard: regular bucket ranges in the flat mode
-// (positions relative to the bases), groups of up to kMaxGroup owned
+// (positions relative to the bases), groups of up to kMaxMembers owned
 // tensors in the whole-tensor mode (absolute positions, zero bases, a 1-D
 // grid over the group's tiles).
 template <class Fn>
@@ -711,7 +728,7 @@ int for_launches(const zs_layout* L, Fn fn)
         SegLoc loc;
         int cnt = 0;
         loc.start[0] = 0;
-        for (; cnt < kMaxGroup && g0 + cnt < nb; ++cnt) {
+        for (; cnt < kMaxMembers && g0 + cnt < nb; ++cnt) {
             const zs_bucket& b = L->buckets[g0 + cnt];
             const int64_t nt = tiles_for(b.slice_numel);
             if (cnt > 0 && loc.start[cnt] + nt > kMaxLaunchTiles)
@@ -866,7 +883,7 @@ int launch_groups(const zs_layout* L, int32_t count, const int32_t* ids,
         GroupArgs a;
         int32_t cnt = 0;
         a.start[0] = 0;
-        for (; cnt < kMaxGroup && g0 + cnt < count; ++cnt) {
+        for (; cnt < kMaxMembers && g0 + cnt < count; ++cnt) {
             const zs_bucket& b = L->buckets[ids[g0 + cnt]];
             const int64_t nt = tiles_for(b.slice_numel);
             if (cnt > 0 && a.start[cnt] + nt > kMaxLaunchTiles)
