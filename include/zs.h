@@ -47,6 +47,9 @@ extern "C" {
 #define ZS_ERANGE  (-3)  /* id out of range, size overflow, short stride    */
 #define ZS_ENOMEM  (-4)  /* host allocation failed                          */
 #define ZS_EDEVICE (-5)  /* HIP launch error                                */
+#define ZS_EIO     (-6)  /* file cannot be opened, read or written; not a
+                            checkpoint, truncated, or its checksum fails    */
+#define ZS_EMISMATCH (-7) /* checkpoint written for another layout         */
 
 /* Opaque host-side layout of one rank.  Created by zs_layout_build, released
  * by zs_layout_free; read-only afterwards, so it may be shared by threads. */
@@ -468,6 +471,63 @@ int zs_stream_arrive(zs_stream* stream, int32_t bucket_id,
                      const uint16_t* src);
 int zs_stream_step_end(zs_stream* stream);
 void zs_stream_free(zs_stream* stream);
+
+/* ---- checkpoint and resume ------------------------------------------------
+ *
+ * A rank's optimizer state means something only together with the layout
+ * that placed it: which tensors, in which order, cut into which buckets,
+ * and which rank's slices.  A checkpoint restored under another layout
+ * pairs moments and master weights with the wrong parameters, and nothing
+ * in the numbers shows it (the DDP-to-ZeRO blog, section 3.3, warns that a
+ * ZeRO checkpoint saved without the right gathering step is unusable).  A
+ * checkpoint therefore carries the layout's fingerprint, and loading refuses
+ * any other layout. */
+
+/* 64-bit FNV-1a (offset basis 0xcbf29ce484222325, prime 0x100000001b3) over
+ * the bytes of these little-endian int64 values, in order: the mode (0 flat,
+ * 1 whole-tensor), world, rank, the alignment in elements, the full bucket
+ * size in elements (0 in the whole-tensor mode), the tensor count, then every
+ * tensor's numel.  Two layouts with equal fingerprints place every element
+ * alike. */
+int zs_layout_fingerprint(const zs_layout* layout, uint64_t* out);
+
+/* Write this rank's tiled optimizer state and the step counter to `path`.
+ *
+ * state: rows = 3, the [n_tiles][3][ZS_TILE] state of zs_step (master, m,
+ *   v); rows = 2, the [n_tiles][2][ZS_TILE] state of zs_step_bf16 (m, v).
+ * step: the counter t of the last completed step (>= 0).
+ * Synchronises hip_stream first (the state must be final), then copies the
+ * state to the file through two pinned host staging buffers of 64 MiB
+ * (allocated for the call), overlapping the device copies with the file
+ * writes.  The file is written as path + ".tmp", flushed to disk and then
+ * renamed over `path`, so an interrupted save leaves an earlier checkpoint
+ * at `path` intact.
+ * Format (little-endian): a 64-byte header {char magic[8] = "ZSCKPT01";
+ * uint32 version = 1; uint32 rows; uint64 fingerprint; int64 step;
+ * int64 n_tiles; int64 shard_numel; int32 world; int32 rank; uint64 payload
+ * bytes}, the payload (the tiled state as it sits in device memory), then a
+ * uint64 checksum of the payload: h = 0xcbf29ce484222325, and for each
+ * little-endian 64-bit word w of it, h = (h ^ w) * 0x100000001b3 (mod 2^64).
+ * Errors: ZS_EINVAL (NULL layout, path or state, rows not 2 or 3, step < 0),
+ * ZS_EALIGN, ZS_EIO, ZS_ENOMEM, ZS_EDEVICE. */
+int zs_checkpoint_save(const zs_layout* layout, const char* path,
+                       const float* state, int32_t rows, int64_t step,
+                       void* hip_stream);
+
+/* Restore a checkpoint written by zs_checkpoint_save into `state` (tiled,
+ * `rows` rows, device memory of the layout's size) and its counter into
+ * *step.  Before any device access it checks the header: ZS_EIO for a file
+ * that cannot be read or is not a checkpoint, ZS_EMISMATCH for one written
+ * for another layout (fingerprint, world, rank, sizes) or another row
+ * count; the state is then untouched.  The payload is copied through pinned
+ * staging on hip_stream and the call returns when the copies are done; the
+ * checksum is checked as the payload streams in, so a truncated or corrupt
+ * payload returns ZS_EIO after the state has been overwritten (restore
+ * another checkpoint).  Errors also: ZS_EINVAL (NULLs, rows), ZS_EALIGN,
+ * ZS_ENOMEM, ZS_EDEVICE. */
+int zs_checkpoint_load(const zs_layout* layout, const char* path,
+                       float* state, int32_t rows, int64_t* step,
+                       void* hip_stream);
 
 /* ---- errors --------------------------------------------------------------- */
 

@@ -1588,6 +1588,78 @@ def test_whole_tensor_bucket_groups_and_gather():
         assert np.all(got[hi - lo:] == 0x5a5a)
 
 
+@pytest.mark.parametrize("tensors", [False, True])
+def test_checkpoint_resume_equals_the_uninterrupted_run(tmp_path, tensors):
+    """Two steps, save, the state destroyed, restore, a third step: each
+    step checked against the oracle, whose run is never interrupted, bit
+    for bit; the restored state equals the saved one; another rank's layout
+    is refused and its state left as it was."""
+    W, rank = 3, 1
+    say(f"case checkpoint W={W} rank={rank} tensors={tensors}")
+    c = Case(TENSOR_LIST, W, rank, layout="tiled", tensors=tensors,
+             warm=(1e-4, 1e-8), seed=7)
+    c.step(1)
+    c.step(2)
+    torch.cuda.synchronize()
+    snap = c.state.clone()
+    path = tmp_path / "rank1.zsck"
+    zs.zs_checkpoint_save(c.lay, path, c.state, step=2)
+    assert path.exists() and not (tmp_path / "rank1.zsck.tmp").exists()
+    c.state.fill_(float("nan"))
+    build = zs.zs_layout_build_tensors if tensors else zs.zs_layout_build
+    other = build(TENSOR_LIST, W, 2)
+    other_state = dev_f32(zs.zs_layout_tiles(other) * 3 * TILE)
+    other_state.fill_(-7.0)
+    with pytest.raises(zs.ZsError) as ei:
+        zs.zs_checkpoint_load(other, path, other_state)
+    assert ei.value.code == zs.ZS_EMISMATCH
+    assert bool((other_state == -7.0).all())
+    assert zs.zs_checkpoint_load(c.lay, path, c.state) == 2
+    torch.cuda.synchronize()
+    assert torch.equal(c.state.view(torch.int32), snap.view(torch.int32))
+    c.step(3)
+
+
+def test_checkpoint_pure_bf16_large_and_damaged(tmp_path):
+    """The two-row state of the pure-bf16 step at GPT-2 size (187 MB with
+    three rows, over three staging pieces): round trips bit for bit;
+    a row-count mismatch is refused; a later save replaces an earlier one;
+    a flipped payload byte or a truncated file fails the load."""
+    w = wl.presets()["gpt2"]
+    lay_o = build_layout(w.numels, w.world, 0)
+    lay = zs.zs_layout_build(w.numels, w.world, 0)
+    say(f"case checkpoint gpt2 tiles={lay_o.n_tiles}")
+    s3 = dev_state(lay, lay_o, 0.02, warm=(1e-4, 1e-8))
+    assert s3.numel() * 4 > 2 * (64 << 20)
+    back = torch.empty_like(s3)
+    back.fill_(float("nan"))
+    path = tmp_path / "gpt2.zsck"
+    zs.zs_checkpoint_save(lay, path, s3, step=11)
+    assert zs.zs_checkpoint_load(lay, path, back) == 11
+    assert torch.equal(back.view(torch.int32), s3.view(torch.int32))
+    # two rows: m and v of the pure-bf16 state
+    s2 = s3[:lay_o.n_tiles * 2 * TILE]
+    zs.zs_checkpoint_save(lay, path, s2, step=12, rows=2)
+    with pytest.raises(zs.ZsError) as ei:
+        zs.zs_checkpoint_load(lay, path, back)
+    assert ei.value.code == zs.ZS_EMISMATCH
+    b2 = back[:lay_o.n_tiles * 2 * TILE]
+    b2.fill_(0.0)
+    assert zs.zs_checkpoint_load(lay, path, b2, rows=2) == 12
+    assert torch.equal(b2.view(torch.int32), s2.view(torch.int32))
+    raw = bytearray(path.read_bytes())
+    assert len(raw) == 64 + s2.numel() * 4 + 8
+    raw[64 + 5 * (64 << 20) // 4] ^= 0x10
+    path.write_bytes(bytes(raw))
+    with pytest.raises(zs.ZsError) as ei:
+        zs.zs_checkpoint_load(lay, path, b2, rows=2)
+    assert ei.value.code == zs.ZS_EIO
+    path.write_bytes(bytes(raw[:-100]))
+    with pytest.raises(zs.ZsError) as ei:
+        zs.zs_checkpoint_load(lay, path, b2, rows=2)
+    assert ei.value.code == zs.ZS_EIO
+
+
 def test_two_runs_are_bit_identical():
     w = wl.presets()["tiny"]
     outs = []

@@ -5,6 +5,8 @@ package is its ctypes binding, with the same names.
 """
 
 from ._zs import (EXPORTS, LIB_PATH, ZS_ACC_ADD, ZS_ACC_FIRST, ZS_ACC_LAST,
+                  ZS_EIO, ZS_EMISMATCH, zs_checkpoint_load,
+                  zs_checkpoint_save, zs_layout_fingerprint,
                   ZS_GATHER_MAX_WORLD, ZS_GRADS_SLICES, ZS_GRADS_TILED,
                   ZS_MAX_GROUP, ZS_TILE, Layout, Prefetch, Stream, ZsError,
                   chunks_bytes, lib, zs_accumulate, zs_adamw, zs_bucket,
@@ -21,6 +23,8 @@ from ._zs import (EXPORTS, LIB_PATH, ZS_ACC_ADD, ZS_ACC_FIRST, ZS_ACC_LAST,
                   zs_strerror)
 
 __all__ = ["EXPORTS", "LIB_PATH", "ZS_ACC_ADD", "ZS_ACC_FIRST", "ZS_ACC_LAST",
+           "ZS_EIO", "ZS_EMISMATCH", "zs_checkpoint_load",
+           "zs_checkpoint_save", "zs_layout_fingerprint",
            "ZS_GATHER_MAX_WORLD", "ZS_GRADS_SLICES", "ZS_GRADS_TILED",
            "ZS_MAX_GROUP", "ZS_TILE", "Layout", "Prefetch", "Stream",
            "ZsError", "chunks_bytes", "lib", "zs_accumulate", "zs_adamw",

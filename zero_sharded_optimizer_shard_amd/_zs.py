@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libzs.so")
 
 ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ERANGE, ZS_ENOMEM, ZS_EDEVICE = \
     0, -1, -2, -3, -4, -5
+ZS_EIO, ZS_EMISMATCH = -6, -7
 ZS_TILE = 8192
 ZS_MAX_GROUP = 16
 ZS_GATHER_MAX_WORLD = 64
@@ -60,6 +61,8 @@ EXPORTS = ["zs_layout_build", "zs_layout_build_tensors", "zs_layout_owners",
            "zs_stream_step_end", "zs_stream_free",
            "zs_prefetch_create", "zs_prefetch_issue", "zs_prefetch_acquire",
            "zs_prefetch_release", "zs_prefetch_free",
+           "zs_layout_fingerprint", "zs_checkpoint_save",
+           "zs_checkpoint_load",
            "zs_strerror", "zs_last_error"]
 
 
@@ -114,6 +117,9 @@ def lib():
     L.zs_prefetch_release.argtypes = [p, i32, p]
     L.zs_prefetch_free.argtypes = [p]
     L.zs_prefetch_free.restype = None
+    L.zs_layout_fingerprint.argtypes = [p, P(ctypes.c_uint64)]
+    L.zs_checkpoint_save.argtypes = [p, ctypes.c_char_p, p, i32, i64, p]
+    L.zs_checkpoint_load.argtypes = [p, ctypes.c_char_p, p, i32, P(i64), p]
     L.zs_strerror.argtypes = [ctypes.c_int]
     L.zs_strerror.restype = ctypes.c_char_p
     L.zs_last_error.argtypes = []
@@ -129,7 +135,9 @@ def lib():
                  "zs_accumulate", "zs_stream_create", "zs_stream_step_begin",
                  "zs_stream_arrive", "zs_stream_step_end",
                  "zs_prefetch_create", "zs_prefetch_issue",
-                 "zs_prefetch_acquire", "zs_prefetch_release"):
+                 "zs_prefetch_acquire", "zs_prefetch_release",
+                 "zs_layout_fingerprint", "zs_checkpoint_save",
+                 "zs_checkpoint_load"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -681,3 +689,42 @@ def zs_prefetch_free(prefetch: Prefetch) -> None:
     if prefetch._h is not None and prefetch._h.value:
         lib().zs_prefetch_free(prefetch._h)
         prefetch._h = None
+
+
+# ---- checkpoint and resume ----------------------------------------------------
+
+def zs_layout_fingerprint(layout: Layout) -> int:
+    """64-bit fingerprint of the layout's defining inputs."""
+    out = ctypes.c_uint64()
+    _check(lib().zs_layout_fingerprint(layout.handle, ctypes.byref(out)),
+           "zs_layout_fingerprint")
+    return out.value
+
+
+def _path(path) -> bytes:
+    return os.fsencode(path)
+
+
+def zs_checkpoint_save(layout: Layout, path, state, step: int, rows: int = 3,
+                       stream=None) -> None:
+    """Write the tiled state (rows 3: master|m|v; 2: m|v) and the step
+    counter to `path`, replacing it atomically."""
+    if rows in (2, 3):
+        _need(state, layout.sizes()[2] * rows * ZS_TILE, "state")
+    _check(lib().zs_checkpoint_save(layout.handle, _path(path),
+                                    _f32(state, "state"), rows, step,
+                                    _stream(stream)), "zs_checkpoint_save")
+
+
+def zs_checkpoint_load(layout: Layout, path, state, rows: int = 3,
+                       stream=None) -> int:
+    """Restore a checkpoint of this layout into the tiled state; returns
+    its step counter."""
+    if rows in (2, 3):
+        _need(state, layout.sizes()[2] * rows * ZS_TILE, "state")
+    step = ctypes.c_int64()
+    _check(lib().zs_checkpoint_load(layout.handle, _path(path),
+                                    _f32(state, "state"), rows,
+                                    ctypes.byref(step), _stream(stream)),
+           "zs_checkpoint_load")
+    return step.value

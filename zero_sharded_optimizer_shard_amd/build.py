@@ -27,7 +27,8 @@ SOURCES = [os.path.join(CSRC, "zs_layout.cpp"),
            os.path.join(CSRC, "zs_gather.hip"),
            os.path.join(CSRC, "zs_accum.hip"),
            os.path.join(CSRC, "zs_stream.cpp"),
-           os.path.join(CSRC, "zs_prefetch.cpp")]
+           os.path.join(CSRC, "zs_prefetch.cpp"),
+           os.path.join(CSRC, "zs_ckpt.cpp")]
 
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",

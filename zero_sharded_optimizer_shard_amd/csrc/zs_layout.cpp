@@ -406,6 +406,32 @@ extern "C" int zs_layout_rank(const zs_layout* L, int32_t* world,
 
 extern "C" void zs_layout_free(zs_layout* L) { delete L; }
 
+extern "C" int zs_layout_fingerprint(const zs_layout* L, uint64_t* out)
+{
+    using zs::fail;
+    zs::clear_error();
+    if (!L || !out) return fail(ZS_EINVAL, "layout or out is NULL");
+    // FNV-1a, 64-bit, over little-endian int64 fields
+    uint64_t h = 0xcbf29ce484222325ull;
+    auto mix = [&h](int64_t v) {
+        const uint64_t u = static_cast<uint64_t>(v);
+        for (int i = 0; i < 8; ++i) {
+            h ^= (u >> (8 * i)) & 0xffu;
+            h *= 0x100000001b3ull;
+        }
+    };
+    mix(L->whole_tensors ? 1 : 0);
+    mix(L->world);
+    mix(L->rank);
+    mix(L->align_elems);
+    mix(L->whole_tensors ? 0 : L->bucket_elems);
+    mix((int64_t)L->tensor_numel.size());
+    for (int64_t n : L->tensor_numel)
+        mix(n);
+    *out = h;
+    return ZS_OK;
+}
+
 extern "C" const char* zs_strerror(int code)
 {
     switch (code) {
@@ -415,6 +441,9 @@ extern "C" const char* zs_strerror(int code)
     case ZS_ERANGE: return "index or size out of range";
     case ZS_ENOMEM: return "host allocation failed";
     case ZS_EDEVICE: return "HIP launch error";
+    case ZS_EIO: return "checkpoint file cannot be read or written, or is "
+                        "not a valid checkpoint";
+    case ZS_EMISMATCH: return "checkpoint written for another layout";
     default: return "unknown error code";
     }
 }
