@@ -31,7 +31,10 @@
 // slice rows; measured on MI355X, that lifts this 2:1 read/write stream
 // from about 5.4 to about 6.4 TB/s.  All loads of a unit are issued before
 // its arithmetic (the W slices in batches of 4 or 8), and every access is
-// non-temporal: nothing is reused.
+// non-temporal: nothing is reused.  The step's stores also carry system
+// scope (sc0 sc1 nt), so the L2 streams them on to HBM instead of holding
+// them as dirty lines: measured on MI355X, 82.0-82.2 % of peak against
+// 80.4 % with plain non-temporal stores on the 8B-shaped W = 8 shard.
 //
 // Grid of the whole-shard step: blockIdx.y = bucket, blockIdx.x = tile
 // (times the workgroups per tile) of that bucket's slice, so no thread
@@ -230,6 +233,35 @@ __device__ __forceinline__ void st4(float* p, f32x4 x)
     __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
 }
 
+// Stores of the step: element jj of a tile row at `row` (wave-uniform) as a
+// raw buffer store, non-temporal with system scope (sc0 sc1 nt).  The
+// descriptor covers the row's ZS_TILE elements only, so the hardware drops
+// any store outside the row.  Word 3 of a gfx9-family buffer descriptor for
+// raw access: DATA_FORMAT = 32 bits (bits 18:15 = 4), all else zero.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kCpolSc0 = 1, kCpolNt = 2, kCpolSc1 = 16;
+constexpr int kStreamOut = kCpolSc0 | kCpolSc1 | kCpolNt;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(void* row,
+                                                          int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(row, 0, bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ void st2_out(uint16_t* row, int jj, u32x2 x)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(
+        x, row_rsrc(row, (int)(kTile * sizeof(uint16_t))),
+        jj * (int)sizeof(uint16_t), 0, kStreamOut);
+}
+
+__device__ __forceinline__ void st4_out(float* row, int jj, f32x4 x)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(
+        x, row_rsrc(row, (int)(kTile * sizeof(float))),
+        jj * (int)sizeof(float), 0, kStreamOut);
+}
+
 struct StepArgs {
     const uint16_t* grads;      // launch base (see zs_step)
     int64_t gstride;            // slices layout: elements between slices
@@ -381,17 +413,17 @@ __device__ __forceinline__ void step_tile(const uint16_t* __restrict__ g0,
             pb[i] = to_bf16(t);
         }
         if constexpr (!PURE)
-            st4(st + jj, f32x4{t4[0], t4[1], t4[2], t4[3]});
-        st4(st + kM * kTile + jj, f32x4{m4[0], m4[1], m4[2], m4[3]});
-        st4(st + (kM + 1) * kTile + jj, f32x4{v4[0], v4[1], v4[2], v4[3]});
+            st4_out(st, jj, f32x4{t4[0], t4[1], t4[2], t4[3]});
+        st4_out(st + kM * kTile, jj, f32x4{m4[0], m4[1], m4[2], m4[3]});
+        st4_out(st + (kM + 1) * kTile, jj, f32x4{v4[0], v4[1], v4[2], v4[3]});
         const u32x2 p = {pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
         if constexpr (PURE) {
-            st2(pp + jj, p);
+            st2_out(pp, jj, p);
         } else {
             if (ps)
-                st2(ps + jj, p);
+                st2_out(ps, jj, p);
             if (fl)
-                st2(fl + jj, p);
+                st2_out(fl, jj, p);
         }
     }
 }
