@@ -51,6 +51,7 @@
 #include <type_traits>
 #include <vector>
 
+#include "zs_device.h"
 #include "zs_internal.h"
 
 namespace {
@@ -233,33 +234,19 @@ __device__ __forceinline__ void st4(float* p, f32x4 x)
     __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
 }
 
-// Stores of the step: element jj of a tile row at `row` (wave-uniform) as a
-// raw buffer store, non-temporal with system scope (sc0 sc1 nt).  The
-// descriptor covers the row's ZS_TILE elements only, so the hardware drops
-// any store outside the row.  Word 3 of a gfx9-family buffer descriptor for
-// raw access: DATA_FORMAT = 32 bits (bits 18:15 = 4), all else zero.
-constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kCpolSc0 = 1, kCpolNt = 2, kCpolSc1 = 16;
-constexpr int kStreamOut = kCpolSc0 | kCpolSc1 | kCpolNt;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(void* row,
-                                                          int bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(row, 0, bytes, kRsrcWord3);
-}
-
+// Stores of the step: element jj of a tile row at `row` (wave-uniform),
+// streamed on to HBM (zsdev::stream_store); the region is the row's ZS_TILE
+// elements, so the hardware drops any store outside the row.
 __device__ __forceinline__ void st2_out(uint16_t* row, int jj, u32x2 x)
 {
-    __builtin_amdgcn_raw_buffer_store_b64(
-        x, row_rsrc(row, (int)(kTile * sizeof(uint16_t))),
-        jj * (int)sizeof(uint16_t), 0, kStreamOut);
+    zsdev::stream_store(row, (uint32_t)(kTile * sizeof(uint16_t)),
+                        (uint32_t)jj * (uint32_t)sizeof(uint16_t), x);
 }
 
 __device__ __forceinline__ void st4_out(float* row, int jj, f32x4 x)
 {
-    __builtin_amdgcn_raw_buffer_store_b128(
-        x, row_rsrc(row, (int)(kTile * sizeof(float))),
-        jj * (int)sizeof(float), 0, kStreamOut);
+    zsdev::stream_store(row, (uint32_t)(kTile * sizeof(float)),
+                        (uint32_t)jj * (uint32_t)sizeof(float), x);
 }
 
 struct StepArgs {
