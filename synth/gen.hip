@@ -215,8 +215,24 @@ extern "C" int synth_read_dev(const void* src, int64_t nbytes, void* sink,
  * 4-element units per thread at stride 512 units; reads W tiled gradient
  * rows (8 B per unit each) and the three tiled fp32 state rows (16 B per
  * unit each), writes the three state rows back and 8 B per unit of bf16
- * into the flat buffer at the rank-0 position of the bucket. */
+ * into the flat buffer at the rank-0 position of the bucket.  Loads are
+ * non-temporal; stores, like the step's, are non-temporal raw buffer stores
+ * with system scope (cache-policy bits sc0 = 1, nt = 2, sc1 = 16), each
+ * through a descriptor over its 8192-element row (descriptor word 3 for raw
+ * access on gfx9-family GPUs: 32-bit data format, 0x00020000). */
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <class T>
+__device__ static inline void mix_store(void* row, unsigned bytes,
+                                        unsigned off, T x)
+{
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(row, 0, (int)bytes, 0x00020000);
+    if constexpr (sizeof(T) == 16)
+        __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)off, 0, 1 | 2 | 16);
+    else
+        __builtin_amdgcn_raw_buffer_store_b64(x, r, (int)off, 0, 1 | 2 | 16);
+}
 
 template <int WT, int NB>
 __global__ __launch_bounds__(512) void k_mix_stream(
@@ -277,11 +293,10 @@ __global__ __launch_bounds__(512) void k_mix_stream(
         a[k] ^= xx;
         b[k] ^= a[k];
         c[k] ^= b[k];
-        __builtin_nontemporal_store(a[k], st + u);
-        __builtin_nontemporal_store(b[k], st + 2048 + u);
-        __builtin_nontemporal_store(c[k], st + 4096 + u);
-        __builtin_nontemporal_store(u32x2{c[k].x ^ c[k].z, c[k].y ^ c[k].w},
-                                    f + u);
+        mix_store(st, 32768u, 16u * u, a[k]);
+        mix_store(st + 2048, 32768u, 16u * u, b[k]);
+        mix_store(st + 4096, 32768u, 16u * u, c[k]);
+        mix_store(f, 16384u, 8u * u, u32x2{c[k].x ^ c[k].z, c[k].y ^ c[k].w});
     }
 }
 
