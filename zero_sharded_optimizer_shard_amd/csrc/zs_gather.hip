@@ -10,11 +10,14 @@
 // the flat buffer, inside bucket q at offset k, comes from rank
 // r = k / slice_q, element q*S + k - r*slice_q of its shard.
 //
-// The kernel pulls: each workgroup copies one 4096-element chunk of one
-// (bucket, rank) slice, clipped to the requested range, from that rank's
-// shard to the output: 8 KiB per workgroup, two 16-byte accesses per thread
-// (on MI355X this beat chunks of 8-32 KiB by 6-12 points of HBM bandwidth
-// over the 34 gathers of a Llama-3-8B-shaped forward).  On one GPU the W
+// The kernel pulls: each workgroup, a single wave64, copies one
+// 1024-element chunk of one (bucket, rank) slice, clipped to the requested
+// range, from that rank's shard to the output: 2 KiB per workgroup, two
+// 16-byte accesses per thread.  Measured on MI355X over the 34 gathers of a
+// Llama-3-8B-shaped forward: 82.1 % of peak HBM bandwidth, against 81.7 %
+// with 128-thread workgroups, 79.1 % with 256 and 76.0 % with 512 (two
+// accesses per thread each); one or four accesses per thread were slower
+// (76.6-79.4 %), and larger chunks slower still.  On one GPU the W
 // shards are W resident buffers; on a node they would be peer-mapped shards
 // of the other GPUs read over xGMI.  2 B read + 2 B written per element,
 // 16-byte non-temporal accesses except at a ragged end; bounded by HBM
@@ -31,10 +34,15 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 64;                     // one wave per workgroup
 constexpr int kVec = 8;                         // bf16 per 16-byte access
 constexpr int kPerThread = 2;                   // accesses per thread
-constexpr int64_t kChunk = (int64_t)kThreads * kVec * kPerThread;  // 4096
+constexpr int64_t kChunk = (int64_t)kThreads * kVec * kPerThread;  // 1024
+// the largest slice the layouts allow (kMaxLaunchTiles tiles) fits one
+// launch: fewer than 2^32 work-items along x
+static_assert((kMaxLaunchTiles * ZS_TILE + kChunk - 1) / kChunk * kThreads <
+                  (int64_t(1) << 32),
+              "a slice's chunks fit one launch");
 constexpr int kMaxGatherWorld = ZS_GATHER_MAX_WORLD;
 constexpr int64_t kMaxGridY = 65535;
 
