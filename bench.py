@@ -42,7 +42,7 @@ METRIC = ("optimizer-step params/s per GPU + achieved HBM GB/s (% of peak), "
 KERNELS = os.path.join(ROOT, "zero_sharded_optimizer_shard_amd",
                        "libzs.kernels.json")
 # the kernel whose HBM counters the roofline's traffic figure comes from
-HEADLINE_KERNEL = ("_ZN12_GLOBAL__N_111step_kernelILi8ELb1ENS_5ShapeILi512ELi4E"
+HEADLINE_KERNEL = ("_ZN12_GLOBAL__N_111step_kernelILi8ELb1ENS_5ShapeILi64ELi1E"
                    "Li4EEELb0EEEvNS_8StepArgsE")
 
 
@@ -120,7 +120,7 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int) -> dict:
     wr = avg(tw) * 1024 * ws
     alg = (2 * W + 26) * n
     rec = {
-        "kernel": f"step_kernel<{W}, true, Shape<512, 4, 4> > (zs_step, "
+        "kernel": f"step_kernel<{W}, true, Shape<64, 1, 4> > (zs_step, "
                   "tiled gradients, tiled state, flat output)",
         "workload": f"llama8b rank-0 shard, W={W}, {n:,} elements",
         "kernel_symbol": HEADLINE_KERNEL,

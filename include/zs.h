@@ -111,8 +111,8 @@ typedef struct {
  * Errors: ZS_EINVAL for null out/tensor_numel (when n_tensors > 0),
  * n_tensors < 0, numel < 0, world < 1, rank outside [0, world),
  * bad align_bytes, or 0 < bucket_cap_bytes < world*align_bytes;
- * ZS_ERANGE on int64 overflow or a bucket slice above 2^23 - 1 tiles
- * (68.7 G elements, the most one kernel launch covers); ZS_ENOMEM. */
+ * ZS_ERANGE on int64 overflow or a bucket slice above 2^21 - 1 tiles
+ * (17.2 G elements, the most one kernel launch covers); ZS_ENOMEM. */
 int zs_layout_build(const int64_t* tensor_numel, int32_t n_tensors,
                     int32_t world, int32_t rank, int64_t bucket_cap_bytes,
                     int32_t align_bytes, zs_layout** out);
@@ -136,7 +136,7 @@ int zs_layout_build(const int64_t* tensor_numel, int32_t n_tensors,
  * the owned tensors arrive as the [W][...] slices of this shard) and the
  * all-gather a broadcast from the owner: zs_step, zs_step_bf16, the bucket
  * steps, the conversions, zs_pack and zs_gather all accept such a layout.
- * Errors as zs_layout_build (the 2^23 - 1 tile limit applies to each
+ * Errors as zs_layout_build (the 2^21 - 1 tile limit applies to each
  * tensor). */
 int zs_layout_build_tensors(const int64_t* tensor_numel, int32_t n_tensors,
                             int32_t world, int32_t rank, int32_t align_bytes,

@@ -105,5 +105,5 @@ def test_c_client_errors(client):
     assert got["error"][0][0] == "-1"
     got = run(client, "flat", 2, 0, 0, 100, [10])          # align % 16
     assert got["error"][0][0] == "-1"
-    got = run(client, "tensors", 1, 0, 0, 256, [(2 ** 23) * 8192])
+    got = run(client, "tensors", 1, 0, 0, 256, [(2 ** 21) * 8192])
     assert got["error"][0][0] == "-3"                      # launch limit

@@ -139,10 +139,11 @@ def test_tensor_layout_errors():
 
 def test_launch_size_limits():
     """A bucket slice (a whole tensor in the whole-tensor mode) beyond
-    2^23 - 1 tiles of 8192 elements would need a launch of 2^32 work-items
-    or more: both builders refuse it; one tile less is accepted."""
+    2^21 - 1 tiles of 8192 elements would need a launch of 2^32 work-items
+    or more (2048 threads per tile): both builders refuse it; the limit
+    itself is accepted."""
     tile = 8192
-    lim = (2 ** 23 - 1) * tile
+    lim = (2 ** 21 - 1) * tile
     cap = 1 << 62
     lay = zs.zs_layout_build([lim], 1, 0, cap)
     assert zs.zs_layout_info(lay)[1] == lim

@@ -103,7 +103,7 @@ def test_sanitized_error_paths(client):
              ("flat", 8, 0, 1000, 256, [5], "-1"),     # cap below W*align
              ("flat", 2, 0, 0, 256, [big, big], "-3"),  # int64 overflow
              ("tensors", 2, 0, 0, 256, [big, big], "-3"),
-             ("tensors", 1, 0, 0, 256, [2 ** 23 * 8192], "-3")]  # launch
+             ("tensors", 1, 0, 0, 256, [2 ** 21 * 8192], "-3")]  # launch
     for mode, world, rank, cap, align, numels, code in cases:
         got = run(client, mode, world, rank, cap, align, numels)
         assert got["error"][0][0] == code, (mode, world, numels, got)

@@ -324,11 +324,12 @@ def test_hyperparameter_edge_cases(name, hp, steps):
 
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("W,tiles", [(2, 300), (2, 4200), (32, 4100),
-                                     (5, 4100), (5, 1100)])
+                                     (5, 4100), (5, 1100), (33, 4100)])
 def test_launch_shapes(W, tiles, layout):
     """Each work shape of the step: fewer than 4096 tiles (four workgroups
-    per tile), 4096 or more at W <= 16, at W >= 32, and the runtime-W
-    kernel on both sides; one bucket per launch, a ragged last tile."""
+    per tile), 4096 or more at W < 32 (one-wave workgroups, compiled and
+    runtime W), at W >= 32 (compiled), and the runtime-W kernel at W >= 32
+    (512-thread workgroups); one bucket per launch, a ragged last tile."""
     n_rank = tiles * TILE - 4096            # the last tile half full
     numels = [W * n_rank - 1000, 1000]
     say(f"case shape W={W} tiles={tiles} {layout}")
@@ -918,10 +919,11 @@ def test_pure_bf16_step(W, layout, flat_params):
 
 
 @pytest.mark.parametrize("W,tiles", [(2, 300), (2, 4200), (8, 4100),
-                                     (5, 4100), (32, 4100)])
+                                     (5, 4100), (32, 4100), (33, 4100)])
 def test_pure_bf16_launch_shapes(W, tiles):
     """Each work shape of the pure-bf16 step: fewer than 4096 tiles, 4096 or
-    more at W < 32 (its own shape), at W >= 32, and the runtime-W kernel;
+    more at W < 32 (one-wave workgroups), at W >= 32, and the runtime-W
+    kernel at W < 32 and W >= 32 (256-thread workgroups);
     one bucket, a ragged last tile, parameters in place in the flat
     buffer, tiled gradients; bit for bit against the oracle."""
     n_rank = tiles * TILE - 4096            # the last tile half full

@@ -27,12 +27,13 @@ struct zs_layout {
     std::vector<int64_t> owner_shard_off;  // per tensor, in the owner's shard
 };
 
-// Most tiles one kernel launch covers: launches put one 512-thread
-// workgroup per tile along x, and HIP allows fewer than 2^32 work-items
-// there.  A bucket slice (a whole tensor in the whole-tensor mode) is at
-// most this many tiles, 68.7 G elements; group launches end a group early
-// rather than pass it.
-constexpr int64_t kMaxLaunchTiles = (int64_t(1) << 23) - 1;
+// Most tiles one kernel launch covers: the step's work shapes put up to
+// 2048 threads per tile along x (32 one-wave workgroups, or 4 of 512
+// threads), and HIP allows fewer than 2^32 work-items there.  A bucket
+// slice (a whole tensor in the whole-tensor mode) is at most this many
+// tiles, 17.2 G elements; group launches end a group early rather than pass
+// it.
+constexpr int64_t kMaxLaunchTiles = (int64_t(1) << 21) - 1;
 
 // Flat position of this rank's slice of bucket b.
 inline int64_t slice_flat_pos(const zs_layout* L, const zs_bucket& b)

@@ -798,41 +798,55 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
         launch_kernel<WT, false, SH, PURE>(a, grid, s);
 }
 
-// Work shapes, chosen by measurement on MI355X (8B-shaped shard at W = 8
-// and 16, 7B-shaped at W = 64, 70B-shaped bucket groups at W = 16):
-//  - Wide: one 512-thread workgroup per tile, 4 units per thread, slices
-//    loaded 4 at a time: 112 VGPRs at W = 8, so two workgroups share a CU;
-//  - Deep (W >= 32, where gradients are most of the bytes): slices loaded
-//    8 at a time, more loads in flight per thread, one workgroup per CU;
+// Work shapes, chosen by measurement on MI355X (8B-shaped shard at W = 4,
+// 5, 8 and 16, 7B-shaped at W = 32, 64 and 100, 70B-shaped bucket groups at
+// W = 16):
+//  - Wave (W < 32, mixed and pure-bf16): one wave per workgroup, one unit
+//    per thread, 32 workgroups per tile: 82-83 % of peak at W = 4, 5, 8 and
+//    16, against 80-81 % for 512-thread workgroups of four units (67 % for
+//    the runtime-W kernel at W = 5); pure bf16 at W = 8 82.6 % vs 80.5 %;
+//  - Deep (W >= 32): 512-thread workgroups, slices loaded 8 at a time, one
+//    workgroup per CU (148 VGPRs): 79-80 % at W = 64, where one-wave shapes
+//    measured 72-79 %;
+//  - Wide / PureWide (runtime W >= 32): 512-thread workgroups of four units
+//    (256 for the two-row pure state): 79-80 % at W = 100, against 75-78 %
+//    with one-wave workgroups;
 //  - Small (launches of fewer than kSmallLaunch tiles: bucket groups of a
 //    streaming step, GPT-2-sized shards): one unit per thread and four
 //    workgroups per tile, so that a few hundred or thousand tiles still
 //    spread evenly over the 256 CUs with a short tail (GPT-2-shaped W = 8
-//    shard, 1899 tiles: 81 % vs 75 % with Wide; at 122 K tiles the two
-//    are equal);
-//  - PureWide (the pure-bf16 step at W < 32, where the state is two rows):
-//    256-thread workgroups, two per tile, 4 units per thread: 80-81 % vs
-//    78-79 % with Wide at W = 4, 8 and 16 on the 8B-shaped shard (at
-//    W = 64 Deep stays ahead).
+//    shard, 1899 tiles: 81 % vs 75 % with Wide).
+using ShapeWave = Shape<64, 1, 4>;
 using ShapeWide = Shape<512, 4, 4>;
 using ShapeDeep = Shape<512, 4, 8>;
 using ShapeSmall = Shape<512, 1, 4>;
 using ShapePureWide = Shape<256, 4, 4>;
 constexpr int64_t kSmallLaunch = 4096;
+// every shape stays within the launch limit of kMaxLaunchTiles tiles
+static_assert(kMaxLaunchTiles * ShapeWave::P * ShapeWave::NT <
+                  (int64_t(1) << 32) &&
+              kMaxLaunchTiles * ShapeSmall::P * ShapeSmall::NT <
+                  (int64_t(1) << 32),
+              "one launch row of tiles fits the grid");
 
 // grid: one x per tile (launch_kernel multiplies by the shape's P)
 template <int WT, bool PURE, class Args>
 void launch_step_w(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 {
     const int64_t tiles = (int64_t)grid.x * grid.y;
-    if (tiles < kSmallLaunch)
+    if (tiles < kSmallLaunch) {
         launch_shape<WT, ShapeSmall, PURE>(a, tiled, grid, s);
-    else if constexpr (WT >= 32)
+    } else if constexpr (WT >= 32) {
         launch_shape<WT, ShapeDeep, PURE>(a, tiled, grid, s);
-    else if constexpr (PURE)
+    } else if constexpr (WT > 0) {
+        launch_shape<WT, ShapeWave, PURE>(a, tiled, grid, s);
+    } else if (a.W < 32) {                  // runtime W
+        launch_shape<WT, ShapeWave, PURE>(a, tiled, grid, s);
+    } else if constexpr (PURE) {
         launch_shape<WT, ShapePureWide, PURE>(a, tiled, grid, s);
-    else
+    } else {
         launch_shape<WT, ShapeWide, PURE>(a, tiled, grid, s);
+    }
 }
 
 template <bool PURE = false, class Args>
