@@ -20,13 +20,13 @@
 //   p   = bf16 of th, round to nearest even
 //
 // Work decomposition.  The shard is cut into tiles of ZS_TILE = 8192
-// elements of one bucket's slice.  A tile is owned by one 512-thread
-// workgroup (8 wave64s) whose threads each own four 4-element units at
-// stride 512 units, or, in launches of few tiles, by four workgroups of
-// one unit per thread (the pure-bf16 step: two 256-thread workgroups of
-// four units); either way every load or store instruction of a wave
-// covers one contiguous run (1 KiB of fp32, 512 B of bf16) and a tile's
-// rows are swept in 8-32 KiB bursts.  With the tiled state the three 32 KiB
+// elements of one bucket's slice.  Below W = 32 a tile is stepped by 32
+// one-wave workgroups of one 4-element unit per thread; at W >= 32 by one
+// 512-thread workgroup (8 wave64s) whose threads each own four units at
+// stride 512 units; in launches of few tiles by four 512-thread workgroups
+// of one unit per thread (the work shapes are chosen below).  Either way
+// every load or store instruction of a wave covers one contiguous run
+// (1 KiB of fp32, 512 B of bf16) and a tile's rows are swept in bursts.  With the tiled state the three 32 KiB
 // rows of a tile are adjacent, and with tiled gradients so are the W 16 KiB
 // slice rows; measured on MI355X, that lifts this 2:1 read/write stream
 // from about 5.4 to about 6.4 TB/s.  All loads of a unit are issued before
