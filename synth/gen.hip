@@ -210,12 +210,13 @@ extern "C" int synth_read_dev(const void* src, int64_t nbytes, void* sink,
     return finish();
 }
 
-/* The step's access pattern with integer XORs in place of the arithmetic:
- * one 512-thread workgroup per 8192-element tile of a bucket slice, four
- * 4-element units per thread at stride 512 units; reads W tiled gradient
- * rows (8 B per unit each) and the three tiled fp32 state rows (16 B per
- * unit each), writes the three state rows back and 8 B per unit of bf16
- * into the flat buffer at the rank-0 position of the bucket.  Loads are
+/* The step's access pattern with integer XORs in place of the arithmetic,
+ * in the step's work shape below W = 32: 32 one-wave workgroups per
+ * 8192-element tile of a bucket slice (blockIdx.x = tile * 32 + part), one
+ * 4-element unit per thread; reads W tiled gradient rows (8 B per unit each,
+ * in batches of NB) and the three tiled fp32 state rows (16 B per unit
+ * each), writes the three state rows back and 8 B per unit of bf16 into the
+ * flat buffer at the rank-0 position of the bucket.  Loads are
  * non-temporal; stores, like the step's, are non-temporal raw buffer stores
  * with system scope (cache-policy bits sc0 = 1, nt = 2, sc1 = 16), each
  * through a descriptor over its 8192-element row (descriptor word 3 for raw
@@ -235,7 +236,7 @@ __device__ static inline void mix_store(void* row, unsigned bytes,
 }
 
 template <int WT, int NB>
-__global__ __launch_bounds__(512) void k_mix_stream(
+__global__ __launch_bounds__(64) void k_mix_stream(
     const u32x2* __restrict__ grads, u32x4* __restrict__ state,
     u32x2* __restrict__ flat, int Wrt, int64_t S, int64_t S_last, int64_t B,
     int64_t tpb, int q_last)
@@ -243,61 +244,44 @@ __global__ __launch_bounds__(512) void k_mix_stream(
     const int W = WT > 0 ? WT : Wrt;
     const int q = blockIdx.y;
     const int64_t slice = q == q_last ? S_last : S;
-    const int64_t j0 = (int64_t)blockIdx.x * 8192;
+    const int64_t x = blockIdx.x / 32;
+    const int part = (int)(blockIdx.x % 32);
+    const int64_t j0 = x * 8192;
     if (j0 >= slice)
         return;
-    const int64_t tile = (int64_t)q * tpb + blockIdx.x;
+    const int64_t tile = (int64_t)q * tpb + x;
     const int64_t nv = slice - j0 < 8192 ? slice - j0 : 8192;
     const u32x2* g = grads + tile * W * 2048;
     u32x4* st = state + tile * 3 * 2048;
     u32x2* f = flat + ((int64_t)q * B + j0) / 4;
-    u32x4 a[4], b[4], c[4];
-    u32x2 x[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int u = k * 512 + threadIdx.x;
-        if (4 * u < nv) {
-            a[k] = __builtin_nontemporal_load(st + u);
-            b[k] = __builtin_nontemporal_load(st + 2048 + u);
-            c[k] = __builtin_nontemporal_load(st + 4096 + u);
-        }
-        x[k] = u32x2{0u, 0u};
-    }
+    const int u = part * 64 + (int)threadIdx.x;      /* unit of the tile */
+    if (4 * u >= nv)
+        return;
+    const u32x4 a0 = __builtin_nontemporal_load(st + u);
+    const u32x4 b0 = __builtin_nontemporal_load(st + 2048 + u);
+    const u32x4 c0 = __builtin_nontemporal_load(st + 4096 + u);
+    u32x2 xx = u32x2{0u, 0u};
     /* slices in batches of NB, all loads of a batch issued before use */
     for (int s0 = 0; s0 < W; s0 += NB) {
-        u32x2 y[4][NB];
+        u32x2 y[NB];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int u = k * 512 + threadIdx.x;
+        for (int i = 0; i < NB; ++i)
+            if (s0 + i < W)
+                y[i] = __builtin_nontemporal_load(
+                    g + (int64_t)(s0 + i) * 2048 + u);
 #pragma unroll
-            for (int i = 0; i < NB; ++i)
-                if (4 * u < nv && s0 + i < W)
-                    y[k][i] = __builtin_nontemporal_load(
-                        g + (int64_t)(s0 + i) * 2048 + u);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int u = k * 512 + threadIdx.x;
-#pragma unroll
-            for (int i = 0; i < NB; ++i)
-                if (4 * u < nv && s0 + i < W)
-                    x[k] ^= y[k][i];
-        }
+        for (int i = 0; i < NB; ++i)
+            if (s0 + i < W)
+                xx ^= y[i];
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int u = k * 512 + threadIdx.x;
-        if (4 * u >= nv)
-            continue;
-        const u32x4 xx = {x[k].x, x[k].y, x[k].x, x[k].y};
-        a[k] ^= xx;
-        b[k] ^= a[k];
-        c[k] ^= b[k];
-        mix_store(st, 32768u, 16u * u, a[k]);
-        mix_store(st + 2048, 32768u, 16u * u, b[k]);
-        mix_store(st + 4096, 32768u, 16u * u, c[k]);
-        mix_store(f, 16384u, 8u * u, u32x2{c[k].x ^ c[k].z, c[k].y ^ c[k].w});
-    }
+    const u32x4 x4 = {xx.x, xx.y, xx.x, xx.y};
+    const u32x4 a = a0 ^ x4;
+    const u32x4 b = b0 ^ a;
+    const u32x4 c = c0 ^ b;
+    mix_store(st, 32768u, 16u * u, a);
+    mix_store(st + 2048, 32768u, 16u * u, b);
+    mix_store(st + 4096, 32768u, 16u * u, c);
+    mix_store(f, 16384u, 8u * u, u32x2{c.x ^ c.z, c.y ^ c.w});
 }
 
 /* grads: tiled [tiles][W][8192] bf16; state: tiled [tiles][3][8192] fp32;
@@ -316,24 +300,25 @@ extern "C" int synth_mix_stream_dev(const void* grads, void* state,
     if (((uintptr_t)grads | (uintptr_t)state | (uintptr_t)flat) & 15u)
         return -2;
     const int64_t tpb = (S + 8191) / 8192;
-    /* the step's shapes: slices 4 at a time up to W = 16, 8 above */
+    /* fewer than 2^32 work-items along x */
+    if (tpb * 32 * 64 >= ((int64_t)1 << 32)) return -3;
+    const dim3 grid((unsigned)(tpb * 32), (unsigned)nb);
+    /* slices 4 at a time below W = 32, 8 above; at W >= 32 the step itself
+     * runs 512-thread workgroups, so there this is the one-wave reference */
     if (W == 8)
-        hipLaunchKernelGGL((k_mix_stream<8, 4>),
-                           dim3((unsigned)tpb, (unsigned)nb),
-                           dim3(512), 0, (hipStream_t)stream,
-                           (const u32x2*)grads, (u32x4*)state, (u32x2*)flat,
-                           (int)W, S, S_last, B, tpb, nb - 1);
-    else if (W <= 16)
-        hipLaunchKernelGGL((k_mix_stream<0, 4>),
-                           dim3((unsigned)tpb, (unsigned)nb),
-                           dim3(512), 0, (hipStream_t)stream,
-                           (const u32x2*)grads, (u32x4*)state, (u32x2*)flat,
-                           (int)W, S, S_last, B, tpb, nb - 1);
+        hipLaunchKernelGGL((k_mix_stream<8, 4>), grid, dim3(64), 0,
+                           (hipStream_t)stream, (const u32x2*)grads,
+                           (u32x4*)state, (u32x2*)flat, (int)W, S, S_last, B,
+                           tpb, nb - 1);
+    else if (W < 32)
+        hipLaunchKernelGGL((k_mix_stream<0, 4>), grid, dim3(64), 0,
+                           (hipStream_t)stream, (const u32x2*)grads,
+                           (u32x4*)state, (u32x2*)flat, (int)W, S, S_last, B,
+                           tpb, nb - 1);
     else
-        hipLaunchKernelGGL((k_mix_stream<0, 8>),
-                           dim3((unsigned)tpb, (unsigned)nb),
-                           dim3(512), 0, (hipStream_t)stream,
-                           (const u32x2*)grads, (u32x4*)state, (u32x2*)flat,
-                           (int)W, S, S_last, B, tpb, nb - 1);
+        hipLaunchKernelGGL((k_mix_stream<0, 8>), grid, dim3(64), 0,
+                           (hipStream_t)stream, (const u32x2*)grads,
+                           (u32x4*)state, (u32x2*)flat, (int)W, S, S_last, B,
+                           tpb, nb - 1);
     return finish();
 }
