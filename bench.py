@@ -220,12 +220,13 @@ def arena_views(parts):
 
     parts: (numel, dtype) pairs; each view starts on a 2 MiB boundary of the
     arena.  The step's bandwidth on MI355X depends on where its buffers land
-    in HBM.  Over 19 processes on three devices, one arena holding the tiled
-    gradients, then the state, then the flat buffer measured 78.8-81.3 % of
-    peak (median 80.7 %).  Separate allocations measured 76.1-81.1 % over 14
-    processes (median 78.4 %), the lowest in processes started after others
-    had used the device.  The other three region orders inside one arena
-    measured 77.4-79.8 %."""
+    in HBM.  With the earlier form of the step (512-thread workgroups, plain
+    non-temporal stores), over 19 processes on three devices, one arena
+    holding the tiled gradients, then the state, then the flat buffer
+    measured 78.8-81.3 % of peak (median 80.7 %).  Separate allocations
+    measured 76.1-81.1 % over 14 processes (median 78.4 %), the lowest in
+    processes started after others had used the device.  The other three
+    region orders inside one arena measured 77.4-79.8 %."""
     import torch
     align = 2 << 20
     offs, total = [], 0

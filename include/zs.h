@@ -295,7 +295,7 @@ int zs_state_unpack(const zs_layout* layout, const float* state,
  * [n] (ZS_ACC_LAST only, may alias grad).  n: a multiple of 4; acc
  * 16-byte aligned, grad and out 8-byte aligned; k >= 2 for ZS_ACC_LAST.
  * Errors: ZS_EINVAL (mode, pointers, k), ZS_EALIGN (alignment, n),
- * ZS_ERANGE (n above 2^34 - 2^11, more than one launch covers). */
+ * ZS_ERANGE (n above 2^34 - 2^8, more than one launch covers). */
 #define ZS_ACC_FIRST 0
 #define ZS_ACC_ADD   1
 #define ZS_ACC_LAST  2
