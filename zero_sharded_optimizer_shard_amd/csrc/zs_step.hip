@@ -634,8 +634,15 @@ __global__ __launch_bounds__(kPackNT) void pack_flat_kernel(
 }
 
 // ---- pack: shard -> per-tensor storage through the chunk table -------------
+//
+// One-wave workgroups, up to kPackGridX of them per chunk striding over it,
+// 8 elements per thread and step.  Measured on MI355X (the 8B-shaped W = 8
+// shard's 650 chunks): 0.60 ms, 6.67 TB/s, against 0.65 ms with 256-thread
+// workgroups and at most 256 per chunk (64 threads and 256 per chunk:
+// 0.67-0.74 ms; 256 threads and 4096: 0.64 ms).
 
-constexpr int kPackThreads = 256;
+constexpr int kPackThreads = 64;
+constexpr int64_t kPackGridX = 4096;
 constexpr int kPackGroup = 8;
 constexpr int64_t kPackTile = kPackThreads * kPackGroup;
 
@@ -1288,7 +1295,7 @@ extern "C" int zs_pack(const zs_layout* L, const uint16_t* param_shard,
         for (const zs_chunk& c : L->chunks)
             longest = c.numel > longest ? c.numel : longest;
         int64_t gx = (longest + kPackTile - 1) / kPackTile;
-        if (gx > 256) gx = 256;
+        if (gx > kPackGridX) gx = kPackGridX;
         for (int32_t c0 = 0; c0 < n_chunks; c0 += (int32_t)kMaxGridY) {
             const int32_t ny = n_chunks - c0 < kMaxGridY ? n_chunks - c0
                                                          : (int32_t)kMaxGridY;
