@@ -178,10 +178,10 @@ void zs_layout_free(zs_layout* layout);
 /* A tile is ZS_TILE consecutive elements of one bucket's slice: slice
  * element j of bucket b lies in tile b.tile_off + j / ZS_TILE at position
  * j % ZS_TILE; a slice's last tile is padded when slice_numel is not a
- * multiple of ZS_TILE.  One workgroup of the step owns one tile, and the
- * tiled layouts keep everything that workgroup reads or writes in a few
- * long contiguous runs, which is what keeps a read/write stream of this mix
- * near the HBM peak on MI355X. */
+ * multiple of ZS_TILE.  The step works tile by tile (one workgroup, or a
+ * fixed set of workgroups, per tile), and the tiled layouts keep everything
+ * a tile reads or writes in a few long contiguous runs, which is what keeps
+ * a read/write stream of this mix near the HBM peak on MI355X. */
 #define ZS_TILE 8192
 
 /* Optimizer state, tiled (the layout zs_step works on): fp32
