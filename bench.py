@@ -393,6 +393,81 @@ def bf16_main(args, w):
     print(json.dumps(out), flush=True)
 
 
+def checkpoint_main(args, w):
+    """Checkpoint and resume of the rank's tiled optimizer state
+    (zs_checkpoint_save / zs_checkpoint_load) at the workload's full size:
+    each save ends with the file flushed to disk and renamed into place; each
+    load restores into a second buffer, which must equal the saved state bit
+    for bit.  The file goes to a temporary directory and is removed."""
+    import shutil
+    import tempfile
+    import time
+
+    import torch
+    import synth
+    import zero_sharded_optimizer_shard_amd as zs
+    W = w.world
+    lay = zs.zs_layout_build(w.numels, W, w.rank)
+    n_tiles = zs.zs_layout_tiles(lay)
+    state = torch.empty(n_tiles * 3 * zs.ZS_TILE, dtype=torch.float32,
+                        device="cuda")
+    synth.dev_normal_f32(state, 0, synth.TAG_MASTER, 0, 0, 0, w.master_sigma)
+    back = torch.empty_like(state)
+    nbytes = state.numel() * 4
+    log(f"checkpoint: {w.name} rank-0 tiled state, {nbytes / 1e9:.2f} GB")
+    d = tempfile.mkdtemp(prefix="zsck-")
+    path = os.path.join(d, "rank0.zsck")
+    saves, loads = [], []
+    try:
+        for k in range(max(1, min(args.steps, 3))):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            zs.zs_checkpoint_save(lay, path, state, step=k + 1)
+            t1 = time.perf_counter()
+            back.fill_(float("nan"))
+            torch.cuda.synchronize()
+            t2 = time.perf_counter()
+            t = zs.zs_checkpoint_load(lay, path, back)
+            t3 = time.perf_counter()
+            if t != k + 1 or not torch.equal(back.view(torch.int32),
+                                             state.view(torch.int32)):
+                raise SystemExit("checkpoint: restored state differs")
+            saves.append(t1 - t0)
+            loads.append(t3 - t2)
+            log(f"  save {t1 - t0:.2f} s ({nbytes / (t1 - t0) / 1e9:.2f} "
+                f"GB/s), load {t3 - t2:.2f} s "
+                f"({nbytes / (t3 - t2) / 1e9:.2f} GB/s)")
+        fsize = os.path.getsize(path)
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    med = lambda x: sorted(x)[len(x) // 2]
+    out = {
+        "metric": "checkpoint of one rank's optimizer state: save (flushed "
+                  "to disk) GB/s, restore GB/s",
+        "value": nbytes / med(saves) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": len(saves),
+        "warmup": 0,
+        "ms_per_step": med(saves) * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} rank-0 shard, W={W}, tiled "
+                               f"[master|m|v] state",
+                   "state_bytes": nbytes, "file_bytes": fsize},
+        "roofline": None,
+        "restore_GBps": nbytes / med(loads) / 1e9,
+        "save_s": saves,
+        "restore_s": loads,
+        "notes": "the restore reads a file the host page cache still holds; "
+                 "the save ends with fsync",
+    }
+    print(json.dumps(out), flush=True)
+
+
 def accumulate_main(args, w):
     """Gradient accumulation over K micro-batches on the full flat bf16
     gradient buffer of the workload (what backward produces on every rank
@@ -828,6 +903,9 @@ def main():
     ap.add_argument("--accumulate", type=int, default=0, metavar="K",
                     help="gradient accumulation over K micro-batches "
                     "(zs_accumulate) on the workload's flat gradient buffer")
+    ap.add_argument("--checkpoint", action="store_true",
+                    help="save and restore the rank's tiled optimizer state "
+                    "(zs_checkpoint_save / zs_checkpoint_load) at full size")
     ap.add_argument("--whole-tensors", action="store_true",
                     help="whole-tensor shard assignment "
                     "(zs_layout_build_tensors): every tensor on one rank, "
@@ -895,6 +973,8 @@ def main():
         return bf16_main(args, w)
     if args.accumulate:
         return accumulate_main(args, w)
+    if args.checkpoint:
+        return checkpoint_main(args, w)
     if w.streaming:
         return stream_main(args, w)
     W = w.world
