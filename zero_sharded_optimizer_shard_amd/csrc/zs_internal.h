@@ -28,7 +28,7 @@ struct zs_layout {
 };
 
 // Most tiles one kernel launch covers: the step's work shapes put up to
-// 2048 threads per tile along x (32 one-wave workgroups, or 4 of 512
+// 2048 threads per tile along x (32 one-wave workgroups, or 16 of 128
 // threads), and HIP allows fewer than 2^32 work-items there.  A bucket
 // slice (a whole tensor in the whole-tensor mode) is at most this many
 // tiles, 17.2 G elements; group launches end a group early rather than pass

@@ -833,14 +833,16 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 //    (256 for the two-row pure state): 79-80 % at W = 100, against 75-78 %
 //    with one-wave workgroups;
 //  - Small (launches of fewer than kSmallLaunch tiles: bucket groups of a
-//    streaming step, GPT-2-sized shards): one unit per thread and four
-//    workgroups per tile, so that a few hundred or thousand tiles still
-//    spread evenly over the 256 CUs with a short tail (GPT-2-shaped W = 8
-//    shard, 1899 tiles: 81 % vs 75 % with Wide).
+//    streaming step, GPT-2-sized shards): one unit per thread and sixteen
+//    128-thread workgroups per tile, so that a few hundred or thousand
+//    tiles still spread evenly over the 256 CUs with a short tail
+//    (GPT-2-shaped W = 8 shard, 1899 tiles: 80.2-80.5 % against 79.6-79.7 %
+//    with four 512-thread workgroups per tile and 75 % with Wide; 70B bucket
+//    groups alone 38.8 vs 39.3-40.0 ms per full step).
 using ShapeWave = Shape<64, 1, 4>;
 using ShapeWide = Shape<512, 4, 4>;
 using ShapeDeep = Shape<512, 4, 8>;
-using ShapeSmall = Shape<512, 1, 4>;
+using ShapeSmall = Shape<128, 1, 4>;
 using ShapePureWide = Shape<256, 4, 4>;
 constexpr int64_t kSmallLaunch = 4096;
 // every shape stays within the launch limit of kMaxLaunchTiles tiles
