@@ -949,9 +949,9 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus "
-              f"{args.gpus} is not supported (the W ranks are simulated on "
-              f"one device)", file=sys.stderr)
+        print(f"bench.py: the step is measured on one GPU, with the W "
+              f"ranks' gradient slices resident on that device; --gpus "
+              f"{args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
     import torch
