@@ -2,7 +2,7 @@
 
 Bars (fixed by the step's contract): fp32 master, m and v within 1e-6
 relative error with an absolute floor of 1e-9; bf16 parameters within one
-ordinal step (1 ulp).  The build also aims for bit-identical results (same
+ordinal step (1 ulp).  The library also aims for bit-identical results (same
 operation order, one rounding per operation, correctly rounded divide and
 square root on both sides); `exact` reports whether it got them.
 """
