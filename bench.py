@@ -823,7 +823,10 @@ def stream_main(args, w):
 
     # the streaming step proper: the library's engine schedules the copies
     # into the staging ring and the grouped steps on the step streams
-    eng = zs.zs_stream_create(lay, G, staging, up, sts)
+    ups = [up] + [torch.cuda.Stream()
+                  for _ in range(max(1, args.upload_streams) - 1)]
+    eng = zs.zs_stream_create(lay, G, staging, up if len(ups) == 1 else ups,
+                              sts)
 
     def engine_step():
         nonlocal t_step
@@ -865,7 +868,7 @@ def stream_main(args, w):
                    "buckets": nb, "bucket_cap_mb": 25,
                    "bytes_per_param": bpp, "arrival": args.arrival,
                    "buckets_per_launch": G, "staging_slots": slots,
-                   "step_streams": len(sts),
+                   "step_streams": len(sts), "upload_streams": len(ups),
                    "scheduler": "zs_stream engine (native)",
                    "grads_layout": "tiled [tile][W][8192]"},
         "roofline": {"bound": "hbm", "achieved": kern_gbs,
@@ -918,6 +921,9 @@ def main():
     ap.add_argument("--group", type=int, default=16,
                     help="streaming mode: landed buckets stepped per launch "
                     "(zs_buckets_step); the ring holds 2*group slots")
+    ap.add_argument("--upload-streams", type=int, default=1,
+                    help="streaming: upload streams the engine copies "
+                    "arriving buckets on, in turn (zs_stream_create_multi)")
     ap.add_argument("--step-streams", type=int, default=2,
                     help="streaming mode: step streams the landed groups "
                     "are spread over, in turn")

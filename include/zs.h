@@ -464,6 +464,19 @@ int zs_stream_create(const zs_layout* layout, int32_t group,
                      int64_t slot_elems, void* upload_stream,
                      void* const* step_streams, int32_t n_step_streams,
                      zs_stream** out);
+/* The same engine with several upload streams (an array of
+ * n_upload_streams, 1..8, read during the call): arrival i is copied on
+ * upload stream i mod n_upload_streams, so host-to-device copies can use
+ * more of the host link at once; each group launch waits for the copies of
+ * its buckets on every upload stream they used.  zs_stream_create is this
+ * call with one upload stream.  Errors as zs_stream_create, and ZS_EINVAL
+ * for n_upload_streams outside [1, 8] or a NULL array. */
+int zs_stream_create_multi(const zs_layout* layout, int32_t group,
+                           uint16_t* const* slots, int32_t n_slots,
+                           int64_t slot_elems, void* const* upload_streams,
+                           int32_t n_upload_streams,
+                           void* const* step_streams, int32_t n_step_streams,
+                           zs_stream** out);
 int zs_stream_step_begin(zs_stream* stream, float* state,
                          uint16_t* param_shard, uint16_t* full_flat,
                          const zs_adamw* hp, int64_t step);

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 37
+    assert len(names) == 38
     L = zs.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -380,6 +380,20 @@ def test_stream_engine_argument_checks_need_no_device():
     assert create(k=9) == -1
     assert create(ss=None) == -1
     assert create(o=None) == -1
+    assert out.value is None
+    # several upload streams: the same checks, and the stream count's own
+    ups = (P_ * 9)(*([None] * 9))
+
+    def create_multi(nu=2, us=ups, group=2, k=2, o=ctypes.byref(out)):
+        return L.zs_stream_create_multi(h, group, slots, 4, need, us, nu,
+                                        sts, k, o)
+
+    assert create_multi(nu=0) == -1
+    assert create_multi(nu=9) == -1
+    assert create_multi(us=None) == -1
+    assert create_multi(group=0) == -1
+    assert create_multi(k=0) == -1
+    assert create_multi(o=None) == -1
     assert out.value is None
     hp = zs.zs_adamw(3e-4, 0.9, 0.95, 1e-8, 0.1)
     assert L.zs_stream_step_begin(None, A, A, None, ctypes.byref(hp), 1) \

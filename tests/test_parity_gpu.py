@@ -1111,13 +1111,14 @@ def test_gradient_accumulation_llama8b_flat_sampled():
         assert np.array_equal(np16(G[k - 1][a:a + m]), O.accumulate(Gh)), a
 
 
-@pytest.mark.parametrize("arrival,tensors", [("device", False),
-                                             ("pinned host", False),
-                                             ("device", True)])
-def test_stream_engine_equals_the_whole_step(arrival, tensors):
+@pytest.mark.parametrize("arrival,tensors,n_up", [
+    ("device", False, 1), ("pinned host", False, 1), ("device", True, 1),
+    ("pinned host", False, 4), ("device", True, 3)])
+def test_stream_engine_equals_the_whole_step(arrival, tensors, n_up):
     """The streaming engine (zs_stream_*): a rank's buckets (owned tensors
     in the whole-tensor layout) arrive one by one in a shuffled order, from
-    device or pinned host memory, into a ring of 2 x 3 staging slots;
+    device or pinned host memory, over one or several upload streams, into
+    a ring of 2 x 3 staging slots;
     groups of 3 alternate over two step streams; two steps; the state, the
     shard and the flat buffer equal zs_step on the whole shard bit for bit.
     A bucket arriving twice is refused."""
@@ -1134,7 +1135,7 @@ def test_stream_engine_equals_the_whole_step(arrival, tensors):
     n, nb, F = lay_o.shard_numel, len(lay_o.buckets), lay_o.flat_numel
     assert nb > 4
     say(f"case stream engine W={W} buckets={nb} arrival={arrival} "
-        f"tensors={tensors}")
+        f"tensors={tensors} upload streams={n_up}")
     ref_state = dev_state(lay, lay_o, 0.02, warm=(1e-4, 1e-8))
     state = ref_state.clone()
     flat_ref, flat = dev_bf16(F), dev_bf16(F)
@@ -1146,9 +1147,10 @@ def test_stream_engine_equals_the_whole_step(arrival, tensors):
     tiles = [-(-b.slice_numel // TILE) for b in lay_o.buckets]
     pool = [dev_bf16(k * W * TILE) for k in tiles]
     slots = [dev_bf16(max(tiles) * W * TILE) for _ in range(6)]
-    up = torch.cuda.Stream()
+    ups = [torch.cuda.Stream() for _ in range(n_up)]
     sts = [torch.cuda.Stream(), torch.cuda.Stream()]
-    eng = zs.zs_stream_create(lay, 3, slots, up, sts)
+    eng = zs.zs_stream_create(lay, 3, slots, ups[0] if n_up == 1 else ups,
+                              sts)
     wide = torch.empty(state.numel() + 4, dtype=torch.float32,
                        device="cuda")
     with pytest.raises(zs.ZsError) as e:             # misaligned state
@@ -1189,7 +1191,8 @@ def test_stream_engine_equals_the_whole_step(arrival, tensors):
 def test_stream_engine_random_configs(seed):
     """The streaming engine under seeded random configurations: group 1..16,
     a ring from the minimum (n_slots = group) to group + 5 slots, 1..3 step
-    streams, random layouts and arrival orders, three steps (slots and
+    streams, 1..4 upload streams, random layouts and arrival orders, three
+    steps (slots and
     launch events reused across steps); state and flat output equal zs_step
     on the whole shard bit for bit after every step."""
     rng = random.Random(900 + seed)
@@ -1204,8 +1207,9 @@ def test_stream_engine_random_configs(seed):
     group = rng.randint(1, min(16, nb))
     n_slots = group + rng.choice([0, 0, 1, group, 5])
     n_streams = rng.randint(1, 3)
+    n_up = rng.choice([1, 1, 2, 3, 4])
     say(f"case engine seed={seed} W={W} buckets={nb} group={group} "
-        f"slots={n_slots} streams={n_streams}")
+        f"slots={n_slots} streams={n_streams} upload streams={n_up}")
     ref_state = dev_state(lay, lay_o, 0.02, warm=(1e-4, 1e-8))
     state = ref_state.clone()
     flat_ref, flat = dev_bf16(F), dev_bf16(F)
@@ -1216,9 +1220,10 @@ def test_stream_engine_random_configs(seed):
     tiles = [-(-b.slice_numel // TILE) for b in lay_o.buckets]
     pool = [dev_bf16(k * W * TILE) for k in tiles]
     slots = [dev_bf16(max(tiles) * W * TILE) for _ in range(n_slots)]
-    up = torch.cuda.Stream()
+    ups = [torch.cuda.Stream() for _ in range(n_up)]
     sts = [torch.cuda.Stream() for _ in range(n_streams)]
-    eng = zs.zs_stream_create(lay, group, slots, up, sts)
+    eng = zs.zs_stream_create(lay, group, slots,
+                              ups[0] if n_up == 1 else ups, sts)
     for t in (1, 2, 3):
         S.dev_grads(G, W, n, t, 1e-3)
         zs.zs_grads_tile(lay, -1, G, n, Gt)

@@ -57,7 +57,8 @@ EXPORTS = ["zs_layout_build", "zs_layout_build_tensors", "zs_layout_owners",
            "zs_state_unpack",
            "zs_grads_tile", "zs_gather", "zs_pack", "zs_step_bf16",
            "zs_state_mv_pack", "zs_state_mv_unpack", "zs_accumulate",
-           "zs_stream_create", "zs_stream_step_begin", "zs_stream_arrive",
+           "zs_stream_create", "zs_stream_create_multi",
+           "zs_stream_step_begin", "zs_stream_arrive",
            "zs_stream_step_end", "zs_stream_free",
            "zs_prefetch_create", "zs_prefetch_issue", "zs_prefetch_acquire",
            "zs_prefetch_release", "zs_prefetch_free",
@@ -106,6 +107,8 @@ def lib():
     L.zs_pack.argtypes = [p, p, p, p, i32, p, p]
     L.zs_stream_create.argtypes = [p, i32, P(p), i32, i64, p, P(p), i32,
                                    P(p)]
+    L.zs_stream_create_multi.argtypes = [p, i32, P(p), i32, i64, P(p), i32,
+                                         P(p), i32, P(p)]
     L.zs_stream_step_begin.argtypes = [p, p, p, p, P(zs_adamw), i64]
     L.zs_stream_arrive.argtypes = [p, i32, p]
     L.zs_stream_step_end.argtypes = [p]
@@ -132,7 +135,8 @@ def lib():
                  "zs_state_unpack",
                  "zs_grads_tile", "zs_gather", "zs_pack", "zs_step_bf16",
                  "zs_state_mv_pack", "zs_state_mv_unpack",
-                 "zs_accumulate", "zs_stream_create", "zs_stream_step_begin",
+                 "zs_accumulate", "zs_stream_create", "zs_stream_create_multi",
+                 "zs_stream_step_begin",
                  "zs_stream_arrive", "zs_stream_step_end",
                  "zs_prefetch_create", "zs_prefetch_issue",
                  "zs_prefetch_acquire", "zs_prefetch_release",
@@ -564,20 +568,31 @@ class Stream:
 
 def zs_stream_create(layout: Layout, group: int, slots, upload_stream,
                      step_streams) -> Stream:
-    """slots: device bf16 staging tensors (the ring); upload_stream and
-    step_streams: torch streams."""
+    """slots: device bf16 staging tensors (the ring); upload_stream: a torch
+    stream, or a list of them (zs_stream_create_multi: arrivals take them in
+    turn); step_streams: torch streams."""
     n = len(slots)
     arr = (ctypes.c_void_p * max(n, 1))(*[_bf16(t, "slots") for t in slots])
     k = len(step_streams)
     ss = (ctypes.c_void_p * max(k, 1))(*[t.cuda_stream for t in step_streams])
     elems = min(t.numel() for t in slots) if n else 0
     out = ctypes.c_void_p()
-    _check(lib().zs_stream_create(layout.handle, group, arr, n, elems,
-                                  ctypes.c_void_p(upload_stream.cuda_stream),
-                                  ss, k, ctypes.byref(out)),
-           "zs_stream_create")
-    return Stream(out.value, (layout, list(slots), upload_stream,
-                              list(step_streams)))
+    if isinstance(upload_stream, (list, tuple)):
+        nu = len(upload_stream)
+        us = (ctypes.c_void_p * max(nu, 1))(*[t.cuda_stream
+                                              for t in upload_stream])
+        _check(lib().zs_stream_create_multi(layout.handle, group, arr, n,
+                                            elems, us, nu, ss, k,
+                                            ctypes.byref(out)),
+               "zs_stream_create_multi")
+        ups = list(upload_stream)
+    else:
+        _check(lib().zs_stream_create(
+            layout.handle, group, arr, n, elems,
+            ctypes.c_void_p(upload_stream.cuda_stream), ss, k,
+            ctypes.byref(out)), "zs_stream_create")
+        ups = upload_stream
+    return Stream(out.value, (layout, list(slots), ups, list(step_streams)))
 
 
 def zs_stream_step_begin(stream: Stream, state, param_shard=None,
