@@ -456,8 +456,9 @@ void zs_prefetch_free(zs_prefetch* prefetch);
  * An argument error has no effect and the step stays usable.  A failed
  * copy or launch abandons the step: its pending group is dropped, later
  * arrivals are refused, and zs_stream_step_end closes it and returns
- * ZS_EINVAL; the step's results are then undefined.  One host thread at a
- * time per engine. */
+ * ZS_EINVAL; the step's results are then undefined.  Abandoning waits on
+ * the host for the copies of the dropped group.  One host thread at a time
+ * per engine. */
 typedef struct zs_stream zs_stream;
 int zs_stream_create(const zs_layout* layout, int32_t group,
                      uint16_t* const* slots, int32_t n_slots,
@@ -466,8 +467,8 @@ int zs_stream_create(const zs_layout* layout, int32_t group,
                      zs_stream** out);
 /* The same engine with several upload streams (an array of
  * n_upload_streams, 1..8, read during the call): arrival i is copied on
- * upload stream i mod n_upload_streams, so host-to-device copies can use
- * more of the host link at once; each group launch waits for the copies of
+ * upload stream i mod n_upload_streams, for hosts where one stream's copies
+ * do not fill the host link; each group launch waits for the copies of
  * its buckets on every upload stream they used.  zs_stream_create is this
  * call with one upload stream.  Errors as zs_stream_create, and ZS_EINVAL
  * for n_upload_streams outside [1, 8] or a NULL array. */

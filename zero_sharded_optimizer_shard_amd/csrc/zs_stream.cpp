@@ -15,9 +15,10 @@
 // stream in turn, after the step that last read that slot; every `group`
 // arrivals become one zs_buckets_step launch on the next step stream in
 // turn, ordered after the group's copies by one event per upload stream
-// they used.  Several upload streams let host-to-device copies use more of
-// the host link (25 MiB pinned copies on MI355X: 47.8 GB/s on one stream,
-// 57.1 on four).  Spreading groups over several step streams lets one
+// they used.  Several upload streams are for hosts where one stream's copies
+// leave the host link idle; on MI355X one stream of 25 MiB pinned copies
+// already filled it (56 GB/s in a 70B-shaped host-fed step, within 1 % of
+// four streams).  Spreading groups over several step streams lets one
 // launch's tail overlap the next launch (groups touch disjoint buckets).
 // HIP events are the only resources it creates, and it enqueues few stream
 // packets: an event record after each group's copies and after each launch,
@@ -90,9 +91,15 @@ bool aligned16(const void* p)
 }
 
 // A device call of the step failed: the step is abandoned (its pending group
-// dropped) and later arrivals are refused until step_end closes it.
+// dropped) and later arrivals are refused until step_end closes it.  No
+// launch reads the dropped group's slots, so no launch event orders their
+// copies before the next copy into the same slot, which may run on another
+// upload stream: the host waits for the upload streams the group used.
 int abandon(zs_stream* S, int rc)
 {
+    for (size_t u = 0; u < S->ups.size(); ++u)
+        if (S->pend_ups & (1u << u))
+            (void)hipStreamSynchronize(S->ups[u]);
     S->failed = true;
     S->pend_ids.clear();
     S->pend_slots.clear();
