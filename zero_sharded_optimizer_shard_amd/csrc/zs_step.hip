@@ -531,74 +531,47 @@ __global__ __launch_bounds__(kThreads) void state_unpack_kernel(
 }
 
 // gradient slices [W][stride] -> tiled [tile][W][kTile]; padding zeroed.
-// 16-byte accesses (slice starts, strides and slice lengths are multiples of
-// 8 elements; a partial group would be copied element-wise), four rows'
-// loads in flight before their stores.  Measured on MI355X over the 8B
-// shard at W = 8 (32 GB moved): 5.82 ms, 69 % of peak (8-byte accesses,
-// one row at a time: 5.96 ms); the W source rows are separate streams.
+// One tile row (tile, rank s) per kGtParts workgroups of kGtThreads, one
+// 16-byte group per thread (slice starts, strides and slice lengths are
+// multiples of 8 elements; a partial group would be copied element-wise).
+// The rank row is blockIdx.z, which the dispatcher advances last, so the
+// workgroups in flight read one slice front to back and write whole 16 KiB
+// rows.  Measured on MI355X over the 8B shard at W = 8 (32 GB moved):
+// 5.27-5.30 ms, 76 % of peak; one 512-thread workgroup per tile sweeping
+// its W rows four at a time took 5.79-5.89 ms (68-69 %), and with the rank
+// row in z, 64-, 128-, 512- and 1024-thread workgroups or two groups per
+// thread measured 63-72 %.
+constexpr int kGtThreads = 256;
+constexpr int kGtParts = (int)(kTile / 8 / kGtThreads);
+static_assert(kMaxLaunchTiles * kGtParts * kGtThreads < (int64_t(1) << 32),
+              "one launch row of tiles fits the grid");
+
 template <class Loc>
-__global__ __launch_bounds__(kThreads) void grads_tile_kernel(
+__global__ __launch_bounds__(kGtThreads) void grads_tile_kernel(
     const uint16_t* __restrict__ slices, int64_t stride,
     uint16_t* __restrict__ tiled, int32_t W, Loc loc)
 {
     TileRef r;
-    if (!loc(r))
+    if (!loc.template at<kGtParts>(r))
         return;
-    uint16_t* dst = tiled + r.tile * (int64_t)W * kTile;
-    const uint16_t* src = slices + r.e0;
-    constexpr int V = (int)(kTile / 8 / kThreads);   // groups per thread
-    const int nv = (int)(r.nvalid / 8);               // whole valid groups
-    // group nv is partial when nvalid % 8 != 0: written below, not here
-    const int skip = r.nvalid % 8 ? nv : -1;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    constexpr int R = 4;
-    int s = 0;
-    for (; s + R <= W; s += R) {
-        u32x4 x[R][V];
-#pragma unroll
-        for (int i = 0; i < R; ++i)
-#pragma unroll
-            for (int v = 0; v < V; ++v) {
-                const int g = v * kThreads + (int)threadIdx.x;
-                x[i][v] = g < nv ? __builtin_nontemporal_load(
-                                       reinterpret_cast<const u32x4*>(
-                                           src + (int64_t)(s + i) * stride) +
-                                       g)
-                                 : z;
-            }
-#pragma unroll
-        for (int i = 0; i < R; ++i)
-#pragma unroll
-            for (int v = 0; v < V; ++v) {
-                const int g = v * kThreads + (int)threadIdx.x;
-                if (g != skip)
-                    __builtin_nontemporal_store(
-                        x[i][v], reinterpret_cast<u32x4*>(
-                                     dst + (int64_t)(s + i) * kTile) + g);
-            }
+    const int64_t s = blockIdx.z;
+    uint16_t* dst = tiled + (r.tile * (int64_t)W + s) * kTile;
+    const uint16_t* src = slices + r.e0 + s * stride;
+    const int g = (int)(blockIdx.x % kGtParts) * kGtThreads + (int)threadIdx.x;
+    const int nv = (int)(r.nvalid / 8);                // whole valid groups
+    if (g < nv) {
+        __builtin_nontemporal_store(
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + g),
+            reinterpret_cast<u32x4*>(dst) + g);
+    } else if (g > nv || r.nvalid % 8 == 0) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(dst) + g);
+    } else {
+        // the partial group (the layouts never produce one): its valid
+        // elements and zeros
+        for (int j = g * 8; j < g * 8 + 8; ++j)
+            dst[j] = j < r.nvalid ? src[j] : (uint16_t)0;
     }
-    for (; s < W; ++s) {
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-            const int g = v * kThreads + (int)threadIdx.x;
-            const u32x4 x = g < nv ? __builtin_nontemporal_load(
-                                         reinterpret_cast<const u32x4*>(
-                                             src + (int64_t)s * stride) + g)
-                                   : z;
-            if (g != skip)
-                __builtin_nontemporal_store(
-                    x, reinterpret_cast<u32x4*>(dst + (int64_t)s * kTile) +
-                           g);
-        }
-    }
-    // the partial group (the layouts never produce one): its valid
-    // elements and zeros, one row per thread
-    if (skip >= 0)
-        for (int s2 = (int)threadIdx.x; s2 < W; s2 += kThreads)
-            for (int j = skip * 8; j < skip * 8 + 8; ++j)
-                dst[(int64_t)s2 * kTile + j] =
-                    j < r.nvalid ? src[(int64_t)s2 * stride + j]
-                                 : (uint16_t)0;
 }
 
 // ---- pack: shard -> flat all-gather buffer ---------------------------------
@@ -1242,15 +1215,20 @@ extern "C" int zs_grads_tile(const zs_layout* L, int32_t bucket_id,
         GeomLoc loc;
         loc.g = bucket_geom(L, L->buckets[bucket_id]);
         hipLaunchKernelGGL(grads_tile_kernel<GeomLoc>,
-                           dim3((unsigned)loc.g.TPB, 1), dim3(kThreads), 0,
-                           s, slices, stride, tiled, W, loc);
+                           dim3((unsigned)(loc.g.TPB * kGtParts), 1,
+                                (unsigned)W),
+                           dim3(kGtThreads), 0, s, slices, stride, tiled, W,
+                           loc);
         return check_launch("grads tile kernel");
     }
     return for_launches(L, [&](const auto& loc, dim3 grid, int64_t e,
                                int64_t t, int64_t) {
         using Loc = std::decay_t<decltype(loc)>;
-        hipLaunchKernelGGL(grads_tile_kernel<Loc>, grid, dim3(kThreads), 0, s,
-                           slices + e, stride, tiled + t * W * kTile, W, loc);
+        grid.x *= kGtParts;                 // kGtParts workgroups per row
+        grid.z = (unsigned)W;               // rank row
+        hipLaunchKernelGGL(grads_tile_kernel<Loc>, grid, dim3(kGtThreads), 0,
+                           s, slices + e, stride, tiled + t * W * kTile, W,
+                           loc);
         return check_launch("grads tile kernel");
     });
 }
