@@ -576,14 +576,19 @@ __global__ __launch_bounds__(kGtThreads) void grads_tile_kernel(
 
 // ---- pack: shard -> flat all-gather buffer ---------------------------------
 
-// One-wave workgroups, eight per tile, two 16-byte copies per thread (as
-// the ZeRO-3 gather): 6.04-6.08 TB/s on the 8B-shaped shard against
-// 5.89-5.93 with one 512-thread workgroup of 8-byte copies per tile.
+// Four 256-thread workgroups per tile, one 16-byte copy per thread (the
+// gradient tiling conversion's shape): 0.636-0.638 ms, 6.30-6.32 TB/s on
+// the 8B-shaped shard, against 0.652-0.665 ms for eight one-wave
+// workgroups of two copies per thread, 0.656-0.668 ms for eight 128-thread
+// workgroups of one, 0.660-0.673 ms for two 256-thread workgroups of two,
+// and 5.89-5.93 TB/s for one 512-thread workgroup of 8-byte copies.
 // Slices and padded tensors are multiples of 8 elements, so a 16-byte group
 // is either wholly inside the tile's valid part or wholly outside.
-constexpr int kPackNT = 64;                       // one wave per workgroup
-constexpr int kPackV = 2;                         // 16-byte copies per thread
-constexpr int kPackP = (int)(kTile / (kPackNT * kPackV * 8));   // 8 per tile
+constexpr int kPackNT = 256;
+constexpr int kPackV = 1;                         // 16-byte copies per thread
+constexpr int kPackP = (int)(kTile / (kPackNT * kPackV * 8));   // 4 per tile
+static_assert(kMaxLaunchTiles * kPackP * kPackNT < (int64_t(1) << 32),
+              "one launch row of tiles fits the grid");
 
 template <class Loc>
 __global__ __launch_bounds__(kPackNT) void pack_flat_kernel(
