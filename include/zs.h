@@ -450,6 +450,10 @@ void zs_prefetch_free(zs_prefetch* prefetch);
  * Returns the number of buckets stepped in the step (>= 0) or an error.
  * The work is then queued on the caller's streams; synchronise them (or
  * wait on an event recorded on each step stream) before reading results.
+ * Steps may be queued back to back with no host synchronisation: each
+ * zs_stream_step_begin after the first orders every step stream after the
+ * work already queued on the others, so a bucket's launch in step t+1 runs
+ * after its launch in step t whichever step streams they use.
  * Errors: ZS_EINVAL (NULL arguments, counts, a step not open or already
  * open, a bucket arriving twice), ZS_EALIGN, ZS_ERANGE (bucket id, slot too
  * small), ZS_EDEVICE (a HIP call failed), and those of zs_buckets_step.

@@ -26,24 +26,12 @@ HIP library):
 * The chunk table lists, for one rank, the maximal runs of its shard that lie
   inside one tensor: (tensor_id, bucket_id, tensor_off, numel, shard_off).
   Padding is in no chunk.
-* Tiles.  The tiled HBM layouts of the optimizer state and of the gradient
-  slices are a storage format of the implementation, not part of the method;
-  they are stated here so that tests can place and read values in them
-  without the library.  Each bucket's slice is cut into ``TILE``-element
-  tiles, the last one padded; tiles are numbered across buckets in bucket
-  order (``Bucket.tile_off`` is the first tile of the slice).  Tiled state:
-  tile i holds ``[master | m | v]`` of ``TILE`` floats each.  Tiled
-  gradients: tile i holds source ranks 0..W-1, ``TILE`` bf16 values each.
 """
 
 from __future__ import annotations
 
 from dataclasses import dataclass, field
 from typing import List, Sequence
-
-import numpy as np
-
-TILE = 8192          # elements per tile of the tiled layouts
 
 
 def _roundup(x: int, a: int) -> int:
@@ -56,7 +44,6 @@ class Bucket:
     numel: int
     slice_numel: int
     shard_off: int
-    tile_off: int = 0
 
 
 @dataclass
@@ -78,8 +65,6 @@ class Layout:
     tensor_flat_off: List[int]
     flat_numel: int
     shard_numel: int
-    n_tiles: int = 0
-    tile: int = TILE
     buckets: List[Bucket] = field(default_factory=list)
     chunks: List[Chunk] = field(default_factory=list)
     # whole-tensor mode: the owner rank of every tensor and its offset in
@@ -95,7 +80,7 @@ class LayoutError(ValueError):
 
 def build_layout(tensor_numel: Sequence[int], world: int, rank: int,
                  bucket_cap_bytes: int = 25 << 20,
-                 align_bytes: int = 256, tile: int = TILE) -> Layout:
+                 align_bytes: int = 256) -> Layout:
     """Build the layout of one rank.  See the module docstring for the rule.
 
     ``bucket_cap_bytes <= 0`` means one bucket holding the whole flat buffer,
@@ -132,14 +117,12 @@ def build_layout(tensor_numel: Sequence[int], world: int, rank: int,
     buckets = []
     off = 0
     shard_off = 0
-    tiles = 0
     while off < content_end:
         numel = min(full, _roundup(content_end - off, unit))
         sl = numel // world
-        buckets.append(Bucket(off, numel, sl, shard_off, tiles))
+        buckets.append(Bucket(off, numel, sl, shard_off))
         off += numel
         shard_off += sl
-        tiles += _roundup(sl, tile) // tile
     flat_numel = off
     shard_numel = shard_off
 
@@ -158,7 +141,7 @@ def build_layout(tensor_numel: Sequence[int], world: int, rank: int,
     return Layout(world=world, rank=rank, align_elems=align, bucket_elems=full,
                   tensor_numel=list(tensor_numel), tensor_flat_off=starts,
                   flat_numel=flat_numel, shard_numel=shard_numel,
-                  n_tiles=tiles, tile=tile, buckets=buckets, chunks=chunks)
+                  buckets=buckets, chunks=chunks)
 
 
 def shard_flat_index(lay: Layout) -> List[range]:
@@ -168,74 +151,8 @@ def shard_flat_index(lay: Layout) -> List[range]:
             for b in lay.buckets]
 
 
-def tile_slot_range(lay: Layout, bucket_id: int, j0: int, k: int):
-    """int64 [k]: tile * T + position, in the tiled layouts (T = lay.tile),
-    of elements j0 .. j0+k-1 of bucket bucket_id's slice: element j sits in
-    tile b.tile_off + j // T at position j % T."""
-    b = lay.buckets[bucket_id]
-    if j0 < 0 or j0 + k > b.slice_numel:
-        raise IndexError("range outside the bucket's slice")
-    T = lay.tile
-    j = np.arange(j0, j0 + k, dtype=np.int64)
-    return (b.tile_off + j // T) * T + j % T
-
-
-def tile_slot(lay: Layout) -> np.ndarray:
-    """int64 [shard_numel]: tile * T + position of every shard element in
-    the tiled layouts (see tile_slot_range)."""
-    out = np.empty(lay.shard_numel, np.int64)
-    for b_id, b in enumerate(lay.buckets):
-        out[b.shard_off:b.shard_off + b.slice_numel] = \
-            tile_slot_range(lay, b_id, 0, b.slice_numel)
-    return out
-
-
-def to_tiled_rows(lay: Layout, rows) -> np.ndarray:
-    """Plain fp32 arrays [shard_numel], one per row, -> a tiled state
-    [n_tiles * len(rows) * lay.tile]; padding positions 0."""
-    R = len(rows)
-    st = np.zeros((lay.n_tiles, R, lay.tile), np.float32)
-    slot = tile_slot(lay)
-    t, p = slot // lay.tile, slot % lay.tile
-    for k, a in enumerate(rows):
-        st[t, k, p] = a
-    return st.reshape(-1)
-
-
-def from_tiled_rows(lay: Layout, state, n_rows: int):
-    """A tiled state of n_rows rows -> the plain arrays, one per row."""
-    st = np.asarray(state, np.float32).reshape(lay.n_tiles, n_rows, lay.tile)
-    slot = tile_slot(lay)
-    t, p = slot // lay.tile, slot % lay.tile
-    return tuple(st[t, k, p].copy() for k in range(n_rows))
-
-
-def to_tiled_state(lay: Layout, master, m, v) -> np.ndarray:
-    """Plain fp32 master/m/v [shard_numel] -> tiled state
-    [n_tiles * 3 * lay.tile]; padding positions 0."""
-    return to_tiled_rows(lay, [master, m, v])
-
-
-def from_tiled_state(lay: Layout, state):
-    """Tiled state -> plain (master, m, v)."""
-    return from_tiled_rows(lay, state, 3)
-
-
-def to_tiled_grads(lay: Layout, G) -> np.ndarray:
-    """Gradient slices uint16 [W][shard_numel] -> tiled [n_tiles*W*lay.tile];
-    padding positions 0."""
-    W = lay.world
-    out = np.zeros((lay.n_tiles, W, lay.tile), np.uint16)
-    slot = tile_slot(lay)
-    t, p = slot // lay.tile, slot % lay.tile
-    for s in range(W):
-        out[t, s, p] = G[s]
-    return out.reshape(-1)
-
-
 def build_tensor_layout(tensor_numel: Sequence[int], world: int, rank: int,
-                        align_bytes: int = 256,
-                        tile: int = TILE) -> Layout:
+                        align_bytes: int = 256) -> Layout:
     """Whole-tensor shard assignment (podcast summary of "Training at
     thousands of GPUs", section "ZeRO optimizer": an optimizer that needs
     whole tensors, such as Muon, cannot work on flattened slices; the
@@ -284,18 +201,15 @@ def build_tensor_layout(tensor_numel: Sequence[int], world: int, rank: int,
         fill[owner[t]] += padded[t]
 
     buckets, chunks = [], []
-    tiles = 0
     for t in range(len(tensor_numel)):
         if owner[t] != rank or tensor_numel[t] == 0:
             continue
         b_id = len(buckets)
-        buckets.append(Bucket(starts[t], padded[t], padded[t], owner_off[t],
-                              tiles))
+        buckets.append(Bucket(starts[t], padded[t], padded[t], owner_off[t]))
         chunks.append(Chunk(t, b_id, 0, tensor_numel[t], owner_off[t]))
-        tiles += _roundup(padded[t], tile) // tile
     return Layout(world=world, rank=rank, align_elems=align, bucket_elems=0,
                   tensor_numel=list(tensor_numel), tensor_flat_off=starts,
                   flat_numel=flat_numel, shard_numel=fill[rank],
-                  n_tiles=tiles, tile=tile, buckets=buckets, chunks=chunks,
+                  buckets=buckets, chunks=chunks,
                   whole_tensors=True, owner=owner,
                   owner_shard_off=owner_off)

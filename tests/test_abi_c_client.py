@@ -11,6 +11,7 @@ import subprocess
 import pytest
 
 from oracle.layout import LayoutError, build_layout, build_tensor_layout
+from tiles import n_tiles, tile_offsets
 from synth import workloads as wl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -46,13 +47,13 @@ def run(exe, mode, world, rank, cap, align, numels):
 
 def expect(lay, world, rank, n_tensors, tensors):
     info = [str(lay.flat_numel), str(lay.shard_numel), str(len(lay.buckets)),
-            str(len(lay.chunks)), str(lay.n_tiles), str(world), str(rank)]
+            str(len(lay.chunks)), str(n_tiles(lay)), str(world), str(rank)]
     out = {"info": [info],
            "tensor": [[str(t), str(o)] for t, o in
                       enumerate(lay.tensor_flat_off)],
            "bucket": [[str(x) for x in (b.flat_off, b.numel, b.slice_numel,
-                                        b.shard_off, b.tile_off)]
-                      for b in lay.buckets],
+                                        b.shard_off, t0)]
+                      for b, t0 in zip(lay.buckets, tile_offsets(lay))],
            "chunk": [[str(x) for x in (c.tensor_id, c.bucket_id,
                                        c.tensor_off, c.numel, c.shard_off)]
                      for c in lay.chunks]}

@@ -12,6 +12,7 @@ import pytest
 
 import zero_sharded_optimizer_shard_amd as zs
 from oracle.layout import LayoutError, build_layout, build_tensor_layout
+from tiles import n_tiles, tile_offsets
 from synth import workloads as wl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -43,11 +44,13 @@ def tables(lay_c, n_tensors):
 
 
 def oracle_tables(lay):
-    b = [(x.flat_off, x.numel, x.slice_numel, x.shard_off, x.tile_off)
-         for x in lay.buckets]
+    """The oracle's tables, with the tile offsets of the library's storage
+    format (tests/tiles.py) beside the bucket records."""
+    b = [(x.flat_off, x.numel, x.slice_numel, x.shard_off, t0)
+         for x, t0 in zip(lay.buckets, tile_offsets(lay))]
     c = [(x.tensor_id, x.bucket_id, x.tensor_off, x.numel, x.shard_off)
          for x in lay.chunks]
-    return (lay.flat_numel, lay.shard_numel, lay.n_tiles, b, c,
+    return (lay.flat_numel, lay.shard_numel, n_tiles(lay), b, c,
             lay.tensor_flat_off)
 
 

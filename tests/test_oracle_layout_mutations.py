@@ -40,9 +40,6 @@ MUTATIONS = [
     ("chunk tensor offset from the slice start", "layout.py",
      "chunks.append(Chunk(t_id, b_id, s - t0, e - s,",
      "chunks.append(Chunk(t_id, b_id, s - lo, e - s,", 0),
-    ("tiles counted by floor", "layout.py",
-     "        tiles += _roundup(sl, tile) // tile\n",
-     "        tiles += sl // tile\n", 0),
     ("whole tensors: shortest first", "layout.py",
      "key=lambda t: (-padded[t], t)", "key=lambda t: (padded[t], t)", 0),
     ("whole tensors: ties to the highest rank", "layout.py",

@@ -25,6 +25,13 @@
 // and one wait on the upload stream per launch whose slots are reused (one
 // record and one wait per bucket slowed a 70B-shaped step by a third on
 // MI355X).
+//
+// Consecutive steps update the same state.  A bucket's launch in step t+1
+// may land on another step stream than its launch in step t, and its slot
+// may be one no launch has read yet, so nothing above orders the two.  Each
+// step_begin after the first therefore makes every step stream wait for
+// the work already queued on every other one (at most 8 x 7 waits per
+// step), so the caller may queue steps back to back with no host sync.
 
 #include <hip/hip_runtime_api.h>
 
@@ -48,6 +55,8 @@ struct zs_stream {
     // launches later: a ring of n_slots + 1 launch events still holds the
     // record of the launch that read it.
     std::vector<hipEvent_t> landed;   // per upload stream
+    std::vector<hipEvent_t> fence;    // per step stream: its tail at the
+                                      // start of a step
     std::vector<hipEvent_t> done;     // launch g at g % done.size()
     std::vector<int64_t> reader;      // per slot: last launch that read it
     std::vector<int64_t> waited;      // per (upload stream, step stream):
@@ -111,6 +120,8 @@ void destroy(zs_stream* S)
 {
     for (hipEvent_t e : S->landed)
         if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : S->fence)
+        if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : S->done)
         if (e) (void)hipEventDestroy(e);
     delete S;
@@ -148,7 +159,12 @@ int launch_pending(zs_stream* S)
                                    S->flat, &S->hp, S->t, s);
     if (rc) return abandon(S, rc);
     e = hipEventRecord(S->done[g % (int64_t)S->done.size()], s);
-    if (e != hipSuccess) return abandon(S, hip_fail(e, "hipEventRecord"));
+    if (e != hipSuccess) {
+        // the launch is queued but no event marks its end, so no later copy
+        // could wait for it before overwriting its slots: wait here
+        (void)hipStreamSynchronize(s);
+        return abandon(S, hip_fail(e, "hipEventRecord"));
+    }
     for (int32_t k : S->pend_slots)
         S->reader[k] = g;
     ++S->launches;
@@ -210,6 +226,7 @@ extern "C" int zs_stream_create_multi(const zs_layout* L, int32_t group,
         for (int32_t i = 0; i < n_step_streams; ++i)
             S->steps.push_back(static_cast<hipStream_t>(step_streams[i]));
         S->landed.assign((size_t)n_upload_streams, nullptr);
+        S->fence.assign((size_t)n_step_streams, nullptr);
         S->done.assign((size_t)n_slots + 1, nullptr);
         S->reader.assign(n_slots, -1);
         S->waited.assign((size_t)n_upload_streams * n_step_streams, -1);
@@ -223,6 +240,8 @@ extern "C" int zs_stream_create_multi(const zs_layout* L, int32_t group,
     hipError_t e = hipSuccess;
     for (size_t j = 0; e == hipSuccess && j < S->landed.size(); ++j)
         e = hipEventCreateWithFlags(&S->landed[j], hipEventDisableTiming);
+    for (size_t j = 0; e == hipSuccess && j < S->fence.size(); ++j)
+        e = hipEventCreateWithFlags(&S->fence[j], hipEventDisableTiming);
     for (size_t j = 0; e == hipSuccess && j < S->done.size(); ++j)
         e = hipEventCreateWithFlags(&S->done[j], hipEventDisableTiming);
     if (e != hipSuccess) {
@@ -260,6 +279,20 @@ extern "C" int zs_stream_step_begin(zs_stream* S, float* state,
     if (!aligned16(state) || (param_shard && !aligned16(param_shard)) ||
         (full_flat && !aligned16(full_flat)))
         return fail(ZS_EALIGN, "device pointers must be 16-byte aligned");
+    // order this step's launches after the previous steps' launches on
+    // every other step stream (see the file header)
+    const size_t ns = S->steps.size();
+    if (S->launches > 0 && ns > 1) {
+        hipError_t e = hipSuccess;
+        for (size_t j = 0; e == hipSuccess && j < ns; ++j)
+            e = hipEventRecord(S->fence[j], S->steps[j]);
+        for (size_t i = 0; e == hipSuccess && i < ns; ++i)
+            for (size_t j = 0; e == hipSuccess && j < ns; ++j)
+                if (i != j)
+                    e = hipStreamWaitEvent(S->steps[i], S->fence[j], 0);
+        if (e != hipSuccess)
+            return hip_fail(e, "ordering the step streams");
+    }
     S->state = state;
     S->pshard = param_shard;
     S->flat = full_flat;
