@@ -382,6 +382,39 @@ int zs_pack(const zs_layout* layout, const uint16_t* param_shard,
             int32_t n_chunks, uint16_t* const* dev_tensor_ptrs,
             void* hip_stream);
 
+/* zs_pack for callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * flat and per-tensor writes, but the chunk table and the tensor pointer
+ * array are staged by the library in a static device array of its own
+ * (ZS_PACK_NOALLOC_MAX_CHUNKS 32-byte chunk records plus
+ * ZS_PACK_NOALLOC_MAX_TENSORS pointers, 1.25 MiB, held on every device the
+ * library runs on until the process ends).  It calls no hipMalloc, hipFree
+ * or other allocating routine.
+ *
+ * param_shard, full_flat: as zs_pack.
+ * tensor_ptrs / n_tensors: a HOST array of the layout's n_tensors per-tensor
+ *   bf16 base pointers (device memory) indexed by tensor_id, or NULL for the
+ *   flat output alone.  Every tensor with a chunk in this rank's shard needs
+ *   a non-NULL pointer.  The array is copied on the stream; from pageable
+ *   host memory that copy completes before the call returns, from pinned
+ *   host memory it runs later, so keep a pinned array unchanged until the
+ *   stream has passed the call.
+ * hip_stream must belong to the current device.
+ * Every call on one device shares the staging and overwrites it: calls
+ * whose work can overlap on one device (on streams with no order between
+ * them, or from several host threads at once) race.  Calls on one stream
+ * are ordered.
+ * Errors: ZS_ERANGE for a layout with more than ZS_PACK_NOALLOC_MAX_CHUNKS
+ * chunks or ZS_PACK_NOALLOC_MAX_TENSORS tensors (checked before anything
+ * else, nothing written); ZS_EINVAL (NULL layout or destinations, n_tensors
+ * other than the layout's, a NULL pointer for a tensor the shard writes, a
+ * stream of another device); ZS_EALIGN as zs_pack; ZS_EDEVICE. */
+#define ZS_PACK_NOALLOC_MAX_CHUNKS 32768
+#define ZS_PACK_NOALLOC_MAX_TENSORS 32768
+int zs_pack_noalloc(const zs_layout* layout, const uint16_t* param_shard,
+                    uint16_t* full_flat, uint16_t* const* tensor_ptrs,
+                    int32_t n_tensors, void* hip_stream);
+
 /* ---- ZeRO-3 / FSDP prefetch -----------------------------------------------
  *
  * Schedules the per-unit parameter gathers of ZeRO-3 / FSDP: a unit's full

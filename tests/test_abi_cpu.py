@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 38
+    assert len(names) == 39
     L = zs.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -320,6 +320,44 @@ def test_step_argument_checks_need_no_device():
     assert L.zs_pack(h, A, A + 2, None, 0, None, None) == -2
     assert L.zs_pack(h, A, None, A, 1, None, None) == -1
     assert L.zs_pack(h, A, None, A, 5, A, None) == -1       # wrong n_chunks
+
+
+def test_pack_noalloc_refuses_before_any_device_use():
+    """zs_pack_noalloc's argument checks and staging limits.  Every case
+    fails before the library touches a device, so the device pointers here
+    are never dereferenced."""
+    L = zs.lib()
+    A = 1 << 20
+    P_ = ctypes.c_void_p
+    numels = [1000, 70000, 129]
+    lay = zs.zs_layout_build(numels, 4, 1, 4 * 256 * 20)
+    h = lay.handle
+    used = {c.tensor_id for c in build_layout(numels, 4, 1,
+                                              4 * 256 * 20).chunks}
+    unused = [t for t in range(3) if t not in used]
+    assert used and unused
+    ptrs = (P_ * 3)(A, A, A)
+    assert L.zs_pack_noalloc(None, A, A, ptrs, 3, None) == -1
+    assert L.zs_pack_noalloc(h, A, None, None, 0, None) == -1   # no output
+    assert L.zs_pack_noalloc(h, A, None, ptrs, 2, None) == -1   # n_tensors
+    holes = (P_ * 3)(*[None if t == min(used) else A for t in range(3)])
+    assert L.zs_pack_noalloc(h, A, None, holes, 3, None) == -1  # NULL, used
+    assert L.zs_pack_noalloc(h, None, A, ptrs, 3, None) == -1   # no shard
+    assert L.zs_pack_noalloc(h, A + 2, A, ptrs, 3, None) == -2
+    assert L.zs_pack_noalloc(h, A, A + 2, ptrs, 3, None) == -2
+    # beyond the static staging: more chunks, or more tensors, than it holds
+    n = zs.ZS_PACK_NOALLOC_MAX_CHUNKS + 1
+    many = zs.zs_layout_build([8] * n, 1, 0, 0)
+    assert zs.zs_layout_info(many)[3] == n
+    assert L.zs_pack_noalloc(many.handle, A, A, (P_ * n)(*([A] * n)), n,
+                             None) == -3
+    assert "chunks" in zs.zs_last_error()
+    n = zs.ZS_PACK_NOALLOC_MAX_TENSORS + 2
+    wide = zs.zs_layout_build([128] * n, 2, 1, 0)     # half of them in rank 1
+    assert zs.zs_layout_info(wide)[3] <= zs.ZS_PACK_NOALLOC_MAX_CHUNKS
+    assert L.zs_pack_noalloc(wide.handle, A, None, (P_ * n)(*([A] * n)), n,
+                             None) == -3
+    assert "tensors" in zs.zs_last_error()
 
 
 def test_empty_layout_calls_are_noops():

@@ -8,14 +8,16 @@ from ._zs import (EXPORTS, LIB_PATH, ZS_ACC_ADD, ZS_ACC_FIRST, ZS_ACC_LAST,
                   ZS_EIO, ZS_EMISMATCH, zs_checkpoint_load,
                   zs_checkpoint_save, zs_layout_fingerprint,
                   ZS_GATHER_MAX_WORLD, ZS_GRADS_SLICES, ZS_GRADS_TILED,
-                  ZS_MAX_GROUP, ZS_TILE, Layout, Prefetch, Stream, ZsError,
+                  ZS_MAX_GROUP, ZS_PACK_NOALLOC_MAX_CHUNKS,
+                  ZS_PACK_NOALLOC_MAX_TENSORS, ZS_TILE, Layout, Prefetch,
+                  Stream, ZsError,
                   chunks_bytes, lib, zs_accumulate, zs_adamw, zs_bucket,
                   zs_bucket_step, zs_buckets_step, zs_chunk, zs_gather,
                   zs_grads_tile, zs_last_error, zs_layout_buckets,
                   zs_layout_build, zs_layout_build_tensors, zs_layout_chunks,
                   zs_layout_info, zs_layout_owners, zs_layout_rank,
                   zs_layout_tensor_offsets, zs_layout_tiles, zs_pack,
-                  zs_prefetch_acquire, zs_prefetch_create, zs_prefetch_free,
+                  zs_pack_noalloc, zs_prefetch_acquire, zs_prefetch_create, zs_prefetch_free,
                   zs_prefetch_issue, zs_prefetch_release, zs_state_mv_pack,
                   zs_state_mv_unpack, zs_state_pack, zs_state_unpack, zs_step,
                   zs_step_bf16, zs_stream_arrive, zs_stream_create,
@@ -26,14 +28,16 @@ __all__ = ["EXPORTS", "LIB_PATH", "ZS_ACC_ADD", "ZS_ACC_FIRST", "ZS_ACC_LAST",
            "ZS_EIO", "ZS_EMISMATCH", "zs_checkpoint_load",
            "zs_checkpoint_save", "zs_layout_fingerprint",
            "ZS_GATHER_MAX_WORLD", "ZS_GRADS_SLICES", "ZS_GRADS_TILED",
-           "ZS_MAX_GROUP", "ZS_TILE", "Layout", "Prefetch", "Stream",
+           "ZS_MAX_GROUP", "ZS_PACK_NOALLOC_MAX_CHUNKS",
+           "ZS_PACK_NOALLOC_MAX_TENSORS", "ZS_TILE", "Layout", "Prefetch",
+           "Stream",
            "ZsError", "chunks_bytes", "lib", "zs_accumulate", "zs_adamw",
            "zs_bucket", "zs_bucket_step", "zs_buckets_step", "zs_chunk",
            "zs_gather", "zs_grads_tile", "zs_last_error", "zs_layout_buckets",
            "zs_layout_build", "zs_layout_build_tensors", "zs_layout_chunks",
            "zs_layout_info", "zs_layout_owners", "zs_layout_rank",
            "zs_layout_tensor_offsets", "zs_layout_tiles", "zs_pack",
-           "zs_prefetch_acquire", "zs_prefetch_create", "zs_prefetch_free",
+           "zs_pack_noalloc", "zs_prefetch_acquire", "zs_prefetch_create", "zs_prefetch_free",
            "zs_prefetch_issue", "zs_prefetch_release", "zs_state_mv_pack",
            "zs_state_mv_unpack", "zs_state_pack", "zs_state_unpack",
            "zs_step", "zs_step_bf16", "zs_stream_arrive", "zs_stream_create",

@@ -18,6 +18,8 @@ ZS_OK, ZS_EINVAL, ZS_EALIGN, ZS_ERANGE, ZS_ENOMEM, ZS_EDEVICE = \
 ZS_EIO, ZS_EMISMATCH = -6, -7
 ZS_TILE = 8192
 ZS_MAX_GROUP = 16
+ZS_PACK_NOALLOC_MAX_CHUNKS = 32768
+ZS_PACK_NOALLOC_MAX_TENSORS = 32768
 ZS_GATHER_MAX_WORLD = 64
 ZS_ACC_FIRST, ZS_ACC_ADD, ZS_ACC_LAST = 0, 1, 2
 ZS_GRADS_SLICES, ZS_GRADS_TILED = 0, 1
@@ -55,7 +57,8 @@ EXPORTS = ["zs_layout_build", "zs_layout_build_tensors", "zs_layout_owners",
            "zs_layout_tensor_offsets", "zs_layout_rank", "zs_layout_free",
            "zs_step", "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
            "zs_state_unpack",
-           "zs_grads_tile", "zs_gather", "zs_pack", "zs_step_bf16",
+           "zs_grads_tile", "zs_gather", "zs_pack", "zs_pack_noalloc",
+           "zs_step_bf16",
            "zs_state_mv_pack", "zs_state_mv_unpack", "zs_accumulate",
            "zs_stream_create", "zs_stream_create_multi",
            "zs_stream_step_begin", "zs_stream_arrive",
@@ -105,6 +108,7 @@ def lib():
     L.zs_state_mv_unpack.argtypes = [p, p, p, p, p]
     L.zs_accumulate.argtypes = [i32, p, p, p, i64, i32, p]
     L.zs_pack.argtypes = [p, p, p, p, i32, p, p]
+    L.zs_pack_noalloc.argtypes = [p, p, p, p, i32, p]
     L.zs_stream_create.argtypes = [p, i32, P(p), i32, i64, p, P(p), i32,
                                    P(p)]
     L.zs_stream_create_multi.argtypes = [p, i32, P(p), i32, i64, P(p), i32,
@@ -133,8 +137,8 @@ def lib():
                  "zs_layout_tensor_offsets", "zs_layout_rank", "zs_step",
                  "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
                  "zs_state_unpack",
-                 "zs_grads_tile", "zs_gather", "zs_pack", "zs_step_bf16",
-                 "zs_state_mv_pack", "zs_state_mv_unpack",
+                 "zs_grads_tile", "zs_gather", "zs_pack", "zs_pack_noalloc",
+                 "zs_step_bf16", "zs_state_mv_pack", "zs_state_mv_unpack",
                  "zs_accumulate", "zs_stream_create", "zs_stream_create_multi",
                  "zs_stream_step_begin",
                  "zs_stream_arrive", "zs_stream_step_end",
@@ -544,6 +548,28 @@ def zs_pack(layout: Layout, param_shard, full_flat=None, dev_chunks=None,
                          _bf16(full_flat, "full_flat"), _ptr(dev_chunks),
                          n_chunks, _ptr(dev_tensor_ptrs), _stream(stream)),
            "zs_pack")
+
+
+def zs_pack_noalloc(layout: Layout, param_shard, full_flat=None,
+                    tensors=None, stream=None) -> None:
+    """zs_pack with the library's own static staging: tensors is a list of
+    per-tensor bf16 device tensors (or device addresses as ints), indexed
+    by tensor id, handed over as a host pointer array; None for the flat
+    output alone."""
+    f, n = layout.sizes()[:2]
+    if n:
+        _need(param_shard, n, "param_shard")
+        _need(full_flat, f, "full_flat")
+    arr, count = None, 0
+    if tensors is not None:
+        count = len(tensors)
+        arr = (ctypes.c_void_p * max(count, 1))(
+            *[x if isinstance(x, int) else _bf16(x, "tensors")
+              for x in tensors])
+    _check(lib().zs_pack_noalloc(layout.handle,
+                                 _bf16(param_shard, "param_shard"),
+                                 _bf16(full_flat, "full_flat"), arr, count,
+                                 _stream(stream)), "zs_pack_noalloc")
 
 
 # ---- ZeRO-2 streaming engine -------------------------------------------------

@@ -48,6 +48,7 @@
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -1251,6 +1252,49 @@ extern "C" int zs_grads_tile(const zs_layout* L, int32_t bucket_id,
     });
 }
 
+namespace {
+
+// The two launches of the pack: the flat all-gather buffer, and every chunk
+// of the chunk table `chunks` (device memory) into the tensors of the
+// device pointer array `tensors`.
+int launch_pack_flat(const zs_layout* L, const uint16_t* param_shard,
+                     uint16_t* full_flat, hipStream_t s)
+{
+    return for_launches(L, [&](const auto& loc, dim3 grid, int64_t e,
+                               int64_t, int64_t f) {
+        using Loc = std::decay_t<decltype(loc)>;
+        grid.x *= kPackP;
+        hipLaunchKernelGGL(pack_flat_kernel<Loc>, grid, dim3(kPackNT), 0, s,
+                           param_shard + e, full_flat + f, loc);
+        return check_launch("pack flat kernel");
+    });
+}
+
+int launch_pack_chunks(const zs_layout* L, const uint16_t* param_shard,
+                       const zs_chunk* chunks, uint16_t* const* tensors,
+                       hipStream_t s)
+{
+    const int32_t n_chunks = (int32_t)L->chunks.size();
+    int64_t longest = 0;
+    for (const zs_chunk& c : L->chunks)
+        longest = c.numel > longest ? c.numel : longest;
+    int64_t gx = (longest + kPackTile - 1) / kPackTile;
+    if (gx > kPackGridX) gx = kPackGridX;
+    for (int32_t c0 = 0; c0 < n_chunks; c0 += (int32_t)kMaxGridY) {
+        const int32_t ny = n_chunks - c0 < kMaxGridY ? n_chunks - c0
+                                                     : (int32_t)kMaxGridY;
+        hipLaunchKernelGGL(pack_chunks_kernel,
+                           dim3((unsigned)gx, (unsigned)ny),
+                           dim3(kPackThreads), 0, s, param_shard, chunks, c0,
+                           tensors);
+        const int rc = check_launch("pack chunks kernel");
+        if (rc) return rc;
+    }
+    return ZS_OK;
+}
+
+}  // namespace
+
 extern "C" int zs_pack(const zs_layout* L, const uint16_t* param_shard,
                        uint16_t* full_flat, const zs_chunk* dev_chunks,
                        int32_t n_chunks, uint16_t* const* dev_tensor_ptrs,
@@ -1278,32 +1322,138 @@ extern "C" int zs_pack(const zs_layout* L, const uint16_t* param_shard,
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
 
     if (full_flat) {
-        const int rc = for_launches(L, [&](const auto& loc, dim3 grid,
-                                           int64_t e, int64_t, int64_t f) {
-            using Loc = std::decay_t<decltype(loc)>;
-            grid.x *= kPackP;
-            hipLaunchKernelGGL(pack_flat_kernel<Loc>, grid, dim3(kPackNT),
-                               0, s, param_shard + e, full_flat + f, loc);
-            return check_launch("pack flat kernel");
-        });
+        const int rc = launch_pack_flat(L, param_shard, full_flat, s);
         if (rc) return rc;
     }
-    if (chunk_mode && n_chunks > 0) {
-        int64_t longest = 0;
-        for (const zs_chunk& c : L->chunks)
-            longest = c.numel > longest ? c.numel : longest;
-        int64_t gx = (longest + kPackTile - 1) / kPackTile;
-        if (gx > kPackGridX) gx = kPackGridX;
-        for (int32_t c0 = 0; c0 < n_chunks; c0 += (int32_t)kMaxGridY) {
-            const int32_t ny = n_chunks - c0 < kMaxGridY ? n_chunks - c0
-                                                         : (int32_t)kMaxGridY;
-            hipLaunchKernelGGL(pack_chunks_kernel,
-                               dim3((unsigned)gx, (unsigned)ny),
-                               dim3(kPackThreads), 0, s, param_shard,
-                               dev_chunks, c0, dev_tensor_ptrs);
-            const int rc = check_launch("pack chunks kernel");
-            if (rc) return rc;
-        }
-    }
+    if (chunk_mode && n_chunks > 0)
+        return launch_pack_chunks(L, param_shard, dev_chunks,
+                                  dev_tensor_ptrs, s);
     return ZS_OK;
+}
+
+// ---- the pack with library-held staging (zs_pack_noalloc) -------------------
+//
+// zs_pack's per-tensor path reads the chunk table and the tensor pointer
+// array from device memory that its caller allocates and uploads.
+// zs_pack_noalloc stages both in `scratch`, a file-scope device array that
+// every call on a device shares (it holds the last call's tables until the
+// process ends; nothing in it needs to start at zero).  The array's name in
+// host code is a host-side stand-in, not a device address: the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and only that address is used (copy destinations, kernel
+// arguments).
+
+constexpr int64_t kNoallocChunkBytes =
+    (int64_t)ZS_PACK_NOALLOC_MAX_CHUNKS * (int64_t)sizeof(zs_chunk);
+constexpr int64_t kNoallocBytes =
+    kNoallocChunkBytes + (int64_t)ZS_PACK_NOALLOC_MAX_TENSORS * 8;
+static_assert(kNoallocChunkBytes % 256 == 0, "pointer table alignment");
+
+static __device__ __align__(256) unsigned char scratch[kNoallocBytes];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch[kScratchDevices] = {};
+
+// The device address of `scratch` on `dev`, which must be the current
+// device; looked up on the first call for that device.
+int scratch_on(int dev, unsigned char** out)
+{
+    using zs::fail;
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(ZS_EDEVICE, "device %d beyond the %d this library tracks",
+                    dev, kScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(ZS_EDEVICE, "hipGetSymbolAddress(scratch): %s",
+                        hipGetErrorString(e));
+        g_scratch[dev] = static_cast<unsigned char*>(p);
+    }
+    *out = g_scratch[dev];
+    return ZS_OK;
+}
+
+}  // namespace
+
+extern "C" int zs_pack_noalloc(const zs_layout* L,
+                               const uint16_t* param_shard,
+                               uint16_t* full_flat,
+                               uint16_t* const* tensor_ptrs,
+                               int32_t n_tensors, void* hip_stream)
+{
+    using zs::fail;
+    zs::clear_error();
+    if (!L) return fail(ZS_EINVAL, "layout is NULL");
+    const int64_t n_chunks = (int64_t)L->chunks.size();
+    const int64_t layout_tensors = (int64_t)L->tensor_numel.size();
+    // the limits first: nothing is touched for a layout beyond them
+    if (n_chunks > ZS_PACK_NOALLOC_MAX_CHUNKS)
+        return fail(ZS_ERANGE, "%lld chunks above the %d the static staging "
+                    "holds", (long long)n_chunks, ZS_PACK_NOALLOC_MAX_CHUNKS);
+    if (layout_tensors > ZS_PACK_NOALLOC_MAX_TENSORS)
+        return fail(ZS_ERANGE, "%lld tensors above the %d the static "
+                    "staging holds", (long long)layout_tensors,
+                    ZS_PACK_NOALLOC_MAX_TENSORS);
+    if (!tensor_ptrs && !full_flat)
+        return fail(ZS_EINVAL, "no destination: full_flat or tensor_ptrs");
+    if (tensor_ptrs && n_tensors != layout_tensors)
+        return fail(ZS_EINVAL, "n_tensors %d != layout's %lld", n_tensors,
+                    (long long)layout_tensors);
+    if (tensor_ptrs)
+        for (const zs_chunk& c : L->chunks)
+            if (!tensor_ptrs[c.tensor_id])
+                return fail(ZS_EINVAL, "tensor_ptrs[%d] is NULL",
+                            c.tensor_id);
+    if (L->shard_numel == 0)
+        return ZS_OK;
+    if (!param_shard) return fail(ZS_EINVAL, "param_shard is NULL");
+    if (!aligned16(param_shard) || (full_flat && !aligned16(full_flat)))
+        return fail(ZS_EALIGN, "param_shard/full_flat not 16-byte aligned");
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+
+    if (full_flat) {
+        const int rc = launch_pack_flat(L, param_shard, full_flat, s);
+        if (rc) return rc;
+    }
+    if (!tensor_ptrs || n_chunks == 0)
+        return ZS_OK;
+    // the staging lives on the stream's device, which must be current
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess)
+        return fail(ZS_EDEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (s) {
+        hipDevice_t sd = 0;
+        e = hipStreamGetDevice(s, &sd);
+        if (e != hipSuccess)
+            return fail(ZS_EDEVICE, "hipStreamGetDevice: %s",
+                        hipGetErrorString(e));
+        if ((int)sd != cur)
+            return fail(ZS_EINVAL, "the stream belongs to device %d, the "
+                        "current device is %d", (int)sd, cur);
+    }
+    unsigned char* base = nullptr;
+    const int rc = scratch_on(cur, &base);
+    if (rc) return rc;
+    zs_chunk* dchunks = reinterpret_cast<zs_chunk*>(base);
+    uint16_t** dptrs =
+        reinterpret_cast<uint16_t**>(base + kNoallocChunkBytes);
+    // copies from the caller's host memory, in stream order after the work
+    // already queued (an earlier call's kernels may still read the staging)
+    e = hipMemcpyAsync(dchunks, L->chunks.data(),
+                       (size_t)n_chunks * sizeof(zs_chunk),
+                       hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(dptrs, tensor_ptrs,
+                           (size_t)n_tensors * sizeof(uint16_t*),
+                           hipMemcpyHostToDevice, s);
+    if (e != hipSuccess)
+        return fail(ZS_EDEVICE, "staging the tables: %s",
+                    hipGetErrorString(e));
+    return launch_pack_chunks(L, param_shard, dchunks, dptrs, s);
 }
