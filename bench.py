@@ -37,8 +37,17 @@ sys.path.insert(0, ROOT)
 
 HP = dict(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
 PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E, 8 TB/s
-METRIC = ("optimizer-step params/s per GPU + achieved HBM GB/s (% of peak), "
-          "8B W=8 shard")
+METRIC_STEM = ("optimizer-step params/s per GPU + achieved HBM GB/s (% of "
+               "peak), ")
+SHARD_LABEL = {"llama8b": "8B W=8 shard", "dense7b": "7B dense W=64 shard",
+               "gpt2": "GPT-2-small W=8 shard", "tiny": "tiny W=4 shard",
+               "llama70b": "70B W=16 shard"}
+METRIC = METRIC_STEM + SHARD_LABEL["llama8b"]
+
+
+def metric_for(workload: str) -> str:
+    """The step metric, labelled with the shard it was measured on."""
+    return METRIC_STEM + SHARD_LABEL[workload]
 KERNELS = os.path.join(ROOT, "zero_sharded_optimizer_shard_amd",
                        "libzs.kernels.json")
 # the kernel whose HBM counters the roofline's traffic figure comes from
@@ -209,10 +218,17 @@ def cpu_baseline(W, seconds: float, threads: int = 1):
                        f"{el:.1f} s")
 
 
-def host_cores() -> int:
-    """Cores this process may use, capped at 16 (one GPU's share of the
-    host on a shared node)."""
-    return max(1, min(16, len(os.sched_getaffinity(0))))
+def host_cores():
+    """(threads for the all-cores oracle, cores in the affinity mask): every
+    core of the process's affinity mask, capped by OMP_NUM_THREADS where the
+    host sets a per-process thread share (a shared GPU node gives each GPU's
+    jobs a slice of its cores and says so there)."""
+    mask = len(os.sched_getaffinity(0))
+    n = mask
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n), mask
 
 
 def arena_views(parts):
@@ -316,6 +332,50 @@ def time_each(fn, K, st):
         b.record(st)
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in evs]
+
+
+def placement_draws(count, new_arena, first, lay, W, n, K, warmup, st,
+                    first_frac):
+    """The same step on further arenas: where the buffers land in HBM moves
+    this stream's bandwidth by a few points, and the runtime gives no way to
+    choose it.  Each new arena is allocated while the earlier ones are still
+    alive, so each lands elsewhere; it gets a copy of the first arena's
+    inputs and K timed launches after `warmup` untimed ones.  The first draw
+    stays the reported value; this is its spread."""
+    import torch
+    import zero_sharded_optimizer_shard_amd as zs
+    keep, fracs = [], [first_frac]
+    t = 1 << 20                  # a step counter of their own
+    for k in range(count):
+        bufs = new_arena()
+        for dst, src in zip(bufs, first):
+            dst.copy_(src)
+        keep.append(bufs)
+        torch.cuda.synchronize()
+
+        def one():
+            nonlocal t
+            t += 1
+            zs.zs_step(lay, bufs[0], bufs[1], None, bufs[2],
+                       grad_layout="tiled", step=t, stream=st, **HP)
+
+        for _ in range(warmup):
+            one()
+        ms, _ = time_steps(one, K, st)
+        fracs.append((2 * W + 26) * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
+        log(f"  placement {k + 2}: {ms:.3f} ms per launch "
+            f"({fracs[-1]:.1%} of 8 TB/s)")
+    del keep
+    torch.cuda.empty_cache()
+    srt = sorted(fracs)
+    mid = len(srt) // 2
+    med = srt[mid] if len(srt) % 2 else (srt[mid - 1] + srt[mid]) / 2
+    log(f"placements: first {first_frac:.1%}, min {srt[0]:.1%}, median "
+        f"{med:.1%}, max {srt[-1]:.1%} over {len(fracs)} arenas")
+    return {"arenas": len(fracs), "frac_of_peak": fracs, "first": first_frac,
+            "min": srt[0], "median": med, "max": srt[-1],
+            "note": "same inputs; each arena a separate allocation, all "
+                    "alive at once; the first draw is the reported value"}
 
 
 def bf16_main(args, w):
@@ -696,7 +756,10 @@ def stream_main(args, w):
     uses pool b mod 4), or a device copy from an HBM pool (--arrival d2d).
     Reported per full step (every bucket once): the wall time, the same
     uploads alone, the same bucket steps alone with the staging resident,
-    and the exposed step time (wall - uploads)."""
+    and the exposed step time, measured inside each streamed full step: the
+    end of the last launch on any step stream minus the end of the last
+    copy on any upload stream (events recorded on every stream after the
+    step's last call)."""
     import torch
     import synth
     import zero_sharded_optimizer_shard_amd as zs
@@ -788,7 +851,7 @@ def stream_main(args, w):
                 for k in sl:
                     done[k] = ev
 
-    K = min(args.steps, w.steps)            # full steps are long here
+    K = w.steps                 # full steps are long here: the config's 2
 
     def timed(**kw):
         torch.cuda.synchronize()
@@ -836,15 +899,40 @@ def stream_main(args, w):
             zs.zs_stream_arrive(eng, b, pool[b % 4])
         zs.zs_stream_step_end(eng)
 
+    def stream_ends():
+        """Events after the last work queued on every upload and every
+        step stream."""
+        ends = []
+        for group in (ups, sts):
+            evs = []
+            for s_ in group:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(s_)
+                evs.append(e)
+            ends.append(evs)
+        return ends
+
     engine_step()
     torch.cuda.synchronize()
+    marks = [stream_ends()]
     t0 = time.perf_counter()
-    for _ in range(K):
+    for _ in range(K):              # steps queued back to back, no host sync
         engine_step()
+        marks.append(stream_ends())
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / K
-    log(f"streaming (zs_stream engine): {wall_ms:.2f} ms per full step, "
-        f"exposed {wall_ms - up_ms:.2f} ms")
+    ref = marks[0][0][0]
+    up_end = [max(ref.elapsed_time(e) for e in eu) for eu, _ in marks]
+    step_end = [max(ref.elapsed_time(e) for e in es) for _, es in marks]
+    # per full step: the last launch's end after the last copy's end, and
+    # the span of the step's copies (from the previous step's last copy:
+    # the host queues far ahead of the copies, so they run back to back)
+    exposed = [step_end[k] - up_end[k] for k in range(1, K + 1)]
+    up_span = [up_end[k] - up_end[k - 1] for k in range(1, K + 1)]
+    log(f"streaming (zs_stream engine): {wall_ms:.2f} ms per full step; "
+        f"copies {', '.join(f'{x:.1f}' for x in up_span)} ms; last launch "
+        f"ends {', '.join(f'{x:.3f}' for x in exposed)} ms after the last "
+        f"copy (wall - uploads alone: {wall_ms - up_ms:.2f} ms)")
     bpp = 2 * W + 26
     arrival_bytes = sum(cnt) * 2
     kern_gbs = bpp * n / (kern_ev_ms * 1e-3) / 1e9
@@ -878,7 +966,13 @@ def stream_main(args, w):
                       "uploads_alone_ms_per_step": up_ms,
                       "bucket_steps_alone_ms_per_step": kern_ms,
                       "bucket_steps_alone_event_ms": kern_ev_ms,
-                      "exposed_step_ms": wall_ms - up_ms,
+                      "exposed_step_ms": sum(exposed) / len(exposed),
+                      "exposed_step_ms_each": exposed,
+                      "exposed_definition": "per full step: end of the "
+                      "last launch on any step stream - end of the last "
+                      "copy on any upload stream, events in the same pass",
+                      "wall_minus_uploads_alone_ms": wall_ms - up_ms,
+                      "copies_in_pass_ms_each": up_span,
                       "python_scheduled_wall_ms": py_ms,
                       "arrival_bytes_per_step": arrival_bytes,
                       "arrival_GBps": arrival_bytes / (up_ms * 1e-3) / 1e9,
@@ -927,6 +1021,11 @@ def main():
     ap.add_argument("--step-streams", type=int, default=2,
                     help="streaming mode: step streams the landed groups "
                     "are spread over, in turn")
+    ap.add_argument("--placements", type=int, default=3,
+                    help="also time the step on this many more arenas "
+                    "(each a separate allocation, all alive at once), same "
+                    "inputs; reported beside the first draw, which stays "
+                    "the headline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ceiling", action="store_true",
@@ -994,23 +1093,32 @@ def main():
 
     n_tiles = zs.zs_layout_tiles(lay)
     T = zs.ZS_TILE
-    # the step's three buffers from one arena, gradients first (see
-    # arena_views); the plain slices, kept for the slices-layout pass,
-    # outside it
-    Gt, state, flat = arena_views([(n_tiles * W * T, torch.bfloat16),
-                                   (n_tiles * 3 * T, torch.float32),
-                                   (flat_n, torch.bfloat16)])
-    flat.zero_()
-    G = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
-    S.dev_grads(G, W, n, 1, w.grad_sigma)
-    zs.zs_grads_tile(lay, -1, G, n, Gt)
+    bpp = 2 * W + 26
+    parts = [(n_tiles * W * T, torch.bfloat16),
+             (n_tiles * 3 * T, torch.float32), (flat_n, torch.bfloat16)]
+    # A working set of a few times the 256 MB Infinity Cache or less would
+    # be served partly from it; such shards (the GPT-2-sized one) are
+    # stepped over R = 4 independent copies of every operand in turn, so
+    # that each launch's bytes come from HBM.
+    R = 1 if bpp * n >= (1 << 30) else 4
+    # each set's three step buffers from one arena, gradients first (see
+    # arena_views); its plain slices, for the slices-layout pass, outside it
+    sets = []
     master = torch.empty(n, dtype=torch.float32, device="cuda")
     synth.dev_normal_f32(master, 0, synth.TAG_MASTER, 0, 0, 0,
                          w.master_sigma)
-    zs.zs_state_pack(lay, master, None, None, state)
+    for _ in range(R):
+        Gt, state, flat = arena_views(parts)
+        flat.zero_()
+        G = torch.empty((W, n), dtype=torch.bfloat16, device="cuda")
+        S.dev_grads(G, W, n, 1, w.grad_sigma)
+        zs.zs_grads_tile(lay, -1, G, n, Gt)
+        zs.zs_state_pack(lay, master, None, None, state)
+        sets.append((Gt, state, flat, G))
     del master
+    Gt, state, flat, G = sets[0]
     torch.cuda.synchronize()
-    log(f"inputs resident ({n_tiles} tiles)")
+    log(f"inputs resident ({n_tiles} tiles, {R} set{'s' if R > 1 else ''})")
 
     st = torch.cuda.current_stream()
     t = 0
@@ -1018,13 +1126,15 @@ def main():
     def step_tiled():
         nonlocal t
         t += 1
-        zs.zs_step(lay, Gt, state, None, flat, grad_layout="tiled", step=t,
-                   stream=st, **HP)
+        Gt_, state_, flat_, _ = sets[t % R]
+        zs.zs_step(lay, Gt_, state_, None, flat_, grad_layout="tiled",
+                   step=t, stream=st, **HP)
 
     def step_slices():
         nonlocal t
         t += 1
-        zs.zs_step(lay, G, state, None, flat, grad_layout="slices",
+        _, state_, flat_, G_ = sets[t % R]
+        zs.zs_step(lay, G_, state_, None, flat_, grad_layout="slices",
                    grad_stride=n, step=t, stream=st, **HP)
 
     for _ in range(args.warmup):
@@ -1032,7 +1142,6 @@ def main():
     torch.cuda.synchronize()
     K = args.steps
     avg_ms, ms_per_step = time_steps(step_tiled, K, st)
-    bpp = 2 * W + 26
     achieved = bpp * n / (avg_ms * 1e-3) / 1e9
     log(f"zs_step (tiled): {avg_ms:.3f} ms per launch, {K} back to back "
         f"-> {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.1%} of 8 TB/s)")
@@ -1093,6 +1202,10 @@ def main():
             f"{len(w.numels)} tensors {ms:.3f} ms "
             f"({extra['pack_GBps']['chunks']:.0f} GB/s)")
         del p, tensors
+    if args.placements > 0 and R == 1:
+        extra["placements"] = placement_draws(
+            args.placements, lambda: arena_views(parts), (Gt, state, flat),
+            lay, W, n, K, args.warmup, st, achieved / PEAK_HBM_GBS)
     if args.ceiling and not args.whole_tensors:
         c = ceiling(Gt, state, flat, lay, W, n)
         c["step_frac_of_same_mix"] = achieved / c["same_mix"]["GBps"]
@@ -1109,9 +1222,11 @@ def main():
               "buckets": nb, "bucket_cap_mb": 25,
               "bytes_per_param": bpp,
               # bytes one step touches, against MI355X's 256 MB Infinity
-              # Cache: a smaller working set would be served from cache
+              # Cache: a smaller working set would be served from cache;
+              # R independent sets are stepped in turn
               "working_set_bytes": bpp * n,
-              "cache_resident": bpp * n < (256 << 20),
+              "state_sets": R,
+              "cache_resident": bpp * n * R < (256 << 20),
               "grads_layout": "tiled [tile][W][8192]",
               "state_layout": "tiled [tile][master|m|v][8192]",
               "allocation": "one arena: tiled gradients, state, flat"}
@@ -1121,7 +1236,7 @@ def main():
                       "first to the least-loaded rank", owned_tensors=nb)
         del config["bucket_cap_mb"]
     out = {
-        "metric": METRIC if not args.whole_tensors else
+        "metric": metric_for(args.workload) if not args.whole_tensors else
         "whole-tensor-assignment optimizer-step params/s per GPU + achieved "
         "HBM GB/s (% of peak)",
         "value": n / (ms_per_step * 1e-3),
@@ -1143,16 +1258,19 @@ def main():
         "achieved_GBps_per_step": bpp * n / (ms_per_step * 1e-3) / 1e9,
         **extra,
     }
-    del G, Gt, state, flat
+    del G, Gt, state, flat, sets
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         out["cpu_baseline"] = cpu_baseline(W, args.cpu_seconds)
-        nc = host_cores()
+        nc, mask = host_cores()
         if nc > 1:
-            log(f"timing the CPU oracle on {nc} cores ...")
-            out["cpu_baseline_all_cores"] = cpu_baseline(W, args.cpu_seconds,
-                                                         nc)
+            log(f"timing the CPU oracle on {nc} cores (affinity mask: "
+                f"{mask}) ...")
+            allc = cpu_baseline(W, args.cpu_seconds, nc)
+            allc["affinity_mask_cores"] = mask
+            allc["thread_share"] = os.environ.get("OMP_NUM_THREADS")
+            out["cpu_baseline_all_cores"] = allc
     print(json.dumps(out), flush=True)
 
 

@@ -62,11 +62,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int64_t kTile = ZS_TILE;
-// the layout conversions and the flat pack: one 512-thread workgroup per
-// tile, four 4-element units per thread
-constexpr int kThreads = 512;
-constexpr int kUnits = 4;
-static_assert(kTile == (int64_t)kThreads * kUnits * 4, "tile shape");
+// Each kernel states its own workgroup shape beside it: the step's work
+// shapes (Shape below), kStThreads / kGtThreads / kPackNT for the layout
+// conversions and the flat pack, kPackThreads for the per-tensor pack.
 constexpr int64_t kMaxGridY = 65535;
 
 // Work shape of the step kernels: NT threads per workgroup, U 4-element
@@ -127,7 +125,7 @@ __device__ __forceinline__ bool tile_of(const Geom& g, TileRef& r)
 
 // element offset of unit k of this thread inside its tile, for a workgroup
 // of NT threads that is part `blockIdx.x % P` of P on the tile
-template <int P = 1, int NT = kThreads>
+template <int P, int NT>
 __device__ __forceinline__ int unit_off(int k)
 {
     const int part = (int)(blockIdx.x % P);
