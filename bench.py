@@ -50,9 +50,16 @@ def metric_for(workload: str) -> str:
     return METRIC_STEM + SHARD_LABEL[workload]
 KERNELS = os.path.join(ROOT, "zero_sharded_optimizer_shard_amd",
                        "libzs.kernels.json")
-# the kernel whose HBM counters the roofline's traffic figure comes from
+# the kernels whose HBM counters the roofline's traffic figure comes from,
+# per workload: the tiled mixed-precision step in its work shape there
 HEADLINE_KERNEL = ("_ZN12_GLOBAL__N_111step_kernelILi8ELb1ENS_5ShapeILi64ELi1E"
                    "Li4EEELb0EEEvNS_8StepArgsE")
+STEP_KERNELS = {
+    "llama8b": (HEADLINE_KERNEL, "step_kernel<8, true, Shape<64, 1, 4> >"),
+    "dense7b": ("_ZN12_GLOBAL__N_111step_kernelILi64ELb1ENS_5ShapeILi512ELi4"
+                "ELi8EEELb0EEEvNS_8StepArgsE",
+                "step_kernel<64, true, Shape<512, 4, 8> >"),
+}
 
 
 def log(*a):
@@ -95,13 +102,15 @@ def read_counter_csv(path: str, counter: str):
     return [(k, v) for _, k, v in rows]
 
 
-def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int) -> dict:
-    """HBM bytes per launch of the headline step from two rocprofv3 --pmc
+def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
+                   workload: str = "llama8b") -> dict:
+    """HBM bytes per launch of the workload's step from two rocprofv3 --pmc
     runs of `bench.py --copy-calibration` (FETCH_SIZE, then WRITE_SIZE, KiB
     per dispatch), each scaled by what the same counter reads for the
-    calibration copy of 4 GiB; written to profiles/traffic_llama8b.json with
-    the digest of the kernel's machine code in the current build (the
+    calibration copy of 4 GiB; written to profiles/traffic_<workload>.json
+    with the digest of the kernel's machine code in the current build (the
     counters must have been taken on that build)."""
+    symbol, kname = STEP_KERNELS[workload]
     fetch = read_counter_csv(fetch_csv, "FETCH_SIZE")
     write = read_counter_csv(write_csv, "WRITE_SIZE")
     copy_bytes = 4 << 30
@@ -129,11 +138,11 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int) -> dict:
     wr = avg(tw) * 1024 * ws
     alg = (2 * W + 26) * n
     rec = {
-        "kernel": f"step_kernel<{W}, true, Shape<64, 1, 4> > (zs_step, "
-                  "tiled gradients, tiled state, flat output)",
-        "workload": f"llama8b rank-0 shard, W={W}, {n:,} elements",
-        "kernel_symbol": HEADLINE_KERNEL,
-        "kernel_sha256_16": kernel_digest(HEADLINE_KERNEL),
+        "kernel": f"{kname} (zs_step, tiled gradients, tiled state, flat "
+                  "output)",
+        "workload": f"{workload} rank-0 shard, W={W}, {n:,} elements",
+        "kernel_symbol": symbol,
+        "kernel_sha256_16": kernel_digest(symbol),
         "copy_calibration": {"bytes_read": copy_bytes,
                              "bytes_written": copy_bytes,
                              "FETCH_SIZE_KiB": cf[0], "WRITE_SIZE_KiB": cw[0],
@@ -151,7 +160,7 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int) -> dict:
         rec["plain_slices"] = {"bytes_read_per_launch": prd,
                                "bytes_written_per_launch": pwr,
                                "ratio_to_algorithmic": (prd + pwr) / alg}
-    with open(os.path.join(ROOT, "profiles", "traffic_llama8b.json"),
+    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"),
               "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -1038,17 +1047,17 @@ def main():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV",
                                                           "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 --pmc counter CSVs of "
-                    "a --copy-calibration run into profiles/"
-                    "traffic_llama8b.json")
+                    "a --copy-calibration run of --workload into profiles/"
+                    "traffic_<workload>.json")
     args = ap.parse_args()
 
     if args.record_traffic:
         import zero_sharded_optimizer_shard_amd as zs
         from synth import workloads as wl
-        w = wl.presets()["llama8b"]
+        w = wl.presets()[args.workload]
         n = zs.zs_layout_info(zs.zs_layout_build(w.numels, w.world,
                                                  w.rank))[1]
-        rec = record_traffic(*args.record_traffic, n, w.world)
+        rec = record_traffic(*args.record_traffic, n, w.world, args.workload)
         print(json.dumps({k: rec[k] for k in
                           ("bytes_per_launch", "ratio_to_algorithmic")}))
         return

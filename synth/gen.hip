@@ -284,6 +284,80 @@ __global__ __launch_bounds__(64) void k_mix_stream(
     mix_store(f, 16384u, 8u * u, u32x2{c.x ^ c.z, c.y ^ c.w});
 }
 
+/* The same access pattern in the step's work shape at W >= 32: one
+ * 512-thread workgroup per tile, thread t owning the 4-element units t,
+ * t + 512, t + 1024 and t + 1536 of the tile; the three state rows first,
+ * then the W gradient rows in batches of NB (all loads of a batch issued
+ * before use), the same stores. */
+template <int WT, int NB>
+__global__ __launch_bounds__(512) void k_mix_stream_deep(
+    const u32x2* __restrict__ grads, u32x4* __restrict__ state,
+    u32x2* __restrict__ flat, int64_t S, int64_t S_last, int64_t B,
+    int64_t tpb, int q_last)
+{
+    constexpr int U = 4;
+    const int q = blockIdx.y;
+    const int64_t slice = q == q_last ? S_last : S;
+    const int64_t x = blockIdx.x;
+    const int64_t j0 = x * 8192;
+    if (j0 >= slice)
+        return;
+    const int64_t tile = (int64_t)q * tpb + x;
+    const int64_t nv = slice - j0 < 8192 ? slice - j0 : 8192;
+    const u32x2* g = grads + tile * WT * 2048;
+    u32x4* st = state + tile * 3 * 2048;
+    u32x2* f = flat + ((int64_t)q * B + j0) / 4;
+    u32x4 a0[U], b0[U], c0[U];
+    u32x2 xx[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int u = k * 512 + (int)threadIdx.x;
+        xx[k] = u32x2{0u, 0u};
+        if (4 * u < nv) {
+            a0[k] = __builtin_nontemporal_load(st + u);
+            b0[k] = __builtin_nontemporal_load(st + 2048 + u);
+            c0[k] = __builtin_nontemporal_load(st + 4096 + u);
+        }
+    }
+#pragma unroll
+    for (int s0 = 0; s0 < WT; s0 += NB) {
+        u32x2 y[U][NB];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int u = k * 512 + (int)threadIdx.x;
+            if (4 * u < nv) {
+#pragma unroll
+                for (int i = 0; i < NB; ++i)
+                    y[k][i] = __builtin_nontemporal_load(
+                        g + (int64_t)(s0 + i) * 2048 + u);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int u = k * 512 + (int)threadIdx.x;
+            if (4 * u < nv) {
+#pragma unroll
+                for (int i = 0; i < NB; ++i)
+                    xx[k] ^= y[k][i];
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int u = k * 512 + (int)threadIdx.x;
+        if (4 * u >= nv)
+            continue;
+        const u32x4 x4 = {xx[k].x, xx[k].y, xx[k].x, xx[k].y};
+        const u32x4 a = a0[k] ^ x4;
+        const u32x4 b = b0[k] ^ a;
+        const u32x4 c = c0[k] ^ b;
+        mix_store(st, 32768u, 16u * u, a);
+        mix_store(st + 2048, 32768u, 16u * u, b);
+        mix_store(st + 4096, 32768u, 16u * u, c);
+        mix_store(f, 16384u, 8u * u, u32x2{c.x ^ c.z, c.y ^ c.w});
+    }
+}
+
 /* grads: tiled [tiles][W][8192] bf16; state: tiled [tiles][3][8192] fp32;
  * flat: the bf16 flat buffer; S, B: slice and numel of a full bucket,
  * S_last the last bucket's slice, nb buckets (all but the last full).
@@ -303,9 +377,15 @@ extern "C" int synth_mix_stream_dev(const void* grads, void* state,
     /* fewer than 2^32 work-items along x */
     if (tpb * 32 * 64 >= ((int64_t)1 << 32)) return -3;
     const dim3 grid((unsigned)(tpb * 32), (unsigned)nb);
-    /* slices 4 at a time below W = 32, 8 above; at W >= 32 the step itself
-     * runs 512-thread workgroups, so there this is the one-wave reference */
-    if (W == 8)
+    /* slices 4 at a time below W = 32, 8 above; at W = 64 the step's own
+     * 512-thread shape, at other W >= 32 the one-wave reference */
+    if (W == 64)
+        hipLaunchKernelGGL((k_mix_stream_deep<64, 8>),
+                           dim3((unsigned)tpb, (unsigned)nb), dim3(512), 0,
+                           (hipStream_t)stream, (const u32x2*)grads,
+                           (u32x4*)state, (u32x2*)flat, S, S_last, B, tpb,
+                           nb - 1);
+    else if (W == 8)
         hipLaunchKernelGGL((k_mix_stream<8, 4>), grid, dim3(64), 0,
                            (hipStream_t)stream, (const u32x2*)grads,
                            (u32x4*)state, (u32x2*)flat, (int)W, S, S_last, B,
