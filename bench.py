@@ -1171,6 +1171,29 @@ def main():
                                   GBps=sl_gbs, frac=sl_gbs / PEAK_HBM_GBS)
     log(f"zs_step (plain slices): {sl_avg:.3f} ms -> {sl_gbs:.0f} GB/s "
         f"({sl_gbs / PEAK_HBM_GBS:.1%})")
+    if R == 1:
+        # the same step on three plain fp32 arrays (zs_step_plain): the
+        # state unpacked from the tiled form, tiled gradients, flat output
+        plain = [torch.empty(n, dtype=torch.float32, device="cuda")
+                 for _ in range(3)]
+        zs.zs_state_unpack(lay, state, *plain)
+
+        def step_plain():
+            nonlocal t
+            t += 1
+            zs.zs_step_plain(lay, Gt, *plain, None, flat,
+                             grad_layout="tiled", step=t, stream=st, **HP)
+
+        for _ in range(2):
+            step_plain()
+        pl_avg, _ = time_steps(step_plain, K, st)
+        pl_gbs = bpp * n / (pl_avg * 1e-3) / 1e9
+        extra["plain_state"] = dict(kernel_ms_avg=pl_avg, GBps=pl_gbs,
+                                    frac=pl_gbs / PEAK_HBM_GBS)
+        log(f"zs_step_plain (plain master/m/v): {pl_avg:.3f} ms -> "
+            f"{pl_gbs:.0f} GB/s ({pl_gbs / PEAK_HBM_GBS:.1%})")
+        del plain
+        torch.cuda.empty_cache()
     if args.unfused:
         p = torch.empty(n, dtype=torch.bfloat16, device="cuda")
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]

@@ -203,7 +203,15 @@ void zs_layout_free(zs_layout* layout);
 
 /* ---- device calls -------------------------------------------------------- */
 
-/* One optimizer step over the whole shard of `layout`'s rank.
+/* One optimizer step over the whole shard of `layout`'s rank: one rank's
+ * ZeRO-1/2 step (CS336 lecture 8 notes, "Code example: ZeRO-1": the
+ * reduce-scatter leaves each rank the summed gradient of its own slice, the
+ * rank updates only that slice with its own fp32 optimizer state, and the
+ * all-gather concatenates the updated slices; "Core concepts": bf16
+ * parameter and gradient, fp32 master and two fp32 Adam moments; the
+ * optimizer is AdamW, DDP-to-ZeRO blog section 3.3).  On one GPU the W
+ * slices are resident, the sum over them is the local arithmetic of the
+ * reduce-scatter, and full_flat is this rank's part of the all-gather.
  *
  * grads, grad_layout, grad_stride: the W gradient slices in one of the two
  *   layouts above.  ZS_GRADS_SLICES: grad_stride >= shard_numel and a
@@ -230,6 +238,21 @@ int zs_step(const zs_layout* layout, const uint16_t* grads,
             int32_t grad_layout, int64_t grad_stride, float* state,
             uint16_t* param_shard, uint16_t* full_flat, const zs_adamw* hp,
             int64_t step, void* hip_stream);
+
+/* zs_step on three plain fp32 arrays instead of the tiled state: master, m
+ * and v are [shard_numel] each, element i the shard's element i (padding
+ * included), updated in place; everything else as zs_step, with the same
+ * arithmetic and the same results bit for bit.  For callers that keep the
+ * optimizer state as plain arrays; the tiled state of zs_step reaches a
+ * higher bandwidth on MI355X (its three rows of a tile are adjacent), and
+ * zs_state_pack / zs_state_unpack convert between the two.  Errors as
+ * zs_step; ZS_EINVAL when master, m or v is NULL, ZS_EALIGN when one is not
+ * 16-byte aligned. */
+int zs_step_plain(const zs_layout* layout, const uint16_t* grads,
+                  int32_t grad_layout, int64_t grad_stride, float* master,
+                  float* m, float* v, uint16_t* param_shard,
+                  uint16_t* full_flat, const zs_adamw* hp, int64_t step,
+                  void* hip_stream);
 
 /* The same step over one bucket's part of the shard, for the ZeRO-2
  * streaming mode in which buckets arrive one by one (podcast summary, "Data

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 39
+    assert len(names) == 40
     L = zs.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -314,6 +314,24 @@ def test_step_argument_checks_need_no_device():
     big = zs.zs_layout_build([1000], 65, 0)
     assert L.zs_gather(big.handle, (P_ * 65)(*([A] * 65)), 0, 8, A,
                        None) == -1
+    # the step on plain arrays: zs_step's checks, and master, m, v each
+    hpp = ctypes.byref(zs.zs_adamw(3e-4, 0.9, 0.95, 1e-8, 0.1))
+    assert L.zs_step_plain(h, A, 0, 1 << 20, A, None, A, A, None, hpp, 1,
+                           None) == -1                       # m NULL
+    assert L.zs_step_plain(h, A, 0, 1 << 20, A, A, None, A, None, hpp, 1,
+                           None) == -1                       # v NULL
+    assert L.zs_step_plain(h, A, 0, 1 << 20, None, A, A, A, None, hpp, 1,
+                           None) == -1                       # master NULL
+    assert L.zs_step_plain(h, A, 0, 1 << 20, A, A + 4, A, A, None, hpp, 1,
+                           None) == -2
+    assert L.zs_step_plain(h, A, 0, 1 << 20, A + 8, A, A, A, None, hpp, 1,
+                           None) == -2
+    assert L.zs_step_plain(h, A, 0, 1 << 20, A, A, A, A, None, hpp, 0,
+                           None) == -1                       # step 0
+    assert L.zs_step_plain(h, A, 2, 1 << 20, A, A, A, A, None, hpp, 1,
+                           None) == -1                       # grad layout
+    assert L.zs_step_plain(h, A, 0, 1 << 20, A, A, A, None, None, hpp, 1,
+                           None) == -1                       # no output
     # pack
     assert L.zs_pack(h, A, None, None, 0, None, None) == -1
     assert L.zs_pack(h, None, A, None, 0, None, None) == -1

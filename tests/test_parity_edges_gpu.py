@@ -226,35 +226,48 @@ SHAPES = [(2, 300), (5, 1100), (8, 4100), (5, 4100), (32, 4100), (33, 4100),
           (64, 300)]
 
 
+@pytest.mark.parametrize("state_form", ["tiled", "plain"])
 @pytest.mark.parametrize("hp_name", list(HPS))
 @pytest.mark.parametrize("layout", ["tiled", "slices"])
 @pytest.mark.parametrize("W,tiles", SHAPES)
-def test_step_edge_values(W, tiles, layout, hp_name):
+def test_step_edge_values(W, tiles, layout, hp_name, state_form):
+    """zs_step (tiled state) and zs_step_plain (three plain arrays)."""
     hp = HPS[hp_name]
-    print(f"case edge step W={W} tiles={tiles} {layout} {hp_name}",
-          flush=True)
+    print(f"case edge step W={W} tiles={tiles} {layout} {hp_name} "
+          f"{state_form} state", flush=True)
     rng = np.random.default_rng(1000 * W + tiles)
     lay, n = one_bucket(W, tiles)
     n_tiles = tiles
     master, m, v = edge_state(rng)
-    state = to_tiled(torch.stack([expand(x, n) for x in (master, m, v)]),
-                     n_tiles)
+    rows = torch.stack([expand(x, n) for x in (master, m, v)])
+    state = to_tiled(rows, n_tiles) if state_form == "tiled" else None
+
+    def step(grads, t, **kw):
+        if state_form == "tiled":
+            zs.zs_step(lay, grads, state, p, None, step=t, **kw, **hp)
+        else:
+            zs.zs_step_plain(lay, grads, rows[0], rows[1], rows[2], p, None,
+                             step=t, **kw, **hp)
+
+    def read_state():
+        if state_form == "tiled":
+            return from_tiled(state, 3, n_tiles, n)
+        return rows.cpu().numpy()
+
     p = torch.empty(n, dtype=torch.int16, device="cuda")
     om, omm, ov = master.copy(), m.copy(), v.copy()
     for t in (1, 2):
         Gp = edge_gradients(W, rng)
         G = expand(Gp.view(np.int16), n)
         if layout == "tiled":
-            zs.zs_step(lay, to_tiled(G, n_tiles), state, p, None,
-                       grad_layout="tiled", step=t, **hp)
+            step(to_tiled(G, n_tiles), t, grad_layout="tiled")
         else:
             Gs = torch.zeros((W, n + 8), dtype=torch.int16, device="cuda")
             Gs[:, :n] = G
-            zs.zs_step(lay, Gs, state, p, None, grad_layout="slices",
-                       grad_stride=n + 8, step=t, **hp)
+            step(Gs, t, grad_layout="slices", grad_stride=n + 8)
         op = O.step(Gp, om, omm, ov, O.AdamW(**hp), t)
         torch.cuda.synchronize()
-        got = from_tiled(state, 3, n_tiles, n)
+        got = read_state()
         for row, name, want in ((0, "master", om), (1, "m", omm),
                                 (2, "v", ov)):
             assert_periodic_equal(got[row], want, f"t={t} {name}")

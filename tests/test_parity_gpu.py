@@ -634,6 +634,80 @@ def test_bucket_groups_match_the_oracle(W, cap, groups, layout):
                   flat_before=flat0)
 
 
+def run_plain(ref, layout, steps, stride_pad=8):
+    """zs_step_plain on the case's shard (three plain fp32 arrays, the bf16
+    shard and a sentinel-filled flat buffer) for the given steps, each
+    checked against the oracle's arrays, bit for bit."""
+    lay, lay_o, n, W = ref.lay, ref.lay_o, ref.n, ref.W
+    master, m, v = dev_f32(n), dev_f32(n), dev_f32(n)
+    S.dev_state(master, m, v, 0.02, ref.seed, ref.pad, ref.warm)
+    p = dev_bf16(n)
+    F = lay_o.flat_numel
+    flat = dev_bf16(F)
+    synth.dev_bits16(flat, 8, synth.TAG_SENTINEL, 0, 0, 0)
+    flat0 = synth.cpu_bits16(F, 8, synth.TAG_SENTINEL, 0, 0, 0)
+    G = torch.empty((W, n + stride_pad), dtype=torch.bfloat16, device="cuda")
+    Gt = dev_bf16(max(n_tiles(lay_o) * W * TILE, 8))
+    offs = tile_offsets(lay_o)
+    for t in steps:
+        ref.oracle_step(t)
+        ref.dev_grads(G, t)
+        if layout == "tiled":
+            for b_id, t0 in enumerate(offs):
+                x = dev_tiled_bucket(G, lay_o, b_id)
+                Gt[t0 * W * TILE:t0 * W * TILE + x.numel()] = x
+            zs.zs_step_plain(lay, Gt, master, m, v, p, flat,
+                             grad_layout="tiled", step=t, **HP)
+        else:
+            zs.zs_step_plain(lay, G, master, m, v, p, flat,
+                             grad_layout="slices", grad_stride=n + stride_pad,
+                             step=t, **HP)
+        torch.cuda.synchronize()
+        where = f"plain W={W} rank={ref.rank} t={t} {layout}"
+        assert_parity(dict(master=npf(master), m=npf(m), v=npf(v),
+                           p=np16(p)),
+                      dict(master=ref.om, m=ref.omm, v=ref.ov, p=ref.op),
+                      where)
+        want = flat0.copy()
+        pack_flat(lay_o, ref.op, want)
+        assert np.array_equal(np16(flat), want), f"{where}: flat buffer"
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("W,tensors", [(1, False), (3, False), (8, False),
+                                       (64, False), (100, False), (3, True),
+                                       (8, True)])
+def test_plain_state_step(W, tensors, layout):
+    """zs_step_plain, the step on three plain fp32 arrays (master, m, v)
+    instead of the tiled state: compiled and runtime W, several buckets with
+    ragged slices (or the owned tensors of the whole-tensor layout), warm
+    moments, three steps; the state, the bf16 shard and the flat buffer
+    against the oracle, bit for bit."""
+    rng = random.Random(500 + W)
+    if tensors:
+        numels, cap = TENSOR_LIST, None
+    else:
+        numels = [rng.choice([7, 129, 1000, 4096, 33333, 65536])
+                  for _ in range(9)]
+        cap = W * 256 * rng.choice([3, 17, 40])
+    say(f"case plain state W={W} tensors={tensors} {layout}")
+    ref = Case(numels, W, W - 1, cap=cap if cap else 25 << 20,
+               tensors=tensors, warm=(1e-4, 1e-8), seed=W, gpu=False)
+    run_plain(ref, layout, (1, 2, 3))
+
+
+@pytest.mark.parametrize("W,tiles", [(8, 4100), (5, 4100), (32, 4100)])
+def test_plain_state_launch_shapes(W, tiles):
+    """zs_step_plain in the work shapes of large launches (one-wave at
+    compiled and runtime W, Deep at W = 32): one bucket, a ragged last
+    tile, plain gradient slices; two steps against the oracle."""
+    n_rank = tiles * TILE - 4096
+    say(f"case plain state shape W={W} tiles={tiles}")
+    ref = Case([W * n_rank], W, W - 1, cap=0, seed=W, gpu=False)
+    assert n_tiles(ref.lay_o) == tiles
+    run_plain(ref, "slices", (1, 2), stride_pad=0)
+
+
 def test_pack_flat_and_per_tensor():
     w = wl.presets()["gpt2"]
     for rank in (0, 5, 7):

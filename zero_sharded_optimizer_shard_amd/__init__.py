@@ -20,7 +20,7 @@ from ._zs import (EXPORTS, LIB_PATH, ZS_ACC_ADD, ZS_ACC_FIRST, ZS_ACC_LAST,
                   zs_pack_noalloc, zs_prefetch_acquire, zs_prefetch_create, zs_prefetch_free,
                   zs_prefetch_issue, zs_prefetch_release, zs_state_mv_pack,
                   zs_state_mv_unpack, zs_state_pack, zs_state_unpack, zs_step,
-                  zs_step_bf16, zs_stream_arrive, zs_stream_create,
+                  zs_step_bf16, zs_step_plain, zs_stream_arrive, zs_stream_create,
                   zs_stream_free, zs_stream_step_begin, zs_stream_step_end,
                   zs_strerror)
 
@@ -40,6 +40,6 @@ __all__ = ["EXPORTS", "LIB_PATH", "ZS_ACC_ADD", "ZS_ACC_FIRST", "ZS_ACC_LAST",
            "zs_pack_noalloc", "zs_prefetch_acquire", "zs_prefetch_create", "zs_prefetch_free",
            "zs_prefetch_issue", "zs_prefetch_release", "zs_state_mv_pack",
            "zs_state_mv_unpack", "zs_state_pack", "zs_state_unpack",
-           "zs_step", "zs_step_bf16", "zs_stream_arrive", "zs_stream_create",
+           "zs_step", "zs_step_bf16", "zs_step_plain", "zs_stream_arrive", "zs_stream_create",
            "zs_stream_free", "zs_stream_step_begin", "zs_stream_step_end",
            "zs_strerror"]

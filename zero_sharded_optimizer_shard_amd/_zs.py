@@ -55,8 +55,8 @@ EXPORTS = ["zs_layout_build", "zs_layout_build_tensors", "zs_layout_owners",
            "zs_layout_info", "zs_layout_tiles",
            "zs_layout_buckets", "zs_layout_chunks",
            "zs_layout_tensor_offsets", "zs_layout_rank", "zs_layout_free",
-           "zs_step", "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
-           "zs_state_unpack",
+           "zs_step", "zs_step_plain", "zs_bucket_step", "zs_buckets_step",
+           "zs_state_pack", "zs_state_unpack",
            "zs_grads_tile", "zs_gather", "zs_pack", "zs_pack_noalloc",
            "zs_step_bf16",
            "zs_state_mv_pack", "zs_state_mv_unpack", "zs_accumulate",
@@ -94,6 +94,8 @@ def lib():
     L.zs_layout_free.argtypes = [p]
     L.zs_layout_free.restype = None
     L.zs_step.argtypes = [p, p, i32, i64, p, p, p, P(zs_adamw), i64, p]
+    L.zs_step_plain.argtypes = [p, p, i32, i64, p, p, p, p, p, P(zs_adamw),
+                                i64, p]
     L.zs_bucket_step.argtypes = [p, i32, p, i32, i64, p, p, p, P(zs_adamw),
                                  i64, p]
     L.zs_buckets_step.argtypes = [p, i32, P(i32), P(p), i32, i64, p, p, p,
@@ -135,7 +137,7 @@ def lib():
                  "zs_layout_owners", "zs_layout_info", "zs_layout_tiles",
                  "zs_layout_buckets", "zs_layout_chunks",
                  "zs_layout_tensor_offsets", "zs_layout_rank", "zs_step",
-                 "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
+                 "zs_step_plain", "zs_bucket_step", "zs_buckets_step", "zs_state_pack",
                  "zs_state_unpack",
                  "zs_grads_tile", "zs_gather", "zs_pack", "zs_pack_noalloc",
                  "zs_step_bf16", "zs_state_mv_pack", "zs_state_mv_unpack",
@@ -370,6 +372,28 @@ def zs_step(layout: Layout, grads, state, param_shard=None, full_flat=None,
                          _bf16(param_shard, "param_shard"),
                          _bf16(full_flat, "full_flat"), ctypes.byref(hp),
                          step, _stream(stream)), "zs_step")
+
+
+def zs_step_plain(layout: Layout, grads, master, m, v, param_shard=None,
+                  full_flat=None, *, grad_layout="slices",
+                  grad_stride: int = 0, lr: float, beta1: float, beta2: float,
+                  eps: float, weight_decay: float, step: int,
+                  stream=None) -> None:
+    """zs_step on three plain fp32 [shard_numel] arrays master, m, v."""
+    hp = _hp(lr, beta1, beta2, eps, weight_decay)
+    _step_need(layout, grads, _layout_code(grad_layout), grad_stride, None,
+               3, param_shard, full_flat)
+    n = layout.sizes()[1]
+    for t, name in ((master, "master"), (m, "m"), (v, "v")):
+        _need(t, n, name)
+    _check(lib().zs_step_plain(layout.handle, _bf16(grads, "grads"),
+                               _layout_code(grad_layout), grad_stride,
+                               _f32(master, "master"), _f32(m, "m"),
+                               _f32(v, "v"),
+                               _bf16(param_shard, "param_shard"),
+                               _bf16(full_flat, "full_flat"),
+                               ctypes.byref(hp), step, _stream(stream)),
+           "zs_step_plain")
 
 
 def zs_bucket_step(layout: Layout, bucket_id: int, grads, state,

@@ -330,18 +330,39 @@ __device__ __forceinline__ void reduce(const uint16_t* __restrict__ g0,
     }
 }
 
+// Where a tile's fp32 state sits.  TileRows: one tile of the tiled state,
+// rows master, m, v (or m, v for the pure-bf16 step) ZS_TILE floats apart.
+// PlainRows: the tile's stretch of three plain arrays.
+template <bool PURE>
+struct TileRows {
+    float* st;
+    static constexpr int kM = PURE ? 0 : 1;     // row of m; v follows
+    __device__ float* th() const { return st; }
+    __device__ float* m() const { return st + kM * kTile; }
+    __device__ float* v() const { return st + (kM + 1) * kTile; }
+};
+
+struct PlainRows {
+    float* th_;
+    float* m_;
+    float* v_;
+    __device__ float* th() const { return th_; }
+    __device__ float* m() const { return m_; }
+    __device__ float* v() const { return v_; }
+};
+
 // One tile of the step, with every pointer already at the tile: g0 the
 // first gradient value of slice 0 (tiled: the tile's W rows, gs = ZS_TILE;
-// slices: gs = the slice stride), st the tile's state rows, ps / fl the
-// tile's first bf16 output (each nullable).  This workgroup is part
-// blockIdx.x % P of SH::P on the tile.
+// slices: gs = the slice stride), rows the tile's fp32 state (TileRows or
+// PlainRows), ps / fl the tile's first bf16 output (each nullable).  This
+// workgroup is part blockIdx.x % P of SH::P on the tile.
 //
-// PURE (the pure-bf16 variant, no fp32 master): the state tile holds only
-// the rows m and v, and the parameter is the bf16 value itself, read from
-// and written back to ps if it is given, else fl.
-template <int WT, class SH, bool PURE = false>
+// PURE (the pure-bf16 variant, no fp32 master): the state holds only m and
+// v, and the parameter is the bf16 value itself, read from and written back
+// to ps if it is given, else fl.
+template <int WT, class SH, bool PURE = false, class Rows>
 __device__ __forceinline__ void step_tile(const uint16_t* __restrict__ g0,
-                                          int64_t gs, float* __restrict__ st,
+                                          int64_t gs, const Rows rows,
                                           uint16_t* __restrict__ ps,
                                           uint16_t* __restrict__ fl,
                                           int64_t nvalid, int W,
@@ -352,7 +373,6 @@ __device__ __forceinline__ void step_tile(const uint16_t* __restrict__ g0,
 
     // state first: its loads do not depend on the gradients
     uint16_t* const pp = PURE ? (ps ? ps : fl) : nullptr;
-    constexpr int kM = PURE ? 0 : 1;        // row of m; v follows
     f32x4 th[U], mm[U], vv[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
@@ -363,10 +383,10 @@ __device__ __forceinline__ void step_tile(const uint16_t* __restrict__ g0,
                 th[k] = f32x4{bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y),
                               bf16_hi(q.y)};
             } else {
-                th[k] = ld4(st + jj);
+                th[k] = ld4(rows.th() + jj);
             }
-            mm[k] = ld4(st + kM * kTile + jj);
-            vv[k] = ld4(st + (kM + 1) * kTile + jj);
+            mm[k] = ld4(rows.m() + jj);
+            vv[k] = ld4(rows.v() + jj);
         }
     }
 
@@ -399,9 +419,9 @@ __device__ __forceinline__ void step_tile(const uint16_t* __restrict__ g0,
             pb[i] = to_bf16(t);
         }
         if constexpr (!PURE)
-            st4_out(st, jj, f32x4{t4[0], t4[1], t4[2], t4[3]});
-        st4_out(st + kM * kTile, jj, f32x4{m4[0], m4[1], m4[2], m4[3]});
-        st4_out(st + (kM + 1) * kTile, jj, f32x4{v4[0], v4[1], v4[2], v4[3]});
+            st4_out(rows.th(), jj, f32x4{t4[0], t4[1], t4[2], t4[3]});
+        st4_out(rows.m(), jj, f32x4{m4[0], m4[1], m4[2], m4[3]});
+        st4_out(rows.v(), jj, f32x4{v4[0], v4[1], v4[2], v4[3]});
         const u32x2 p = {pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
         if constexpr (PURE) {
             st2_out(pp, jj, p);
@@ -425,9 +445,43 @@ __global__ __launch_bounds__(SH::NT) void step_kernel(StepArgs a)
     const uint16_t* g0 = TILED ? a.grads + r.tile * (int64_t)W * kTile
                                : a.grads + r.e0;
     step_tile<WT, SH, PURE>(g0, TILED ? kTile : a.gstride,
-                      a.state + r.tile * ((PURE ? 2 : 3) * kTile),
+                      TileRows<PURE>{a.state + r.tile * ((PURE ? 2 : 3) *
+                                                         kTile)},
                       a.pshard ? a.pshard + r.e0 : nullptr,
                       a.flat ? a.flat + r.fpos : nullptr, r.nvalid, W, a.c);
+}
+
+// The whole-shard step on three plain [shard_numel] fp32 arrays (master, m,
+// v) instead of the tiled state: the tile's stretch of each array takes the
+// place of its state row.
+struct PlainArgs {
+    const uint16_t* grads;      // launch base (see zs_step)
+    int64_t gstride;            // slices layout: elements between slices
+    float* master;              // plain arrays at the launch's first element
+    float* m;
+    float* v;
+    uint16_t* pshard;           // nullable, at the launch's first element
+    uint16_t* flat;             // nullable, at the launch's first bucket
+    Geom g;
+    int32_t W;
+    Consts c;
+};
+
+template <int WT, bool TILED, class SH>
+__global__ __launch_bounds__(SH::NT) void step_plain_kernel(PlainArgs a)
+{
+    TileRef r;
+    if (!tile_of<SH::P>(a.g, r))
+        return;
+    const int W = WT > 0 ? WT : a.W;
+    const uint16_t* g0 = TILED ? a.grads + r.tile * (int64_t)W * kTile
+                               : a.grads + r.e0;
+    step_tile<WT, SH, false>(g0, TILED ? kTile : a.gstride,
+                             PlainRows{a.master + r.e0, a.m + r.e0,
+                                       a.v + r.e0},
+                             a.pshard ? a.pshard + r.e0 : nullptr,
+                             a.flat ? a.flat + r.fpos : nullptr, r.nvalid, W,
+                             a.c);
 }
 
 // A group of buckets, each from its own staging buffer: blockIdx.x runs
@@ -471,7 +525,7 @@ __global__ __launch_bounds__(SH::NT) void group_step_kernel(GroupArgs a)
     const uint16_t* g0 = TILED ? mb.grads + x * (int64_t)W * kTile
                                : mb.grads + j0;
     step_tile<WT, SH, PURE>(g0, TILED ? kTile : a.gstride,
-                      mb.state + x * (PURE ? 2 : 3) * kTile,
+                      TileRows<PURE>{mb.state + x * (PURE ? 2 : 3) * kTile},
                       mb.pshard ? mb.pshard + j0 : nullptr,
                       mb.flat ? mb.flat + j0 : nullptr, nvalid, W, a.c);
 }
@@ -791,6 +845,9 @@ void launch_kernel(const Args& a, dim3 grid, hipStream_t s)
     if constexpr (std::is_same<Args, StepArgs>::value)
         hipLaunchKernelGGL((step_kernel<WT, TILED, SH, PURE>), grid,
                            dim3(SH::NT), 0, s, a);
+    else if constexpr (std::is_same<Args, PlainArgs>::value)
+        hipLaunchKernelGGL((step_plain_kernel<WT, TILED, SH>), grid,
+                           dim3(SH::NT), 0, s, a);
     else
         hipLaunchKernelGGL((group_step_kernel<WT, TILED, SH, PURE>), grid,
                            dim3(SH::NT), 0, s, a);
@@ -988,7 +1045,75 @@ int shard_step(const zs_layout* L, const uint16_t* grads, bool tiled,
     });
 }
 
+// Whole-shard step on three plain arrays: one launch per range of regular
+// buckets in the flat mode, one per owned tensor in the whole-tensor mode.
+int plain_step(const zs_layout* L, const uint16_t* grads, bool tiled,
+               int64_t grad_stride, float* master, float* m, float* v,
+               uint16_t* pshard, uint16_t* flat, const Consts& c,
+               hipStream_t s)
+{
+    const int32_t W = L->world;
+    auto args = [&](const zs_bucket& b0, const Geom& g, int64_t fpos) {
+        PlainArgs a;
+        a.grads = tiled ? grads + b0.tile_off * W * kTile
+                        : grads + b0.shard_off;
+        a.gstride = grad_stride;
+        a.master = master + b0.shard_off;
+        a.m = m + b0.shard_off;
+        a.v = v + b0.shard_off;
+        a.pshard = pshard ? pshard + b0.shard_off : nullptr;
+        a.flat = flat ? flat + fpos : nullptr;
+        a.g = g;
+        a.W = W;
+        a.c = c;
+        return a;
+    };
+    if (L->whole_tensors) {
+        for (const zs_bucket& b : L->buckets) {
+            Geom g = bucket_geom(L, b);
+            g.rank = 0;               // the tensor's flat offset is absolute
+            const int rc = launch_step<false>(
+                args(b, g, slice_flat_pos(L, b)), tiled,
+                dim3((unsigned)g.TPB, 1), s);
+            if (rc) return rc;
+        }
+        return ZS_OK;
+    }
+    return for_shard_ranges(L, [&](const Range& R) {
+        const zs_bucket& b0 = L->buckets[R.y0];
+        return launch_step<false>(args(b0, R.g, b0.flat_off), tiled,
+                                  dim3((unsigned)R.g.TPB, (unsigned)R.ny), s);
+    });
+}
+
 }  // namespace
+
+extern "C" int zs_step_plain(const zs_layout* L, const uint16_t* grads,
+                             int32_t grad_layout, int64_t grad_stride,
+                             float* master, float* m, float* v,
+                             uint16_t* param_shard, uint16_t* full_flat,
+                             const zs_adamw* hp, int64_t step,
+                             void* hip_stream)
+{
+    zs::clear_error();
+    if (!L) return zs::fail(ZS_EINVAL, "layout is NULL");
+    if (!hp) return zs::fail(ZS_EINVAL, "hp is NULL");
+    if (step < 1) return zs::fail(ZS_EINVAL, "step %lld < 1", (long long)step);
+    if (L->shard_numel == 0)
+        return ZS_OK;
+    if (!m || !v)
+        return zs::fail(ZS_EINVAL, "master, m and v must be non-NULL");
+    if (!aligned16(m) || !aligned16(v))
+        return zs::fail(ZS_EALIGN, "device pointers must be 16-byte aligned");
+    int rc = check_step_args(L, grads, grad_layout, grad_stride,
+                             L->shard_numel, master, param_shard, full_flat,
+                             hp, step);
+    if (rc) return rc;
+    return plain_step(L, grads, grad_layout == ZS_GRADS_TILED, grad_stride,
+                      master, m, v, param_shard, full_flat,
+                      make_consts(*hp, step, L->world),
+                      static_cast<hipStream_t>(hip_stream));
+}
 
 extern "C" int zs_step(const zs_layout* L, const uint16_t* grads,
                        int32_t grad_layout, int64_t grad_stride, float* state,
