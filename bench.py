@@ -221,10 +221,22 @@ def cpu_baseline(W, seconds: float, threads: int = 1):
             f"the single-threaded C oracle in {threads} host threads, one "
             f"window each")
     return dict(value=n * sum(reps) / el, unit="params/s", cores=threads,
-                kind="oracle",
+                kind="oracle", cpu_model=cpu_model(),
                 sample=f"{sum(reps)} steps over {threads} x {n}-element "
                        f"windows of the rank-0 shard (W={W}), {what}, "
                        f"{el:.1f} s")
+
+
+def cpu_model() -> str:
+    """The host CPU's model name, as the kernel reports it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def host_cores():
@@ -1037,8 +1049,13 @@ def main():
                     "the headline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--ceiling", action="store_true",
-                    help="also time the same-mix copy kernel")
+    ap.add_argument("--no-ceiling", dest="ceiling", action="store_false",
+                    help="skip the device ceilings (the step's access "
+                    "pattern with XORs for the arithmetic, a read-only "
+                    "stream and a plain copy), timed by default")
+    ap.add_argument("--ceiling", dest="ceiling", action="store_true",
+                    help=argparse.SUPPRESS)
+    ap.set_defaults(ceiling=True)
     ap.add_argument("--unfused", action="store_true",
                     help="also time step-to-shard + separate pack")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -1238,7 +1255,7 @@ def main():
         extra["placements"] = placement_draws(
             args.placements, lambda: arena_views(parts), (Gt, state, flat),
             lay, W, n, K, args.warmup, st, achieved / PEAK_HBM_GBS)
-    if args.ceiling and not args.whole_tensors:
+    if args.ceiling and not args.whole_tensors and R == 1:
         c = ceiling(Gt, state, flat, lay, W, n)
         c["step_frac_of_same_mix"] = achieved / c["same_mix"]["GBps"]
         extra["ceilings"] = c
