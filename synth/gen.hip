@@ -377,6 +377,18 @@ extern "C" int synth_mix_stream_dev(const void* grads, void* state,
     /* fewer than 2^32 work-items along x */
     if (tpb * 32 * 64 >= ((int64_t)1 << 32)) return -3;
     const dim3 grid((unsigned)(tpb * 32), (unsigned)nb);
+    /* the step's launches at W = 1, 2, 4, 8, 16 reserve LDS they do not use
+     * so that at most 16 waves share a CU (half of the 32 one-wave
+     * workgroups a CU would hold); this reference does the same */
+    unsigned lds = 0;
+    if (W == 1 || W == 2 || W == 4 || W == 8 || W == 16) {
+        int dev = 0, per_cu = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&per_cu,
+                                  hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                                  dev) == hipSuccess && per_cu > 0)
+            lds = (unsigned)((per_cu / 16 + 15) / 16 * 16);
+    }
     /* slices 4 at a time below W = 32, 8 above; at W = 64 the step's own
      * 512-thread shape, at other W >= 32 the one-wave reference */
     if (W == 64)
@@ -386,12 +398,12 @@ extern "C" int synth_mix_stream_dev(const void* grads, void* state,
                            (u32x4*)state, (u32x2*)flat, S, S_last, B, tpb,
                            nb - 1);
     else if (W == 8)
-        hipLaunchKernelGGL((k_mix_stream<8, 4>), grid, dim3(64), 0,
+        hipLaunchKernelGGL((k_mix_stream<8, 4>), grid, dim3(64), lds,
                            (hipStream_t)stream, (const u32x2*)grads,
                            (u32x4*)state, (u32x2*)flat, (int)W, S, S_last, B,
                            tpb, nb - 1);
     else if (W < 32)
-        hipLaunchKernelGGL((k_mix_stream<0, 4>), grid, dim3(64), 0,
+        hipLaunchKernelGGL((k_mix_stream<0, 4>), grid, dim3(64), lds,
                            (hipStream_t)stream, (const u32x2*)grads,
                            (u32x4*)state, (u32x2*)flat, (int)W, S, S_last, B,
                            tpb, nb - 1);

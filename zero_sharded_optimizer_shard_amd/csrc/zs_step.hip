@@ -45,6 +45,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
@@ -838,19 +839,63 @@ Geom bucket_geom(const zs_layout* L, const zs_bucket& b)
 }
 
 // Kernel choice: Args = StepArgs (whole shard) or GroupArgs (buckets).
+// Residency cap.  The step's small workgroups (one wave, or two in the
+// Small shape) would fill a CU with 32 waves, the tiles of about 256 of
+// them in flight over the device.  Measured on MI355X, the stream runs
+// faster with half of that in flight: the device then sweeps fewer tiles'
+// rows at a time (about 14 MB still in flight, the bandwidth-latency
+// product at these rates), as a wider active window of tiles measured
+// slower.  Nothing in the kernels uses LDS, so reserving LDS at launch is
+// what caps residency: LDS per CU / 16 per wave of a workgroup keeps at
+// most 16 waves per CU.  8B-shaped W = 8 shard, interleaved processes,
+// four arenas each: 84.1-84.3 % first draw against 80.5-81.5 % uncapped;
+// W = 4 and 16 and the pure-bf16 and whole-tensor steps gain 0.7-2.9
+// points, the 70B-shaped bucket groups 2 %.  The runtime-W kernel lost
+// (W = 5: 79-82 % against 82-84 %), and the 512- and 256-thread shapes of
+// W >= 32 are held to one or two workgroups per CU by their registers, so
+// only the compiled W < 32 shapes take the cap.
+constexpr int kCapWavesPerCU = 16;
+constexpr int kCapDevices = 64;
+std::atomic<int> g_lds_per_cu[kCapDevices];     // bytes; 0 = not known yet
+
+// LDS bytes to reserve per workgroup of `waves` waves, or 0 (no cap) when
+// the device's LDS size cannot be had.
+unsigned residency_cap_lds(int waves)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kCapDevices)
+        return 0;
+    int lds = g_lds_per_cu[dev].load(std::memory_order_relaxed);
+    if (lds == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(
+                &v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                dev) != hipSuccess || v <= 0)
+            v = -1;
+        g_lds_per_cu[dev].store(v, std::memory_order_relaxed);
+        lds = v;
+    }
+    if (lds <= 0)
+        return 0;
+    const int wgs = kCapWavesPerCU / waves;      // workgroups per CU
+    return (unsigned)((lds / wgs + 15) / 16 * 16);
+}
+
 template <int WT, bool TILED, class SH, bool PURE, class Args>
 void launch_kernel(const Args& a, dim3 grid, hipStream_t s)
 {
     grid.x *= SH::P;
+    constexpr bool kCap = WT > 0 && WT < 32 && SH::NT <= 128;
+    const unsigned lds = kCap ? residency_cap_lds(SH::NT / 64) : 0u;
     if constexpr (std::is_same<Args, StepArgs>::value)
         hipLaunchKernelGGL((step_kernel<WT, TILED, SH, PURE>), grid,
-                           dim3(SH::NT), 0, s, a);
+                           dim3(SH::NT), lds, s, a);
     else if constexpr (std::is_same<Args, PlainArgs>::value)
         hipLaunchKernelGGL((step_plain_kernel<WT, TILED, SH>), grid,
-                           dim3(SH::NT), 0, s, a);
+                           dim3(SH::NT), lds, s, a);
     else
         hipLaunchKernelGGL((group_step_kernel<WT, TILED, SH, PURE>), grid,
-                           dim3(SH::NT), 0, s, a);
+                           dim3(SH::NT), lds, s, a);
 }
 
 template <int WT, class SH, bool PURE, class Args>
