@@ -53,12 +53,12 @@ KERNELS = os.path.join(ROOT, "zero_sharded_optimizer_shard_amd",
 # the kernels whose HBM counters the roofline's traffic figure comes from,
 # per workload: the tiled mixed-precision step in its work shape there
 HEADLINE_KERNEL = ("_ZN12_GLOBAL__N_111step_kernelILi8ELb1ENS_5ShapeILi64ELi1E"
-                   "Li4EEELb0EEEvNS_8StepArgsE")
+                   "Li8EEELb0EEEvNS_8StepArgsE")
 STEP_KERNELS = {
-    "llama8b": (HEADLINE_KERNEL, "step_kernel<8, true, Shape<64, 1, 4> >"),
-    "dense7b": ("_ZN12_GLOBAL__N_111step_kernelILi64ELb1ENS_5ShapeILi512ELi4"
-                "ELi8EEELb0EEEvNS_8StepArgsE",
-                "step_kernel<64, true, Shape<512, 4, 8> >"),
+    "llama8b": (HEADLINE_KERNEL, "step_kernel<8, true, Shape<64, 1, 8> >"),
+    "dense7b": ("_ZN12_GLOBAL__N_111step_kernelILi64ELb1ENS_5ShapeILi64ELi1E"
+                "Li64EEELb0EEEvNS_8StepArgsE",
+                "step_kernel<64, true, Shape<64, 1, 64> >"),
 }
 
 

@@ -235,11 +235,13 @@ void zs_layout_free(zs_layout* layout);
  * All device pointers must be 16-byte aligned (ZS_EALIGN otherwise);
  * ZS_EINVAL for an unknown grad_layout.
  *
- * Launches: at W = 1, 2, 4, 8 or 16 the step's workgroups (one or two
- * waves) reserve LDS they do not use, 1/16 of a CU's LDS per wave, so that
- * at most 16 waves of the step share a CU (fewer tiles in flight: measured
- * faster on MI355X).  Kernels of other streams running at the same time
- * share the CU's LDS with them.  The same holds for zs_step_plain,
+ * Launches: at W = 1, 2, 4, 8, 16, 32 or 64 the step's workgroups (one or
+ * two waves) reserve LDS they do not use, so that only a few of them share
+ * a CU: 5 to 16 by W (at W = 8, 12, each holding 1/12 of the CU's LDS; at
+ * W = 64, 5), which keeps fewer tiles in flight, measured faster on MI355X
+ * (the 512-thread workgroups of plain slices and bucket groups at W >= 32,
+ * and of other W, reserve none).  Kernels of other streams running at the same time share the CU's LDS
+ * with them.  The same holds for zs_step_plain,
  * zs_bucket_step, zs_buckets_step and zs_step_bf16. */
 int zs_step(const zs_layout* layout, const uint16_t* grads,
             int32_t grad_layout, int64_t grad_stride, float* state,

@@ -211,7 +211,7 @@ extern "C" int synth_read_dev(const void* src, int64_t nbytes, void* sink,
 }
 
 /* The step's access pattern with integer XORs in place of the arithmetic,
- * in the step's work shape below W = 32: 32 one-wave workgroups per
+ * in the step's one-wave work shape: 32 one-wave workgroups per
  * 8192-element tile of a bucket slice (blockIdx.x = tile * 32 + part), one
  * 4-element unit per thread; reads W tiled gradient rows (8 B per unit each,
  * in batches of NB) and the three tiled fp32 state rows (16 B per unit
@@ -284,80 +284,6 @@ __global__ __launch_bounds__(64) void k_mix_stream(
     mix_store(f, 16384u, 8u * u, u32x2{c.x ^ c.z, c.y ^ c.w});
 }
 
-/* The same access pattern in the step's work shape at W >= 32: one
- * 512-thread workgroup per tile, thread t owning the 4-element units t,
- * t + 512, t + 1024 and t + 1536 of the tile; the three state rows first,
- * then the W gradient rows in batches of NB (all loads of a batch issued
- * before use), the same stores. */
-template <int WT, int NB>
-__global__ __launch_bounds__(512) void k_mix_stream_deep(
-    const u32x2* __restrict__ grads, u32x4* __restrict__ state,
-    u32x2* __restrict__ flat, int64_t S, int64_t S_last, int64_t B,
-    int64_t tpb, int q_last)
-{
-    constexpr int U = 4;
-    const int q = blockIdx.y;
-    const int64_t slice = q == q_last ? S_last : S;
-    const int64_t x = blockIdx.x;
-    const int64_t j0 = x * 8192;
-    if (j0 >= slice)
-        return;
-    const int64_t tile = (int64_t)q * tpb + x;
-    const int64_t nv = slice - j0 < 8192 ? slice - j0 : 8192;
-    const u32x2* g = grads + tile * WT * 2048;
-    u32x4* st = state + tile * 3 * 2048;
-    u32x2* f = flat + ((int64_t)q * B + j0) / 4;
-    u32x4 a0[U], b0[U], c0[U];
-    u32x2 xx[U];
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-        const int u = k * 512 + (int)threadIdx.x;
-        xx[k] = u32x2{0u, 0u};
-        if (4 * u < nv) {
-            a0[k] = __builtin_nontemporal_load(st + u);
-            b0[k] = __builtin_nontemporal_load(st + 2048 + u);
-            c0[k] = __builtin_nontemporal_load(st + 4096 + u);
-        }
-    }
-#pragma unroll
-    for (int s0 = 0; s0 < WT; s0 += NB) {
-        u32x2 y[U][NB];
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int u = k * 512 + (int)threadIdx.x;
-            if (4 * u < nv) {
-#pragma unroll
-                for (int i = 0; i < NB; ++i)
-                    y[k][i] = __builtin_nontemporal_load(
-                        g + (int64_t)(s0 + i) * 2048 + u);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int u = k * 512 + (int)threadIdx.x;
-            if (4 * u < nv) {
-#pragma unroll
-                for (int i = 0; i < NB; ++i)
-                    xx[k] ^= y[k][i];
-            }
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-        const int u = k * 512 + (int)threadIdx.x;
-        if (4 * u >= nv)
-            continue;
-        const u32x4 x4 = {xx[k].x, xx[k].y, xx[k].x, xx[k].y};
-        const u32x4 a = a0[k] ^ x4;
-        const u32x4 b = b0[k] ^ a;
-        const u32x4 c = c0[k] ^ b;
-        mix_store(st, 32768u, 16u * u, a);
-        mix_store(st + 2048, 32768u, 16u * u, b);
-        mix_store(st + 4096, 32768u, 16u * u, c);
-        mix_store(f, 16384u, 8u * u, u32x2{c.x ^ c.z, c.y ^ c.w});
-    }
-}
-
 /* grads: tiled [tiles][W][8192] bf16; state: tiled [tiles][3][8192] fp32;
  * flat: the bf16 flat buffer; S, B: slice and numel of a full bucket,
  * S_last the last bucket's slice, nb buckets (all but the last full).
@@ -377,40 +303,50 @@ extern "C" int synth_mix_stream_dev(const void* grads, void* state,
     /* fewer than 2^32 work-items along x */
     if (tpb * 32 * 64 >= ((int64_t)1 << 32)) return -3;
     const dim3 grid((unsigned)(tpb * 32), (unsigned)nb);
-    /* the step's launches at W = 1, 2, 4, 8, 16 reserve LDS they do not use
-     * so that at most 16 waves share a CU (half of the 32 one-wave
-     * workgroups a CU would hold); this reference does the same */
+    /* the step's launches at compiled W take one-wave workgroups that load
+     * all W slices at once, and reserve LDS they do not use so that only a
+     * few share a CU (12 at W = 4 and 8, 7 at 16, 6 at 32, 5 at 64); this
+     * reference takes the same shape and the same cap at those W, and the
+     * one-wave form with slices 4 (W < 32) or 8 at a time, uncapped, at
+     * any other W */
+    int wgs = 0;
+    if (W == 4 || W == 8) wgs = 12;
+    else if (W == 16) wgs = 7;
+    else if (W == 32) wgs = 6;
+    else if (W == 64) wgs = 5;
     unsigned lds = 0;
-    if (W == 1 || W == 2 || W == 4 || W == 8 || W == 16) {
+    if (wgs) {
         int dev = 0, per_cu = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
             hipDeviceGetAttribute(&per_cu,
                                   hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
                                   dev) == hipSuccess && per_cu > 0)
-            lds = (unsigned)((per_cu / 16 + 15) / 16 * 16);
+            lds = (unsigned)(per_cu / wgs / 512 * 512);
     }
-    /* slices 4 at a time below W = 32, 8 above; at W = 64 the step's own
-     * 512-thread shape, at other W >= 32 the one-wave reference */
-    if (W == 64)
-        hipLaunchKernelGGL((k_mix_stream_deep<64, 8>),
-                           dim3((unsigned)tpb, (unsigned)nb), dim3(512), 0,
-                           (hipStream_t)stream, (const u32x2*)grads,
-                           (u32x4*)state, (u32x2*)flat, S, S_last, B, tpb,
-                           nb - 1);
+    const hipStream_t st = (hipStream_t)stream;
+    const u32x2* g = (const u32x2*)grads;
+    u32x4* sp = (u32x4*)state;
+    u32x2* fp = (u32x2*)flat;
+    if (W == 4)
+        hipLaunchKernelGGL((k_mix_stream<4, 4>), grid, dim3(64), lds, st, g,
+                           sp, fp, (int)W, S, S_last, B, tpb, nb - 1);
     else if (W == 8)
-        hipLaunchKernelGGL((k_mix_stream<8, 4>), grid, dim3(64), lds,
-                           (hipStream_t)stream, (const u32x2*)grads,
-                           (u32x4*)state, (u32x2*)flat, (int)W, S, S_last, B,
-                           tpb, nb - 1);
+        hipLaunchKernelGGL((k_mix_stream<8, 8>), grid, dim3(64), lds, st, g,
+                           sp, fp, (int)W, S, S_last, B, tpb, nb - 1);
+    else if (W == 16)
+        hipLaunchKernelGGL((k_mix_stream<16, 16>), grid, dim3(64), lds, st,
+                           g, sp, fp, (int)W, S, S_last, B, tpb, nb - 1);
+    else if (W == 32)
+        hipLaunchKernelGGL((k_mix_stream<32, 32>), grid, dim3(64), lds, st,
+                           g, sp, fp, (int)W, S, S_last, B, tpb, nb - 1);
+    else if (W == 64)
+        hipLaunchKernelGGL((k_mix_stream<64, 64>), grid, dim3(64), lds, st,
+                           g, sp, fp, (int)W, S, S_last, B, tpb, nb - 1);
     else if (W < 32)
-        hipLaunchKernelGGL((k_mix_stream<0, 4>), grid, dim3(64), lds,
-                           (hipStream_t)stream, (const u32x2*)grads,
-                           (u32x4*)state, (u32x2*)flat, (int)W, S, S_last, B,
-                           tpb, nb - 1);
+        hipLaunchKernelGGL((k_mix_stream<0, 4>), grid, dim3(64), 0, st, g,
+                           sp, fp, (int)W, S, S_last, B, tpb, nb - 1);
     else
-        hipLaunchKernelGGL((k_mix_stream<0, 8>), grid, dim3(64), 0,
-                           (hipStream_t)stream, (const u32x2*)grads,
-                           (u32x4*)state, (u32x2*)flat, (int)W, S, S_last, B,
-                           tpb, nb - 1);
+        hipLaunchKernelGGL((k_mix_stream<0, 8>), grid, dim3(64), 0, st, g,
+                           sp, fp, (int)W, S, S_last, B, tpb, nb - 1);
     return finish();
 }

@@ -839,29 +839,25 @@ Geom bucket_geom(const zs_layout* L, const zs_bucket& b)
 }
 
 // Kernel choice: Args = StepArgs (whole shard) or GroupArgs (buckets).
-// Residency cap.  The step's small workgroups (one wave, or two in the
-// Small shape) would fill a CU with 32 waves, the tiles of about 256 of
-// them in flight over the device.  Measured on MI355X, the stream runs
-// faster with half of that in flight: the device then sweeps fewer tiles'
-// rows at a time (about 14 MB still in flight, the bandwidth-latency
-// product at these rates), as a wider active window of tiles measured
-// slower.  Nothing in the kernels uses LDS, so reserving LDS at launch is
-// what caps residency: LDS per CU / 16 per wave of a workgroup keeps at
-// most 16 waves per CU.  8B-shaped W = 8 shard, interleaved processes,
-// four arenas each: 84.1-84.3 % first draw against 80.5-81.5 % uncapped;
-// W = 4 and 16 and the pure-bf16 and whole-tensor steps gain 0.7-2.9
-// points, the 70B-shaped bucket groups 2 %.  The runtime-W kernel lost
-// (W = 5: 79-82 % against 82-84 %), and the 512- and 256-thread shapes of
-// W >= 32 are held to one or two workgroups per CU by their registers, so
-// only the compiled W < 32 shapes take the cap.
-constexpr int kCapWavesPerCU = 16;
+// Residency cap.  Nothing in the step kernels uses LDS, so reserving LDS
+// at launch is what sets how many of their small workgroups share a CU:
+// LDS per CU / k (rounded down to 512 bytes) lets k of them in.  Measured
+// on MI355X, the stream runs faster with far fewer workgroups in flight
+// than would fit (32 one-wave workgroups per CU): the device then sweeps
+// fewer tiles' rows at a time, as a wider active window of tiles measured
+// slower (the device's achievable read/write mix rises from 82-83 % to
+// 84-86 % of peak).  The right k depends on the work shape and W; see the
+// shape table below.  Where the device's LDS size cannot be had the step
+// launches uncapped.
 constexpr int kCapDevices = 64;
 std::atomic<int> g_lds_per_cu[kCapDevices];     // bytes; 0 = not known yet
 
-// LDS bytes to reserve per workgroup of `waves` waves, or 0 (no cap) when
-// the device's LDS size cannot be had.
-unsigned residency_cap_lds(int waves)
+// LDS bytes to reserve per workgroup so that at most `wgs` share a CU, or 0
+// (no cap) for wgs == 0 or when the device's LDS size cannot be had.
+unsigned residency_cap_lds(int wgs)
 {
+    if (wgs <= 0)
+        return 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kCapDevices)
         return 0;
@@ -877,16 +873,15 @@ unsigned residency_cap_lds(int waves)
     }
     if (lds <= 0)
         return 0;
-    const int wgs = kCapWavesPerCU / waves;      // workgroups per CU
-    return (unsigned)((lds / wgs + 15) / 16 * 16);
+    return (unsigned)(lds / wgs / 512 * 512);
 }
 
-template <int WT, bool TILED, class SH, bool PURE, class Args>
+// WGS: workgroups per CU (0 = uncapped).
+template <int WT, bool TILED, class SH, bool PURE, int WGS, class Args>
 void launch_kernel(const Args& a, dim3 grid, hipStream_t s)
 {
     grid.x *= SH::P;
-    constexpr bool kCap = WT > 0 && WT < 32 && SH::NT <= 128;
-    const unsigned lds = kCap ? residency_cap_lds(SH::NT / 64) : 0u;
+    const unsigned lds = residency_cap_lds(WGS);
     if constexpr (std::is_same<Args, StepArgs>::value)
         hipLaunchKernelGGL((step_kernel<WT, TILED, SH, PURE>), grid,
                            dim3(SH::NT), lds, s, a);
@@ -898,41 +893,85 @@ void launch_kernel(const Args& a, dim3 grid, hipStream_t s)
                            dim3(SH::NT), lds, s, a);
 }
 
-template <int WT, class SH, bool PURE, class Args>
+template <int WT, class SH, bool PURE, int WGS, class Args>
 void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 {
     if (tiled)
-        launch_kernel<WT, true, SH, PURE>(a, grid, s);
+        launch_kernel<WT, true, SH, PURE, WGS>(a, grid, s);
     else
-        launch_kernel<WT, false, SH, PURE>(a, grid, s);
+        launch_kernel<WT, false, SH, PURE, WGS>(a, grid, s);
 }
 
-// Work shapes, chosen by measurement on MI355X (8B-shaped shard at W = 4,
-// 5, 8 and 16, 7B-shaped at W = 32, 64 and 100, 70B-shaped bucket groups at
-// W = 16):
-//  - Wave (W < 32, mixed and pure-bf16): one wave per workgroup, one unit
-//    per thread, 32 workgroups per tile: 82-83 % of peak at W = 4, 5, 8 and
-//    16, against 80-81 % for 512-thread workgroups of four units (67 % for
-//    the runtime-W kernel at W = 5); pure bf16 at W = 8 82.6 % vs 80.5 %;
-//  - Deep (W >= 32): 512-thread workgroups, slices loaded 8 at a time, one
-//    workgroup per CU (148 VGPRs): 79-80 % at W = 64, where one-wave shapes
-//    measured 72-79 %;
+// Work shapes and residency, chosen by measurement on MI355X (8B-shaped
+// shard at W = 4, 5, 8 and 16, 7B-shaped at W = 32, 64 and 100, 70B-shaped
+// bucket groups at W = 16; three arenas per process, several processes):
+//  - One (compiled W, 4096 tiles or more): one wave per workgroup, one
+//    4-element unit per thread, all W gradient slices loaded in one batch
+//    (at least 4), 32 workgroups per tile, and few of them per CU (one_wgs):
+//      W = 8:  12 per CU, 85.0 % in three processes (the same shape with 16
+//              per CU 84.5-85.1 %, with 11 or 14 84.3-84.7 %; slices loaded
+//              4 at a time, 16 per CU, 83.4-84.9 %; uncapped 80.5-83.3 %);
+//              pure bf16 10 per CU, 86.0-86.6 % (12 per CU: 82.9-83.5 %);
+//      W = 4:  12 per CU, 85.3-85.9 % (16: 83.6-84.0 %; uncapped 82.2 %);
+//      W = 16: 7 per CU, 82.3-87.0 % (8: 80.9-84.2 %, 6: 75-76 %; slices 4
+//              at a time with 16 per CU 82.9 %);
+//      W = 32: 6 per CU, 84.5-85.7 % (5 or 7: 81.4-81.8 %); 512-thread
+//              workgroups of 8-slice batches (the earlier Deep shape, 148
+//              VGPRs, one per CU) 77.4-80.3 %;
+//      W = 64: 5 per CU, 82.7-84.6 % (4: 82.9-84.1 %, 3: 67 %); pure bf16 6
+//              per CU, 82.6-84.5 %; Deep 79.0-80.7 % (pure 80.4-81.2 %);
+//      W = 1, 2: 16 per CU (not measured apart).
+//    The cap and the batch depth act together (more slices per wave, fewer
+//    waves), and the optimum is narrow at W = 16 and 32: one more or one
+//    fewer workgroup per CU costs 3-10 points there.
+//  - Wave (runtime W < 32): the same one-wave unit, slices 4 at a time,
+//    uncapped (W = 5: the cap lost, 79-82 % against 82-84 %); and, 16 per
+//    CU, large group launches at compiled W < 32 (the whole-tensor step's
+//    owned tensors, 32 per launch: 84.7-85.0 % on the 8B-shaped W = 8
+//    shard, where One at 12 per CU gave 79.7-82.6 %);
+//  - Deep (512-thread workgroups of four units, slices 8 at a time, one
+//    per CU by its 148 VGPRs), uncapped: plain slice rows at compiled
+//    W >= 32 (7B-shaped W = 64: 73-77 %, One 66 %) and large group launches
+//    there;
 //  - Wide / PureWide (runtime W >= 32): 512-thread workgroups of four units
 //    (256 for the two-row pure state): 79-80 % at W = 100, against 75-78 %
 //    with one-wave workgroups;
 //  - Small (launches of fewer than kSmallLaunch tiles: bucket groups of a
 //    streaming step, GPT-2-sized shards): one unit per thread and sixteen
 //    128-thread workgroups per tile, so that a few hundred or thousand
-//    tiles still spread evenly over the 256 CUs with a short tail
-//    (GPT-2-shaped W = 8 shard, 1899 tiles: 80.2-80.5 % against 79.6-79.7 %
-//    with four 512-thread workgroups per tile and 75 % with Wide; 70B bucket
-//    groups alone 38.8 vs 39.3-40.0 ms per full step).
+//    tiles still spread evenly over the 256 CUs with a short tail, 8 per CU
+//    at compiled W < 32 (GPT-2-shaped W = 8 shard, 1899 tiles: 81.4-81.5 %
+//    against 80.3 % uncapped, 79.6-79.7 % with four 512-thread workgroups
+//    per tile, 75 % with Wide; 70B bucket groups 38.3 ms per full step
+//    against 38.6-38.8 ms uncapped).
+template <int WT>
+using ShapeOne = Shape<64, 1, (WT < 4 ? 4 : WT)>;
 using ShapeWave = Shape<64, 1, 4>;
-using ShapeWide = Shape<512, 4, 4>;
 using ShapeDeep = Shape<512, 4, 8>;
+using ShapeWide = Shape<512, 4, 4>;
 using ShapeSmall = Shape<128, 1, 4>;
 using ShapePureWide = Shape<256, 4, 4>;
 constexpr int64_t kSmallLaunch = 4096;
+constexpr int kSmallWgs = 8;
+constexpr int kWaveWgs = 16;
+
+template <int WT, bool PURE>
+constexpr int one_wgs()
+{
+    if constexpr (WT == 8)
+        return PURE ? 10 : 12;
+    else if constexpr (WT == 64)
+        return PURE ? 6 : 5;
+    else if constexpr (WT == 4)
+        return 12;
+    else if constexpr (WT == 16)
+        return 7;
+    else if constexpr (WT == 32)
+        return 6;
+    else
+        return 16;
+}
+
 // every shape stays within the launch limit of kMaxLaunchTiles tiles
 static_assert(kMaxLaunchTiles * ShapeWave::P * ShapeWave::NT <
                   (int64_t(1) << 32) &&
@@ -945,18 +984,29 @@ template <int WT, bool PURE, class Args>
 void launch_step_w(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 {
     const int64_t tiles = (int64_t)grid.x * grid.y;
+    constexpr bool kGroup = std::is_same<Args, GroupArgs>::value;
     if (tiles < kSmallLaunch) {
-        launch_shape<WT, ShapeSmall, PURE>(a, tiled, grid, s);
-    } else if constexpr (WT >= 32) {
-        launch_shape<WT, ShapeDeep, PURE>(a, tiled, grid, s);
+        constexpr int kWgs = WT > 0 && WT < 32 ? kSmallWgs : 0;
+        launch_shape<WT, ShapeSmall, PURE, kWgs>(a, tiled, grid, s);
+    } else if constexpr (WT > 0 && kGroup) {
+        // large group launches (the whole-tensor step's owned tensors):
+        // the member lookup of every workgroup wants more of them per CU
+        if constexpr (WT < 32)
+            launch_shape<WT, ShapeWave, PURE, kWaveWgs>(a, tiled, grid, s);
+        else
+            launch_shape<WT, ShapeDeep, PURE, 0>(a, tiled, grid, s);
     } else if constexpr (WT > 0) {
-        launch_shape<WT, ShapeWave, PURE>(a, tiled, grid, s);
+        if (tiled || WT < 32)
+            launch_shape<WT, ShapeOne<WT>, PURE, one_wgs<WT, PURE>()>(
+                a, tiled, grid, s);
+        else                                // W plain slice rows, W >= 32
+            launch_kernel<WT, false, ShapeDeep, PURE, 0>(a, grid, s);
     } else if (a.W < 32) {                  // runtime W
-        launch_shape<WT, ShapeWave, PURE>(a, tiled, grid, s);
+        launch_shape<WT, ShapeWave, PURE, 0>(a, tiled, grid, s);
     } else if constexpr (PURE) {
-        launch_shape<WT, ShapePureWide, PURE>(a, tiled, grid, s);
+        launch_shape<WT, ShapePureWide, PURE, 0>(a, tiled, grid, s);
     } else {
-        launch_shape<WT, ShapeWide, PURE>(a, tiled, grid, s);
+        launch_shape<WT, ShapeWide, PURE, 0>(a, tiled, grid, s);
     }
 }
 
