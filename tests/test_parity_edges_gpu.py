@@ -217,13 +217,16 @@ def one_bucket(W, tiles):
     return lay, n_rank
 
 
-# (W, tiles): which work shape runs
-#   (2, 300)    Small, compiled W        (5, 1100)  Small, runtime W
-#   (8, 4100)   Wave, compiled W         (5, 4100)  Wave, runtime W
-#   (32, 4100)  Deep, compiled W         (33, 4100) Wide, runtime W
-#   (64, 300)   Small at W = 64
-SHAPES = [(2, 300), (5, 1100), (8, 4100), (5, 4100), (32, 4100), (33, 4100),
-          (64, 300)]
+# (W, tiles): which work shape runs (a launch of 4096 tiles or more takes
+# the shape of its W; smaller ones take Small)
+#   (2, 300)    Small, compiled W         (5, 1100)  Small, runtime W
+#   (1, 4100)   One <64, 1, 4>, W = 1     (8, 4100)  One <64, 1, 8>
+#   (16, 4100)  One <64, 1, 16>           (5, 4100)  Wave, runtime W
+#   (32, 4100)  One <64, 1, 32> tiled, Deep on plain slices
+#   (64, 4100)  One <64, 1, 64> tiled, Deep on plain slices
+#   (33, 4100)  Wide, runtime W           (64, 300)  Small at W = 64
+SHAPES = [(2, 300), (5, 1100), (1, 4100), (8, 4100), (16, 4100), (5, 4100),
+          (32, 4100), (64, 4100), (33, 4100), (64, 300)]
 
 
 @pytest.mark.parametrize("state_form", ["tiled", "plain"])
@@ -279,9 +282,10 @@ def test_step_edge_values(W, tiles, layout, hp_name, state_form):
     assert np.isnan(om).any()
 
 
-# the pure-bf16 step's shapes: Small, Wave (compiled and runtime W), Deep,
-# PureWide (runtime W >= 32)
-PURE_SHAPES = [(2, 300), (8, 4100), (5, 4100), (32, 4100), (33, 4100)]
+# the pure-bf16 step's shapes: Small, One (W = 8, 16, 32, 64; Deep on plain
+# slices at W >= 32), Wave (runtime W), PureWide (runtime W >= 32)
+PURE_SHAPES = [(2, 300), (8, 4100), (16, 4100), (5, 4100), (32, 4100),
+               (64, 4100), (33, 4100)]
 
 
 @pytest.mark.parametrize("layout", ["tiled", "slices"])
@@ -317,4 +321,42 @@ def test_pure_bf16_step_edge_values(W, tiles, layout):
         assert_periodic_equal(got[0], om, f"t={t} m")
         assert_periodic_equal(got[1], ov, f"t={t} v")
         assert_periodic_equal(params.cpu().numpy().view(np.uint16), p16,
+                              f"t={t} bf16 param")
+
+
+# the bucket-group kernel (zs_bucket_step: a group of one bucket): Small,
+# Wave at compiled and runtime W, Deep at compiled W >= 32, Wide at runtime
+# W >= 32
+GROUP_SHAPES = [(2, 300), (8, 4100), (5, 4100), (64, 4100), (33, 4100)]
+
+
+@pytest.mark.parametrize("layout", ["tiled", "slices"])
+@pytest.mark.parametrize("W,tiles", GROUP_SHAPES)
+def test_bucket_step_edge_values(W, tiles, layout):
+    hp = HPS["default"]
+    print(f"case edge bucket step W={W} tiles={tiles} {layout}", flush=True)
+    rng = np.random.default_rng(3000 * W + tiles)
+    lay, n = one_bucket(W, tiles)
+    master, m, v = edge_state(rng)
+    state = to_tiled(torch.stack([expand(x, n) for x in (master, m, v)]),
+                     tiles)
+    p = torch.empty(n, dtype=torch.int16, device="cuda")
+    om, omm, ov = master.copy(), m.copy(), v.copy()
+    for t in (1, 2):
+        Gp = edge_gradients(W, rng)
+        G = expand(Gp.view(np.int16), n)
+        if layout == "tiled":
+            zs.zs_bucket_step(lay, 0, to_tiled(G, tiles), state, p, None,
+                              grad_layout="tiled", step=t, **hp)
+        else:
+            zs.zs_bucket_step(lay, 0, G, state, p, None,
+                              grad_layout="slices", grad_stride=n, step=t,
+                              **hp)
+        op = O.step(Gp, om, omm, ov, O.AdamW(**hp), t)
+        torch.cuda.synchronize()
+        got = from_tiled(state, 3, tiles, n)
+        for row, name, want in ((0, "master", om), (1, "m", omm),
+                                (2, "v", ov)):
+            assert_periodic_equal(got[row], want, f"t={t} {name}")
+        assert_periodic_equal(p.cpu().numpy().view(np.uint16), op,
                               f"t={t} bf16 param")
