@@ -237,12 +237,13 @@ void zs_layout_free(zs_layout* layout);
  *
  * Launches: at W = 1, 2, 4, 8, 16, 32 or 64 the step's workgroups (one or
  * two waves) reserve LDS they do not use, so that only a few of them share
- * a CU: 5 to 16 by W (at W = 8, 12, each holding 1/12 of the CU's LDS; at
- * W = 64, 5), which keeps fewer tiles in flight, measured faster on MI355X
- * (the 512-thread workgroups of plain slices and bucket groups at W >= 32,
- * and of other W, reserve none).  Kernels of other streams running at the same time share the CU's LDS
- * with them.  The same holds for zs_step_plain,
- * zs_bucket_step, zs_buckets_step and zs_step_bf16. */
+ * a CU: 5 to 16 by W and launch size (at W = 8, 12, each holding 1/12 of
+ * the CU's LDS; at W = 64, 5), which keeps fewer tiles in flight, measured
+ * faster on MI355X (the workgroups of plain slices at W >= 32, of bucket
+ * groups of 4096 tiles or more at W >= 32, and of every other W reserve
+ * none).  Kernels of other streams running at the same time share the
+ * CU's LDS with them.  The same holds for zs_step_plain, zs_bucket_step,
+ * zs_buckets_step and zs_step_bf16. */
 int zs_step(const zs_layout* layout, const uint16_t* grads,
             int32_t grad_layout, int64_t grad_stride, float* state,
             uint16_t* param_shard, uint16_t* full_flat, const zs_adamw* hp,

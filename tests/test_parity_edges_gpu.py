@@ -217,14 +217,16 @@ def one_bucket(W, tiles):
     return lay, n_rank
 
 
-# (W, tiles): which work shape runs (a launch of 4096 tiles or more takes
-# the shape of its W; smaller ones take Small)
-#   (2, 300)    Small, compiled W         (5, 1100)  Small, runtime W
+# (W, tiles): which work shape runs (launches of fewer than 4096 tiles
+# differ from larger ones in the workgroups allowed per CU, and at runtime W
+# in the shape)
+#   (2, 300)    One <64, 1, 4>, W = 2     (5, 1100)  Small, runtime W
 #   (1, 4100)   One <64, 1, 4>, W = 1     (8, 4100)  One <64, 1, 8>
 #   (16, 4100)  One <64, 1, 16>           (5, 4100)  Wave, runtime W
 #   (32, 4100)  One <64, 1, 32> tiled, Deep on plain slices
 #   (64, 4100)  One <64, 1, 64> tiled, Deep on plain slices
-#   (33, 4100)  Wide, runtime W           (64, 300)  Small at W = 64
+#   (33, 4100)  Wide, runtime W
+#   (64, 300)   One <64, 1, 64> tiled, Small on plain slices
 SHAPES = [(2, 300), (5, 1100), (1, 4100), (8, 4100), (16, 4100), (5, 4100),
           (32, 4100), (64, 4100), (33, 4100), (64, 300)]
 
@@ -282,10 +284,11 @@ def test_step_edge_values(W, tiles, layout, hp_name, state_form):
     assert np.isnan(om).any()
 
 
-# the pure-bf16 step's shapes: Small, One (W = 8, 16, 32, 64; Deep on plain
-# slices at W >= 32), Wave (runtime W), PureWide (runtime W >= 32)
-PURE_SHAPES = [(2, 300), (8, 4100), (16, 4100), (5, 4100), (32, 4100),
-               (64, 4100), (33, 4100)]
+# the pure-bf16 step's shapes: One (W = 2, 8, 16, 32, 64; Deep on plain
+# slices at W >= 32), Wave (runtime W), PureWide (runtime W >= 32), Small
+# (runtime W, and plain slices at W = 64, below 4096 tiles)
+PURE_SHAPES = [(2, 300), (5, 1100), (64, 300), (8, 4100), (16, 4100),
+               (5, 4100), (32, 4100), (64, 4100), (33, 4100)]
 
 
 @pytest.mark.parametrize("layout", ["tiled", "slices"])
@@ -324,10 +327,12 @@ def test_pure_bf16_step_edge_values(W, tiles, layout):
                               f"t={t} bf16 param")
 
 
-# the bucket-group kernel (zs_bucket_step: a group of one bucket): Small,
-# Wave at compiled and runtime W, Deep at compiled W >= 32, Wide at runtime
-# W >= 32
-GROUP_SHAPES = [(2, 300), (8, 4100), (5, 4100), (64, 4100), (33, 4100)]
+# the bucket-group kernel (zs_bucket_step: a group of one bucket): One
+# below 4096 tiles at compiled W (Small on plain slices at W = 64), Small at
+# runtime W; at 4096 tiles or more Wave (compiled and runtime W < 32), Deep
+# at compiled W >= 32, Wide at runtime W >= 32
+GROUP_SHAPES = [(2, 300), (8, 300), (16, 300), (64, 300), (5, 300),
+                (8, 4100), (5, 4100), (64, 4100), (33, 4100)]
 
 
 @pytest.mark.parametrize("layout", ["tiled", "slices"])

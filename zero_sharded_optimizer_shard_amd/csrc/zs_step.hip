@@ -905,9 +905,10 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 // Work shapes and residency, chosen by measurement on MI355X (8B-shaped
 // shard at W = 4, 5, 8 and 16, 7B-shaped at W = 32, 64 and 100, 70B-shaped
 // bucket groups at W = 16; three arenas per process, several processes):
-//  - One (compiled W, 4096 tiles or more): one wave per workgroup, one
-//    4-element unit per thread, all W gradient slices loaded in one batch
-//    (at least 4), 32 workgroups per tile, and few of them per CU (one_wgs):
+//  - One (compiled W; on plain slices only below W = 32): one wave per
+//    workgroup, one 4-element unit per thread, all W gradient slices
+//    loaded in one batch (at least 4), 32 workgroups per tile, and few of
+//    them per CU.  Launches of 4096 tiles or more (one_wgs):
 //      W = 8:  12 per CU, 85.0 % in three processes (the same shape with 16
 //              per CU 84.5-85.1 %, with 11 or 14 84.3-84.7 %; slices loaded
 //              4 at a time, 16 per CU, 83.4-84.9 %; uncapped 80.5-83.3 %);
@@ -921,6 +922,17 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 //      W = 64: 5 per CU, 82.7-84.6 % (4: 82.9-84.1 %, 3: 67 %); pure bf16 6
 //              per CU, 82.6-84.5 %; Deep 79.0-80.7 % (pure 80.4-81.2 %);
 //      W = 1, 2: 16 per CU (not measured apart).
+//    Launches of fewer tiles (small_wgs: bucket groups of a streaming
+//    step, GPT-2-sized shards), in one process each, against Small:
+//      W = 8:  16 per CU: GPT-2-shaped shard (1899 tiles) 82.8-82.9 % (12:
+//              82.1 %, 20: 82.1 %, 8: 76.6 %; Small 81.8-81.9 %); 8B-shaped
+//              groups of 16 buckets (3200 tiles) on two streams 83.6-83.8 %
+//              (12: 82.5 %, 20: 83.2 %; Small 81.6-82.0 %);
+//      W = 16: 7 per CU: 70B-shaped groups of 16 (1600 tiles) 37.06-37.15
+//              ms per full step, 86.1-86.3 % (8: 85.6-85.8 %, 6: 72.5 %;
+//              Small 38.7-38.8 ms, 82.4-82.6 %);
+//      W = 64: 5 per CU: 7B-shaped groups of 16 (400 tiles) 81.7 % (4:
+//              82.2 %, 6: 80.8 %; Small uncapped 77.6 %).
 //    The cap and the batch depth act together (more slices per wave, fewer
 //    waves), and the optimum is narrow at W = 16 and 32: one more or one
 //    fewer workgroup per CU costs 3-10 points there.
@@ -928,7 +940,8 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 //    uncapped (W = 5: the cap lost, 79-82 % against 82-84 %); and, 16 per
 //    CU, large group launches at compiled W < 32 (the whole-tensor step's
 //    owned tensors, 32 per launch: 84.7-85.0 % on the 8B-shaped W = 8
-//    shard, where One at 12 per CU gave 79.7-82.6 %);
+//    shard, where One at 12 per CU gave 79.7-82.6 %; interleaved in one
+//    process, Wave 84.1 % against One at 12-24 per CU 83.3-84.0 %);
 //  - Deep (512-thread workgroups of four units, slices 8 at a time, one
 //    per CU by its 148 VGPRs), uncapped: plain slice rows at compiled
 //    W >= 32 (7B-shaped W = 64: 73-77 %, One 66 %) and large group launches
@@ -936,14 +949,13 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 //  - Wide / PureWide (runtime W >= 32): 512-thread workgroups of four units
 //    (256 for the two-row pure state): 79-80 % at W = 100, against 75-78 %
 //    with one-wave workgroups;
-//  - Small (launches of fewer than kSmallLaunch tiles: bucket groups of a
-//    streaming step, GPT-2-sized shards): one unit per thread and sixteen
+//  - Small (launches of fewer than kSmallLaunch tiles at runtime W, and
+//    on plain slices at W >= 32): one unit per thread and sixteen
 //    128-thread workgroups per tile, so that a few hundred or thousand
-//    tiles still spread evenly over the 256 CUs with a short tail, 8 per CU
-//    at compiled W < 32 (GPT-2-shaped W = 8 shard, 1899 tiles: 81.4-81.5 %
-//    against 80.3 % uncapped, 79.6-79.7 % with four 512-thread workgroups
-//    per tile, 75 % with Wide; 70B bucket groups 38.3 ms per full step
-//    against 38.6-38.8 ms uncapped).
+//    tiles still spread evenly over the 256 CUs with a short tail,
+//    uncapped (it ran the compiled-W small launches before One: GPT-2-
+//    shaped W = 8 shard 81.4-81.5 % at 8 per CU, against 79.6-79.7 % for
+//    four 512-thread workgroups per tile and 75 % for Wide).
 template <int WT>
 using ShapeOne = Shape<64, 1, (WT < 4 ? 4 : WT)>;
 using ShapeWave = Shape<64, 1, 4>;
@@ -952,7 +964,6 @@ using ShapeWide = Shape<512, 4, 4>;
 using ShapeSmall = Shape<128, 1, 4>;
 using ShapePureWide = Shape<256, 4, 4>;
 constexpr int64_t kSmallLaunch = 4096;
-constexpr int kSmallWgs = 8;
 constexpr int kWaveWgs = 16;
 
 template <int WT, bool PURE>
@@ -972,6 +983,14 @@ constexpr int one_wgs()
         return 16;
 }
 
+// launches of fewer than kSmallLaunch tiles: more workgroups per CU at
+// W <= 8, where the tail of a short launch weighs more
+template <int WT, bool PURE>
+constexpr int small_wgs()
+{
+    return WT <= 8 ? 16 : one_wgs<WT, PURE>();
+}
+
 // every shape stays within the launch limit of kMaxLaunchTiles tiles
 static_assert(kMaxLaunchTiles * ShapeWave::P * ShapeWave::NT <
                   (int64_t(1) << 32) &&
@@ -986,8 +1005,14 @@ void launch_step_w(const Args& a, bool tiled, dim3 grid, hipStream_t s)
     const int64_t tiles = (int64_t)grid.x * grid.y;
     constexpr bool kGroup = std::is_same<Args, GroupArgs>::value;
     if (tiles < kSmallLaunch) {
-        constexpr int kWgs = WT > 0 && WT < 32 ? kSmallWgs : 0;
-        launch_shape<WT, ShapeSmall, PURE, kWgs>(a, tiled, grid, s);
+        if constexpr (WT > 0) {
+            if (tiled || WT < 32) {
+                launch_shape<WT, ShapeOne<WT>, PURE, small_wgs<WT, PURE>()>(
+                    a, tiled, grid, s);
+                return;
+            }
+        }
+        launch_shape<WT, ShapeSmall, PURE, 0>(a, tiled, grid, s);
     } else if constexpr (WT > 0 && kGroup) {
         // large group launches (the whole-tensor step's owned tensors):
         // the member lookup of every workgroup wants more of them per CU
