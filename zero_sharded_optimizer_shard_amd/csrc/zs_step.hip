@@ -921,7 +921,13 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 //              VGPRs, one per CU) 77.4-80.3 %;
 //      W = 64: 5 per CU, 82.7-84.6 % (4: 82.9-84.1 %, 3: 67 %); pure bf16 6
 //              per CU, 82.6-84.5 %; Deep 79.0-80.7 % (pure 80.4-81.2 %);
-//      W = 1, 2: 16 per CU (not measured apart).
+//      W = 1, 2: 16 per CU (not measured apart);
+//      the step on three plain state arrays (plain_wgs), interleaved over
+//      three placements of the arrays: W = 8 8 per CU, 85.4-85.7 % (12:
+//      82.1-82.5 %, 7: 84.7-85.4 %, 9: 83.6-83.9 %, 10: 83.6-83.8 %, 6:
+//      71 %, 16: 78 %); W = 4 10 per CU, 84.0-85.0 % (12: 82.3-82.5 %, 8:
+//      82.8-83.9 %); at W = 16, 32 and 64 the mixed caps held (W = 16 6 per
+//      CU 80.8-84.1 % against 80.3-82.0 %, too close to the drop at 5).
 //    Launches of fewer tiles (small_wgs: bucket groups of a streaming
 //    step, GPT-2-sized shards), in one process each, against Small:
 //      W = 8:  16 per CU: GPT-2-shaped shard (1899 tiles) 82.8-82.9 % (12:
@@ -983,6 +989,15 @@ constexpr int one_wgs()
         return 16;
 }
 
+// the step on three plain state arrays (zs_step_plain), launches of
+// kSmallLaunch tiles or more: its state rows lie in three separate arrays,
+// and fewer workgroups per CU pay at W = 4 and 8
+template <int WT>
+constexpr int plain_wgs()
+{
+    return WT == 8 ? 8 : WT == 4 ? 10 : one_wgs<WT, false>();
+}
+
 // launches of fewer than kSmallLaunch tiles: more workgroups per CU at
 // W <= 8, where the tail of a short launch weighs more
 template <int WT, bool PURE>
@@ -1004,6 +1019,7 @@ void launch_step_w(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 {
     const int64_t tiles = (int64_t)grid.x * grid.y;
     constexpr bool kGroup = std::is_same<Args, GroupArgs>::value;
+    constexpr bool kPlain = std::is_same<Args, PlainArgs>::value;
     if (tiles < kSmallLaunch) {
         if constexpr (WT > 0) {
             if (tiled || WT < 32) {
@@ -1021,9 +1037,9 @@ void launch_step_w(const Args& a, bool tiled, dim3 grid, hipStream_t s)
         else
             launch_shape<WT, ShapeDeep, PURE, 0>(a, tiled, grid, s);
     } else if constexpr (WT > 0) {
+        constexpr int kWgs = kPlain ? plain_wgs<WT>() : one_wgs<WT, PURE>();
         if (tiled || WT < 32)
-            launch_shape<WT, ShapeOne<WT>, PURE, one_wgs<WT, PURE>()>(
-                a, tiled, grid, s);
+            launch_shape<WT, ShapeOne<WT>, PURE, kWgs>(a, tiled, grid, s);
         else                                // W plain slice rows, W >= 32
             launch_kernel<WT, false, ShapeDeep, PURE, 0>(a, grid, s);
     } else if (a.W < 32) {                  // runtime W
