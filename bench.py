@@ -59,6 +59,11 @@ STEP_KERNELS = {
     "dense7b": ("_ZN12_GLOBAL__N_111step_kernelILi64ELb1ENS_5ShapeILi64ELi1E"
                 "Li64EEELb0EEEvNS_8StepArgsE",
                 "step_kernel<64, true, Shape<64, 1, 64> >"),
+    # the streaming step's bucket groups: traffic per full step (every
+    # group launch of one pass over the buckets)
+    "llama70b": ("_ZN12_GLOBAL__N_117group_step_kernelILi16ELb1ENS_5ShapeILi64"
+                 "ELi1ELi16EEELb0EEEvNS_9GroupArgsE",
+                 "group_step_kernel<16, true, Shape<64, 1, 16> >"),
 }
 
 
@@ -103,13 +108,17 @@ def read_counter_csv(path: str, counter: str):
 
 
 def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
-                   workload: str = "llama8b") -> dict:
+                   workload: str = "llama8b", per_step: int = 0,
+                   out_path: str = None) -> dict:
     """HBM bytes per launch of the workload's step from two rocprofv3 --pmc
     runs of `bench.py --copy-calibration` (FETCH_SIZE, then WRITE_SIZE, KiB
     per dispatch), each scaled by what the same counter reads for the
     calibration copy of 4 GiB; written to profiles/traffic_<workload>.json
     with the digest of the kernel's machine code in the current build (the
-    counters must have been taken on that build)."""
+    counters must have been taken on that build).  per_step > 0: the
+    kernel is the streaming step's group kernel, launched per_step times per
+    full step; the record is per full step (sums of per_step consecutive
+    dispatches, averaged)."""
     symbol, kname = STEP_KERNELS[workload]
     fetch = read_counter_csv(fetch_csv, "FETCH_SIZE")
     write = read_counter_csv(write_csv, "WRITE_SIZE")
@@ -121,6 +130,10 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
     is_copy = lambda k: "k_copy16" in k
     tiled = lambda k: (k.startswith("void (anonymous namespace)::step_kernel<"
                                     f"{W}, true,") and "true>" not in k)
+    if per_step:
+        tiled = lambda k: (k.startswith("void (anonymous namespace)::"
+                                        f"group_step_kernel<{W}, true,")
+                           and "true>" not in k)
     plain = lambda k: (k.startswith("void (anonymous namespace)::step_kernel<"
                                     f"{W}, false,") and "true>" not in k)
     cf, cw = pick(fetch, is_copy), pick(write, is_copy)
@@ -133,13 +146,23 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
     pf, pw = pick(fetch, plain), pick(write, plain)
     if not tf or not tw:
         raise SystemExit("record-traffic: no tiled step dispatches found")
+    if per_step:
+        if len(tf) % per_step or len(tw) % per_step:
+            raise SystemExit(f"record-traffic: {len(tf)} / {len(tw)} group "
+                             f"dispatches, not whole full steps of "
+                             f"{per_step}")
+        tf = [sum(tf[i:i + per_step]) for i in range(0, len(tf), per_step)]
+        tw = [sum(tw[i:i + per_step]) for i in range(0, len(tw), per_step)]
     avg = lambda x: sum(x) / len(x)
     rd = avg(tf) * 1024 * rs
     wr = avg(tw) * 1024 * ws
     alg = (2 * W + 26) * n
+    what = ("zs_buckets_step, groups of 16 tiled buckets, tiled state, flat "
+            f"output; bytes per full step of {per_step} launches"
+            if per_step else "zs_step, tiled gradients, tiled state, flat "
+            "output")
     rec = {
-        "kernel": f"{kname} (zs_step, tiled gradients, tiled state, flat "
-                  "output)",
+        "kernel": f"{kname} ({what})",
         "workload": f"{workload} rank-0 shard, W={W}, {n:,} elements",
         "kernel_symbol": symbol,
         "kernel_sha256_16": kernel_digest(symbol),
@@ -160,8 +183,9 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
         rec["plain_slices"] = {"bytes_read_per_launch": prd,
                                "bytes_written_per_launch": pwr,
                                "ratio_to_algorithmic": (prd + pwr) / alg}
-    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"),
-              "w") as f:
+    if out_path is None:
+        out_path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     return rec
@@ -900,6 +924,25 @@ def stream_main(args, w):
     kern_ms = timed(do_upload=False)
     log(f"bucket steps alone: {kern_ms:.2f} ms per full step "
         f"(events {kern_ev_ms:.2f} ms)")
+    if args.kernels_only:
+        # the group launches alone (for counter runs): no arrival passes
+        bpp = 2 * W + 26
+        kern_gbs = bpp * n / (kern_ev_ms * 1e-3) / 1e9
+        print(json.dumps({
+            "metric": "ZeRO-2 bucket-group steps alone, params/s per GPU",
+            "value": n / (kern_ev_ms * 1e-3), "unit": "params/s",
+            "n_gpus": 1, "steps": K, "warmup": 1, "ms_per_step": kern_ev_ms,
+            "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"{w.name} rank-0 shard, W={W}, bucket "
+                                   f"groups of {G} without arrival",
+                       "shard_params": n, "buckets": nb,
+                       "bytes_per_param": bpp, "step_streams": len(sts)},
+            "roofline": {"bound": "hbm", "achieved": kern_gbs,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": kern_gbs / PEAK_HBM_GBS,
+                         "traffic": traffic_record(args.workload)}}))
+        return
     up_ms = timed(do_step=False)
     log(f"uploads alone: {up_ms:.2f} ms per full step")
     py_ms = timed()
@@ -982,7 +1025,8 @@ def stream_main(args, w):
                    "grads_layout": "tiled [tile][W][8192]"},
         "roofline": {"bound": "hbm", "achieved": kern_gbs,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": kern_gbs / PEAK_HBM_GBS, "traffic": None},
+                     "frac": kern_gbs / PEAK_HBM_GBS,
+                     "traffic": traffic_record(args.workload)},
         "streaming": {"wall_ms_per_step": wall_ms,
                       "uploads_alone_ms_per_step": up_ms,
                       "bucket_steps_alone_ms_per_step": kern_ms,
@@ -1058,6 +1102,9 @@ def main():
     ap.set_defaults(ceiling=True)
     ap.add_argument("--unfused", action="store_true",
                     help="also time step-to-shard + separate pack")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="llama70b: time the bucket-group launches alone "
+                    "and skip the arrival passes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="launch one plain 4 GiB device copy before the "
                     "steps (the reference dispatch for rocprofv3 counters)")
@@ -1074,7 +1121,13 @@ def main():
         w = wl.presets()[args.workload]
         n = zs.zs_layout_info(zs.zs_layout_build(w.numels, w.world,
                                                  w.rank))[1]
-        rec = record_traffic(*args.record_traffic, n, w.world, args.workload)
+        per_step = 0
+        if w.streaming:
+            nb = zs.zs_layout_info(zs.zs_layout_build(w.numels, w.world,
+                                                      w.rank))[2]
+            per_step = -(-nb // min(args.group, zs.ZS_MAX_GROUP))
+        rec = record_traffic(*args.record_traffic, n, w.world, args.workload,
+                             per_step)
         print(json.dumps({k: rec[k] for k in
                           ("bytes_per_launch", "ratio_to_algorithmic")}))
         return

@@ -1,5 +1,6 @@
-"""The benchmark's command-line contract that needs no GPU: more than one
-GPU is refused with a message and exit status 2."""
+"""The benchmark's host logic that needs no GPU: more than one GPU is
+refused with a message and exit status 2, and rocprofv3 counter CSVs turn
+into the traffic record as stated."""
 
 import os
 import subprocess
@@ -17,3 +18,65 @@ def test_more_than_one_gpu_is_refused():
         assert f"--gpus {n} is not supported" in p.stderr
         assert "one GPU" in p.stderr
         assert p.stdout == ""
+
+
+def _counter_csv(path, counter, rows):
+    """A rocprofv3 counter-collection CSV with the columns the bench reads."""
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i, (k, v) in enumerate(rows):
+            f.write(f'{i},"{k}",{counter},{v}\n')
+
+
+def test_record_traffic_scales_by_the_calibration_copy(tmp_path):
+    """Bytes per launch = counter KiB x 1024 x (4 GiB / the counter's reading
+    for the 4 GiB copy); only the tiled step's dispatches count."""
+    sys.path.insert(0, ROOT)
+    import bench
+    W, n = 8, 1000
+    step = "void (anonymous namespace)::step_kernel<8, true, Shape<64, 1, 8>, false>(StepArgs)"
+    plain = "void (anonymous namespace)::step_kernel<8, false, Shape<64, 1, 8>, false>(StepArgs)"
+    pure = "void (anonymous namespace)::step_kernel<8, true, Shape<64, 1, 8>, true>(StepArgs)"
+    copy = "void k_copy16(...)"
+    kib = 4 << 20                       # 4 GiB in KiB
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE",
+                 [(copy, kib / 2), (step, 10.0), (step, 14.0), (plain, 20.0),
+                  (pure, 999.0)])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE",
+                 [(copy, kib), (step, 5.0), (step, 5.0), (plain, 6.0),
+                  (pure, 999.0)])
+    rec = bench.record_traffic(str(tmp_path / "f.csv"),
+                               str(tmp_path / "w.csv"), n, W, "llama8b",
+                               out_path=str(tmp_path / "t.json"))
+    assert rec["copy_calibration"]["read_scale"] == 2.0
+    assert rec["bytes_read_per_launch"] == 12.0 * 1024 * 2
+    assert rec["bytes_written_per_launch"] == 5.0 * 1024
+    assert rec["algorithmic_bytes_per_launch"] == (2 * W + 26) * n
+    assert rec["plain_slices"]["bytes_read_per_launch"] == 20.0 * 1024 * 2
+    assert (tmp_path / "t.json").exists()
+
+
+def test_record_traffic_sums_group_launches_per_full_step(tmp_path):
+    """The streaming step's record is per full step: per_step consecutive
+    group dispatches summed, the sums averaged; a partial step is refused."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import pytest
+    W = 16
+    grp = "void (anonymous namespace)::group_step_kernel<16, true, Shape<64, 1, 16>, false>(GroupArgs)"
+    copy = "void k_copy16(...)"
+    kib = 4 << 20
+    f = [(copy, kib)] + [(grp, v) for v in (1, 2, 3, 3, 3, 3)]
+    w = [(copy, kib)] + [(grp, 1.0)] * 6
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", f)
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", w)
+    rec = bench.record_traffic(str(tmp_path / "f.csv"),
+                               str(tmp_path / "w.csv"), 100, W, "llama70b",
+                               per_step=3, out_path=str(tmp_path / "t.json"))
+    assert rec["FETCH_SIZE_KiB_per_launch"] == [6, 9]
+    assert rec["bytes_read_per_launch"] == 7.5 * 1024
+    assert rec["bytes_written_per_launch"] == 3.0 * 1024
+    with pytest.raises(SystemExit):
+        bench.record_traffic(str(tmp_path / "f.csv"),
+                             str(tmp_path / "w.csv"), 100, W, "llama70b",
+                             per_step=4, out_path=str(tmp_path / "u.json"))
