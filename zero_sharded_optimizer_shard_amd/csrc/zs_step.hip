@@ -20,21 +20,24 @@
 //   p   = bf16 of th, round to nearest even
 //
 // Work decomposition.  The shard is cut into tiles of ZS_TILE = 8192
-// elements of one bucket's slice.  Below W = 32 a tile is stepped by 32
-// one-wave workgroups of one 4-element unit per thread; at W >= 32 by one
-// 512-thread workgroup (8 wave64s) whose threads each own four units at
-// stride 512 units; in launches of few tiles by four 512-thread workgroups
-// of one unit per thread (the work shapes are chosen below).  Either way
-// every load or store instruction of a wave covers one contiguous run
-// (1 KiB of fp32, 512 B of bf16) and a tile's rows are swept in bursts.  With the tiled state the three 32 KiB
-// rows of a tile are adjacent, and with tiled gradients so are the W 16 KiB
-// slice rows; measured on MI355X, that lifts this 2:1 read/write stream
-// from about 5.4 to about 6.4 TB/s.  All loads of a unit are issued before
-// its arithmetic (the W slices in batches of 4 or 8), and every access is
-// non-temporal: nothing is reused.  The step's stores also carry system
-// scope (sc0 sc1 nt), so the L2 streams them on to HBM instead of holding
-// them as dirty lines: measured on MI355X, 82.0-82.2 % of peak against
-// 80.4 % with plain non-temporal stores on the 8B-shaped W = 8 shard.
+// elements of one bucket's slice.  At a compiled W a tile is stepped by 32
+// one-wave workgroups, one 4-element unit per thread, each thread loading
+// its unit of all W gradient slices at once, and only a few of these
+// workgroups may share a CU (the launch reserves LDS the kernel does not
+// use); runtime W, plain slice rows at W >= 32 and large bucket groups take
+// other shapes (listed with the launchers below).  Either way every load or
+// store instruction of a wave covers one contiguous run (1 KiB of fp32,
+// 512 B of bf16) and a tile's rows are swept in bursts.  With the tiled
+// state the three 32 KiB rows of a tile are adjacent, and with tiled
+// gradients so are the W 16 KiB slice rows; measured on MI355X, that lifts
+// this 2:1 read/write stream from about 5.4 to about 6.4 TB/s with the
+// earlier 512-thread shapes.  All loads of a unit are issued before its
+// arithmetic (all W slices at a compiled W, batches of 4 or 8 otherwise),
+// and every access is non-temporal: nothing is reused.  The step's stores
+// also carry system scope (sc0 sc1 nt), so the L2 streams them on to HBM
+// instead of holding them as dirty lines: measured on MI355X, 82.0-82.2 %
+// of peak against 80.4 % with plain non-temporal stores on the 8B-shaped
+// W = 8 shard (512-thread workgroups then).
 //
 // Grid of the whole-shard step: blockIdx.y = bucket, blockIdx.x = tile
 // (times the workgroups per tile) of that bucket's slice, so no thread
