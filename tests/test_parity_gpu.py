@@ -375,13 +375,16 @@ def test_hyperparameter_edge_cases(name, hp, steps):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("W,tiles", [(2, 300), (2, 4200), (32, 4100),
-                                     (5, 4100), (5, 1100), (33, 4100)])
+@pytest.mark.parametrize("W,tiles", [(2, 300), (2, 4200), (16, 4100),
+                                     (32, 4100), (64, 4100), (5, 4100),
+                                     (5, 1100), (33, 4100)])
 def test_launch_shapes(W, tiles, layout):
-    """Each work shape of the step: fewer than 4096 tiles (four workgroups
-    per tile), 4096 or more at W < 32 (one-wave workgroups, compiled and
-    runtime W), at W >= 32 (compiled), and the runtime-W kernel at W >= 32
-    (512-thread workgroups); one bucket per launch, a ragged last tile."""
+    """Each work shape of the step: at a compiled W one-wave workgroups
+    loading all W slices at once, in launches of fewer and of 4096 or more
+    tiles (plain slice rows at W >= 32: Deep); at runtime W the Small shape
+    below 4096 tiles, one-wave workgroups of 4-slice batches at W < 32 and
+    512-thread workgroups at W >= 32; one bucket per launch, a ragged last
+    tile."""
     n_rank = tiles * TILE - 4096            # the last tile half full
     numels = [W * n_rank - 1000, 1000]
     say(f"case shape W={W} tiles={tiles} {layout}")
@@ -1022,9 +1025,9 @@ def test_pure_bf16_step(W, layout, flat_params):
 @pytest.mark.parametrize("W,tiles", [(2, 300), (2, 4200), (8, 4100),
                                      (5, 4100), (32, 4100), (33, 4100)])
 def test_pure_bf16_launch_shapes(W, tiles):
-    """Each work shape of the pure-bf16 step: fewer than 4096 tiles, 4096 or
-    more at W < 32 (one-wave workgroups), at W >= 32, and the runtime-W
-    kernel at W < 32 and W >= 32 (256-thread workgroups);
+    """Each work shape of the pure-bf16 step: one-wave workgroups at a
+    compiled W (fewer and 4096 or more tiles), and the runtime-W kernel at
+    W < 32 (one-wave) and W >= 32 (256-thread workgroups);
     one bucket, a ragged last tile, parameters in place in the flat
     buffer, tiled gradients; bit for bit against the oracle."""
     n_rank = tiles * TILE - 4096            # the last tile half full
