@@ -235,8 +235,8 @@ void zs_layout_free(zs_layout* layout);
  * All device pointers must be 16-byte aligned (ZS_EALIGN otherwise);
  * ZS_EINVAL for an unknown grad_layout.
  *
- * Launches: at W = 1, 2, 4, 8, 16, 32 or 64 the step's workgroups (one or
- * two waves) reserve LDS they do not use, so that only a few of them share
+ * Launches: at W = 1, 2, 4, 8, 16, 32 or 64 the step's one-wave
+ * workgroups reserve LDS they do not use, so that only a few of them share
  * a CU: 5 to 16 by W and launch size (at W = 8, 12, each holding 1/12 of
  * the CU's LDS; at W = 64, 5), which keeps fewer tiles in flight, measured
  * faster on MI355X (the workgroups of plain slices at W >= 32, of bucket
