@@ -222,13 +222,16 @@ def one_bucket(W, tiles):
 # in the shape)
 #   (2, 300)    One <64, 1, 4>, W = 2     (5, 1100)  Small, runtime W
 #   (1, 4100)   One <64, 1, 4>, W = 1     (8, 4100)  One <64, 1, 8>
-#   (16, 4100)  One <64, 1, 16>           (5, 4100)  Wave, runtime W
+#   (16, 4100)  One <64, 1, 16>
 #   (32, 4100)  One <64, 1, 32> tiled, Deep on plain slices
 #   (64, 4100)  One <64, 1, 64> tiled, Deep on plain slices
-#   (33, 4100)  Wide, runtime W
 #   (64, 300)   One <64, 1, 64> tiled, Small on plain slices
+#   runtime W, 4100 tiles: one-wave workgroups with batches of 8 (5), 16
+#   (12), 32 (20, 33) and 64 (100) on tiled gradients (and at W = 5 on
+#   plain slices); Wave (12, 20) and Wide (33, 100) on plain slices
 SHAPES = [(2, 300), (5, 1100), (1, 4100), (8, 4100), (16, 4100), (5, 4100),
-          (32, 4100), (64, 4100), (33, 4100), (64, 300)]
+          (12, 4100), (20, 4100), (32, 4100), (64, 4100), (33, 4100),
+          (100, 4100), (64, 300)]
 
 
 @pytest.mark.parametrize("state_form", ["tiled", "plain"])

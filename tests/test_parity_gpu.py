@@ -377,13 +377,15 @@ def test_hyperparameter_edge_cases(name, hp, steps):
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("W,tiles", [(2, 300), (2, 4200), (16, 4100),
                                      (32, 4100), (64, 4100), (5, 4100),
-                                     (5, 1100), (33, 4100)])
+                                     (5, 1100), (12, 4100), (20, 4100),
+                                     (33, 4100)])
 def test_launch_shapes(W, tiles, layout):
     """Each work shape of the step: at a compiled W one-wave workgroups
     loading all W slices at once, in launches of fewer and of 4096 or more
     tiles (plain slice rows at W >= 32: Deep); at runtime W the Small shape
-    below 4096 tiles, one-wave workgroups of 4-slice batches at W < 32 and
-    512-thread workgroups at W >= 32; one bucket per launch, a ragged last
+    below 4096 tiles, above it one-wave workgroups batching 8, 16 or 32
+    slices (plain slice rows above W = 8: 4-slice batches below W = 32,
+    512-thread workgroups above); one bucket per launch, a ragged last
     tile."""
     n_rank = tiles * TILE - 4096            # the last tile half full
     numels = [W * n_rank - 1000, 1000]
@@ -699,16 +701,19 @@ def test_plain_state_step(W, tensors, layout):
     run_plain(ref, layout, (1, 2, 3))
 
 
-@pytest.mark.parametrize("W,tiles", [(8, 4100), (5, 4100), (32, 4100)])
-def test_plain_state_launch_shapes(W, tiles):
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("W,tiles", [(8, 4100), (5, 4100), (20, 4100),
+                                     (32, 4100), (48, 4100)])
+def test_plain_state_launch_shapes(W, tiles, layout):
     """zs_step_plain in the work shapes of large launches (one-wave at
-    compiled and runtime W, Deep at W = 32): one bucket, a ragged last
-    tile, plain gradient slices; two steps against the oracle."""
+    compiled and runtime W; on plain slices Deep at W = 32, Wave at W = 20,
+    Wide at W = 48): one bucket, a ragged last tile; two steps against the
+    oracle."""
     n_rank = tiles * TILE - 4096
-    say(f"case plain state shape W={W} tiles={tiles}")
+    say(f"case plain state shape W={W} tiles={tiles} {layout}")
     ref = Case([W * n_rank], W, W - 1, cap=0, seed=W, gpu=False)
     assert n_tiles(ref.lay_o) == tiles
-    run_plain(ref, "slices", (1, 2), stride_pad=0)
+    run_plain(ref, layout, (1, 2), stride_pad=0)
 
 
 def test_pack_flat_and_per_tensor():

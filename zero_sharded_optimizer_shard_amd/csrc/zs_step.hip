@@ -945,7 +945,20 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 //    The cap and the batch depth act together (more slices per wave, fewer
 //    waves), and the optimum is narrow at W = 16 and 32: one more or one
 //    fewer workgroup per CU costs 3-10 points there.
-//  - Wave (runtime W < 32): the same one-wave unit, slices 4 at a time,
+//  - Runtime W, mixed precision, 4096 tiles or more (launch_runtime_one):
+//    one-wave workgroups, slices in batches of 8 (W <= 8), 16 (W <= 16) or
+//    32 (W <= 64) or 64, 12 / 12 / 8 (W <= 32) / 7 / 6 per CU; tiled
+//    gradients, and plain slices at W <= 8.  Against the earlier Wave and
+//    Wide shapes, interleaved in one process each: W = 3 85.9 % (80.9 %),
+//    W = 5 85.7 % (81.3 %; plain slices 85.9 %, 82.7 %; plain state 83.0 %,
+//    77.5 %), W = 12 84.4-84.6 % (82.7-82.8 %), W = 20 86.0-86.2 %
+//    (78.8-79.4 %), W = 33 82.5-83.1 % (76.8-77.7 %), W = 48 83.0-83.1 %
+//    (78.7-79.6 %; plain state 78.8 %, 74.2 %), W = 100 82.4-82.7 %
+//    (78.9-81.0 %), W = 128 82.8-82.9 % (79.7 %).  The pure-bf16 step lost
+//    with these shapes (W = 5: 76 % against 82 %) and keeps Wave / PureWide;
+//    plain slices at W = 20 fell to 53 % with a 32-slice batch;
+//  - Wave (runtime W < 32 for the pure-bf16 step, plain slices above W = 8
+//    and bucket groups): the same one-wave unit, slices 4 at a time,
 //    uncapped (W = 5: the cap lost, 79-82 % against 82-84 %); and, 16 per
 //    CU, large group launches at compiled W < 32 (the whole-tensor step's
 //    owned tensors, 32 per launch: 84.7-85.0 % on the 8B-shaped W = 8
@@ -955,9 +968,10 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 //    per CU by its 148 VGPRs), uncapped: plain slice rows at compiled
 //    W >= 32 (7B-shaped W = 64: 73-77 %, One 66 %) and large group launches
 //    there;
-//  - Wide / PureWide (runtime W >= 32): 512-thread workgroups of four units
-//    (256 for the two-row pure state): 79-80 % at W = 100, against 75-78 %
-//    with one-wave workgroups;
+//  - Wide / PureWide (runtime W >= 32 for plain slices, bucket groups and
+//    the pure-bf16 step): 512-thread workgroups of four units (256 for the
+//    two-row pure state): 79-80 % at W = 100, against 75-78 % with uncapped
+//    one-wave workgroups;
 //  - Small (launches of fewer than kSmallLaunch tiles at runtime W, and
 //    on plain slices at W >= 32): one unit per thread and sixteen
 //    128-thread workgroups per tile, so that a few hundred or thousand
@@ -1016,6 +1030,25 @@ static_assert(kMaxLaunchTiles * ShapeWave::P * ShapeWave::NT <
                   (int64_t(1) << 32),
               "one launch row of tiles fits the grid");
 
+// Runtime W (outside the compiled set), mixed-precision step, 4096 tiles
+// or more: one-wave workgroups whose batch covers W up to 32 at once, and
+// few of them per CU; on plain slice rows only for W <= 8 (a W = 20 batch of
+// 32 slice rows ran at 53 %).
+template <class Args>
+void launch_runtime_one(const Args& a, bool tiled, dim3 grid, hipStream_t s)
+{
+    if (a.W <= 8)
+        launch_shape<0, Shape<64, 1, 8>, false, 12>(a, tiled, grid, s);
+    else if (a.W <= 16)
+        launch_kernel<0, true, Shape<64, 1, 16>, false, 12>(a, grid, s);
+    else if (a.W <= 32)
+        launch_kernel<0, true, Shape<64, 1, 32>, false, 8>(a, grid, s);
+    else if (a.W <= 64)
+        launch_kernel<0, true, Shape<64, 1, 32>, false, 7>(a, grid, s);
+    else
+        launch_kernel<0, true, Shape<64, 1, 64>, false, 6>(a, grid, s);
+}
+
 // grid: one x per tile (launch_kernel multiplies by the shape's P)
 template <int WT, bool PURE, class Args>
 void launch_step_w(const Args& a, bool tiled, dim3 grid, hipStream_t s)
@@ -1045,12 +1078,19 @@ void launch_step_w(const Args& a, bool tiled, dim3 grid, hipStream_t s)
             launch_shape<WT, ShapeOne<WT>, PURE, kWgs>(a, tiled, grid, s);
         else                                // W plain slice rows, W >= 32
             launch_kernel<WT, false, ShapeDeep, PURE, 0>(a, grid, s);
-    } else if (a.W < 32) {                  // runtime W
-        launch_shape<WT, ShapeWave, PURE, 0>(a, tiled, grid, s);
-    } else if constexpr (PURE) {
-        launch_shape<WT, ShapePureWide, PURE, 0>(a, tiled, grid, s);
-    } else {
-        launch_shape<WT, ShapeWide, PURE, 0>(a, tiled, grid, s);
+    } else {                                // runtime W
+        if constexpr (!PURE && !kGroup) {
+            if (tiled || a.W <= 8) {
+                launch_runtime_one(a, tiled, grid, s);
+                return;
+            }
+        }
+        if (a.W < 32)
+            launch_shape<WT, ShapeWave, PURE, 0>(a, tiled, grid, s);
+        else if constexpr (PURE)
+            launch_shape<WT, ShapePureWide, PURE, 0>(a, tiled, grid, s);
+        else
+            launch_shape<WT, ShapeWide, PURE, 0>(a, tiled, grid, s);
     }
 }
 
