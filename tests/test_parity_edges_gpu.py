@@ -288,10 +288,13 @@ def test_step_edge_values(W, tiles, layout, hp_name, state_form):
 
 
 # the pure-bf16 step's shapes: One (W = 2, 8, 16, 32, 64; Deep on plain
-# slices at W >= 32), Wave (runtime W), PureWide (runtime W >= 32), Small
-# (runtime W, and plain slices at W = 64, below 4096 tiles)
+# slices at W >= 32; at runtime W above 8 on tiled gradients, batches of 16,
+# 32 and 64 for W = 12, 33, 100), Wave (runtime W up to 8, and plain slices
+# below 32), PureWide (plain slices at runtime W >= 32), Small (runtime W,
+# and plain slices at W = 64, below 4096 tiles)
 PURE_SHAPES = [(2, 300), (5, 1100), (64, 300), (8, 4100), (16, 4100),
-               (5, 4100), (32, 4100), (64, 4100), (33, 4100)]
+               (5, 4100), (12, 4100), (32, 4100), (64, 4100), (33, 4100),
+               (100, 4100)]
 
 
 @pytest.mark.parametrize("layout", ["tiled", "slices"])

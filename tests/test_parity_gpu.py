@@ -1028,11 +1028,13 @@ def test_pure_bf16_step(W, layout, flat_params):
 
 
 @pytest.mark.parametrize("W,tiles", [(2, 300), (2, 4200), (8, 4100),
-                                     (5, 4100), (32, 4100), (33, 4100)])
+                                     (5, 4100), (12, 4100), (32, 4100),
+                                     (33, 4100)])
 def test_pure_bf16_launch_shapes(W, tiles):
     """Each work shape of the pure-bf16 step: one-wave workgroups at a
-    compiled W (fewer and 4096 or more tiles), and the runtime-W kernel at
-    W < 32 (one-wave) and W >= 32 (256-thread workgroups);
+    compiled W (fewer and 4096 or more tiles), and at runtime W one-wave
+    workgroups of 4-slice batches up to W = 8 and of 16- or 32-slice
+    batches above;
     one bucket, a ragged last tile, parameters in place in the flat
     buffer, tiled gradients; bit for bit against the oracle."""
     n_rank = tiles * TILE - 4096            # the last tile half full

@@ -954,11 +954,13 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 //    77.5 %), W = 12 84.4-84.6 % (82.7-82.8 %), W = 20 86.0-86.2 %
 //    (78.8-79.4 %), W = 33 82.5-83.1 % (76.8-77.7 %), W = 48 83.0-83.1 %
 //    (78.7-79.6 %; plain state 78.8 %, 74.2 %), W = 100 82.4-82.7 %
-//    (78.9-81.0 %), W = 128 82.8-82.9 % (79.7 %).  The pure-bf16 step lost
-//    with these shapes (W = 5: 76 % against 82 %) and keeps Wave / PureWide;
-//    plain slices at W = 20 fell to 53 % with a 32-slice batch;
-//  - Wave (runtime W < 32 for the pure-bf16 step, plain slices above W = 8
-//    and bucket groups): the same one-wave unit, slices 4 at a time,
+//    (78.9-81.0 %), W = 128 82.8-82.9 % (79.7 %).  The pure-bf16 step on
+//    tiled gradients above W = 8, with 14 per CU at W <= 16: W = 12 84.9 %
+//    (81.4 %), W = 20 80.0 % (76.2 %), W = 24 81.9 % (78.0 %), W = 48 79.9 %
+//    (77.0 %), W = 100 81.8 % (80.9 %); at W = 5 it lost (76 % against
+//    82 %).  Plain slices at W = 20 fell to 53 % with a 32-slice batch;
+//  - Wave (runtime W < 32: the pure-bf16 step up to W = 8, plain slices
+//    above W = 8, bucket groups): the same one-wave unit, slices 4 at a time,
 //    uncapped (W = 5: the cap lost, 79-82 % against 82-84 %); and, 16 per
 //    CU, large group launches at compiled W < 32 (the whole-tensor step's
 //    owned tensors, 32 per launch: 84.7-85.0 % on the 8B-shaped W = 8
@@ -968,8 +970,7 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 //    per CU by its 148 VGPRs), uncapped: plain slice rows at compiled
 //    W >= 32 (7B-shaped W = 64: 73-77 %, One 66 %) and large group launches
 //    there;
-//  - Wide / PureWide (runtime W >= 32 for plain slices, bucket groups and
-//    the pure-bf16 step): 512-thread workgroups of four units (256 for the
+//  - Wide / PureWide (runtime W >= 32 for plain slices and bucket groups): 512-thread workgroups of four units (256 for the
 //    two-row pure state): 79-80 % at W = 100, against 75-78 % with uncapped
 //    one-wave workgroups;
 //  - Small (launches of fewer than kSmallLaunch tiles at runtime W, and
@@ -1030,23 +1031,27 @@ static_assert(kMaxLaunchTiles * ShapeWave::P * ShapeWave::NT <
                   (int64_t(1) << 32),
               "one launch row of tiles fits the grid");
 
-// Runtime W (outside the compiled set), mixed-precision step, 4096 tiles
-// or more: one-wave workgroups whose batch covers W up to 32 at once, and
-// few of them per CU; on plain slice rows only for W <= 8 (a W = 20 batch of
-// 32 slice rows ran at 53 %).
-template <class Args>
+// Runtime W (outside the compiled set), 4096 tiles or more: one-wave
+// workgroups whose batch covers W up to 32 at once, and few of them per
+// CU.  The mixed-precision step takes it on tiled gradients, and on plain
+// slice rows for W <= 8 (a W = 20 batch of 32 slice rows ran at 53 %); the
+// pure-bf16 step on tiled gradients above W = 8 (at W = 5 it lost).
+template <bool PURE, class Args>
 void launch_runtime_one(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 {
-    if (a.W <= 8)
-        launch_shape<0, Shape<64, 1, 8>, false, 12>(a, tiled, grid, s);
-    else if (a.W <= 16)
-        launch_kernel<0, true, Shape<64, 1, 16>, false, 12>(a, grid, s);
-    else if (a.W <= 32)
-        launch_kernel<0, true, Shape<64, 1, 32>, false, 8>(a, grid, s);
-    else if (a.W <= 64)
-        launch_kernel<0, true, Shape<64, 1, 32>, false, 7>(a, grid, s);
-    else
-        launch_kernel<0, true, Shape<64, 1, 64>, false, 6>(a, grid, s);
+    if (a.W <= 8) {
+        if constexpr (!PURE)
+            launch_shape<0, Shape<64, 1, 8>, false, 12>(a, tiled, grid, s);
+    } else if (a.W <= 16) {
+        launch_kernel<0, true, Shape<64, 1, 16>, PURE, PURE ? 14 : 12>(
+            a, grid, s);
+    } else if (a.W <= 32) {
+        launch_kernel<0, true, Shape<64, 1, 32>, PURE, 8>(a, grid, s);
+    } else if (a.W <= 64) {
+        launch_kernel<0, true, Shape<64, 1, 32>, PURE, 7>(a, grid, s);
+    } else {
+        launch_kernel<0, true, Shape<64, 1, 64>, PURE, 6>(a, grid, s);
+    }
 }
 
 // grid: one x per tile (launch_kernel multiplies by the shape's P)
@@ -1079,9 +1084,9 @@ void launch_step_w(const Args& a, bool tiled, dim3 grid, hipStream_t s)
         else                                // W plain slice rows, W >= 32
             launch_kernel<WT, false, ShapeDeep, PURE, 0>(a, grid, s);
     } else {                                // runtime W
-        if constexpr (!PURE && !kGroup) {
-            if (tiled || a.W <= 8) {
-                launch_runtime_one(a, tiled, grid, s);
+        if constexpr (!kGroup) {
+            if (PURE ? tiled && a.W > 8 : tiled || a.W <= 8) {
+                launch_runtime_one<PURE>(a, tiled, grid, s);
                 return;
             }
         }
