@@ -228,10 +228,12 @@ def one_bucket(W, tiles):
 #   (64, 300)   One <64, 1, 64> tiled, Small on plain slices
 #   runtime W, 4100 tiles: one-wave workgroups with batches of 8 (5), 16
 #   (12), 32 (20, 33) and 64 (100) on tiled gradients (and at W = 5 on
-#   plain slices); Wave (12, 20) and Wide (33, 100) on plain slices
+#   plain slices); Wave (12, 20) and Wide (33, 100) on plain slices;
+#   (12, 300): one-wave batches of 16 below 4096 tiles on tiled gradients,
+#   Small on plain slices
 SHAPES = [(2, 300), (5, 1100), (1, 4100), (8, 4100), (16, 4100), (5, 4100),
           (12, 4100), (20, 4100), (32, 4100), (64, 4100), (33, 4100),
-          (100, 4100), (64, 300)]
+          (100, 4100), (64, 300), (12, 300)]
 
 
 @pytest.mark.parametrize("state_form", ["tiled", "plain"])
@@ -334,11 +336,13 @@ def test_pure_bf16_step_edge_values(W, tiles, layout):
 
 
 # the bucket-group kernel (zs_bucket_step: a group of one bucket): One
-# below 4096 tiles at compiled W (Small on plain slices at W = 64), Small at
-# runtime W; at 4096 tiles or more Wave (compiled and runtime W < 32), Deep
-# at compiled W >= 32, Wide at runtime W >= 32
+# below 4096 tiles at compiled W (Small on plain slices at W = 64), at
+# runtime W above 8 one-wave batches on tiled gradients (Small on plain
+# slices), Small at runtime W up to 8; at 4096 tiles or more Wave (compiled
+# and runtime W < 32), Deep at compiled W >= 32, Wide at runtime W >= 32
 GROUP_SHAPES = [(2, 300), (8, 300), (16, 300), (64, 300), (5, 300),
-                (8, 4100), (5, 4100), (64, 4100), (33, 4100)]
+                (12, 300), (48, 300), (8, 4100), (5, 4100), (64, 4100),
+                (33, 4100)]
 
 
 @pytest.mark.parametrize("layout", ["tiled", "slices"])

@@ -377,16 +377,16 @@ def test_hyperparameter_edge_cases(name, hp, steps):
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("W,tiles", [(2, 300), (2, 4200), (16, 4100),
                                      (32, 4100), (64, 4100), (5, 4100),
-                                     (5, 1100), (12, 4100), (20, 4100),
-                                     (33, 4100)])
+                                     (5, 1100), (20, 1100), (12, 4100),
+                                     (20, 4100), (33, 4100)])
 def test_launch_shapes(W, tiles, layout):
     """Each work shape of the step: at a compiled W one-wave workgroups
     loading all W slices at once, in launches of fewer and of 4096 or more
-    tiles (plain slice rows at W >= 32: Deep); at runtime W the Small shape
-    below 4096 tiles, above it one-wave workgroups batching 8, 16 or 32
-    slices (plain slice rows above W = 8: 4-slice batches below W = 32,
-    512-thread workgroups above); one bucket per launch, a ragged last
-    tile."""
+    tiles (plain slice rows at W >= 32: Deep); at runtime W one-wave
+    workgroups batching 8, 16 or 32 slices (below 4096 tiles only above
+    W = 8, else Small; plain slice rows above W = 8: Small below 4096
+    tiles, 4-slice batches below W = 32, 512-thread workgroups above); one
+    bucket per launch, a ragged last tile."""
     n_rank = tiles * TILE - 4096            # the last tile half full
     numels = [W * n_rank - 1000, 1000]
     say(f"case shape W={W} tiles={tiles} {layout}")

@@ -973,8 +973,12 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 //  - Wide / PureWide (runtime W >= 32 for plain slices and bucket groups): 512-thread workgroups of four units (256 for the
 //    two-row pure state): 79-80 % at W = 100, against 75-78 % with uncapped
 //    one-wave workgroups;
-//  - Small (launches of fewer than kSmallLaunch tiles at runtime W, and
-//    on plain slices at W >= 32): one unit per thread and sixteen
+//  - Runtime W above 8, mixed precision on tiled gradients, launches of
+//    fewer tiles too (bucket groups of 16 on two streams): W = 12 84.8 %
+//    (Small 79.9 %), W = 24 85.0 % (78.3 %), W = 48 82.0 % (76.0 %), W = 100
+//    80.1 % (75.7 %);
+//  - Small (launches of fewer than kSmallLaunch tiles at runtime W up to 8
+//    and for the pure-bf16 step, and on plain slices at W >= 32): one unit per thread and sixteen
 //    128-thread workgroups per tile, so that a few hundred or thousand
 //    tiles still spread evenly over the 256 CUs with a short tail,
 //    uncapped (it ran the compiled-W small launches before One: GPT-2-
@@ -1066,6 +1070,11 @@ void launch_step_w(const Args& a, bool tiled, dim3 grid, hipStream_t s)
             if (tiled || WT < 32) {
                 launch_shape<WT, ShapeOne<WT>, PURE, small_wgs<WT, PURE>()>(
                     a, tiled, grid, s);
+                return;
+            }
+        } else if constexpr (!PURE) {
+            if (tiled && a.W > 8) {         // runtime W, as for large launches
+                launch_runtime_one<PURE>(a, tiled, grid, s);
                 return;
             }
         }
