@@ -1035,11 +1035,13 @@ static_assert(kMaxLaunchTiles * ShapeWave::P * ShapeWave::NT <
                   (int64_t(1) << 32),
               "one launch row of tiles fits the grid");
 
-// Runtime W (outside the compiled set), 4096 tiles or more: one-wave
-// workgroups whose batch covers W up to 32 at once, and few of them per
-// CU.  The mixed-precision step takes it on tiled gradients, and on plain
-// slice rows for W <= 8 (a W = 20 batch of 32 slice rows ran at 53 %); the
-// pure-bf16 step on tiled gradients above W = 8 (at W = 5 it lost).
+// Runtime W (outside the compiled set): one-wave workgroups whose batch
+// covers W up to 32 at once, and few of them per CU.  Launches of
+// kSmallLaunch tiles or more of the mixed-precision step take it on tiled
+// gradients, and on plain slice rows for W <= 8 (a W = 20 batch of 32 slice
+// rows ran at 53 %); those of the pure-bf16 step on tiled gradients above
+// W = 8 (at W = 5 it lost); smaller launches of the mixed-precision step on
+// tiled gradients above W = 8 (bucket groups).
 template <bool PURE, class Args>
 void launch_runtime_one(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 {
