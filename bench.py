@@ -59,6 +59,10 @@ STEP_KERNELS = {
     "dense7b": ("_ZN12_GLOBAL__N_111step_kernelILi64ELb1ENS_5ShapeILi64ELi1E"
                 "Li64EEELb0EEEvNS_8StepArgsE",
                 "step_kernel<64, true, Shape<64, 1, 64> >"),
+    # the pure-bf16 step (record key <workload>_bf16)
+    "llama8b_bf16": ("_ZN12_GLOBAL__N_111step_kernelILi8ELb1ENS_5ShapeILi64ELi1E"
+                     "Li8EEELb1EEEvNS_8StepArgsE",
+                     "step_kernel<8, true, Shape<64, 1, 8>, true>"),
     # the streaming step's bucket groups: traffic per full step (every
     # group launch of one pass over the buckets)
     "llama70b": ("_ZN12_GLOBAL__N_117group_step_kernelILi16ELb1ENS_5ShapeILi64"
@@ -120,6 +124,7 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
     full step; the record is per full step (sums of per_step consecutive
     dispatches, averaged)."""
     symbol, kname = STEP_KERNELS[workload]
+    pure = workload.endswith("_bf16")
     fetch = read_counter_csv(fetch_csv, "FETCH_SIZE")
     write = read_counter_csv(write_csv, "WRITE_SIZE")
     copy_bytes = 4 << 30
@@ -129,13 +134,13 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
 
     is_copy = lambda k: "k_copy16" in k
     tiled = lambda k: (k.startswith("void (anonymous namespace)::step_kernel<"
-                                    f"{W}, true,") and "true>" not in k)
+                                    f"{W}, true,") and ("true>" in k) == pure)
     if per_step:
         tiled = lambda k: (k.startswith("void (anonymous namespace)::"
                                         f"group_step_kernel<{W}, true,")
                            and "true>" not in k)
     plain = lambda k: (k.startswith("void (anonymous namespace)::step_kernel<"
-                                    f"{W}, false,") and "true>" not in k)
+                                    f"{W}, false,") and ("true>" in k) == pure)
     cf, cw = pick(fetch, is_copy), pick(write, is_copy)
     if len(cf) != 1 or len(cw) != 1:
         raise SystemExit("record-traffic: expected one calibration copy per "
@@ -156,11 +161,12 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
     avg = lambda x: sum(x) / len(x)
     rd = avg(tf) * 1024 * rs
     wr = avg(tw) * 1024 * ws
-    alg = (2 * W + 26) * n
+    alg = (2 * W + (20 if pure else 26)) * n
     what = ("zs_buckets_step, groups of 16 tiled buckets, tiled state, flat "
             f"output; bytes per full step of {per_step} launches"
-            if per_step else "zs_step, tiled gradients, tiled state, flat "
-            "output")
+            if per_step else "zs_step_bf16, tiled gradients, tiled m|v state, "
+            "bf16 parameters in place in the flat buffer" if pure else
+            "zs_step, tiled gradients, tiled state, flat output")
     rec = {
         "kernel": f"{kname} ({what})",
         "workload": f"{workload} rank-0 shard, W={W}, {n:,} elements",
@@ -492,7 +498,8 @@ def bf16_main(args, w):
                    "allocation": "one arena: tiled gradients, state, flat"},
         "roofline": {"bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+                     "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic_record(f"{args.workload}_bf16")},
         "kernel_ms": {"avg": avg_ms},
     }
     print(json.dumps(out), flush=True)
@@ -1126,8 +1133,8 @@ def main():
             nb = zs.zs_layout_info(zs.zs_layout_build(w.numels, w.world,
                                                       w.rank))[2]
             per_step = -(-nb // min(args.group, zs.ZS_MAX_GROUP))
-        rec = record_traffic(*args.record_traffic, n, w.world, args.workload,
-                             per_step)
+        key = args.workload + ("_bf16" if args.pure_bf16 else "")
+        rec = record_traffic(*args.record_traffic, n, w.world, key, per_step)
         print(json.dumps({k: rec[k] for k in
                           ("bytes_per_launch", "ratio_to_algorithmic")}))
         return

@@ -80,3 +80,25 @@ def test_record_traffic_sums_group_launches_per_full_step(tmp_path):
         bench.record_traffic(str(tmp_path / "f.csv"),
                              str(tmp_path / "w.csv"), 100, W, "llama70b",
                              per_step=4, out_path=str(tmp_path / "u.json"))
+
+
+def test_record_traffic_pure_bf16_counts_only_the_pure_step(tmp_path):
+    """The <workload>_bf16 record takes the pure-bf16 step's dispatches
+    (kernel names ending in `true>`) and 2W + 20 algorithmic bytes."""
+    sys.path.insert(0, ROOT)
+    import bench
+    W, n = 8, 1000
+    mixed = "void (anonymous namespace)::step_kernel<8, true, Shape<64, 1, 8>, false>(StepArgs)"
+    pure = "void (anonymous namespace)::step_kernel<8, true, Shape<64, 1, 8>, true>(StepArgs)"
+    copy = "void k_copy16(...)"
+    kib = 4 << 20
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE",
+                 [(copy, kib), (mixed, 99.0), (pure, 3.0), (pure, 5.0)])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE",
+                 [(copy, kib), (mixed, 99.0), (pure, 2.0), (pure, 2.0)])
+    rec = bench.record_traffic(str(tmp_path / "f.csv"),
+                               str(tmp_path / "w.csv"), n, W, "llama8b_bf16",
+                               out_path=str(tmp_path / "t.json"))
+    assert rec["bytes_read_per_launch"] == 4.0 * 1024
+    assert rec["bytes_written_per_launch"] == 2.0 * 1024
+    assert rec["algorithmic_bytes_per_launch"] == (2 * W + 20) * n
