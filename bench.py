@@ -63,6 +63,15 @@ STEP_KERNELS = {
     "llama8b_bf16": ("_ZN12_GLOBAL__N_111step_kernelILi8ELb1ENS_5ShapeILi64ELi1E"
                      "Li8EEELb1EEEvNS_8StepArgsE",
                      "step_kernel<8, true, Shape<64, 1, 8>, true>"),
+    # the ZeRO-3 gather: traffic per forward (every unit's gather once)
+    "llama8b_zero3": ("_ZN12_GLOBAL__N_113gather_kernelENS_10GatherArgsE",
+                      "gather_kernel"),
+    # gradient accumulation over k = 2 micro-batches: traffic per cycle
+    # (the first-micro-batch launch and the last one); both kernels' digests
+    # are checked
+    "llama8b_accum": (("_ZN12_GLOBAL__N_112accum_kernelILi0EEEvNS_7AccArgsE",
+                       "_ZN12_GLOBAL__N_112accum_kernelILi2EEEvNS_7AccArgsE"),
+                      "accum_kernel<first> + accum_kernel<last>"),
     # the streaming step's bucket groups: traffic per full step (every
     # group launch of one pass over the buckets)
     "llama70b": ("_ZN12_GLOBAL__N_117group_step_kernelILi16ELb1ENS_5ShapeILi64"
@@ -91,8 +100,12 @@ def traffic_record(workload: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    now = kernel_digest(rec.get("kernel_symbol", ""))
-    if now is None or rec.get("kernel_sha256_16") != now:
+    syms = rec.get("kernel_symbol", "")
+    want = rec.get("kernel_sha256_16")
+    if isinstance(syms, str):
+        syms, want = [syms], [want]
+    now = [kernel_digest(x) for x in syms]
+    if None in now or now != want:
         return None
     return rec.get("bytes_per_launch")
 
@@ -125,6 +138,7 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
     dispatches, averaged)."""
     symbol, kname = STEP_KERNELS[workload]
     pure = workload.endswith("_bf16")
+    mode = workload.rsplit("_", 1)[1] if "_" in workload else ""
     fetch = read_counter_csv(fetch_csv, "FETCH_SIZE")
     write = read_counter_csv(write_csv, "WRITE_SIZE")
     copy_bytes = 4 << 30
@@ -135,7 +149,11 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
     is_copy = lambda k: "k_copy16" in k
     tiled = lambda k: (k.startswith("void (anonymous namespace)::step_kernel<"
                                     f"{W}, true,") and ("true>" in k) == pure)
-    if per_step:
+    if mode == "zero3":         # (the profiler names a plain function
+        tiled = lambda k: "(anonymous namespace)::gather_kernel(" in k
+    elif mode == "accum":       # without its return type)
+        tiled = lambda k: "(anonymous namespace)::accum_kernel<" in k
+    elif per_step:
         tiled = lambda k: (k.startswith("void (anonymous namespace)::"
                                         f"group_step_kernel<{W}, true,")
                            and "true>" not in k)
@@ -162,16 +180,27 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
     rd = avg(tf) * 1024 * rs
     wr = avg(tw) * 1024 * ws
     alg = (2 * W + (20 if pure else 26)) * n
-    what = ("zs_buckets_step, groups of 16 tiled buckets, tiled state, flat "
-            f"output; bytes per full step of {per_step} launches"
-            if per_step else "zs_step_bf16, tiled gradients, tiled m|v state, "
-            "bf16 parameters in place in the flat buffer" if pure else
-            "zs_step, tiled gradients, tiled state, flat output")
+    if mode == "zero3":         # n: elements gathered per forward
+        alg = 4 * n
+        what = f"zs_gather, bytes per forward of {per_step} unit gathers"
+    elif mode == "accum":       # n: elements of the flat gradient buffer
+        alg = (6 + 8) * n
+        what = ("zs_accumulate, k = 2: bytes per cycle (first micro-batch "
+                "and last)")
+    elif per_step:
+        what = ("zs_buckets_step, groups of 16 tiled buckets, tiled state, "
+                f"flat output; bytes per full step of {per_step} launches")
+    elif pure:
+        what = ("zs_step_bf16, tiled gradients, tiled m|v state, bf16 "
+                "parameters in place in the flat buffer")
+    else:
+        what = "zs_step, tiled gradients, tiled state, flat output"
     rec = {
         "kernel": f"{kname} ({what})",
-        "workload": f"{workload} rank-0 shard, W={W}, {n:,} elements",
+        "workload": f"{workload}, W={W}, {n:,} elements",
         "kernel_symbol": symbol,
-        "kernel_sha256_16": kernel_digest(symbol),
+        "kernel_sha256_16": (kernel_digest(symbol) if isinstance(symbol, str)
+                             else [kernel_digest(x) for x in symbol]),
         "copy_calibration": {"bytes_read": copy_bytes,
                              "bytes_written": copy_bytes,
                              "FETCH_SIZE_KiB": cf[0], "WRITE_SIZE_KiB": cw[0],
@@ -641,7 +670,8 @@ def accumulate_main(args, w):
                    "bytes_per_element_per_cycle": bpe},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                     "traffic": None},
+                     "traffic": (traffic_record(f"{args.workload}_accum")
+                                 if K == 2 else None)},
         "kernel_ms": {"avg": avg_ms},
     }
     print(json.dumps(out), flush=True)
@@ -789,7 +819,8 @@ def zero3_main(args, w):
                    "bytes_per_param": 4, "tokens": args.tokens},
         "roofline": {"bound": "hbm", "achieved": g_gbs,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": g_gbs / PEAK_HBM_GBS, "traffic": None},
+                     "frac": g_gbs / PEAK_HBM_GBS,
+                     "traffic": traffic_record(f"{args.workload}_zero3")},
         "zero3": {"gathers_alone_ms": g_ms, "compute_alone_ms": c_ms,
                   "pipelined_ms": p_ms, "exposed_gather_ms": p_ms - c_ms,
                   "elements_per_forward": elems},
@@ -1134,6 +1165,18 @@ def main():
                                                       w.rank))[2]
             per_step = -(-nb // min(args.group, zs.ZS_MAX_GROUP))
         key = args.workload + ("_bf16" if args.pure_bf16 else "")
+        if args.zero3:                      # as zero3_main gathers them
+            key = args.workload + "_zero3"
+            lay = zs.zs_layout_build(w.numels, w.world, 0)
+            offs = zs.zs_layout_tensor_offsets(lay, len(w.numels))
+            units = fsdp_units(w.numels)
+            n = sum(offs[b] + w.numels[b] - offs[a] for a, b in units)
+            per_step = len(units)
+        elif args.accumulate:
+            key = args.workload + "_accum"
+            n = zs.zs_layout_info(zs.zs_layout_build(w.numels, w.world,
+                                                     w.rank))[0]
+            per_step = 2
         rec = record_traffic(*args.record_traffic, n, w.world, key, per_step)
         print(json.dumps({k: rec[k] for k in
                           ("bytes_per_launch", "ratio_to_algorithmic")}))

@@ -102,3 +102,42 @@ def test_record_traffic_pure_bf16_counts_only_the_pure_step(tmp_path):
     assert rec["bytes_read_per_launch"] == 4.0 * 1024
     assert rec["bytes_written_per_launch"] == 2.0 * 1024
     assert rec["algorithmic_bytes_per_launch"] == (2 * W + 20) * n
+
+
+def test_record_traffic_accumulation_per_cycle(tmp_path):
+    """The <workload>_accum record sums each cycle's two accumulation
+    dispatches (first and last micro-batch) against 14 B per element, and
+    keeps one digest per kernel; the gather record matches the plain
+    function name the profiler gives it."""
+    sys.path.insert(0, ROOT)
+    import bench
+    first = "void (anonymous namespace)::accum_kernel<0>(AccArgs)"
+    last = "void (anonymous namespace)::accum_kernel<2>(AccArgs)"
+    copy = "void k_copy16(...)"
+    kib = 4 << 20
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE",
+                 [(copy, kib), (first, 2.0), (last, 6.0), (first, 2.0),
+                  (last, 6.0)])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE",
+                 [(copy, kib), (first, 4.0), (last, 2.0), (first, 4.0),
+                  (last, 2.0)])
+    rec = bench.record_traffic(str(tmp_path / "f.csv"),
+                               str(tmp_path / "w.csv"), 1024, 8,
+                               "llama8b_accum", per_step=2,
+                               out_path=str(tmp_path / "t.json"))
+    assert rec["bytes_read_per_launch"] == 8.0 * 1024
+    assert rec["bytes_written_per_launch"] == 6.0 * 1024
+    assert rec["algorithmic_bytes_per_launch"] == 14 * 1024
+    assert isinstance(rec["kernel_symbol"], tuple) or \
+        isinstance(rec["kernel_symbol"], list)
+    gather = "(anonymous namespace)::gather_kernel((anonymous namespace)::GatherArgs)"
+    _counter_csv(tmp_path / "gf.csv", "FETCH_SIZE",
+                 [(copy, kib), (gather, 1.0), (gather, 3.0)])
+    _counter_csv(tmp_path / "gw.csv", "WRITE_SIZE",
+                 [(copy, kib), (gather, 1.0), (gather, 3.0)])
+    rec = bench.record_traffic(str(tmp_path / "gf.csv"),
+                               str(tmp_path / "gw.csv"), 1024, 8,
+                               "llama8b_zero3", per_step=2,
+                               out_path=str(tmp_path / "g.json"))
+    assert rec["bytes_read_per_launch"] == 4.0 * 1024
+    assert rec["algorithmic_bytes_per_launch"] == 4 * 1024
