@@ -63,6 +63,10 @@ STEP_KERNELS = {
     "llama8b_bf16": ("_ZN12_GLOBAL__N_111step_kernelILi8ELb1ENS_5ShapeILi64ELi1E"
                      "Li8EEELb1EEEvNS_8StepArgsE",
                      "step_kernel<8, true, Shape<64, 1, 8>, true>"),
+    # the whole-tensor step: one group launch over the owned tensors
+    "llama8b_tensors": ("_ZN12_GLOBAL__N_117group_step_kernelILi8ELb1ENS_5Shape"
+                        "ILi64ELi1ELi4EEELb0EEEvNS_9GroupArgsE",
+                        "group_step_kernel<8, true, Shape<64, 1, 4> >"),
     # the ZeRO-3 gather: traffic per forward (every unit's gather once)
     "llama8b_zero3": ("_ZN12_GLOBAL__N_113gather_kernelENS_10GatherArgsE",
                       "gather_kernel"),
@@ -153,7 +157,7 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
         tiled = lambda k: "(anonymous namespace)::gather_kernel(" in k
     elif mode == "accum":       # without its return type)
         tiled = lambda k: "(anonymous namespace)::accum_kernel<" in k
-    elif per_step:
+    elif per_step or mode == "tensors":
         tiled = lambda k: (k.startswith("void (anonymous namespace)::"
                                         f"group_step_kernel<{W}, true,")
                            and "true>" not in k)
@@ -187,6 +191,9 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
         alg = (6 + 8) * n
         what = ("zs_accumulate, k = 2: bytes per cycle (first micro-batch "
                 "and last)")
+    elif mode == "tensors":
+        what = ("zs_step on the whole-tensor layout: one group launch over "
+                "the owned tensors, tiled gradients and state, flat output")
     elif per_step:
         what = ("zs_buckets_step, groups of 16 tiled buckets, tiled state, "
                 f"flat output; bytes per full step of {per_step} launches")
@@ -1165,6 +1172,10 @@ def main():
                                                       w.rank))[2]
             per_step = -(-nb // min(args.group, zs.ZS_MAX_GROUP))
         key = args.workload + ("_bf16" if args.pure_bf16 else "")
+        if args.whole_tensors:
+            key = args.workload + "_tensors"
+            n = zs.zs_layout_info(zs.zs_layout_build_tensors(
+                w.numels, w.world, w.rank))[1]
         if args.zero3:                      # as zero3_main gathers them
             key = args.workload + "_zero3"
             lay = zs.zs_layout_build(w.numels, w.world, 0)
@@ -1368,7 +1379,8 @@ def main():
             f"{c['copy']['GBps']:.0f} GB/s; the step runs at "
             f"{c['step_frac_of_same_mix']:.1%} of the same-mix ceiling")
 
-    traffic = None if args.whole_tensors else traffic_record(args.workload)
+    traffic = traffic_record(args.workload + ("_tensors" if args.whole_tensors
+                                              else ""))
     config = {"workload": f"{w.name} rank-0 shard, W={W}",
               "params_total": sum(w.numels), "shard_params": n,
               "buckets": nb, "bucket_cap_mb": 25,
