@@ -56,6 +56,8 @@ HEADLINE_KERNEL = ("_ZN12_GLOBAL__N_111step_kernelILi8ELb1ENS_5ShapeILi64ELi1E"
                    "Li8EEELb0EEEvNS_8StepArgsE")
 STEP_KERNELS = {
     "llama8b": (HEADLINE_KERNEL, "step_kernel<8, true, Shape<64, 1, 8> >"),
+    # the GPT-2-sized shard: the same kernel in a launch of 1899 tiles
+    "gpt2": (HEADLINE_KERNEL, "step_kernel<8, true, Shape<64, 1, 8> >"),
     "dense7b": ("_ZN12_GLOBAL__N_111step_kernelILi64ELb1ENS_5ShapeILi64ELi1E"
                 "Li64EEELb0EEEvNS_8StepArgsE",
                 "step_kernel<64, true, Shape<64, 1, 64> >"),
