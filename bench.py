@@ -1158,8 +1158,9 @@ def main():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV",
                                                           "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 --pmc counter CSVs of "
-                    "a --copy-calibration run of --workload into profiles/"
-                    "traffic_<workload>.json")
+                    "a --copy-calibration run of --workload (and of "
+                    "--pure-bf16, --whole-tensors, --zero3 or --accumulate 2 "
+                    "for those modes) into profiles/traffic_<key>.json")
     args = ap.parse_args()
 
     if args.record_traffic:
