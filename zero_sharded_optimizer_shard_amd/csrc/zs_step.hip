@@ -968,8 +968,9 @@ void launch_shape(const Args& a, bool tiled, dim3 grid, hipStream_t s)
 //    process, Wave 84.1 % against One at 12-24 per CU 83.3-84.0 %);
 //  - Deep (512-thread workgroups of four units, slices 8 at a time, one
 //    per CU by its 148 VGPRs), uncapped: plain slice rows at compiled
-//    W >= 32 (7B-shaped W = 64: 73-77 %, One 66 %) and large group launches
-//    there;
+//    W >= 32 (7B-shaped W = 64: 73-77 %, One 66 %), also in large group
+//    launches (on tiled gradients those take One: the 7B-shaped whole-tensor
+//    step at W = 64 83.3-83.5 % at 4-5 per CU against Deep's 80.3 %);
 //  - Wide / PureWide (runtime W >= 32 for plain slices and bucket groups): 512-thread workgroups of four units (256 for the
 //    two-row pure state): 79-80 % at W = 100, against 75-78 % with uncapped
 //    one-wave workgroups;
@@ -1083,11 +1084,17 @@ void launch_step_w(const Args& a, bool tiled, dim3 grid, hipStream_t s)
         launch_shape<WT, ShapeSmall, PURE, 0>(a, tiled, grid, s);
     } else if constexpr (WT > 0 && kGroup) {
         // large group launches (the whole-tensor step's owned tensors):
-        // the member lookup of every workgroup wants more of them per CU
-        if constexpr (WT < 32)
+        // below W = 32 the member lookup of every workgroup wants more of
+        // them per CU; at W >= 32 the One shape on tiled gradients
+        if constexpr (WT < 32) {
             launch_shape<WT, ShapeWave, PURE, kWaveWgs>(a, tiled, grid, s);
-        else
-            launch_shape<WT, ShapeDeep, PURE, 0>(a, tiled, grid, s);
+        } else {
+            if (tiled)
+                launch_kernel<WT, true, ShapeOne<WT>, PURE,
+                              one_wgs<WT, PURE>()>(a, grid, s);
+            else
+                launch_kernel<WT, false, ShapeDeep, PURE, 0>(a, grid, s);
+        }
     } else if constexpr (WT > 0) {
         constexpr int kWgs = kPlain ? plain_wgs<WT>() : one_wgs<WT, PURE>();
         if (tiled || WT < 32)
