@@ -249,6 +249,18 @@ int zs_step(const zs_layout* layout, const uint16_t* grads,
             uint16_t* param_shard, uint16_t* full_flat, const zs_adamw* hp,
             int64_t step, void* hip_stream);
 
+/* Turn the step launches' LDS reservation (the residency cap described at
+ * zs_step) on (on != 0, the default) or off for the whole process; returns
+ * the previous setting (1 or 0).  Off, the step's workgroups reserve no
+ * LDS and fill the CUs as far as their registers allow.  Measured on
+ * MI355X the cap pays alone (the 8B-shaped W = 8 step 6.2 against 6.5 ms)
+ * and beside bf16 GEMMs on another stream (10 steps and 55 8192^3 GEMMs
+ * together 104.0 against 106.4-107.0 ms); the switch is for callers who
+ * measure their own mix of concurrent kernels.  Applies to every step
+ * entry point, for launches issued after the call; results are the same
+ * bits either way.  No device call, no error. */
+int32_t zs_set_residency_cap(int32_t on);
+
 /* zs_step on three plain fp32 arrays instead of the tiled state: master, m
  * and v are [shard_numel] each, element i the shard's element i (padding
  * included), updated in place; everything else as zs_step, with the same

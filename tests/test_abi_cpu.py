@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 40
+    assert len(names) == 41
     L = zs.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -565,3 +565,15 @@ def test_bindings_refuse_buffers_shorter_than_the_layout():
     check(lambda acc, out: zs.zs_accumulate(zs.ZS_ACC_LAST, acc, bf(4096),
                                             out, k=2),
           dict(acc=(f32, 4096), out=(bf, 4096)))
+
+
+def test_residency_cap_switch_returns_the_previous_setting():
+    """zs_set_residency_cap needs no device: it flips a process-wide
+    setting (on by default) and returns the one before."""
+    assert zs.zs_set_residency_cap(False) is True
+    try:
+        assert zs.zs_set_residency_cap(False) is False
+        assert zs.zs_set_residency_cap(True) is False
+        assert zs.zs_set_residency_cap(True) is True
+    finally:
+        zs.zs_set_residency_cap(True)

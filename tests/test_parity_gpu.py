@@ -396,6 +396,23 @@ def test_launch_shapes(W, tiles, layout):
         c.step(t)
 
 
+def test_step_without_residency_cap():
+    """zs_set_residency_cap(False): the same launches without the LDS
+    reservation (only the dispatch differs), bit for bit against the oracle
+    in a capped large launch, a capped small one and a runtime-W one."""
+    prev = zs.zs_set_residency_cap(False)
+    try:
+        for W, tiles in ((8, 4100), (16, 300), (12, 4100)):
+            n_rank = tiles * TILE - 4096
+            say(f"case no residency cap W={W} tiles={tiles}")
+            c = Case([W * n_rank], W, W - 1, cap=0, layout="tiled")
+            for t in (1, 2):
+                c.step(t)
+    finally:
+        zs.zs_set_residency_cap(prev)
+    assert zs.zs_set_residency_cap(True) is True
+
+
 @pytest.mark.parametrize("W,tiles,layout", [
     (3, 10, "tiled"), (8, 10, "slices"), (8, 4100, "tiled"),
     (5, 4100, "tiled"), (32, 4100, "tiled"), (64, 300, "tiled"),

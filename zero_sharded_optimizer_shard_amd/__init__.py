@@ -17,12 +17,12 @@ from ._zs import (EXPORTS, LIB_PATH, ZS_ACC_ADD, ZS_ACC_FIRST, ZS_ACC_LAST,
                   zs_layout_build, zs_layout_build_tensors, zs_layout_chunks,
                   zs_layout_info, zs_layout_owners, zs_layout_rank,
                   zs_layout_tensor_offsets, zs_layout_tiles, zs_pack,
-                  zs_pack_noalloc, zs_prefetch_acquire, zs_prefetch_create, zs_prefetch_free,
-                  zs_prefetch_issue, zs_prefetch_release, zs_state_mv_pack,
+                  zs_pack_noalloc, zs_prefetch_acquire, zs_prefetch_create,
+                  zs_prefetch_free, zs_prefetch_issue, zs_prefetch_release, zs_state_mv_pack,
                   zs_state_mv_unpack, zs_state_pack, zs_state_unpack, zs_step,
                   zs_step_bf16, zs_step_plain, zs_stream_arrive, zs_stream_create,
-                  zs_stream_free, zs_stream_step_begin, zs_stream_step_end,
-                  zs_strerror)
+                  zs_set_residency_cap, zs_stream_free, zs_stream_step_begin,
+                  zs_stream_step_end, zs_strerror)
 
 __all__ = ["EXPORTS", "LIB_PATH", "ZS_ACC_ADD", "ZS_ACC_FIRST", "ZS_ACC_LAST",
            "ZS_EIO", "ZS_EMISMATCH", "zs_checkpoint_load",
@@ -37,9 +37,9 @@ __all__ = ["EXPORTS", "LIB_PATH", "ZS_ACC_ADD", "ZS_ACC_FIRST", "ZS_ACC_LAST",
            "zs_layout_build", "zs_layout_build_tensors", "zs_layout_chunks",
            "zs_layout_info", "zs_layout_owners", "zs_layout_rank",
            "zs_layout_tensor_offsets", "zs_layout_tiles", "zs_pack",
-           "zs_pack_noalloc", "zs_prefetch_acquire", "zs_prefetch_create", "zs_prefetch_free",
-           "zs_prefetch_issue", "zs_prefetch_release", "zs_state_mv_pack",
+           "zs_pack_noalloc", "zs_prefetch_acquire", "zs_prefetch_create",
+           "zs_prefetch_free", "zs_prefetch_issue", "zs_prefetch_release", "zs_state_mv_pack",
            "zs_state_mv_unpack", "zs_state_pack", "zs_state_unpack",
            "zs_step", "zs_step_bf16", "zs_step_plain", "zs_stream_arrive", "zs_stream_create",
-           "zs_stream_free", "zs_stream_step_begin", "zs_stream_step_end",
-           "zs_strerror"]
+           "zs_set_residency_cap", "zs_stream_free", "zs_stream_step_begin",
+           "zs_stream_step_end", "zs_strerror"]

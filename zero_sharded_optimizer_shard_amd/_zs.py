@@ -67,7 +67,7 @@ EXPORTS = ["zs_layout_build", "zs_layout_build_tensors", "zs_layout_owners",
            "zs_prefetch_release", "zs_prefetch_free",
            "zs_layout_fingerprint", "zs_checkpoint_save",
            "zs_checkpoint_load",
-           "zs_strerror", "zs_last_error"]
+           "zs_set_residency_cap", "zs_strerror", "zs_last_error"]
 
 
 def lib():
@@ -133,6 +133,8 @@ def lib():
     L.zs_strerror.restype = ctypes.c_char_p
     L.zs_last_error.argtypes = []
     L.zs_last_error.restype = ctypes.c_char_p
+    L.zs_set_residency_cap.argtypes = [ctypes.c_int32]
+    L.zs_set_residency_cap.restype = ctypes.c_int32
     for name in ("zs_layout_build", "zs_layout_build_tensors",
                  "zs_layout_owners", "zs_layout_info", "zs_layout_tiles",
                  "zs_layout_buckets", "zs_layout_chunks",
@@ -572,6 +574,12 @@ def zs_pack(layout: Layout, param_shard, full_flat=None, dev_chunks=None,
                          _bf16(full_flat, "full_flat"), _ptr(dev_chunks),
                          n_chunks, _ptr(dev_tensor_ptrs), _stream(stream)),
            "zs_pack")
+
+
+def zs_set_residency_cap(on: bool) -> bool:
+    """Switch the step launches' LDS reservation on or off for the process;
+    returns the previous setting."""
+    return bool(lib().zs_set_residency_cap(1 if on else 0))
 
 
 def zs_pack_noalloc(layout: Layout, param_shard, full_flat=None,

@@ -854,12 +854,13 @@ Geom bucket_geom(const zs_layout* L, const zs_bucket& b)
 // launches uncapped.
 constexpr int kCapDevices = 64;
 std::atomic<int> g_lds_per_cu[kCapDevices];     // bytes; 0 = not known yet
+std::atomic<int> g_cap_on{1};                   // zs_set_residency_cap
 
 // LDS bytes to reserve per workgroup so that at most `wgs` share a CU, or 0
 // (no cap) for wgs == 0 or when the device's LDS size cannot be had.
 unsigned residency_cap_lds(int wgs)
 {
-    if (wgs <= 0)
+    if (wgs <= 0 || !g_cap_on.load(std::memory_order_relaxed))
         return 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kCapDevices)
@@ -1704,6 +1705,11 @@ int scratch_on(int dev, unsigned char** out)
 }
 
 }  // namespace
+
+extern "C" int32_t zs_set_residency_cap(int32_t on)
+{
+    return g_cap_on.exchange(on ? 1 : 0);
+}
 
 extern "C" int zs_pack_noalloc(const zs_layout* L,
                                const uint16_t* param_shard,
