@@ -229,11 +229,12 @@ def one_bucket(W, tiles):
 #   runtime W, 4100 tiles: one-wave workgroups with batches of 8 (5), 16
 #   (12), 32 (20, 33) and 64 (100) on tiled gradients (and at W = 5 on
 #   plain slices); Wave (12, 20) and Wide (33, 100) on plain slices;
-#   (12, 300): one-wave batches of 16 below 4096 tiles on tiled gradients,
-#   Small on plain slices
+#   (128, 4100): two full batches of 64; (12, 300) and (65, 300): one-wave
+#   batches of 16 and of 64 + 1 below 4096 tiles on tiled gradients, Small
+#   on plain slices
 SHAPES = [(2, 300), (5, 1100), (1, 4100), (8, 4100), (16, 4100), (5, 4100),
           (12, 4100), (20, 4100), (32, 4100), (64, 4100), (33, 4100),
-          (100, 4100), (64, 300), (12, 300)]
+          (100, 4100), (128, 4100), (64, 300), (12, 300), (65, 300)]
 
 
 @pytest.mark.parametrize("state_form", ["tiled", "plain"])
