@@ -608,6 +608,7 @@ def test_bucket_steps_in_any_order_match_the_oracle(layout):
 @pytest.mark.parametrize("W,cap,groups", [
     (8, 25 << 20, [3, 1, 4, 2]),                 # GPT-2-shaped, 10 buckets
     (4, 4 * 256 * 8, [16, 16, 7, 1, 5]),         # 45 small buckets
+    (12, 12 * 256 * 8, [6, 1, 5, 3]),            # runtime W, 15 buckets
 ])
 def test_bucket_groups_match_the_oracle(W, cap, groups, layout):
     """zs_buckets_step over groups of buckets in a shuffled order, each
@@ -1325,13 +1326,14 @@ def test_stream_engine_matches_the_oracle(arrival, tensors, n_up):
 
 @pytest.mark.parametrize("seed", range(12))
 def test_stream_engine_random_configs(seed):
-    """The streaming engine under seeded random configurations: group 1..16,
+    """The streaming engine under seeded random configurations: W from 2 to
+    64 (compiled and runtime), group 1..16,
     a ring from the minimum (n_slots = group) to group + 5 slots, 1..3 step
     streams, 1..4 upload streams, random layouts, ranks and arrival orders,
     three steps (slots and launch events reused across steps); state and
     flat output equal the oracle's after every step, bit for bit."""
     rng = random.Random(900 + seed)
-    W = rng.choice([2, 3, 4, 8])
+    W = rng.choice([2, 3, 4, 8, 12, 16, 64])
     numels = [rng.choice([7, 129, 1000, 4096, 9000, 33333, 70000])
               for _ in range(rng.randint(3, 12))]
     cap = W * 256 * rng.choice([1, 2, 5, 13])
