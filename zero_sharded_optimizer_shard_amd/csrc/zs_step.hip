@@ -155,7 +155,6 @@ struct Seg {
 
 struct GeomLoc {
     Geom g;
-    __device__ bool operator()(TileRef& r) const { return tile_of(g, r); }
     // P workgroups per tile (blockIdx.x = tile * P + part)
     template <int P>
     __device__ bool at(TileRef& r) const { return tile_of<P>(g, r); }
@@ -183,7 +182,6 @@ struct SegLoc {
     Seg s[kMaxMembers];
     int64_t start[kMaxMembers + 1];
     int count;
-    __device__ bool operator()(TileRef& r) const { return at<1>(r); }
     template <int P>
     __device__ bool at(TileRef& r) const
     {
