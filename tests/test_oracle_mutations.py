@@ -2,10 +2,14 @@
 
 Each case plants one mistake in a copy of oracle/zs_oracle.c (on the CPU,
 in a temporary directory), builds it with the oracle's own flags, and runs
-the step and accumulation pins (tests/test_oracle_step.py and
-tests/test_oracle_accumulate.py) against that build through ZS_ORACLE_LIB;
-at least one pin must fail with an assertion.  The unmodified source, built
-the same way, must pass them all, so a failure is the mutation's doing."""
+the step and accumulation pins (tests/test_oracle_step.py,
+tests/test_oracle_accumulate.py and the exact-rational emulation in
+tests/test_oracle_ieee_emulation.py) against that build through
+ZS_ORACLE_LIB; at least one pin must fail with an assertion.  The
+unmodified source, built the same way, must pass them all, so a failure is
+the mutation's doing.  Two more cases build the unmodified source with
+flags that change its arithmetic: contracted multiply-adds, and fast math
+(reassociation, reciprocals, flushed denormals)."""
 
 import os
 import subprocess
@@ -17,7 +21,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "zs_oracle.c")
 PINS = [os.path.join(ROOT, "tests", "test_oracle_step.py"),
-        os.path.join(ROOT, "tests", "test_oracle_accumulate.py")]
+        os.path.join(ROOT, "tests", "test_oracle_accumulate.py"),
+        os.path.join(ROOT, "tests", "test_oracle_ieee_emulation.py")]
 FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
          "-shared", "-w"]
 
@@ -70,12 +75,31 @@ MUTATIONS = [
 ]
 
 
-def build(src_text, d, name):
+
+def _host_has_fma():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return any(l.startswith("flags") and " fma " in l + " "
+                       for l in f)
+    except OSError:
+        return False
+
+
+# (name, flags appended after the oracle's own, which they override)
+FLAG_MUTATIONS = [
+    ("multiply-adds contracted", ["-ffp-contract=fast", "-mfma"]),
+    ("fast math", ["-ffast-math"]),
+]
+if not _host_has_fma():
+    FLAG_MUTATIONS = FLAG_MUTATIONS[1:]
+
+
+def build(src_text, d, name, extra=()):
     c = os.path.join(d, f"{name}.c")
     so = os.path.join(d, f"{name}.so")
     with open(c, "w") as f:
         f.write(src_text)
-    subprocess.run(["gcc", *FLAGS, c, "-o", so, "-lm"], check=True,
+    subprocess.run(["gcc", *FLAGS, *extra, c, "-o", so, "-lm"], check=True,
                    capture_output=True, text=True)
     return so
 
@@ -104,6 +128,8 @@ def results(tmp_path_factory):
     libs = {"control": build(src, d, "control")}
     for i, (name, old, new, which) in enumerate(MUTATIONS):
         libs[name] = build(plant(src, old, new, which), d, f"m{i}")
+    for i, (name, extra) in enumerate(FLAG_MUTATIONS):
+        libs[name] = build(src, d, f"f{i}", extra)
     workers = max(1, min(8, os.cpu_count() or 1))
     with ThreadPoolExecutor(workers) as ex:
         done = dict(zip(libs, ex.map(run_pins, libs.values())))
@@ -115,7 +141,8 @@ def test_unmodified_oracle_passes_the_pins(results):
     assert p.returncode == 0, p.stdout[-3000:]
 
 
-@pytest.mark.parametrize("name", [m[0] for m in MUTATIONS])
+@pytest.mark.parametrize("name", [m[0] for m in MUTATIONS] +
+                         [m[0] for m in FLAG_MUTATIONS])
 def test_pins_catch_the_mutation(results, name):
     p = results[name]
     # 1: a test failed (an assertion, not a crash or a collection error)
