@@ -218,3 +218,53 @@ def test_pin_catches_a_plausible_mistake(mistake):
         assert got == right, i
         differs += wrong != got
     assert differs > 0, mistake
+
+
+def bf16_value(bits) -> Fraction:
+    return Fraction(float(O.bf16_to_f32(np.uint16(bits))))
+
+
+@pytest.mark.parametrize("W", [1, 3, 8])
+def test_pure_bf16_step_equals_exact_per_operation_rounding(W):
+    """The step without an fp32 master: the same statements on the bf16
+    parameter widened to fp32, the result rounded back to bf16 nearest-even
+    in place (the pure-bf16 reading of the DDP-to-ZeRO blog's mixed
+    precision, section 3.3)."""
+    n = 300
+    hp = O.AdamW(lr=1e-2, weight_decay=0.1)
+    p = O.bf16_round(synth.cpu_normal_f32(n, 11, synth.TAG_MASTER, 0, 0, 0,
+                                          0.02))
+    m = synth.cpu_normal_f32(n, 12, synth.TAG_MASTER, 0, 0, 0, 1e-3)
+    v = synth.cpu_normal_f32(n, 13, synth.TAG_MASTER, 0, 0, 0, 1e-6,
+                             absval=True)
+    em = [(bf16_value(a), Fraction(float(b)), Fraction(float(c)))
+          for a, b, c in zip(p, m, v)]
+    for t in (1, 2, 5):
+        G = np.stack([synth.cpu_normal_bf16(n, 14, synth.TAG_GRAD, t, s, 0,
+                                            1e-3 * 16.0 ** s)
+                      for s in range(W)])
+        O.step_bf16(G, p, m, v, hp, t)
+        for i in range(n):
+            _, mi, vi, pb = emulate(G[:, i], *em[i], hp, t)
+            em[i] = (bf16_value(pb), mi, vi)
+            where = f"W={W} t={t} i={i}"
+            assert int(p[i]) == pb, where
+            assert Fraction(float(m[i])) == mi, where
+            assert Fraction(float(v[i])) == vi, where
+
+
+@pytest.mark.parametrize("k", [2, 3, 6])
+def test_accumulation_equals_exact_per_operation_rounding(k):
+    """Gradient accumulation: the fp32 sum of the k micro-batch gradients
+    in micro-batch order, one rounding per addition, divided by k with one
+    rounding, then bf16 nearest-even (podcast summary of "Training at
+    thousands of GPUs", glossary; DDP-to-ZeRO blog, section 3.3)."""
+    n = 2000
+    G = np.stack([synth.cpu_normal_bf16(n, 15, synth.TAG_GRAD, j, 0, 0,
+                                        1e-4 * 16.0 ** j) for j in range(k)])
+    out = O.accumulate(G)
+    for i in range(n):
+        acc = bf16_value(G[0, i])
+        for j in range(1, k):
+            acc = r32(acc + bf16_value(G[j, i]))
+        assert int(out[i]) == bf16_bits(r32(acc / k)), (k, i)
