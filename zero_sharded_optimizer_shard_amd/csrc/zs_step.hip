@@ -640,17 +640,21 @@ __global__ __launch_bounds__(kGtThreads) void grads_tile_kernel(
 
 // ---- pack: shard -> flat all-gather buffer ---------------------------------
 
-// Four 256-thread workgroups per tile, one 16-byte copy per thread (the
-// gradient tiling conversion's shape): 0.636-0.638 ms, 6.30-6.32 TB/s on
-// the 8B-shaped shard, against 0.652-0.665 ms for eight one-wave
-// workgroups of two copies per thread, 0.656-0.668 ms for eight 128-thread
-// workgroups of one, 0.660-0.673 ms for two 256-thread workgroups of two,
-// and 5.89-5.93 TB/s for one 512-thread workgroup of 8-byte copies.
+// Sixteen one-wave workgroups per tile, one 16-byte copy per thread: on the
+// 8B-shaped shard 0.602-0.603 ms, 6.65-6.67 TB/s (83.2-83.4 % of peak),
+// against 0.637-0.642 ms (78.2-78.8 %) for four 256-thread workgroups of
+// one copy and 0.671 ms for eight 128-thread ones, interleaved in one
+// process.  Reserving LDS to hold fewer of them per CU only slowed it
+// (28 per CU 78.8 %, 16 per CU 69.5 %): a copy needs every load in flight
+// the device takes.  Earlier trials of the same stream: eight one-wave
+// workgroups of two copies per thread 0.652-0.665 ms, two 256-thread
+// workgroups of two 0.660-0.673 ms, one 512-thread workgroup of 8-byte
+// copies 5.89-5.93 TB/s.
 // Slices and padded tensors are multiples of 8 elements, so a 16-byte group
 // is either wholly inside the tile's valid part or wholly outside.
-constexpr int kPackNT = 256;
+constexpr int kPackNT = 64;
 constexpr int kPackV = 1;                         // 16-byte copies per thread
-constexpr int kPackP = (int)(kTile / (kPackNT * kPackV * 8));   // 4 per tile
+constexpr int kPackP = (int)(kTile / (kPackNT * kPackV * 8));  // 16 per tile
 static_assert(kMaxLaunchTiles * kPackP * kPackNT < (int64_t(1) << 32),
               "one launch row of tiles fits the grid");
 
