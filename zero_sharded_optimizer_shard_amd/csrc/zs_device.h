@@ -21,9 +21,12 @@ constexpr int kCpolSc0 = 1, kCpolNt = 2, kCpolSc1 = 16;
 // eviction.  Measured on MI355X, it pays in a stream that reads twice what
 // it writes: the 8B-shaped W = 8 optimizer step at 82.0-82.2 % of peak HBM
 // bandwidth against 80.4 % with plain non-temporal stores, with the same
-// HBM bytes.  Plain copies (1 : 1) lose by it (the ZeRO-3 gather 75 % vs
-// 77-78 %, the flat pack 5.7 vs 5.9-6.0 TB/s, gradient accumulation 81-82 %
-// vs 82 %), so they keep plain non-temporal stores.
+// HBM bytes.  For 1 : 1 copies it depends on the form: the one-wave packs
+// gain (flat pack 84.7-85.0 % against 83.2-83.4 %, per-tensor pack 84.5 %
+// against 83.1 %); the one-wave ZeRO-3 gather (81.8-81.9 %) and gradient
+// accumulation (84.1-84.2 % per cycle) measured level, and lost in their
+// earlier 256- and 512-thread forms, so those two keep plain non-temporal
+// stores.
 constexpr int kStreamOut = kCpolSc0 | kCpolSc1 | kCpolNt;
 
 // Store x (4, 8 or 16 bytes) at byte offset `off` of the output region

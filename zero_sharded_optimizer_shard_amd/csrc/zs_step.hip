@@ -640,11 +640,12 @@ __global__ __launch_bounds__(kGtThreads) void grads_tile_kernel(
 
 // ---- pack: shard -> flat all-gather buffer ---------------------------------
 
-// Sixteen one-wave workgroups per tile, one 16-byte copy per thread: on the
-// 8B-shaped shard 0.602-0.603 ms, 6.65-6.67 TB/s (83.2-83.4 % of peak),
-// against 0.637-0.642 ms (78.2-78.8 %) for four 256-thread workgroups of
-// one copy and 0.671 ms for eight 128-thread ones, interleaved in one
-// process.  Reserving LDS to hold fewer of them per CU only slowed it
+// Sixteen one-wave workgroups per tile, one 16-byte copy per thread, the
+// stores streamed on to HBM with system scope (zsdev::stream_store): on the
+// 8B-shaped shard 0.590-0.593 ms (84.7-85.0 % of peak) against 0.602-0.603
+// ms (83.2-83.4 %) with plain non-temporal stores, 0.637-0.642 ms
+// (78.2-78.8 %) for four 256-thread workgroups of one copy and 0.671 ms for
+// eight 128-thread ones, interleaved in one process.  Reserving LDS to hold fewer of them per CU only slowed it
 // (28 per CU 78.8 %, 16 per CU 69.5 %): a copy needs every load in flight
 // the device takes.  Earlier trials of the same stream: eight one-wave
 // workgroups of two copies per thread 0.652-0.665 ms, two 256-thread
@@ -672,20 +673,23 @@ __global__ __launch_bounds__(kPackNT) void pack_flat_kernel(
         const int jj = part * (int)(kTile / kPackP) +
                        8 * (v * kPackNT + (int)threadIdx.x);
         if (jj < r.nvalid)
-            __builtin_nontemporal_store(
+            zsdev::stream_store(
+                flat + r.fpos, (uint32_t)(r.nvalid * sizeof(uint16_t)),
+                (uint32_t)jj * (uint32_t)sizeof(uint16_t),
                 __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(shard + r.e0 + jj)),
-                reinterpret_cast<u32x4*>(flat + r.fpos + jj));
+                    reinterpret_cast<const u32x4*>(shard + r.e0 + jj)));
     }
 }
 
 // ---- pack: shard -> per-tensor storage through the chunk table -------------
 //
 // One-wave workgroups, up to kPackGridX of them per chunk striding over it,
-// 8 elements per thread and step.  Measured on MI355X (the 8B-shaped W = 8
-// shard's 650 chunks): 0.60 ms, 6.67 TB/s, against 0.65 ms with 256-thread
-// workgroups and at most 256 per chunk (64 threads and 256 per chunk:
-// 0.67-0.74 ms; 256 threads and 4096: 0.64 ms).
+// 8 elements per thread and step, the 16-byte stores streamed on to HBM
+// with system scope.  Measured on MI355X (the 8B-shaped W = 8 shard's 650
+// chunks): 0.593-0.594 ms (84.5-84.6 % of peak) against 0.604 ms (83.1 %)
+// with plain non-temporal stores, interleaved in one process; 0.65 ms with
+// 256-thread workgroups and at most 256 per chunk (64 threads and 256 per
+// chunk: 0.67-0.74 ms; 256 threads and 4096: 0.64 ms).
 
 constexpr int kPackThreads = 64;
 constexpr int64_t kPackGridX = 4096;
@@ -705,14 +709,22 @@ __global__ __launch_bounds__(kPackThreads) void pack_chunks_kernel(
     const int64_t step = (int64_t)gridDim.x * kPackTile;
     const bool vec = ((reinterpret_cast<uintptr_t>(dst) |
                        reinterpret_cast<uintptr_t>(src)) & 15u) == 0;
-    for (int64_t j = ((int64_t)blockIdx.x * kPackThreads + threadIdx.x) *
-                     kPackGroup;
-         j < n; j += step) {
+    // jw: the wave's first element this step (wave-uniform), the base of
+    // its store region
+    for (int64_t jw = (int64_t)blockIdx.x * kPackTile; jw < n; jw += step) {
+        const int64_t j = jw + (int64_t)threadIdx.x * kPackGroup;
+        if (j >= n)
+            continue;
         if (vec && j + kPackGroup <= n) {
-            __builtin_nontemporal_store(
+            const int64_t left = n - jw;
+            zsdev::stream_store(
+                dst + jw,
+                (uint32_t)((left < kPackTile ? left : kPackTile) *
+                           (int64_t)sizeof(uint16_t)),
+                (uint32_t)threadIdx.x * (uint32_t)(kPackGroup *
+                                                   sizeof(uint16_t)),
                 __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(src + j)),
-                reinterpret_cast<u32x4*>(dst + j));
+                    reinterpret_cast<const u32x4*>(src + j)));
         } else {
             const int64_t end = j + kPackGroup < n ? j + kPackGroup : n;
             for (int64_t k = j; k < end; ++k)
