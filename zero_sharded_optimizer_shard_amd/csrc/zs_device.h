@@ -23,10 +23,11 @@ constexpr int kCpolSc0 = 1, kCpolNt = 2, kCpolSc1 = 16;
 // bandwidth against 80.4 % with plain non-temporal stores, with the same
 // HBM bytes.  For 1 : 1 copies it depends on the form: the one-wave packs
 // gain (flat pack 84.7-85.0 % against 83.2-83.4 %, per-tensor pack 84.5 %
-// against 83.1 %); the one-wave ZeRO-3 gather (81.8-81.9 %) and gradient
-// accumulation (84.1-84.2 % per cycle) measured level, and lost in their
-// earlier 256- and 512-thread forms, so those two keep plain non-temporal
-// stores.
+// against 83.1 %), and so does the ZeRO-3 gather with one copy per thread
+// (82.6-82.7 % against 81.9-82.0 %); the one-wave gradient accumulation
+// measured level (84.1-84.2 % per cycle) and keeps plain non-temporal
+// stores.  In their earlier 256- and 512-thread forms all the copies lost
+// by it.
 constexpr int kStreamOut = kCpolSc0 | kCpolSc1 | kCpolNt;
 
 // Store x (4, 8 or 16 bytes) at byte offset `off` of the output region

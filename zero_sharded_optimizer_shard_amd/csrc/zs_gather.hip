@@ -11,13 +11,19 @@
 // r = k / slice_q, element q*S + k - r*slice_q of its shard.
 //
 // The kernel pulls: each workgroup, a single wave64, copies one
-// 1024-element chunk of one (bucket, rank) slice, clipped to the requested
-// range, from that rank's shard to the output: 2 KiB per workgroup, two
-// 16-byte accesses per thread.  Measured on MI355X over the 34 gathers of a
-// Llama-3-8B-shaped forward: 82.1 % of peak HBM bandwidth, against 81.7 %
-// with 128-thread workgroups, 79.1 % with 256 and 76.0 % with 512 (two
-// accesses per thread each); one or four accesses per thread were slower
-// (76.6-79.4 %), and larger chunks slower still.  On one GPU the W
+// 512-element chunk of one (bucket, rank) slice, clipped to the requested
+// range, from that rank's shard to the output: 1 KiB per workgroup, one
+// 16-byte access per thread, the stores streamed on to HBM with system
+// scope (zsdev::stream_store).  Measured on MI355X over the 34 gathers of a
+// Llama-3-8B-shaped forward, two interleaved rounds: 82.6-82.7 % of peak
+// HBM bandwidth, and 27.75 ms per forward pipelined beside the stand-in
+// GEMMs, against 82.1 % and 28.0-28.2 ms for two accesses per thread with
+// plain non-temporal stores (the form before it); one access with plain
+// stores 81.9-82.0 %, two with streamed stores 82.2 %.  Gathering the
+// whole flat buffer in one launch separates them further: 84.6-84.8 %
+// against 71 %.  Earlier, with two accesses per thread: 81.7 % with
+// 128-thread workgroups, 79.1 % with 256 and 76.0 % with 512; four
+// accesses per thread and larger chunks were slower.  On one GPU the W
 // shards are W resident buffers; on a node they would be peer-mapped shards
 // of the other GPUs read over xGMI.  2 B read + 2 B written per element,
 // 16-byte non-temporal accesses except at a ragged end; bounded by HBM
@@ -28,6 +34,7 @@
 
 #include <cstdint>
 
+#include "zs_device.h"
 #include "zs_internal.h"
 
 namespace {
@@ -36,8 +43,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 64;                     // one wave per workgroup
 constexpr int kVec = 8;                         // bf16 per 16-byte access
-constexpr int kPerThread = 2;                   // accesses per thread
-constexpr int64_t kChunk = (int64_t)kThreads * kVec * kPerThread;  // 1024
+constexpr int kPerThread = 1;                   // accesses per thread
+constexpr int64_t kChunk = (int64_t)kThreads * kVec * kPerThread;  // 512
 // the largest slice the layouts allow (kMaxLaunchTiles tiles) fits one
 // launch: fewer than 2^32 work-items along x
 static_assert((kMaxLaunchTiles * ZS_TILE + kChunk - 1) / kChunk * kThreads <
@@ -79,10 +86,11 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a)
     for (int k = 0; k < kPerThread; ++k) {
         const int64_t v = (int64_t)k * kThreads + threadIdx.x;
         if (v < nvec)
-            __builtin_nontemporal_store(
+            zsdev::stream_store(
+                dst, (uint32_t)(n * (int64_t)sizeof(uint16_t)),
+                (uint32_t)(v * (int64_t)sizeof(u32x4)),
                 __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(src) + v),
-                reinterpret_cast<u32x4*>(dst) + v);
+                    reinterpret_cast<const u32x4*>(src) + v));
     }
     // ragged end (only where hi cuts a 16-byte group)
     const int64_t t = nvec * kVec + threadIdx.x;
@@ -93,8 +101,12 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a)
 // Whole-tensor layouts: every tensor comes whole from its owner's shard
 // (a broadcast from the owner in place of an all-gather of slices); the
 // padded tensors partition the flat buffer, so [lo, hi) is a list of
-// contiguous copies, up to kMaxSegs per launch.
+// contiguous copies, up to kMaxSegs per launch, in 1024-element chunks of
+// two plain non-temporal 16-byte copies per thread (the flat gather's
+// earlier form; no benchmark times this mode).
 constexpr int kMaxSegs = 16;
+constexpr int kSegPerThread = 2;
+constexpr int64_t kSegChunk = (int64_t)kThreads * kVec * kSegPerThread;
 // chunks per launch: kThreads work-items each stay below 2^32
 constexpr int64_t kMaxLaunchChunks = ((int64_t(1) << 32) - 1) / kThreads;
 
@@ -118,15 +130,15 @@ __global__ __launch_bounds__(kThreads) void copy_segments_kernel(CopyArgs a)
     while (i + 1 < a.count && a.start[i + 1] <= t)
         ++i;
     const CopySeg& sg = a.s[i];
-    const int64_t c0 = (t - a.start[i]) * kChunk;
+    const int64_t c0 = (t - a.start[i]) * kSegChunk;
     if (c0 >= sg.n)
         return;
-    const int64_t n = sg.n - c0 < kChunk ? sg.n - c0 : kChunk;
+    const int64_t n = sg.n - c0 < kSegChunk ? sg.n - c0 : kSegChunk;
     const uint16_t* src = sg.src + c0;     // both 16-byte aligned
     uint16_t* dst = sg.dst + c0;
     const int64_t nvec = n / kVec;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
+    for (int k = 0; k < kSegPerThread; ++k) {
         const int64_t v = (int64_t)k * kThreads + threadIdx.x;
         if (v < nvec)
             __builtin_nontemporal_store(
@@ -167,7 +179,7 @@ int gather_tensors(const zs_layout* L, const uint16_t* const* shards,
         const int64_t t1 = t0 + (n + A - 1) / A * A;     // padded extent
         const int64_t x0 = t0 > lo ? t0 : lo, x1 = t1 < hi ? t1 : hi;
         if (x1 <= x0) continue;
-        const int64_t nc = (x1 - x0 + kChunk - 1) / kChunk;
+        const int64_t nc = (x1 - x0 + kSegChunk - 1) / kSegChunk;
         if (cnt > 0 && a.start[cnt] + nc > kMaxLaunchChunks) {
             const int rc = flush();
             if (rc) return rc;
