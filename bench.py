@@ -72,6 +72,10 @@ STEP_KERNELS = {
     # the ZeRO-3 gather: traffic per forward (every unit's gather once)
     "llama8b_zero3": ("_ZN12_GLOBAL__N_113gather_kernelENS_10GatherArgsE",
                       "gather_kernel"),
+    # the same forward on the whole-tensor layout: each tensor copied whole
+    # from its owner's shard
+    "llama8b_zero3_tensors": ("_ZN12_GLOBAL__N_120copy_segments_kernelENS_8"
+                              "CopyArgsE", "copy_segments_kernel"),
     # gradient accumulation over k = 2 micro-batches: traffic per cycle
     # (the first-micro-batch launch and the last one); both kernels' digests
     # are checked
@@ -145,6 +149,8 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
     symbol, kname = STEP_KERNELS[workload]
     pure = workload.endswith("_bf16")
     mode = workload.rsplit("_", 1)[1] if "_" in workload else ""
+    if workload.endswith("_zero3_tensors"):
+        mode = "zero3_tensors"
     fetch = read_counter_csv(fetch_csv, "FETCH_SIZE")
     write = read_counter_csv(write_csv, "WRITE_SIZE")
     copy_bytes = 4 << 30
@@ -157,6 +163,8 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
                                     f"{W}, true,") and ("true>" in k) == pure)
     if mode == "zero3":         # (the profiler names a plain function
         tiled = lambda k: "(anonymous namespace)::gather_kernel(" in k
+    elif mode == "zero3_tensors":
+        tiled = lambda k: "(anonymous namespace)::copy_segments_kernel(" in k
     elif mode == "accum":       # without its return type)
         tiled = lambda k: "(anonymous namespace)::accum_kernel<" in k
     elif per_step or mode == "tensors":
@@ -186,9 +194,10 @@ def record_traffic(fetch_csv: str, write_csv: str, n: int, W: int,
     rd = avg(tf) * 1024 * rs
     wr = avg(tw) * 1024 * ws
     alg = (2 * W + (20 if pure else 26)) * n
-    if mode == "zero3":         # n: elements gathered per forward
+    if mode in ("zero3", "zero3_tensors"):  # n: elements gathered per forward
         alg = 4 * n
-        what = f"zs_gather, bytes per forward of {per_step} unit gathers"
+        what = (f"zs_gather{' on the whole-tensor layout' if mode != 'zero3' else ''}, "
+                f"bytes per forward of {per_step} unit gathers")
     elif mode == "accum":       # n: elements of the flat gradient buffer
         alg = (6 + 8) * n
         what = ("zs_accumulate, k = 2: bytes per cycle (first micro-batch "
@@ -712,17 +721,23 @@ def zero3_main(args, w):
     import zero_sharded_optimizer_shard_amd as zs
 
     W = w.world
-    lay = zs.zs_layout_build(w.numels, W, 0)
+    # whole tensors: every tensor comes whole from its owner's shard, and
+    # the ranks' shards differ in size
+    build = (zs.zs_layout_build_tensors if args.whole_tensors
+             else zs.zs_layout_build)
+    lay = build(w.numels, W, 0)
     flat_n, n, nb, nc = zs.zs_layout_info(lay)
     offs = zs.zs_layout_tensor_offsets(lay, len(w.numels))
     units = fsdp_units(w.numels)
     ranges = [(offs[a], offs[b] + w.numels[b]) for a, b in units]
     biggest = max(hi - lo for lo, hi in ranges)
     log(f"workload {w.name} ZeRO-3: W={W} shard={n} units={len(units)} "
-        f"largest unit {biggest} elements")
+        f"largest unit {biggest} elements"
+        f"{' (whole tensors)' if args.whole_tensors else ''}")
     shards = []
     for r in range(W):
-        t = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        n_r = zs.zs_layout_info(build(w.numels, W, r))[1]
+        t = torch.empty(max(n_r, 8), dtype=torch.bfloat16, device="cuda")
         synth.dev_normal_bf16(t, 0, synth.TAG_MASTER, 0, r, 0, 0.02)
         shards.append(t)
     bufs = [torch.empty(biggest, dtype=torch.bfloat16, device="cuda")
@@ -823,13 +838,17 @@ def zero3_main(args, w):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name} parameters, W={W} shards, "
-                               f"ZeRO-3 gather per FSDP unit",
+                               f"ZeRO-3 gather per FSDP unit"
+                               + (", whole tensors from their owners"
+                                  if args.whole_tensors else ""),
                    "params_total": sum(w.numels), "fsdp_units": NU,
                    "bytes_per_param": 4, "tokens": args.tokens},
         "roofline": {"bound": "hbm", "achieved": g_gbs,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": g_gbs / PEAK_HBM_GBS,
-                     "traffic": traffic_record(f"{args.workload}_zero3")},
+                     "traffic": traffic_record(
+                         f"{args.workload}_zero3"
+                         + ("_tensors" if args.whole_tensors else ""))},
         "zero3": {"gathers_alone_ms": g_ms, "compute_alone_ms": c_ms,
                   "pipelined_ms": p_ms, "exposed_gather_ms": p_ms - c_ms,
                   "elements_per_forward": elems},
@@ -1118,7 +1137,8 @@ def main():
     ap.add_argument("--whole-tensors", action="store_true",
                     help="whole-tensor shard assignment "
                     "(zs_layout_build_tensors): every tensor on one rank, "
-                    "same step kernel over the rank's owned tensors")
+                    "same step kernel over the rank's owned tensors; with "
+                    "--zero3, each tensor gathered whole from its owner")
     ap.add_argument("--zero3", action="store_true",
                     help="ZeRO-3 / FSDP mode: per-layer parameter gather "
                     "(zs_gather) with prefetch, on the workload's layout")
@@ -1181,7 +1201,11 @@ def main():
                 w.numels, w.world, w.rank))[1]
         if args.zero3:                      # as zero3_main gathers them
             key = args.workload + "_zero3"
-            lay = zs.zs_layout_build(w.numels, w.world, 0)
+            build = zs.zs_layout_build
+            if args.whole_tensors:
+                key += "_tensors"
+                build = zs.zs_layout_build_tensors
+            lay = build(w.numels, w.world, 0)
             offs = zs.zs_layout_tensor_offsets(lay, len(w.numels))
             units = fsdp_units(w.numels)
             n = sum(offs[b] + w.numels[b] - offs[a] for a, b in units)

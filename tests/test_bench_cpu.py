@@ -141,3 +141,21 @@ def test_record_traffic_accumulation_per_cycle(tmp_path):
                                out_path=str(tmp_path / "g.json"))
     assert rec["bytes_read_per_launch"] == 4.0 * 1024
     assert rec["algorithmic_bytes_per_launch"] == 4 * 1024
+    # the whole-tensor gather's segment copies, not the flat gather's
+    seg = ("(anonymous namespace)::copy_segments_kernel((anonymous "
+           "namespace)::CopyArgs)")
+    _counter_csv(tmp_path / "sf.csv", "FETCH_SIZE",
+                 [(copy, kib), (gather, 9.0), (seg, 1.0), (seg, 1.0),
+                  (seg, 2.0), (seg, 2.0)])
+    _counter_csv(tmp_path / "sw.csv", "WRITE_SIZE",
+                 [(copy, kib), (gather, 9.0), (seg, 2.0), (seg, 2.0),
+                  (seg, 1.0), (seg, 1.0)])
+    rec = bench.record_traffic(str(tmp_path / "sf.csv"),
+                               str(tmp_path / "sw.csv"), 1024, 8,
+                               "llama8b_zero3_tensors", per_step=2,
+                               out_path=str(tmp_path / "s.json"))
+    assert rec["FETCH_SIZE_KiB_per_launch"] == [2.0, 4.0]
+    assert rec["bytes_read_per_launch"] == 3.0 * 1024
+    assert rec["bytes_written_per_launch"] == 3.0 * 1024
+    assert rec["algorithmic_bytes_per_launch"] == 4 * 1024
+    assert "copy_segments_kernel" in rec["kernel"]
