@@ -67,8 +67,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int64_t kTile = ZS_TILE;
 // Each kernel states its own workgroup shape beside it: the step's work
-// shapes (Shape below), kStThreads / kGtThreads / kPackNT for the layout
-// conversions and the flat pack, kPackThreads for the per-tensor pack.
+// shapes (Shape below), kStWave / kStWide / kGtThreads / kPackNT for the
+// layout conversions and the flat pack, kPackThreads for the per-tensor
+// pack.
 constexpr int64_t kMaxGridY = 65535;
 
 // Work shape of the step kernels: NT threads per workgroup, U 4-element
@@ -228,11 +229,6 @@ __device__ __forceinline__ u32x2 ld2(const uint16_t* p)
 __device__ __forceinline__ f32x4 ld4(const float* p)
 {
     return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-}
-
-__device__ __forceinline__ void st4(float* p, f32x4 x)
-{
-    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
 }
 
 // Stores of the step: element jj of a tile row at `row` (wave-uniform),
@@ -541,56 +537,74 @@ struct Rows {
     float* out[3];              // unpack: destinations, NULL = skipped
 };
 
-// One state row of one tile per kStParts workgroups of kStThreads, one
+// One state row of one tile per 8192 / (4 NT) workgroups of NT threads, one
 // 16-byte group per thread, the row on the grid's z axis: the dispatcher
 // advances z last, so the workgroups in flight stream one plain array in
-// order (the gradient tiling conversion's scheme).  Measured on MI355X over
-// the 8B-shaped W = 8 shard's state (24 GB moved): pack 3.84 ms, unpack
-// 3.79 ms (78-79 % of peak), against 4.57 and 4.44 ms (66-68 %) with one
-// 512-thread workgroup per tile walking all rows, and 4.14 / 3.97 ms with
-// 512-thread workgroups on z.
-constexpr int kStThreads = 256;
-constexpr int kStParts = (int)(kTile / 4 / kStThreads);
-static_assert(kMaxLaunchTiles * kStParts * kStThreads < (int64_t(1) << 32),
+// order (the gradient tiling conversion's scheme); the stores are streamed
+// on to HBM with system scope.  Measured on MI355X over the 8B-shaped W = 8
+// shard's state, interleaved rounds:
+//  - unpack (24 B per element): one-wave workgroups 3.56-3.57 ms, 84.4-84.6
+//    % of peak, against 3.80 ms (79 %) for 256-thread ones with plain
+//    non-temporal stores, 3.65 ms for one-wave ones with plain stores and
+//    3.70 ms for 256-thread ones with streamed stores;
+//  - pack of all three rows: one-wave 3.63-3.65 ms (82.5-83.1 %) against
+//    3.84 ms (78.4 %) for 256-thread workgroups with plain stores, 3.69 ms
+//    one-wave with plain stores, 3.74 ms 256-thread with streamed stores;
+//  - pack of the master alone, m and v written as zeros (16 B per element,
+//    three quarters of it writes): 256-thread workgroups 2.49-2.52 ms
+//    (79.6-80.6 %) against 2.61 ms with plain stores and 2.87-2.90 ms
+//    (69-70 %) for one-wave ones either way.
+// So the unpack and a pack that reads every row take one-wave workgroups,
+// and a pack with a zero row 256-thread ones.  (Earlier forms: 4.57 and
+// 4.44 ms, 66-68 %, with one 512-thread workgroup per tile walking all
+// rows; 4.14 / 3.97 ms with 512-thread workgroups on z.)
+constexpr int kStWave = 64, kStWide = 256;
+template <int NT>
+constexpr int st_parts() { return (int)(kTile / 4 / NT); }
+static_assert(kMaxLaunchTiles * kTile / 4 < (int64_t(1) << 32),
               "one launch row of tiles fits the grid");
 
 // offset of this thread's 4 floats inside its tile row
+template <int NT>
 __device__ __forceinline__ int state_off()
 {
-    return (int)(blockIdx.x % kStParts) * (int)(kTile / kStParts) +
-           4 * (int)threadIdx.x;
+    constexpr int P = st_parts<NT>();
+    return (int)(blockIdx.x % P) * (int)(kTile / P) + 4 * (int)threadIdx.x;
 }
 
-// plain rows -> tiled state; padding positions written as zero
-template <int ROWS, class Loc>
-__global__ __launch_bounds__(kStThreads) void state_pack_kernel(
+// plain rows -> tiled state; padding positions and rows without a source
+// written as zero
+template <int ROWS, class Loc, int NT>
+__global__ __launch_bounds__(NT) void state_pack_kernel(
     Rows rw, float* __restrict__ state, Loc loc)
 {
     TileRef r;
-    if (!loc.template at<kStParts>(r))
+    if (!loc.template at<st_parts<NT>()>(r))
         return;
     const int row = (int)blockIdx.z;
-    const int jj = state_off();
+    const int jj = state_off<NT>();
     const float* in = rw.in[row];
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
     if (jj < r.nvalid && in)
         x = ld4(in + r.e0 + jj);
-    st4(state + r.tile * (ROWS * kTile) + row * kTile + jj, x);
+    st4_out(state + r.tile * (ROWS * kTile) + row * kTile, jj, x);
 }
 
 // tiled state -> plain rows (each nullable)
 template <int ROWS, class Loc>
-__global__ __launch_bounds__(kStThreads) void state_unpack_kernel(
+__global__ __launch_bounds__(kStWave) void state_unpack_kernel(
     const float* __restrict__ state, Rows rw, Loc loc)
 {
     TileRef r;
-    if (!loc.template at<kStParts>(r))
+    if (!loc.template at<st_parts<kStWave>()>(r))
         return;
     const int row = (int)blockIdx.z;
-    const int jj = state_off();
+    const int jj = state_off<kStWave>();
     float* out = rw.out[row];
     if (jj < r.nvalid && out)
-        st4(out + r.e0 + jj,
+        zsdev::stream_store(
+            out + r.e0, (uint32_t)(r.nvalid * (int64_t)sizeof(float)),
+            (uint32_t)jj * (uint32_t)sizeof(float),
             ld4(state + r.tile * (ROWS * kTile) + row * kTile + jj));
 }
 
@@ -600,11 +614,13 @@ __global__ __launch_bounds__(kStThreads) void state_unpack_kernel(
 // multiples of 8 elements; a partial group would be copied element-wise).
 // The rank row is blockIdx.z, which the dispatcher advances last, so the
 // workgroups in flight read one slice front to back and write whole 16 KiB
-// rows.  Measured on MI355X over the 8B shard at W = 8 (32 GB moved):
-// 5.27-5.30 ms, 76 % of peak; one 512-thread workgroup per tile sweeping
-// its W rows four at a time took 5.79-5.89 ms (68-69 %), and with the rank
-// row in z, 64-, 128-, 512- and 1024-thread workgroups or two groups per
-// thread measured 63-72 %.
+// rows, streamed on to HBM with system scope.  Measured on MI355X over the
+// 8B shard at W = 8 (32 GB moved), two interleaved rounds: 5.12 ms, 78.5 %
+// of peak, against 5.20 ms (77.1 %) with plain non-temporal stores and
+// 5.56-5.86 ms (68-72 %) for one-wave workgroups either way; earlier, one
+// 512-thread workgroup per tile sweeping its W rows four at a time took
+// 5.79-5.89 ms (68-69 %), and with the rank row in z, 128-, 512- and
+// 1024-thread workgroups or two groups per thread measured 63-72 %.
 constexpr int kGtThreads = 256;
 constexpr int kGtParts = (int)(kTile / 8 / kGtThreads);
 static_assert(kMaxLaunchTiles * kGtParts * kGtThreads < (int64_t(1) << 32),
@@ -623,13 +639,16 @@ __global__ __launch_bounds__(kGtThreads) void grads_tile_kernel(
     const uint16_t* src = slices + r.e0 + s * stride;
     const int g = (int)(blockIdx.x % kGtParts) * kGtThreads + (int)threadIdx.x;
     const int nv = (int)(r.nvalid / 8);                // whole valid groups
+    const uint32_t row_bytes = (uint32_t)(kTile * sizeof(uint16_t));
     if (g < nv) {
-        __builtin_nontemporal_store(
-            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + g),
-            reinterpret_cast<u32x4*>(dst) + g);
+        zsdev::stream_store(
+            dst, row_bytes, (uint32_t)g * (uint32_t)sizeof(u32x4),
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) +
+                                       g));
     } else if (g > nv || r.nvalid % 8 == 0) {
         const u32x4 z = {0u, 0u, 0u, 0u};
-        __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(dst) + g);
+        zsdev::stream_store(dst, row_bytes,
+                            (uint32_t)g * (uint32_t)sizeof(u32x4), z);
     } else {
         // the partial group (the layouts never produce one): its valid
         // elements and zeros
@@ -1418,22 +1437,28 @@ int convert_state(const zs_layout* L, bool pack, const float* const* in,
     return for_launches(L, [&](const auto& loc, dim3 grid, int64_t e,
                                int64_t t, int64_t) {
         Rows rw{};
+        bool every_row = true;              // (pack) every row has a source
         for (int row = 0; row < ROWS; ++row) {
             rw.in[row] = (pack && in[row]) ? in[row] + e : nullptr;
             rw.out[row] = (!pack && out[row]) ? out[row] + e : nullptr;
+            every_row = every_row && in && in[row];
         }
         using Loc = std::decay_t<decltype(loc)>;
         const int64_t t0 = t * ROWS * kTile;
-        grid.x *= kStParts;                 // kStParts workgroups per row
         grid.z = ROWS;                      // state row
-        if (pack)
-            hipLaunchKernelGGL((state_pack_kernel<ROWS, Loc>), grid,
-                               dim3(kStThreads), 0, s, rw, state_w + t0,
-                               loc);
-        else
+        if (pack && !every_row) {
+            grid.x *= st_parts<kStWide>();  // workgroups per row
+            hipLaunchKernelGGL((state_pack_kernel<ROWS, Loc, kStWide>), grid,
+                               dim3(kStWide), 0, s, rw, state_w + t0, loc);
+        } else if (pack) {
+            grid.x *= st_parts<kStWave>();
+            hipLaunchKernelGGL((state_pack_kernel<ROWS, Loc, kStWave>), grid,
+                               dim3(kStWave), 0, s, rw, state_w + t0, loc);
+        } else {
+            grid.x *= st_parts<kStWave>();
             hipLaunchKernelGGL((state_unpack_kernel<ROWS, Loc>), grid,
-                               dim3(kStThreads), 0, s, state_r + t0, rw,
-                               loc);
+                               dim3(kStWave), 0, s, state_r + t0, rw, loc);
+        }
         return check_launch(pack ? "state pack kernel"
                                  : "state unpack kernel");
     });
