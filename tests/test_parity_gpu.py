@@ -994,6 +994,44 @@ def test_gather_matches_the_oracle(W, cap):
         assert np.all(got[hi - lo:] == 0x5a5a), (lo, hi)
 
 
+def test_gather_across_launches():
+    """A gather whose range spans more buckets than one launch holds (W = 64,
+    8192-element buckets: 1023 buckets per launch): the first launch starts
+    at the range's first rank row, the last ends at its last, the rows in
+    between whole; against the oracle bit for bit, nothing written past the
+    range."""
+    W, cap = 64, 64 * 256
+    numels = [3_000_000, 5_000_000, 700_001, 129, 40_000]
+    lay_o = build_layout(numels, W, 0, cap)
+    lay = zs.zs_layout_build(numels, W, 0, cap)
+    n, F = lay_o.shard_numel, lay_o.flat_numel
+    B = lay_o.buckets[0].numel
+    per_launch = 65535 // W
+    assert len(lay_o.buckets) > per_launch + 1
+    say(f"case gather across launches W={W} buckets={len(lay_o.buckets)}")
+    host = [synth.cpu_bits16(n, 5, synth.TAG_SENTINEL, 0, r, 0)
+            for r in range(W)]
+    dev = [torch.from_numpy(h.view(np.int16)).cuda() for h in host]
+    full = gather(numels, W, host, 0, F, cap)
+    out = torch.empty(F + 64, dtype=torch.int16, device="cuda")
+    S = B // W
+    edge = per_launch * B                       # first bucket of launch 2
+    ranges = [(0, F), (8, F - 3), (edge - 5 * S + 40, edge + 3 * S + 17),
+              (edge, edge + B), (edge - B + 2 * S, edge + 1),
+              (S * 3 + 8, S * 5 - 1), (F - S - 800, F)]
+    rng = random.Random(7)
+    for _ in range(4):
+        lo = rng.randrange(0, edge) // 8 * 8
+        ranges.append((lo, rng.randrange(edge, F + 1)))
+    for lo, hi in ranges:
+        assert 0 <= lo < hi <= F and lo % 8 == 0, (lo, hi)
+        out.fill_(0x5a5a)
+        zs.zs_gather(lay, dev, lo, hi, out)
+        got = np16(out)
+        assert np.array_equal(got[:hi - lo], full[lo:hi]), (lo, hi)
+        assert np.all(got[hi - lo:] == 0x5a5a), (lo, hi)
+
+
 def test_gather_llama8b_layers_sampled():
     """Full-size Llama-3-8B-shaped W=8 layout: the embedding, a middle
     block and the final norm + lm_head gathered from 8 resident shards;

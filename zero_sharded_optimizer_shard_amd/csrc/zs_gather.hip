@@ -14,14 +14,18 @@
 // 512-element chunk of one (bucket, rank) slice, clipped to the requested
 // range, from that rank's shard to the output: 1 KiB per workgroup, one
 // 16-byte access per thread, the stores streamed on to HBM with system
-// scope (zsdev::stream_store).  Measured on MI355X over the 34 gathers of a
-// Llama-3-8B-shaped forward, two interleaved rounds: 82.6-82.7 % of peak
-// HBM bandwidth, and 27.75 ms per forward pipelined beside the stand-in
-// GEMMs, against 82.1 % and 28.0-28.2 ms for two accesses per thread with
-// plain non-temporal stores (the form before it); one access with plain
-// stores 81.9-82.0 %, two with streamed stores 82.2 %.  Gathering the
-// whole flat buffer in one launch separates them further: 84.6-84.8 %
-// against 71 %.  Earlier, with two accesses per thread: 81.7 % with
+// scope (zsdev::stream_store); a launch covers only the (bucket, rank) rows
+// that meet the range.  Measured on MI355X over the 34 gathers of a
+// Llama-3-8B-shaped forward (stand-alone, three interleaved rounds): 85.2-
+// 85.3 % of peak HBM bandwidth, against 82.6-82.8 % when every row of the
+// first and last buckets is launched (5.2 % of the workgroups then find
+// nothing to copy, at the start and end of each launch).  With all rows
+// launched, in the benchmark, two interleaved rounds: one access per
+// thread with streamed stores 82.6-82.7 % and 27.75 ms per forward
+// pipelined beside the stand-in GEMMs, against 82.1 % and 28.0-28.2 ms for
+// two accesses per thread with plain non-temporal stores; one access with
+// plain stores 81.9-82.0 %, two with streamed stores 82.2 %.  Gathering
+// the whole flat buffer in one launch: 84.6-84.8 % against 71 %.  Earlier, with two accesses per thread: 81.7 % with
 // 128-thread workgroups, 79.1 % with 256 and 76.0 % with 512; four
 // accesses per thread and larger chunks were slower.  On one GPU the W
 // shards are W resident buffers; on a node they would be peer-mapped shards
@@ -61,11 +65,14 @@ struct GatherArgs {
     int64_t B, S, S_last;       // full bucket numel and slice; last slice
     int64_t nb;                 // buckets in the layout
     int32_t W;
+    int32_t r_skip;             // rows of bucket q0 before the first launched
 };
 
+// blockIdx.y runs over the (bucket, rank) rows q0 * W + r_skip, ...: the
+// host launches only rows that meet [lo, hi)
 __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a)
 {
-    const int64_t y = blockIdx.y;
+    const int64_t y = (int64_t)blockIdx.y + a.r_skip;
     const int64_t q = a.q0 + y / a.W;
     const int r = (int)(y % a.W);
     const int64_t S_q = q == a.nb - 1 ? a.S_last : a.S;
@@ -250,11 +257,22 @@ extern "C" int zs_gather(const zs_layout* L, const uint16_t* const* shards,
     const unsigned gx = (unsigned)((a.S + kChunk - 1) / kChunk);
     const int64_t per_launch = kMaxGridY / W;           // buckets per launch
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    // rank rows of the first and last buckets that hold lo and hi - 1; the
+    // rows before the first and after the last are not launched (their
+    // workgroups would find nothing to copy)
+    auto slice_of = [&](int64_t q) { return q == nb - 1 ? a.S_last : a.S; };
+    int64_t r_first = (flat_lo - q_first * a.B) / slice_of(q_first);
+    int64_t r_last = (flat_hi - 1 - q_last * a.B) / slice_of(q_last);
+    if (r_first > W - 1) r_first = W - 1;
+    if (r_last > W - 1) r_last = W - 1;
     for (int64_t q = q_first; q <= q_last; q += per_launch) {
         const int64_t nq = q_last + 1 - q < per_launch ? q_last + 1 - q
                                                        : per_launch;
         a.q0 = q;
-        hipLaunchKernelGGL(gather_kernel, dim3(gx, (unsigned)(nq * W)),
+        a.r_skip = q == q_first ? (int32_t)r_first : 0;
+        const int64_t r_trim = q + nq - 1 == q_last ? W - 1 - r_last : 0;
+        const int64_t rows = nq * W - a.r_skip - r_trim;
+        hipLaunchKernelGGL(gather_kernel, dim3(gx, (unsigned)rows),
                            dim3(kThreads), 0, s, a);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess)
