@@ -445,6 +445,11 @@ int zs_pack(const zs_layout* layout, const uint16_t* param_shard,
  *   host memory it runs later, so keep a pinned array unchanged until the
  *   stream has passed the call.
  * hip_stream must belong to the current device.
+ * Under stream capture the flat output alone records kernel launches only
+ * (a test replays it in a graph); with tensor_ptrs the two table copies are
+ * recorded as copies from the host arrays (the layout's chunk table and
+ * tensor_ptrs), which then must stay valid and unchanged for as long as the
+ * graph can run (that case is not tested).
  * Every call on one device shares the staging and overwrites it: calls
  * whose work can overlap on one device (on streams with no order between
  * them, or from several host threads at once) race.  Calls on one stream

@@ -1853,3 +1853,82 @@ def test_two_runs_are_bit_identical():
         torch.cuda.synchronize()
         outs.append(npf(c.state).view(np.uint32))
     assert np.array_equal(outs[0], outs[1])
+
+
+def test_step_and_pack_replay_in_a_graph():
+    """zs_step (tiled gradients, bf16 shard and flat output), zs_pack
+    (per-tensor storage through a device chunk table) and zs_pack_noalloc
+    (flat output alone) captured in one HIP graph on torch's capture stream
+    and replayed three times, with the process's own eager work and a
+    synchronisation between replays: after every replay the graph's buffers
+    equal those of the same calls run eagerly on a twin set, bit for bit,
+    and both equal the oracle's steps.  None of these calls allocates or
+    clears memory: they record kernel launches only."""
+    numels = [1000, 70000, 129, 20000, 9000]
+    c = Case(numels, 4, 1, layout="tiled")
+    lay, lay_o, n = c.lay, c.lay_o, c.n
+    F = lay_o.flat_numel
+    say(f"case graph replay W=4 rank=1 shard={n}")
+    c.dev_grads(c.G, 1)
+    zs.zs_grads_tile(lay, -1, c.G, c.stride, c.Gt)
+    chunks = zs.zs_layout_chunks(lay)
+    dch = torch.from_numpy(np.frombuffer(zs.chunks_bytes(chunks),
+                                         np.uint8).copy()).cuda()
+    sets = []
+    for k in range(2):
+        flat = dev_bf16(F)
+        flat.view(torch.int16).fill_(0x1234)
+        flat2 = dev_bf16(F)
+        flat2.view(torch.int16).fill_(0x2345)
+        tens = [torch.full((m,), 7, dtype=torch.int16, device="cuda")
+                for m in numels]
+        ptrs = torch.tensor([t.data_ptr() for t in tens], dtype=torch.int64,
+                            device="cuda")
+        sets.append(dict(state=c.dev_state(), p=dev_bf16(n), flat=flat,
+                         flat2=flat2, tens=tens, ptrs=ptrs))
+    flat_before = np16(sets[0]["flat"])
+    flat2_before = np16(sets[0]["flat2"])
+
+    def calls(k):
+        d = sets[k]
+        zs.zs_step(lay, c.Gt, d["state"], d["p"], d["flat"],
+                   grad_layout="tiled", step=1, **HP)
+        zs.zs_pack(lay, d["p"], None, dch, len(chunks), d["ptrs"])
+        zs.zs_pack_noalloc(lay, d["p"], d["flat2"], None)
+
+    def snapshot(k):
+        d = sets[k]
+        return ([npf(d["state"]).view(np.uint32), np16(d["p"]),
+                 np16(d["flat"]), np16(d["flat2"])] +
+                [t.cpu().numpy() for t in d["tens"]])
+
+    # both sets once, eagerly (the kernels are loaded before the capture)
+    calls(0)
+    calls(1)
+    c.oracle_step(1)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(0)
+    torch.cuda.synchronize()
+    junk = torch.ones(1 << 20, device="cuda")
+    for r in range(3):
+        g.replay()
+        junk.mul_(1.5).add_(1.0)            # the process's own eager work
+        calls(1)
+        c.oracle_step(1)
+        torch.cuda.synchronize()
+        a, b = snapshot(0), snapshot(1)
+        for i, (x, y) in enumerate(zip(a, b)):
+            assert np.array_equal(x, y), f"replay {r}: buffer {i}"
+        c.check(sets[1]["state"], f"graph replay {r}", p=sets[1]["p"],
+                flat=sets[1]["flat"], flat_before=flat_before)
+        ref2 = flat2_before.copy()
+        pack_flat(lay_o, c.op, ref2)
+        assert np.array_equal(np16(sets[0]["flat2"]), ref2), \
+            f"replay {r}: no-alloc flat pack"
+        ts = [np.full(m, 7, np.uint16) for m in numels]
+        pack_tensors(lay_o, c.op, ts)
+        for k, (t, want) in enumerate(zip(sets[0]["tens"], ts)):
+            assert np.array_equal(t.cpu().numpy().view(np.uint16), want), \
+                f"replay {r}: tensor {k}"
