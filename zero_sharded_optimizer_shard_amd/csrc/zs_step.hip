@@ -37,7 +37,9 @@
 // also carry system scope (sc0 sc1 nt), so the L2 streams them on to HBM
 // instead of holding them as dirty lines: measured on MI355X, 82.0-82.2 %
 // of peak against 80.4 % with plain non-temporal stores on the 8B-shaped
-// W = 8 shard (512-thread workgroups then).
+// W = 8 shard (512-thread workgroups then).  The pack and the layout
+// conversions, plain copies, store the same way; their workgroup shapes,
+// measured one by one, are given with each kernel below.
 //
 // Grid of the whole-shard step: blockIdx.y = bucket, blockIdx.x = tile
 // (times the workgroups per tile) of that bucket's slice, so no thread
