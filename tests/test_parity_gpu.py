@@ -1932,3 +1932,35 @@ def test_step_and_pack_replay_in_a_graph():
         for k, (t, want) in enumerate(zip(sets[0]["tens"], ts)):
             assert np.array_equal(t.cpu().numpy().view(np.uint16), want), \
                 f"replay {r}: tensor {k}"
+
+
+def test_grads_tile_across_launches():
+    """zs_grads_tile over a slice of more tiles than one launch covers (a
+    single 35 M-element bucket at W = 2: 4273 tiles, launches of 4096): the
+    tiles on both sides of the split, the ragged last tile and its zero
+    padding equal the tiling rule, for the whole-shard call and the
+    one-bucket call, bit for bit."""
+    W, numels = 2, [40_000_000, 30_000_000]
+    lay_o = build_layout(numels, W, 1, 0)
+    lay = zs.zs_layout_build(numels, W, 1, 0)
+    n = lay_o.shard_numel
+    nt = n_tiles(lay_o)
+    assert len(lay_o.buckets) == 1 and nt > 4096 + 1
+    say(f"case grads tile across launches W={W} shard={n} tiles={nt}")
+    stride = n + 24
+    host = np.stack([synth.cpu_bits16(stride, 9, synth.TAG_SENTINEL, 0, s, 0)
+                     for s in range(W)])
+    dG = torch.from_numpy(host.view(np.int16)).cuda()
+    pick = [0, 1, 4095, 4096, 4097, nt - 2, nt - 1]
+    for bucket in (-1, 0):
+        tiled = torch.empty(nt * W * TILE, dtype=torch.int16, device="cuda")
+        tiled.fill_(0x5a5a)
+        zs.zs_grads_tile(lay, bucket, dG, stride, tiled)
+        got = np16(tiled).reshape(nt, W, TILE)
+        for t in pick:
+            a = t * TILE
+            k = min(TILE, n - a)
+            for s in range(W):
+                want = np.zeros(TILE, np.uint16)
+                want[:k] = host[s, a:a + k]
+                assert np.array_equal(got[t, s], want), (bucket, t, s)

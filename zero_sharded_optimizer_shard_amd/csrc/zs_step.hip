@@ -130,6 +130,22 @@ __device__ __forceinline__ bool tile_of(const Geom& g, TileRef& r)
     return true;
 }
 
+// The same for an explicit tile x of bucket blockIdx.y (the gradient tiling
+// conversion, whose workgroups are not in tile-major order).
+__device__ __forceinline__ bool tile_at(const Geom& g, int64_t x, TileRef& r)
+{
+    const int32_t q = blockIdx.y;
+    const int64_t slice = (q == g.q_last) ? g.S_last : g.S;
+    const int64_t j0 = x * kTile;
+    if (j0 >= slice)
+        return false;
+    r.tile = (int64_t)q * g.TPB + x;
+    r.e0 = (int64_t)q * g.S + j0;
+    r.nvalid = slice - j0 < kTile ? slice - j0 : kTile;
+    r.fpos = (int64_t)q * g.B + (int64_t)g.rank * slice + j0;
+    return true;
+}
+
 // element offset of unit k of this thread inside its tile, for a workgroup
 // of NT threads that is part `blockIdx.x % P` of P on the tile
 template <int P, int NT>
@@ -161,6 +177,11 @@ struct GeomLoc {
     // P workgroups per tile (blockIdx.x = tile * P + part)
     template <int P>
     __device__ bool at(TileRef& r) const { return tile_of<P>(g, r); }
+    // tile x of the launch's row of tiles
+    __device__ bool at_tile(int64_t x, TileRef& r) const
+    {
+        return tile_at(g, x, r);
+    }
 };
 
 // Member i of a group launch owns the launch's tiles [start[i], start[i+1])
@@ -189,6 +210,21 @@ struct SegLoc {
     __device__ bool at(TileRef& r) const
     {
         const int64_t t = blockIdx.x / P;
+        const int i = member_of(start, count, t);
+        const Seg& sg = s[i];
+        const int64_t x = t - start[i];
+        const int64_t j0 = x * kTile;
+        if (j0 >= sg.slice)
+            return false;
+        r.tile = sg.tile_off + x;
+        r.e0 = sg.shard_off + j0;
+        r.nvalid = sg.slice - j0 < kTile ? sg.slice - j0 : kTile;
+        r.fpos = sg.fpos + j0;
+        return true;
+    }
+    // the same for an explicit tile t of the launch's members
+    __device__ bool at_tile(int64_t t, TileRef& r) const
+    {
         const int i = member_of(start, count, t);
         const Seg& sg = s[i];
         const int64_t x = t - start[i];
@@ -611,32 +647,35 @@ __global__ __launch_bounds__(kStWave) void state_unpack_kernel(
 }
 
 // gradient slices [W][stride] -> tiled [tile][W][kTile]; padding zeroed.
-// One tile row (tile, rank s) per kGtParts workgroups of kGtThreads, one
-// 16-byte group per thread (slice starts, strides and slice lengths are
-// multiples of 8 elements; a partial group would be copied element-wise).
-// The rank row is blockIdx.z, which the dispatcher advances last, so the
-// workgroups in flight read one slice front to back and write whole 16 KiB
-// rows, streamed on to HBM with system scope.  Measured on MI355X over the
-// 8B shard at W = 8 (32 GB moved), two interleaved rounds: 5.12 ms, 78.5 %
-// of peak, against 5.20 ms (77.1 %) with plain non-temporal stores and
-// 5.56-5.86 ms (68-72 %) for one-wave workgroups either way; earlier, one
-// 512-thread workgroup per tile sweeping its W rows four at a time took
-// 5.79-5.89 ms (68-69 %), and with the rank row in z, 128-, 512- and
-// 1024-thread workgroups or two groups per thread measured 63-72 %.
-constexpr int kGtThreads = 256;
-constexpr int kGtParts = (int)(kTile / 8 / kGtThreads);
-static_assert(kMaxLaunchTiles * kGtParts * kGtThreads < (int64_t(1) << 32),
-              "one launch row of tiles fits the grid");
+// One tile row (tile, rank s) per kGtParts one-wave workgroups, one 16-byte
+// group per thread (slice starts, strides and slice lengths are multiples
+// of 8 elements; a partial group would be copied element-wise), in the
+// order of the output: blockIdx.x = ((x - x0) * W + s) * kGtParts + part for
+// tile x of the launch's row of tiles, so consecutive workgroups write
+// consecutive memory, each reading its piece of slice s; the stores are
+// streamed on to HBM with system scope.  A launch covers at most
+// kGtLaunchTiles tiles (x0 is its first).  Measured on MI355X over the 8B
+// shard at W = 8 (32 GB moved), three interleaved rounds: 4.72-4.74 ms,
+// 84.7-85.1 % of peak, against 4.94-4.96 ms for 256-thread workgroups in
+// this order and 5.09-5.10 ms (78.8 %) for the order it replaced, the rank
+// row on the grid's z axis (workgroups in flight reading one slice front to
+// back and writing 16 KiB rows W rows apart; 256 threads, streamed stores;
+// 5.20 ms with plain stores; 64 to 1024 threads 5.48-6.02 ms).
+constexpr int kGtThreads = 64;
+constexpr int kGtParts = (int)(kTile / 8 / kGtThreads);   // 16 per row
+constexpr int64_t kGtLaunchTiles = 4096;
 
 template <class Loc>
 __global__ __launch_bounds__(kGtThreads) void grads_tile_kernel(
     const uint16_t* __restrict__ slices, int64_t stride,
-    uint16_t* __restrict__ tiled, int32_t W, Loc loc)
+    uint16_t* __restrict__ tiled, int32_t W, int64_t x0, Loc loc)
 {
+    const int64_t row = blockIdx.x / kGtParts;      // (x - x0) * W + s
+    const int64_t xr = row / W;
+    const int64_t s = row - xr * W;
     TileRef r;
-    if (!loc.template at<kGtParts>(r))
+    if (!loc.at_tile(x0 + xr, r))
         return;
-    const int64_t s = blockIdx.z;
     uint16_t* dst = tiled + (r.tile * (int64_t)W + s) * kTile;
     const uint16_t* src = slices + r.e0 + s * stride;
     const int g = (int)(blockIdx.x % kGtParts) * kGtThreads + (int)threadIdx.x;
@@ -1595,27 +1634,39 @@ extern "C" int zs_grads_tile(const zs_layout* L, int32_t bucket_id,
                     (long long)stride, (long long)len);
     if (stride > INT64_MAX / 2 / W)
         return fail(ZS_ERANGE, "W * stride overflows");
+    // tiles per launch: at most kGtLaunchTiles, and fewer than 2^32
+    // work-items along x
+    const int64_t per_tile = (int64_t)W * kGtParts * kGtThreads;
+    int64_t chunk = (((int64_t)1 << 32) - 1) / per_tile;
+    if (chunk > kGtLaunchTiles) chunk = kGtLaunchTiles;
+    if (chunk < 1)
+        return fail(ZS_ERANGE, "world %d too large for the tiling launch", W);
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    // launches over tiles [x0, x0 + nx) of each row of the locator
+    auto launch = [&](const auto& loc, int64_t tiles, unsigned rows,
+                      const uint16_t* src, uint16_t* dst) {
+        using Loc = std::decay_t<decltype(loc)>;
+        for (int64_t x0 = 0; x0 < tiles; x0 += chunk) {
+            const int64_t nx = tiles - x0 < chunk ? tiles - x0 : chunk;
+            hipLaunchKernelGGL(grads_tile_kernel<Loc>,
+                               dim3((unsigned)(nx * W * kGtParts), rows),
+                               dim3(kGtThreads), 0, s, src, stride, dst, W,
+                               x0, loc);
+            const int rc = check_launch("grads tile kernel");
+            if (rc) return rc;
+        }
+        return (int)ZS_OK;
+    };
     if (bucket_id >= 0) {
         // one bucket's staging: positions relative to the bucket
         GeomLoc loc;
         loc.g = bucket_geom(L, L->buckets[bucket_id]);
-        hipLaunchKernelGGL(grads_tile_kernel<GeomLoc>,
-                           dim3((unsigned)(loc.g.TPB * kGtParts), 1,
-                                (unsigned)W),
-                           dim3(kGtThreads), 0, s, slices, stride, tiled, W,
-                           loc);
-        return check_launch("grads tile kernel");
+        return launch(loc, loc.g.TPB, 1u, slices, tiled);
     }
     return for_launches(L, [&](const auto& loc, dim3 grid, int64_t e,
                                int64_t t, int64_t) {
-        using Loc = std::decay_t<decltype(loc)>;
-        grid.x *= kGtParts;                 // kGtParts workgroups per row
-        grid.z = (unsigned)W;               // rank row
-        hipLaunchKernelGGL(grads_tile_kernel<Loc>, grid, dim3(kGtThreads), 0,
-                           s, slices + e, stride, tiled + t * W * kTile, W,
-                           loc);
-        return check_launch("grads tile kernel");
+        return launch(loc, (int64_t)grid.x, grid.y, slices + e,
+                      tiled + t * W * kTile);
     });
 }
 
