@@ -1964,3 +1964,46 @@ def test_grads_tile_across_launches():
                 want = np.zeros(TILE, np.uint16)
                 want[:k] = host[s, a:a + k]
                 assert np.array_equal(got[t, s], want), (bucket, t, s)
+
+
+def test_state_pack_across_launches():
+    """zs_state_pack over a slice of more tiles than one launch covers (a
+    single 35 M-element bucket at W = 2: 4273 tiles, launches of 4096), with
+    all three rows read (one-wave workgroups) and with the master alone (m
+    and v written as zeros, 256-thread workgroups): the tiles on both sides
+    of the split and the ragged last tile equal the tiling rule, bit for
+    bit; the unpack returns the arrays."""
+    W, numels = 2, [40_000_000, 30_000_000]
+    lay_o = build_layout(numels, W, 1, 0)
+    lay = zs.zs_layout_build(numels, W, 1, 0)
+    n = lay_o.shard_numel
+    nt = n_tiles(lay_o)
+    assert len(lay_o.buckets) == 1 and nt > 4096 + 1
+    say(f"case state pack across launches W={W} shard={n} tiles={nt}")
+    arrs = [synth.cpu_normal_f32(n, 11, tag, 0, 0, 0, 1.0)
+            for tag in (synth.TAG_MASTER, synth.TAG_M, synth.TAG_V)]
+    dev = [torch.from_numpy(a).cuda() for a in arrs]
+    pick = [0, 1, 4095, 4096, 4097, nt - 2, nt - 1]
+    for rows in ("all", "master"):
+        state = dev_f32(nt * 3 * TILE)
+        state.fill_(float("nan"))
+        if rows == "all":
+            zs.zs_state_pack(lay, *dev, state)
+        else:
+            zs.zs_state_pack(lay, dev[0], None, None, state)
+        got = npf(state).view(np.uint32).reshape(nt, 3, TILE)
+        for t in pick:
+            a = t * TILE
+            k = min(TILE, n - a)
+            for r in range(3):
+                want = np.zeros(TILE, np.float32)
+                if rows == "all" or r == 0:
+                    want[:k] = arrs[r][a:a + k]
+                assert np.array_equal(got[t, r], want.view(np.uint32)), \
+                    (rows, t, r)
+        if rows == "all":
+            outs = [dev_f32(n) for _ in range(3)]
+            zs.zs_state_unpack(lay, state, *outs)
+            for o, x in zip(outs, arrs):
+                assert np.array_equal(npf(o).view(np.uint32),
+                                      x.view(np.uint32))

@@ -576,27 +576,32 @@ struct Rows {
 };
 
 // One state row of one tile per 8192 / (4 NT) workgroups of NT threads, one
-// 16-byte group per thread, the row on the grid's z axis: the dispatcher
-// advances z last, so the workgroups in flight stream one plain array in
-// order (the gradient tiling conversion's scheme); the stores are streamed
-// on to HBM with system scope.  Measured on MI355X over the 8B-shaped W = 8
-// shard's state, interleaved rounds:
+// 16-byte group per thread, the stores streamed on to HBM with system scope.
+// Each conversion runs in the order of its output, so that consecutive
+// workgroups write consecutive memory: the unpack with the row on the
+// grid's z axis (the dispatcher advances z last, so the workgroups in
+// flight write one plain array in order), the pack with blockIdx.x =
+// ((x - x0) * ROWS + row) * P + part for tile x (each launch covers at most
+// kOrderedLaunchTiles tiles, x0 its first).  Measured on MI355X over the
+// 8B-shaped W = 8 shard's state, interleaved rounds:
 //  - unpack (24 B per element): one-wave workgroups 3.56-3.57 ms, 84.4-84.6
 //    % of peak, against 3.80 ms (79 %) for 256-thread ones with plain
 //    non-temporal stores, 3.65 ms for one-wave ones with plain stores and
 //    3.70 ms for 256-thread ones with streamed stores;
-//  - pack of all three rows: one-wave 3.63-3.65 ms (82.5-83.1 %) against
-//    3.84 ms (78.4 %) for 256-thread workgroups with plain stores, 3.69 ms
-//    one-wave with plain stores, 3.74 ms 256-thread with streamed stores;
+//  - pack of all three rows: one-wave workgroups 3.51-3.52 ms (85.5-85.8
+//    %), 256-thread ones 3.73-3.74 ms; with the row on z instead (reading
+//    one plain array in order), 3.63-3.65 ms one-wave, 3.84 ms (78.4 %)
+//    256-thread with plain stores;
 //  - pack of the master alone, m and v written as zeros (16 B per element,
-//    three quarters of it writes): 256-thread workgroups 2.49-2.52 ms
-//    (79.6-80.6 %) against 2.61 ms with plain stores and 2.87-2.90 ms
-//    (69-70 %) for one-wave ones either way.
-// So the unpack and a pack that reads every row take one-wave workgroups,
-// and a pack with a zero row 256-thread ones.  (Earlier forms: 4.57 and
-// 4.44 ms, 66-68 %, with one 512-thread workgroup per tile walking all
-// rows; 4.14 / 3.97 ms with 512-thread workgroups on z.)
+//    three quarters of it writes): 256-thread workgroups 2.39-2.40 ms
+//    (83.8-83.9 %), one-wave ones 2.50-2.51 ms; with the row on z, 2.48-
+//    2.51 ms and 2.87-2.90 ms, and 2.61 ms with plain stores.
+// So a pack that reads every row takes one-wave workgroups and a pack with
+// a zero row 256-thread ones.  (Earlier forms: 4.57 and 4.44 ms, 66-68 %,
+// with one 512-thread workgroup per tile walking all rows; 4.14 / 3.97 ms
+// with 512-thread workgroups on z.)
 constexpr int kStWave = 64, kStWide = 256;
+constexpr int64_t kOrderedLaunchTiles = 4096;
 template <int NT>
 constexpr int st_parts() { return (int)(kTile / 4 / NT); }
 static_assert(kMaxLaunchTiles * kTile / 4 < (int64_t(1) << 32),
@@ -614,12 +619,15 @@ __device__ __forceinline__ int state_off()
 // written as zero
 template <int ROWS, class Loc, int NT>
 __global__ __launch_bounds__(NT) void state_pack_kernel(
-    Rows rw, float* __restrict__ state, Loc loc)
+    Rows rw, float* __restrict__ state, int64_t x0, Loc loc)
 {
+    constexpr int P = st_parts<NT>();
+    const int64_t rr = blockIdx.x / P;              // (x - x0) * ROWS + row
+    const int64_t xr = rr / ROWS;
+    const int row = (int)(rr - xr * ROWS);
     TileRef r;
-    if (!loc.template at<st_parts<NT>()>(r))
+    if (!loc.at_tile(x0 + xr, r))
         return;
-    const int row = (int)blockIdx.z;
     const int jj = state_off<NT>();
     const float* in = rw.in[row];
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
@@ -663,7 +671,7 @@ __global__ __launch_bounds__(kStWave) void state_unpack_kernel(
 // 5.20 ms with plain stores; 64 to 1024 threads 5.48-6.02 ms).
 constexpr int kGtThreads = 64;
 constexpr int kGtParts = (int)(kTile / 8 / kGtThreads);   // 16 per row
-constexpr int64_t kGtLaunchTiles = 4096;
+constexpr int64_t kGtLaunchTiles = kOrderedLaunchTiles;
 
 template <class Loc>
 __global__ __launch_bounds__(kGtThreads) void grads_tile_kernel(
@@ -1486,22 +1494,32 @@ int convert_state(const zs_layout* L, bool pack, const float* const* in,
         }
         using Loc = std::decay_t<decltype(loc)>;
         const int64_t t0 = t * ROWS * kTile;
-        grid.z = ROWS;                      // state row
-        if (pack && !every_row) {
-            grid.x *= st_parts<kStWide>();  // workgroups per row
-            hipLaunchKernelGGL((state_pack_kernel<ROWS, Loc, kStWide>), grid,
-                               dim3(kStWide), 0, s, rw, state_w + t0, loc);
-        } else if (pack) {
-            grid.x *= st_parts<kStWave>();
-            hipLaunchKernelGGL((state_pack_kernel<ROWS, Loc, kStWave>), grid,
-                               dim3(kStWave), 0, s, rw, state_w + t0, loc);
-        } else {
-            grid.x *= st_parts<kStWave>();
+        if (!pack) {
+            grid.x *= st_parts<kStWave>();  // workgroups per row
+            grid.z = ROWS;                  // state row
             hipLaunchKernelGGL((state_unpack_kernel<ROWS, Loc>), grid,
                                dim3(kStWave), 0, s, state_r + t0, rw, loc);
+            return check_launch("state unpack kernel");
         }
-        return check_launch(pack ? "state pack kernel"
-                                 : "state unpack kernel");
+        // the pack: tiles [x0, x0 + nx) of each row of the locator per launch
+        const int64_t tiles = grid.x;
+        for (int64_t x0 = 0; x0 < tiles; x0 += kOrderedLaunchTiles) {
+            const int64_t nx = tiles - x0 < kOrderedLaunchTiles
+                                   ? tiles - x0 : kOrderedLaunchTiles;
+            if (every_row)
+                hipLaunchKernelGGL(
+                    (state_pack_kernel<ROWS, Loc, kStWave>),
+                    dim3((unsigned)(nx * ROWS * st_parts<kStWave>()), grid.y),
+                    dim3(kStWave), 0, s, rw, state_w + t0, x0, loc);
+            else
+                hipLaunchKernelGGL(
+                    (state_pack_kernel<ROWS, Loc, kStWide>),
+                    dim3((unsigned)(nx * ROWS * st_parts<kStWide>()), grid.y),
+                    dim3(kStWide), 0, s, rw, state_w + t0, x0, loc);
+            const int rc = check_launch("state pack kernel");
+            if (rc) return rc;
+        }
+        return (int)ZS_OK;
     });
 }
 
