@@ -432,3 +432,35 @@ def test_bf16_zero_lr_keeps_the_parameter_and_small_updates_vanish():
         O.step_bf16(grads_bf16(W, n, t), one, m, v,
                     hp_f32(lr=1e-5, weight_decay=0.0), t)
     assert np.all(one == 0x3f80)
+
+
+@pytest.mark.parametrize("threads", [1, 2, 3, 8])
+def test_step_is_deterministic_over_threads_and_windows(threads):
+    """The step is elementwise, so any split of a run of elements into
+    windows stepped concurrently in host threads gives the bits of one call
+    over the whole run, and a second run gives them again (the benchmark's
+    all-cores oracle leg relies on it)."""
+    from concurrent.futures import ThreadPoolExecutor
+    W, n = 8, 40_000
+    hp = O.AdamW()
+    G = np.stack([synth.cpu_normal_bf16(n, 2, synth.TAG_GRAD, 1, s, 0, 1e-3)
+                  for s in range(W)])
+    init = [synth.cpu_normal_f32(n, 2, tag, 0, 0, 0, 0.02, tag == synth.TAG_V)
+            for tag in (synth.TAG_MASTER, synth.TAG_M, synth.TAG_V)]
+    ref = [a.copy() for a in init]
+    p_ref = O.step(G, *ref, hp, 3)
+    edges = np.linspace(0, n, threads + 1).astype(int)
+    for _ in range(2):
+        got = [a.copy() for a in init]
+        p = np.empty(n, np.uint16)
+
+        def window(k):
+            a, b = edges[k], edges[k + 1]
+            views = [x[a:b] for x in got]           # contiguous slices
+            p[a:b] = O.step(np.ascontiguousarray(G[:, a:b]), *views, hp, 3)
+
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(window, range(threads)))
+        assert np.array_equal(p, p_ref)
+        for x, y in zip(got, ref):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))

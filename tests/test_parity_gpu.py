@@ -2007,3 +2007,29 @@ def test_state_pack_across_launches():
             for o, x in zip(outs, arrs):
                 assert np.array_equal(npf(o).view(np.uint32),
                                       x.view(np.uint32))
+
+
+def test_step_is_deterministic_run_to_run():
+    """Two runs of the same step on the same inputs, one after the other on
+    separate copies of the state and outputs, give the same bits (GPT-2-
+    shaped W = 8 shard, tiled gradients, three steps)."""
+    w = wl.presets()["gpt2"]
+    c = Case(w.numels, w.world, 3, layout="tiled")
+    lay, n = c.lay, c.n
+    F = c.lay_o.flat_numel
+    say(f"case determinism gpt2 W={w.world} rank=3 shard={n}")
+    runs = []
+    for _ in range(2):
+        st = c.dev_state()
+        p = dev_bf16(n)
+        flat = dev_bf16(F)
+        flat.view(torch.int16).fill_(0)
+        for t in (1, 2, 3):
+            c.dev_grads(c.G, t)
+            zs.zs_grads_tile(lay, -1, c.G, c.stride, c.Gt)
+            zs.zs_step(lay, c.Gt, st, p, flat, grad_layout="tiled", step=t,
+                       **HP)
+        torch.cuda.synchronize()
+        runs.append((npf(st).view(np.uint32), np16(p), np16(flat)))
+    for x, y in zip(*runs):
+        assert np.array_equal(x, y)
