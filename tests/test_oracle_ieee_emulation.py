@@ -155,6 +155,7 @@ def emulate(Gcol, master, m, v, hp, t, mistake=None):
     (5, 1e-6, dict(eps=1e-6)),                  # eps comparable to sqrt(v)
     (4, 1e-2, dict(lr=0.05, weight_decay=0.3, beta1=0.8, beta2=0.9)),
     (6, 1e-4, dict(spread=16.0)),             # sums that round, rank order
+    (3, 1e-21, {}),                           # g*g and v in the subnormals
 ])
 def test_step_equals_exact_per_operation_rounding(W, sigma, kw):
     n = 300
